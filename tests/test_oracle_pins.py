@@ -1,0 +1,510 @@
+"""Pins of the CPU oracle to things other than itself (no GPU needed).
+
+Each test checks one oracle function against an independent authority:
+torch's CPU bf16 conversion and eager bf16 ops (library routines), exact
+rational arithmetic (``fractions`` / ``decimal``), closed forms, torch's own
+float64 LayerNorm / RMSNorm, and exact metamorphic invariants.  The cases are
+chosen so that a plausible slip in the oracle (a dropped term, N-1 instead of
+N, a fused single-rounding modulate, a wrong operand order, a transposed
+batch index) fails at least one of them.
+"""
+from decimal import Decimal, getcontext
+from fractions import Fraction
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from dit_adaln_row_amd.inputs import bf16_bits_from_f32, f32_from_u16, from_u16, to_u16
+from dit_adaln_row_amd.workloads import Launch
+
+getcontext().prec = 80
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+# ---------------------------------------------------------------------------
+# exact helpers (test side)
+# ---------------------------------------------------------------------------
+
+def rn_f32(fr: Fraction) -> np.float32:
+    """Round a rational to the nearest binary32, ties to even (exact)."""
+    f = np.float32(float(fr))
+    cands = {float(f), float(np.nextafter(f, np.float32(np.inf))),
+             float(np.nextafter(f, np.float32(-np.inf)))}
+    def key(c):
+        return (abs(Fraction(c) - fr), int(np.float32(c).view(np.uint32)) & 1)
+    return np.float32(min(cands, key=key))
+
+
+def rn_bf16_exact(fr: Fraction, negative_zero=False) -> int:
+    """Round a rational to the nearest bf16, ties to even (exact).  A result of
+    zero takes the sign of the rational (or ``negative_zero`` for fr == 0)."""
+    if fr == 0:
+        return 0x8000 if negative_zero else 0x0000
+    f = float(fr)
+    u = int(np.float32(f).view(np.uint32)) >> 16
+    cands = set()
+    for d in (-2, -1, 0, 1, 2):
+        v = (u + d) & 0xFFFF
+        if (v & 0x7F80) == 0x7F80:
+            continue
+        cands.add(v)
+    def key(v):
+        val = Fraction(float(f32_from_u16(np.array([v], np.uint16))[0]))
+        return (abs(val - fr), v & 1)
+    best = min(cands, key=key)
+    if (best & 0x7FFF) == 0:
+        best = 0x8000 if fr < 0 else 0x0000
+    return best
+
+
+def dec(fr: Fraction) -> Decimal:
+    return Decimal(fr.numerator) / Decimal(fr.denominator)
+
+
+def exact_rstd(var: Fraction, eps32: float) -> Fraction:
+    v = dec(var) + Decimal(float(np.float32(eps32)))
+    return Fraction(Decimal(1) / v.sqrt())
+
+
+def exact_ln(row_f32):
+    vals = [Fraction(float(v)) for v in row_f32]
+    n = len(vals)
+    mean = sum(vals) / n
+    var = sum((v - mean) ** 2 for v in vals) / n
+    return mean, var
+
+
+def ulp_bf16(v):
+    v = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def rand_bf16(shape, mu, sigma, seed):
+    g = torch.Generator().manual_seed(seed)
+    return to_u16((torch.randn(shape, generator=g) * sigma + mu).to(torch.bfloat16))
+
+
+def t_bf16(a):
+    return from_u16(a)
+
+
+def same_bits(a, b):
+    """bitwise equality with NaNs compared by class."""
+    a = np.asarray(a, np.uint16)
+    b = np.asarray(b, np.uint16)
+    an = (a & 0x7F80) == 0x7F80
+    an &= (a & 0x7F) != 0
+    bn = (b & 0x7F80) == 0x7F80
+    bn &= (b & 0x7F) != 0
+    return np.array_equal(an, bn) and np.array_equal(a[~an], b[~bn])
+
+
+# ---------------------------------------------------------------------------
+# rounding helpers
+# ---------------------------------------------------------------------------
+
+def test_round_f32_to_bf16_matches_torch_on_every_tie_class(orc):
+    """All 2^16 upper halves x the low halves that decide RNE (exact, just below
+    / at / just above the halfway point, all ones) + 2M random patterns,
+    against torch's CPU float->bf16 conversion."""
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    pats = (hi[:, None] | lows[None, :]).ravel()
+    rng = np.random.default_rng(7)
+    pats = np.concatenate([pats, rng.integers(0, 1 << 32, 2_000_000, dtype=np.uint64).astype(np.uint32)])
+    f = pats.view(np.float32)
+    ours = orc.round_f32_to_bf16(f)
+    ref = to_u16(torch.from_numpy(f.copy()).to(torch.bfloat16))
+    assert same_bits(ours, ref)
+
+
+def test_round_f64_to_bf16_single_rounding(orc):
+    """Doubles straddling bf16 halfway points (where rounding through binary32
+    would round twice) against exact rational rounding."""
+    rng = np.random.default_rng(11)
+    base = rng.standard_normal(400) * 10.0 ** rng.integers(-30, 30, 400)
+    bits = bf16_bits_from_f32(base.astype(np.float32)).astype(np.uint32)
+    lo = f32_from_u16(bits.astype(np.uint16)).astype(np.float64)
+    hi = f32_from_u16(((bits + 1) & 0xFFFF).astype(np.uint16)).astype(np.float64)
+    mid = (lo + hi) / 2.0
+    tiny = np.abs(mid) * 2.0 ** -40
+    cases = np.concatenate([mid, mid + tiny, mid - tiny, mid + np.abs(mid) * 2.0 ** -30,
+                            base, np.array([0.0, -0.0, 1e-45, -3e-41, 1e300, -1e300])])
+    cases = cases[np.isfinite(cases)]
+    ours = orc.round_f64_to_bf16(cases)
+    for d, o in zip(cases, ours):
+        if abs(d) > 3.3e38:
+            continue
+        assert o == rn_bf16_exact(Fraction(float(d)), bool(np.signbit(d))), (d, hex(o))
+
+
+def test_silu_bf16_is_correctly_rounded(orc):
+    """SiLU(t) = t / (1 + e^-t) rounded once to bf16, against 80-digit decimal."""
+    rng = np.random.default_rng(3)
+    t = np.concatenate([rng.standard_normal(600).astype(np.float32) * 3,
+                        np.array([0.0, -0.0, 1e-30, -1e-30, 1.0, -1.0, 20.0, -20.0, 80.0,
+                                  -80.0, -87.5, -100.0, 88.0, 1e10], np.float32)])
+    # add t whose binary32-rounded SiLU lands exactly on a bf16 halfway point:
+    # there rounding through binary32 first would round twice
+    r = np.random.default_rng(5).standard_normal(4_000_000).astype(np.float32) * 4
+    s64 = r.astype(np.float64) / (1.0 + np.exp(-r.astype(np.float64)))
+    s32 = s64.astype(np.float32)
+    hard = (s32.view(np.uint32) & 0xFFFF) == 0x8000
+    hard &= s32.astype(np.float64) != s64
+    assert hard.sum() >= 10
+    t = np.concatenate([t, r[hard][:40]])
+    ours = orc.silu_bf16(t)
+    for tv, o in zip(t, ours):
+        x = Decimal(float(tv))
+        s = x / (1 + (-x).exp())
+        assert o == rn_bf16_exact(Fraction(s), bool(np.signbit(tv))), (tv, hex(o))
+
+
+# ---------------------------------------------------------------------------
+# elementwise stages vs torch's eager bf16 chain (per-op rounding)
+# ---------------------------------------------------------------------------
+
+SPECIAL = np.array([0x0000, 0x8000, 0x3F80, 0xBF80, 0x0001, 0x8001, 0x007F, 0x7F7F, 0xFF7F,
+                    0x3F81, 0x4000, 0x3C00, 0xC2C8, 0x0080], np.uint16)
+
+
+def test_modulate_matches_eager_chain(orc):
+    """out = y * (1 + scale) + shift evaluated by torch on bf16 tensors (three
+    kernels, each rounding to bf16), with a [B, 1, D] broadcast."""
+    B, S, D = 3, 37, 64
+    y = rand_bf16((B * S, D), 0, 1.5, 1)
+    y[:len(SPECIAL), :len(SPECIAL)] = SPECIAL[None, :]
+    sc = rand_bf16((B, D), 0, 0.3, 2)
+    sh = rand_bf16((B, D), 0, 0.3, 3)
+    sc[0, :len(SPECIAL)] = SPECIAL
+    ref = t_bf16(y).view(B, S, D) * (1 + t_bf16(sc).view(B, 1, D)) + t_bf16(sh).view(B, 1, D)
+    ours = orc.modulate(y, sc, sh, rows_per_batch=S)
+    assert same_bits(ours, to_u16(ref.reshape(B * S, D)))
+
+
+def test_modulate_strided_chunk_rows(orc):
+    """Modulation rows taken from a [B, 6*D] embedding (adaLN chunk views):
+    row stride 6*D, scale = chunk 1, shift = chunk 0."""
+    B, S, D = 2, 5, 16
+    emb = rand_bf16((B, 6 * D), 0, 0.2, 4)
+    y = rand_bf16((B * S, D), 0, 1.0, 5)
+    shift_view = emb[:, 0:D]
+    scale_view = emb[:, D:2 * D]
+    ref = t_bf16(y).view(B, S, D) * (1 + t_bf16(np.ascontiguousarray(scale_view)).view(B, 1, D)) \
+        + t_bf16(np.ascontiguousarray(shift_view)).view(B, 1, D)
+    # [B, 6*D] arrays whose row b starts where the chunk view's row b starts:
+    # the same memory a strided chunk view addresses, row stride 6*D
+    sc = np.concatenate([emb.ravel()[D:], np.zeros(D, np.uint16)]).reshape(B, 6 * D)
+    sh = np.ascontiguousarray(emb)
+    ours = orc.modulate(y, sc, sh, rows_per_batch=S)
+    assert same_bits(ours, to_u16(ref.reshape(B * S, D)))
+
+
+def test_gate_matches_eager_chain(orc):
+    """h = residual + gate * update on bf16 tensors (two rounded kernels)."""
+    B, S, D = 2, 29, 96
+    upd = rand_bf16((B * S, D), 0, 1.5, 6)
+    res = rand_bf16((B * S, D), 0, 1.0, 7)
+    gate = rand_bf16((B, D), 0, 0.1, 8)
+    upd[0, :len(SPECIAL)] = SPECIAL
+    res[1, :len(SPECIAL)] = SPECIAL
+    ref = t_bf16(res).view(B, S, D) + t_bf16(gate).view(B, 1, D) * t_bf16(upd).view(B, S, D)
+    ours = orc.gate_residual(upd, res, gate, rows_per_batch=S)
+    assert same_bits(ours, to_u16(ref.reshape(B * S, D)))
+
+
+def test_bias_add_matches_aten_add_(orc):
+    """xb = x.add_(bias.to(bf16)) with an fp32 bias, channels_last rows."""
+    rows, C = 1000, 96
+    x = rand_bf16((rows, C), 0, 1.0, 9)
+    x[0, :len(SPECIAL)] = SPECIAL
+    g = torch.Generator().manual_seed(10)
+    bias = (torch.randn(C, generator=g) * 0.05).numpy()
+    bias[:4] = [1e-9, -3.0e-3, 0.5 + 2 ** -9, 65504.0]
+    ref = t_bf16(x).clone().add_(torch.from_numpy(bias).to(torch.bfloat16))
+    assert same_bits(orc.bias_add(x, bias), to_u16(ref))
+
+
+def test_conv_bias_epilogue_matches_eager(orc):
+    """bf16(bf16(x + bf16(bias)) + h): the two roundings of conv(x) + h."""
+    rows, C = 777, 384
+    x = rand_bf16((rows, C), 0, 1.0, 12)
+    h = rand_bf16((rows, C), 0, 1.0, 13)
+    g = torch.Generator().manual_seed(14)
+    bias = (torch.randn(C, generator=g) * 0.05).numpy()
+    xb = t_bf16(x).clone().add_(torch.from_numpy(bias).to(torch.bfloat16))
+    assert same_bits(orc.conv_bias_epilogue(x, bias), to_u16(xb))
+    assert same_bits(orc.conv_bias_epilogue(x, bias, h), to_u16(xb + t_bf16(h)))
+
+
+# ---------------------------------------------------------------------------
+# statistics vs exact rational arithmetic
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,mu,sigma", [(4, 0, 1), (8, 3, 0.5), (16, -2, 4), (128, 0, 2),
+                                        (96, 64, 0.1), (1024, 0, 1.5), (3072, 0.3, 1)])
+def test_ln_stats_exact(orc, n, mu, sigma):
+    x = rand_bf16((3, n), mu, sigma, 100 + n)
+    mean, rstd = orc.ln_stats(x, 1e-6)
+    for r in range(3):
+        m, v = exact_ln(f32_from_u16(x[r]))
+        assert mean[r] == rn_f32(m), (r, mean[r], float(m))
+        assert rstd[r] == rn_f32(exact_rstd(v, 1e-6)), (r, rstd[r])
+
+
+@pytest.mark.parametrize("n,sigma", [(8, 1), (96, 1), (384, 0.7), (4096, 1)])
+def test_rms_stats_exact(orc, n, sigma):
+    x = rand_bf16((3, n), 0.1, sigma, 200 + n)
+    rstd = orc.rms_stats(x, 1e-6)
+    for r in range(3):
+        vals = [Fraction(float(v)) for v in f32_from_u16(x[r])]
+        ms = sum(v * v for v in vals) / n
+        assert rstd[r] == rn_f32(exact_rstd(ms, 1e-6)), r
+
+
+def test_high_offset_row_guard(orc):
+    """A row ~N(64, 0.1): the variance is 4e5 times smaller than E[x^2].  The
+    oracle's rstd is still the correctly rounded value, while the naive fp32
+    E[x^2]-E[x]^2 misses the 2e-6 tolerance by orders of magnitude (so this
+    row separates a sound statistics algorithm from an unsound one)."""
+    x = rand_bf16((1, 3072), 64.0, 0.1, 300)
+    _, rstd = orc.ln_stats(x, 1e-6)
+    m, v = exact_ln(f32_from_u16(x[0]))
+    want = rn_f32(exact_rstd(v, 1e-6))
+    assert rstd[0] == want
+    xf = f32_from_u16(x[0]).astype(np.float32)
+    naive_var = np.float32(np.mean(xf * xf, dtype=np.float32) - np.float32(np.mean(xf, dtype=np.float32)) ** 2)
+    naive = 1 / math.sqrt(max(float(naive_var), 0.0) + 1e-6)
+    assert abs(naive - float(want)) / float(want) > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+def test_ln_constant_row_closed_form(orc):
+    """A constant row has variance exactly 0: mean = c, rstd = fp32(1/sqrt(eps)),
+    y = +0, and the modulate returns shift bit for bit."""
+    cols = 256
+    for c in (0x3FC0, 0xC120, 0x0000, 0x4B00):
+        x = np.full((1, cols), c, np.uint16)
+        sc = rand_bf16((1, cols), 0, 0.1, 400)
+        sh = rand_bf16((1, cols), 0, 0.1, 401)
+        r = orc.ln_modulate(x, sc, sh, 1e-6)
+        assert r["mean"][0] == f32_from_u16(np.array([c], np.uint16))[0]
+        assert r["rstd"][0] == rn_f32(exact_rstd(Fraction(0), 1e-6))
+        assert np.all(r["y"] == 0)
+        nz = (sh[0] & 0x7FFF) != 0
+        assert np.array_equal(r["out"][0][nz], sh[0][nz])
+
+
+def test_ln_two_valued_row_closed_form(orc):
+    """Equal counts of a and b: mean = (a+b)/2 and var = (a-b)^2/4 exactly;
+    y is +-rstd*(a-b)/2 rounded."""
+    for a, b in ((1.0, 3.0), (-0.5, 0.25), (100.0, 96.0)):
+        row = np.array([a, b] * 64, np.float32)
+        x = bf16_bits_from_f32(row).reshape(1, -1)
+        mean, rstd = orc.ln_stats(x, 1e-5)
+        assert mean[0] == np.float32((a + b) / 2)
+        want = rn_f32(exact_rstd(Fraction(a - b) ** 2 / 4, 1e-5))
+        assert rstd[0] == want
+        y = f32_from_u16(orc.ln_normalize(x, mean, rstd))
+        half = np.float32(np.float32(a) - mean[0]) * rstd[0]
+        assert np.all(y[0, 0::2] == f32_from_u16(bf16_bits_from_f32(np.array([half])))[0])
+
+
+def test_zero_scale_shift_is_plain_layernorm(orc):
+    rows, cols = 8, 512
+    x = rand_bf16((rows, cols), 0, 1, 500)
+    z = np.zeros((1, cols), np.uint16)
+    r = orc.ln_modulate(x, z, z, 1e-6)
+    # y * 1 + 0: equal up to the sign of zero
+    assert np.array_equal(f32_from_u16(r["out"]), f32_from_u16(r["y"]))
+
+
+def test_zero_gate_returns_residual(orc):
+    rows, cols = 16, 128
+    upd = rand_bf16((rows, cols), 0, 1.5, 501)
+    res = rand_bf16((rows, cols), 0, 1, 502)
+    h = orc.gate_residual(upd, res, np.zeros((1, cols), np.uint16))
+    assert np.array_equal(f32_from_u16(h), f32_from_u16(res))
+
+
+def test_rms_closed_forms(orc):
+    cols = 4096
+    w = rand_bf16((cols,), 1, 0.05, 503)
+    sc = rand_bf16((1, cols), 0, 0.1, 504)
+    sh = rand_bf16((1, cols), 0, 0.1, 505)
+    # zero row: rstd = 1/sqrt(eps), y = 0, out = shift
+    r = orc.rms_modulate(np.zeros((1, cols), np.uint16), w, sc, sh, 1e-6)
+    assert r["rstd"][0] == rn_f32(exact_rstd(Fraction(0), 1e-6))
+    assert np.all(f32_from_u16(r["y"]) == 0)
+    assert np.array_equal(f32_from_u16(r["out"]), f32_from_u16(sh))
+    # w = 1, scale = shift = 0 -> out == y; a constant row c -> y = bf16(c * rstd)
+    one = np.full(cols, 0x3F80, np.uint16)
+    z = np.zeros((1, cols), np.uint16)
+    x = np.full((1, cols), 0x4040, np.uint16)  # 3.0
+    r = orc.rms_modulate(x, one, z, z, 1e-6)
+    assert r["rstd"][0] == rn_f32(exact_rstd(Fraction(9), 1e-6))
+    assert np.array_equal(f32_from_u16(r["out"]), f32_from_u16(r["y"]))
+    assert np.all(r["y"] == bf16_bits_from_f32(np.array([np.float32(3.0) * r["rstd"][0]]))[0])
+
+
+# ---------------------------------------------------------------------------
+# library cross-checks: torch float64 LayerNorm / RMSNorm
+# ---------------------------------------------------------------------------
+
+def test_ln_normalize_vs_torch_layer_norm(orc):
+    rows, cols = 64, 3072
+    x = rand_bf16((rows, cols), 0.2, 1.5, 600)
+    mean, rstd = orc.ln_stats(x, 1e-6)
+    y = f32_from_u16(orc.ln_normalize(x, mean, rstd)).astype(np.float64)
+    xt = torch.from_numpy(f32_from_u16(x).astype(np.float64))
+    ref = torch.nn.functional.layer_norm(xt, (cols,), eps=1e-6).numpy()
+    slack = 0.5 * ulp_bf16(ref) + 4e-7 * np.abs(ref) + rstd[:, None] * np.abs(mean[:, None]) * 2.0 ** -23 + 1e-30
+    assert np.all(np.abs(y - ref) <= slack)
+
+
+def test_rms_normalize_vs_torch_rms_norm(orc):
+    rows, cols = 64, 4096
+    x = rand_bf16((rows, cols), 0, 1, 601)
+    w = rand_bf16((cols,), 1, 0.05, 602)
+    rstd = orc.rms_stats(x, 1e-6)
+    y = f32_from_u16(orc.rms_normalize(x, rstd, w)).astype(np.float64)
+    xt = torch.from_numpy(f32_from_u16(x).astype(np.float64))
+    wt = torch.from_numpy(f32_from_u16(w).astype(np.float64))
+    ref = torch.nn.functional.rms_norm(xt, (cols,), weight=wt, eps=1e-6).numpy()
+    slack = 0.5 * ulp_bf16(ref) + 4e-7 * np.abs(ref) + 1e-30
+    assert np.all(np.abs(y - ref) <= slack)
+
+
+def test_wan_silu_path_vs_torch(orc):
+    """channels_last rows: bias fold like add_, RMS over C, gamma, SiLU, against
+    torch float64 rms_norm + silu on the bias-folded input."""
+    rows, C = 2000, 96
+    x = rand_bf16((rows, C), 0, 1, 603)
+    g = torch.Generator().manual_seed(604)
+    bias = (torch.randn(C, generator=g) * 0.05).numpy()
+    gamma = f32_from_u16(rand_bf16((C,), 1, 0.05, 605))
+    r = orc.rmsnorm_silu_bias(x, bias, gamma, 1e-6)
+    xb_ref = t_bf16(x).clone().add_(torch.from_numpy(bias).to(torch.bfloat16))
+    assert same_bits(r["xb"], to_u16(xb_ref))
+    xt = xb_ref.double()
+    ref = torch.nn.functional.silu(torch.nn.functional.rms_norm(
+        xt, (C,), weight=torch.from_numpy(gamma.astype(np.float64)), eps=1e-6)).numpy()
+    out = f32_from_u16(r["out"]).astype(np.float64)
+    slack = 0.5 * ulp_bf16(ref) + 1e-6 * np.abs(ref) + 1e-30
+    assert np.all(np.abs(out - ref) <= slack)
+    # and the rstd is the correctly rounded exact value
+    for i in (0, 1, 1999):
+        vals = [Fraction(float(v)) for v in f32_from_u16(r["xb"][i])]
+        assert r["rstd"][i] == rn_f32(exact_rstd(sum(v * v for v in vals) / C, 1e-6))
+
+
+def test_normalised_moments(orc):
+    """fp64 moments of y: mean ~ 0 and variance ~ var/(var+eps) ~ 1, within the
+    bf16 rounding of the elements."""
+    x = rand_bf16((32, 4096), -0.7, 2.0, 606)
+    mean, rstd = orc.ln_stats(x, 1e-6)
+    y = f32_from_u16(orc.ln_normalize(x, mean, rstd)).astype(np.float64)
+    assert np.all(np.abs(y.mean(1)) <= 2.0 ** -9)
+    assert np.all(np.abs(y.var(1) - 1.0) <= 2.0 ** -8)
+
+
+# ---------------------------------------------------------------------------
+# metamorphic invariants
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k", [-3, 5])
+def test_power_of_two_scaling_invariance(orc, k):
+    """f(2^k x, 4^k eps) == f(x, eps) bit for bit: every op involved scales
+    exactly, and sqrt / division are correctly rounded."""
+    x = rand_bf16((16, 1024), 0.5, 1.2, 700)
+    xs = bf16_bits_from_f32(f32_from_u16(x) * np.float32(2.0 ** k))
+    eps = 1e-6
+    eps_s = float(np.float32(eps) * np.float32(4.0 ** k))
+    m0, r0 = orc.ln_stats(x, eps)
+    m1, r1 = orc.ln_stats(xs, eps_s)
+    assert np.array_equal(m1, m0 * np.float32(2.0 ** k))
+    assert np.array_equal(r1, r0 * np.float32(2.0 ** -k))
+    assert np.array_equal(orc.ln_normalize(xs, m1, r1), orc.ln_normalize(x, m0, r0))
+    w = rand_bf16((1024,), 1, 0.05, 701)
+    q0 = orc.rms_stats(x, eps)
+    q1 = orc.rms_stats(xs, eps_s)
+    assert np.array_equal(q1, q0 * np.float32(2.0 ** -k))
+    assert np.array_equal(orc.rms_normalize(xs, q1, w), orc.rms_normalize(x, q0, w))
+
+
+def test_composites_equal_stage_chains(orc):
+    """Each composite is its stages in sequence, and batch rows index the
+    modulation row r // rows_per_batch."""
+    B, S, D = 2, 33, 256
+    x = rand_bf16((B * S, D), 0, 1.5, 800)
+    res = rand_bf16((B * S, D), 0, 1, 801)
+    gate = rand_bf16((B, D), 0, 0.1, 802)
+    sc = rand_bf16((B, D), 0, 0.1, 803)
+    sh = rand_bf16((B, D), 0, 0.1, 804)
+    w = rand_bf16((D,), 1, 0.05, 805)
+    r = orc.ln_modulate(x, sc, sh, 1e-6, rows_per_batch=S)
+    m, s = orc.ln_stats(x, 1e-6)
+    assert np.array_equal(r["mean"], m) and np.array_equal(r["rstd"], s)
+    y = orc.ln_normalize(x, m, s)
+    assert np.array_equal(r["y"], y)
+    assert np.array_equal(r["out"], orc.modulate(y, sc, sh, rows_per_batch=S))
+    for b in range(B):   # batch b only sees modulation row b
+        rb = orc.ln_modulate(x[b * S:(b + 1) * S], sc[b:b + 1], sh[b:b + 1], 1e-6)
+        assert np.array_equal(rb["out"], r["out"][b * S:(b + 1) * S])
+    g = orc.gated_ln_modulate(x, res, gate, sc, sh, 1e-6, rows_per_batch=S)
+    h = orc.gate_residual(x, res, gate, rows_per_batch=S)
+    assert np.array_equal(g["h"], h)
+    assert np.array_equal(g["out"], orc.ln_modulate(h, sc, sh, 1e-6, rows_per_batch=S)["out"])
+    rr = orc.rms_modulate(x, w, sc, sh, 1e-6, residual=res, gate=gate, rows_per_batch=S)
+    assert np.array_equal(rr["h"], h)
+    q = orc.rms_stats(h, 1e-6)
+    assert np.array_equal(rr["rstd"], q)
+    assert np.array_equal(rr["out"], orc.modulate(orc.rms_normalize(h, q, w), sc, sh, rows_per_batch=S))
+
+
+def test_qk_is_per_row_layernorm_q_then_k(orc):
+    q = rand_bf16((300, 128), 0, 2, 900)
+    k = rand_bf16((77, 128), 0.1, 2, 901)
+    r = orc.qk_layernorm(q, k, 1e-5)
+    mq, sq = orc.ln_stats(q, 1e-5)
+    mk, sk = orc.ln_stats(k, 1e-5)
+    assert np.array_equal(r["mean"], np.concatenate([mq, mk]))
+    assert np.array_equal(r["rstd"], np.concatenate([sq, sk]))
+    assert np.array_equal(r["q_out"], orc.ln_normalize(q, mq, sq))
+    assert np.array_equal(r["k_out"], orc.ln_normalize(k, mk, sk))
+    # row 5 of q against exact arithmetic
+    m, v = exact_ln(f32_from_u16(q[5]))
+    assert r["mean"][5] == rn_f32(m) and r["rstd"][5] == rn_f32(exact_rstd(v, 1e-5))
+
+
+def test_rejects_bad_arguments(orc):
+    x = np.zeros((4, 8), np.uint16)
+    with pytest.raises(ValueError):
+        orc.ln_modulate(x, np.zeros((1, 8), np.uint16), np.zeros((1, 8), np.uint16), 1e-6,
+                        rows_per_batch=3)
+
+
+# ---------------------------------------------------------------------------
+# the byte model against the page's printed bandwidths
+# ---------------------------------------------------------------------------
+
+def test_byte_model_reproduces_page_bandwidths():
+    with open(os.path.join(HERE, "golden", "page_bandwidth.json")) as f:
+        g = json.load(f)
+    n, c, d, hh, ww = g["shape"]
+    rows = n * d * hh * ww
+    for e in g["entries"]:
+        if e["entry"] == "conv_bias_epilogue":
+            l = Launch("e", "conv_bias_epilogue", rows, c, (), 0.0)
+        else:
+            l = Launch("e", "rmsnorm_silu_bias", rows, c, (), 1e-6, extra={"bias": False})
+        tbps = l.algorithmic_bytes() / (e["ms"] * 1e-3) / 1e12
+        assert abs(tbps - e["tbps_printed"]) <= e["printed_precision"], (e["what"], tbps)
