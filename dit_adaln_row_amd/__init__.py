@@ -1,0 +1,302 @@
+"""dit_adaln_row_amd -- fused adaLN row normalisation kernels for MI355X (gfx950).
+
+Python binding of ``libditnorm.so`` (C ABI in ``include/ditnorm.h``).  The
+binding only marshals arguments: it checks dtypes / devices / layouts,
+allocates outputs with torch when the caller does not pass them, and hands
+raw device pointers and the current HIP stream to the library.  Every step of
+the computation runs in the library's HIP kernels; there is no other
+implementation to fall back to -- if the library is missing or rejects a call,
+the call raises.
+
+Entry points (same names as the C ABI):
+    ln_modulate, gated_ln_modulate, rms_modulate, qk_layernorm,
+    rmsnorm_silu_bias, conv_bias_epilogue, copy
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["load", "ln_modulate", "gated_ln_modulate", "rms_modulate", "qk_layernorm",
+           "rmsnorm_silu_bias", "conv_bias_epilogue", "copy", "DitnormError", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditnorm.so")
+
+OK, INVALID_ARGUMENT, UNSUPPORTED, DEVICE_ERROR = 0, 1, 2, 3
+
+
+class DitnormError(RuntimeError):
+    def __init__(self, fn, status, hip_error):
+        self.status = status
+        self.hip_error = hip_error
+        name = _lib.ditnorm_status_string(status).decode() if _lib else str(status)
+        super().__init__(f"{fn}: {name} (status {status}, last hipError {hip_error})")
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+
+_SIGNATURES = {
+    "ln_modulate": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp],
+    "gated_ln_modulate": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32,
+                          _vp, _vp, _vp, _vp],
+    "rms_modulate": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32,
+                     _vp, _vp, _vp],
+    "qk_layernorm": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp, _vp, _vp],
+    "rmsnorm_silu_bias": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp, _vp],
+    "conv_bias_epilogue": [_vp, _vp, _vp, _vp, _i64, _i64, _vp],
+    "ditnorm_copy": [_vp, _vp, _i64, _vp],
+    "ln_modulate_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp],
+    "gated_ln_modulate_supported": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                    _f32, _vp, _vp, _vp],
+    "rms_modulate_supported": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                               _f32, _vp, _vp],
+    "qk_layernorm_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp, _vp],
+    "rmsnorm_silu_bias_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp],
+    "conv_bias_epilogue_supported": [_vp, _vp, _vp, _vp, _i64, _i64],
+    "ditnorm_last_hip_error": [],
+    "ditnorm_version": [],
+}
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (once).  Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m dit_adaln_row_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, args in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        lib.ditnorm_status_string.argtypes = [ctypes.c_int]
+        lib.ditnorm_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _call(name, *args):
+    lib = load()
+    st = getattr(lib, name)(*args)
+    if st != OK:
+        raise DitnormError(name, st, lib.ditnorm_last_hip_error())
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _act(t, name, dtype=torch.bfloat16):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+    return t
+
+
+def _mod(t, name, cols, device):
+    """Modulation rows: (cols,), (B, cols) or (B, 1, cols), last dim dense; the
+    batch stride may exceed cols (a chunk view of an adaLN embedding).
+    Returns (tensor, B, batch_stride)."""
+    if t.dtype != torch.bfloat16 or t.device != device:
+        raise TypeError(f"{name} must be bf16 on {device}")
+    if t.shape[-1] != cols or t.stride(-1) != 1:
+        raise ValueError(f"{name}: last dim must be {cols} and dense")
+    if t.dim() == 1:
+        return t, 1, cols
+    if t.dim() == 3:
+        if t.shape[1] != 1:
+            raise ValueError(f"{name}: expected (B, 1, {cols})")
+        b, stride = t.shape[0], t.stride(0)
+    elif t.dim() == 2:
+        b, stride = t.shape[0], t.stride(0)
+    else:
+        raise ValueError(f"{name}: expected (cols,), (B, cols) or (B, 1, cols)")
+    return t, b, (stride if b > 1 else cols)
+
+
+def _f32_out(t, n, name):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous fp32 tensor of {n} elements")
+    return t
+
+
+def _rows_cols(x):
+    cols = x.shape[-1]
+    return x.numel() // cols if cols else 0, cols
+
+
+def _batch(rows, b):
+    if b < 1 or rows % b != 0:
+        raise ValueError(f"{rows} rows are not divisible by {b} modulation rows")
+    return max(rows // b, 1)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def ln_modulate(x, scale, shift, eps=1e-6, out=None, *, mean_out=None, rstd_out=None,
+                y_out=None):
+    """out = bf16(bf16(LN(x) * bf16(1+scale)) + shift); x (..., D) bf16."""
+    _act(x, "x")
+    rows, cols = _rows_cols(x)
+    scale, b, stride = _mod(scale, "scale", cols, x.device)
+    shift, b2, stride2 = _mod(shift, "shift", cols, x.device)
+    if (b, stride) != (b2, stride2):
+        raise ValueError("scale and shift must have the same batch count and stride")
+    out = torch.empty_like(x) if out is None else _act(out, "out")
+    _call("ln_modulate", _p(x), _p(scale), _p(shift), _p(out), rows, cols, _batch(rows, b),
+          stride, eps, _p(_f32_out(mean_out, rows, "mean_out")),
+          _p(_f32_out(rstd_out, rows, "rstd_out")),
+          _p(None if y_out is None else _act(y_out, "y_out")), _stream(x))
+    return out
+
+
+def gated_ln_modulate(x, residual, gate, scale, shift, eps=1e-6, out=None, residual_out=None,
+                      *, mean_out=None, rstd_out=None, y_out=None):
+    """h = bf16(residual + bf16(gate * x)); out = ln_modulate(h).  Returns (h, out)."""
+    _act(x, "x")
+    _act(residual, "residual")
+    rows, cols = _rows_cols(x)
+    gate, b, stride = _mod(gate, "gate", cols, x.device)
+    scale, b2, s2 = _mod(scale, "scale", cols, x.device)
+    shift, b3, s3 = _mod(shift, "shift", cols, x.device)
+    if not (b == b2 == b3 and stride == s2 == s3):
+        raise ValueError("gate, scale and shift must share batch count and stride")
+    h = torch.empty_like(x) if residual_out is None else _act(residual_out, "residual_out")
+    out = torch.empty_like(x) if out is None else _act(out, "out")
+    _call("gated_ln_modulate", _p(x), _p(residual), _p(gate), _p(scale), _p(shift), _p(h),
+          _p(out), rows, cols, _batch(rows, b), stride, eps,
+          _p(_f32_out(mean_out, rows, "mean_out")), _p(_f32_out(rstd_out, rows, "rstd_out")),
+          _p(None if y_out is None else _act(y_out, "y_out")), _stream(x))
+    return h, out
+
+
+def rms_modulate(x, weight, scale, shift, eps=1e-6, out=None, *, residual=None, gate=None,
+                 residual_out=None, rstd_out=None, y_out=None):
+    """Weighted RMSNorm + modulate.  With residual and gate (the gated site) the
+    norm runs on h = bf16(residual + bf16(gate * x)) and (h, out) is returned;
+    otherwise out."""
+    _act(x, "x")
+    rows, cols = _rows_cols(x)
+    _act(weight, "weight")
+    if weight.numel() != cols:
+        raise ValueError("weight must have cols elements")
+    scale, b, stride = _mod(scale, "scale", cols, x.device)
+    shift, b2, s2 = _mod(shift, "shift", cols, x.device)
+    gated = residual is not None
+    if gated != (gate is not None):
+        raise ValueError("residual and gate go together")
+    if gated:
+        _act(residual, "residual")
+        gate, b3, s3 = _mod(gate, "gate", cols, x.device)
+        if (b3, s3) != (b, stride):
+            raise ValueError("gate must share batch count and stride with scale")
+        residual_out = torch.empty_like(x) if residual_out is None else _act(residual_out,
+                                                                             "residual_out")
+    if (b, stride) != (b2, s2):
+        raise ValueError("scale and shift must share batch count and stride")
+    out = torch.empty_like(x) if out is None else _act(out, "out")
+    _call("rms_modulate", _p(x), _p(weight), _p(scale), _p(shift), _p(out), _p(residual),
+          _p(gate), _p(residual_out if gated else None), rows, cols, _batch(rows, b), stride,
+          eps, _p(_f32_out(rstd_out, rows, "rstd_out")),
+          _p(None if y_out is None else _act(y_out, "y_out")), _stream(x))
+    return (residual_out, out) if gated else out
+
+
+def qk_layernorm(q, k, eps=1e-5, q_out=None, k_out=None, *, mean_out=None, rstd_out=None):
+    """Per-head LayerNorm(128) of q (..., 128) and k (..., 128) in one launch."""
+    _act(q, "q")
+    rows_q = q.numel() // 128 if q.shape[-1] == 128 else -1
+    if k is not None:
+        _act(k, "k")
+    rows_k = 0 if k is None else (k.numel() // 128 if k.shape[-1] == 128 else -1)
+    if rows_q < 0 or rows_k < 0:
+        raise ValueError("head_dim must be 128")
+    q_out = torch.empty_like(q) if q_out is None else _act(q_out, "q_out")
+    if k is not None:
+        k_out = torch.empty_like(k) if k_out is None else _act(k_out, "k_out")
+    n = rows_q + rows_k
+    _call("qk_layernorm", _p(q), _p(k), _p(q_out), _p(k_out if k is not None else None),
+          rows_q, rows_k, 128, eps, _p(_f32_out(mean_out, n, "mean_out")),
+          _p(_f32_out(rstd_out, n, "rstd_out")), _stream(q))
+    return q_out, k_out
+
+
+def _channels_last_rows(x):
+    """[rows, C] view of a channels_last(_3d) tensor or of a dense (..., C) tensor."""
+    if x.dim() in (4, 5) and not x.is_contiguous():
+        fmt = torch.channels_last if x.dim() == 4 else torch.channels_last_3d
+        if not x.is_contiguous(memory_format=fmt):
+            raise ValueError("x must be channels_last (NCDHW/NCHW-contiguous is rejected)")
+        c = x.shape[1]
+        return x.permute(0, *range(2, x.dim()), 1).reshape(-1, c), c
+    if x.dim() in (4, 5):
+        raise ValueError("x must be channels_last (NCDHW/NCHW-contiguous is rejected)")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    return x.reshape(-1, x.shape[-1]), x.shape[-1]
+
+
+def _out_like(x, out):
+    if out is None:
+        return torch.empty_like(x)  # keeps channels_last strides
+    if out.shape != x.shape or out.stride() != x.stride() or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape, strides and dtype")
+    return out
+
+
+def rmsnorm_silu_bias(x, gamma, bias=None, eps=1e-6, out=None, *, rstd_out=None, xb_out=None):
+    """channels_last x: out = bf16(SiLU(RMSNorm_C(bf16(x + bf16(bias))) * gamma))."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda:
+        raise TypeError("x must be a bf16 device tensor")
+    rows2d, c = _channels_last_rows(x)
+    rows = rows2d.shape[0]
+    for t, n in ((gamma, "gamma"), (bias, "bias")):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != c or not t.is_contiguous()
+                              or t.device != x.device):
+            raise ValueError(f"{n} must be a dense fp32 [{c}] device tensor")
+    out = _out_like(x, out)
+    if xb_out is not None:
+        xb_out = _out_like(x, xb_out)
+    _call("rmsnorm_silu_bias", _p(x), _p(bias), _p(gamma), _p(out), rows, c, eps,
+          _p(_f32_out(rstd_out, rows, "rstd_out")), _p(xb_out), _stream(x))
+    return out
+
+
+def conv_bias_epilogue(x, bias, h=None, out=None):
+    """channels_last x: out = bf16(x + bf16(bias)) [then bf16(out + h)]."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda:
+        raise TypeError("x must be a bf16 device tensor")
+    rows2d, c = _channels_last_rows(x)
+    if bias.dtype != torch.float32 or bias.numel() != c or not bias.is_contiguous():
+        raise ValueError(f"bias must be a dense fp32 [{c}] tensor")
+    if h is not None and (h.shape != x.shape or h.stride() != x.stride() or h.dtype != x.dtype):
+        raise ValueError("h must match x in shape, strides and dtype")
+    out = _out_like(x, out)
+    _call("conv_bias_epilogue", _p(x), _p(bias), _p(h), _p(out), rows2d.shape[0], c, _stream(x))
+    return out
+
+
+def copy(src, dst):
+    """Plain device copy through the library's 16-byte copy kernel (measurement utility)."""
+    _call("ditnorm_copy", _p(src), _p(dst), src.numel() * src.element_size(), _stream(src))
+    return dst

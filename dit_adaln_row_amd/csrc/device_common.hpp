@@ -1,0 +1,162 @@
+// Device-side building blocks shared by the ditnorm kernels (gfx950 / CDNA4).
+//
+// bf16 handling: a bf16 value widens to fp32 exactly by a 16-bit shift; fp32
+// results round back to bf16 nearest-even with the hardware v_cvt_pk_bf16_f32
+// (two values per instruction).  That is the per-op-boundary rounding of the
+// eager chain the GLM-Image page describes ("What rounding-faithful means
+// here": every elementwise boundary rounds to bf16).
+//
+// Row statistics are accumulated in binary64.  Sums of bf16 values and of
+// their squares are exact (or within 1e-16) in binary64, so the fp32 mean and
+// rstd derived from them do not depend on the order of the reduction.  The
+// wavefront reductions use DPP lane permutations (quad_perm, row_half_mirror,
+// row_mirror) arranged as an xor-butterfly, so that every lane of a group ends
+// with the same bits; cross-wave combination goes through LDS in a fixed order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ditnorm {
+
+// --------------------------------------------------------------------------
+// bf16 <-> fp32
+// --------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round two fp32 values to bf16 (nearest-even) and pack them (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_rn(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Round-trip through bf16: the value an eager bf16 kernel boundary would keep.
+__device__ __forceinline__ void round2(float &a, float &b) {
+  uint32_t p = pack_rn(a, b);
+  a = bf_lo(p);
+  b = bf_hi(p);
+}
+
+// 8 bf16 values of a 16-byte vector <-> 8 floats.
+__device__ __forceinline__ void unpack8(const uint4 v, float f[8]) {
+  f[0] = bf_lo(v.x); f[1] = bf_hi(v.x);
+  f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+  f[4] = bf_lo(v.z); f[5] = bf_hi(v.z);
+  f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float f[8]) {
+  uint4 v;
+  v.x = pack_rn(f[0], f[1]);
+  v.y = pack_rn(f[2], f[3]);
+  v.z = pack_rn(f[4], f[5]);
+  v.w = pack_rn(f[6], f[7]);
+  return v;
+}
+
+// --------------------------------------------------------------------------
+// global memory: 16-byte vectors
+// --------------------------------------------------------------------------
+
+__device__ __forceinline__ uint4 ld16(const uint16_t *p) {
+  return *reinterpret_cast<const uint4 *>(p);
+}
+__device__ __forceinline__ void st16(uint16_t *p, uint4 v) {
+  *reinterpret_cast<uint4 *>(p) = v;
+}
+__device__ __forceinline__ float4 ld16f(const float *p) {
+  return *reinterpret_cast<const float4 *>(p);
+}
+
+// --------------------------------------------------------------------------
+// DPP reductions in binary64
+// --------------------------------------------------------------------------
+
+// DPP control codes (GFX9 encoding).
+constexpr int DPP_QUAD_XOR1 = 0xB1;      // quad_perm(1,0,3,2)
+constexpr int DPP_QUAD_XOR2 = 0x4E;      // quad_perm(2,3,0,1)
+constexpr int DPP_ROW_MIRROR = 0x140;    // lane i <- lane 15-i within a row of 16
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <- lane 7-i within 8 lanes
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Sum over each aligned group of 4 lanes; every lane of the group gets the
+// same bits (each step adds the same two operands, in either order).
+__device__ __forceinline__ double sum4(double v) {
+  v += dpp_f64<DPP_QUAD_XOR1>(v);
+  v += dpp_f64<DPP_QUAD_XOR2>(v);
+  return v;
+}
+
+// Sum over each aligned group of 8 lanes (quads hold equal values, so the
+// half-row mirror pairs quad 0 with quad 1).
+__device__ __forceinline__ double sum8(double v) {
+  v = sum4(v);
+  v += dpp_f64<DPP_ROW_HALF_MIRROR>(v);
+  return v;
+}
+
+// Sum over each row of 16 lanes, identical in all 16 lanes.
+__device__ __forceinline__ double sum16(double v) {
+  v = sum8(v);
+  v += dpp_f64<DPP_ROW_MIRROR>(v);
+  return v;
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the whole wavefront of 64 lanes; uniform result.
+__device__ __forceinline__ double sum64(double v) {
+  v = sum16(v);
+  const double r0 = readlane_f64(v, 0), r1 = readlane_f64(v, 16);
+  const double r2 = readlane_f64(v, 32), r3 = readlane_f64(v, 48);
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Sum over aligned groups of L lanes (L = 4, 8, 16 or 64).
+template <int L>
+__device__ __forceinline__ double group_sum(double v) {
+  static_assert(L == 4 || L == 8 || L == 16 || L == 64, "unsupported group");
+  if constexpr (L == 4) return sum4(v);
+  else if constexpr (L == 8) return sum8(v);
+  else if constexpr (L == 16) return sum16(v);
+  else return sum64(v);
+}
+
+// --------------------------------------------------------------------------
+// workgroup barrier for LDS traffic only (global loads stay in flight)
+// --------------------------------------------------------------------------
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// --------------------------------------------------------------------------
+// statistics -> the fp32 values the chain consumes
+// --------------------------------------------------------------------------
+
+// rstd = fp32(1 / sqrt(v)), v = var + eps in binary64 (correctly rounded
+// binary64 square root and division, then one rounding to binary32).
+__device__ __forceinline__ float rstd_from(double v) {
+  return (float)(1.0 / __builtin_sqrt(v));
+}
+
+}  // namespace ditnorm

@@ -1,0 +1,94 @@
+// Internal interface between the C-ABI layer (abi.hip) and the kernel files.
+// Every launcher assumes its arguments were validated by the ABI layer:
+// sizes in range, pointers 16-byte aligned, no illegal aliasing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ditnorm {
+
+struct DeviceInfo {
+  int num_cu;        // compute units
+  int device;        // HIP device ordinal
+};
+
+// Row kernels: LayerNorm or RMSNorm of each row + adaLN modulate, with an
+// optional gated-residual stage in front.
+struct RowArgs {
+  const uint16_t *x;         // update (gated) or input rows, bf16 [rows, cols]
+  const uint16_t *residual;  // gated only
+  const uint16_t *gate;      // gated only, [B, mod_stride]
+  const uint16_t *scale;     // [B, mod_stride]
+  const uint16_t *shift;     // [B, mod_stride]
+  const uint16_t *weight;    // RMS only, [cols]
+  uint16_t *residual_out;    // gated only
+  uint16_t *out;
+  float *mean_out;           // optional (LN only)
+  float *rstd_out;           // optional
+  uint16_t *y_out;           // optional
+  int64_t rows;
+  int64_t rows_per_batch;
+  int64_t mod_stride;
+  int32_t cols;
+  float eps;
+};
+hipError_t launch_row(const RowArgs &a, bool rms, bool gated, const DeviceInfo &dev,
+                      hipStream_t stream);
+
+// Per-head LayerNorm over 128-wide rows of q then k.
+struct QkArgs {
+  const uint16_t *q;
+  const uint16_t *k;
+  uint16_t *q_out;
+  uint16_t *k_out;
+  float *mean_out;  // optional [rows_q + rows_k]
+  float *rstd_out;  // optional
+  int64_t rows_q;
+  int64_t rows_k;
+  float eps;
+};
+hipError_t launch_qk(const QkArgs &a, const DeviceInfo &dev, hipStream_t stream);
+
+// channels_last [bias] + RMSNorm over C + gamma + SiLU.
+struct WanArgs {
+  const uint16_t *x;
+  const float *bias;   // nullable
+  const float *gamma;
+  uint16_t *out;
+  float *rstd_out;     // optional
+  uint16_t *xb_out;    // optional
+  int64_t rows;
+  int32_t channels;
+  float eps;
+};
+hipError_t launch_wan(const WanArgs &a, const DeviceInfo &dev, hipStream_t stream);
+
+// channels_last conv-bias epilogue (+ residual).
+struct EpilogueArgs {
+  const uint16_t *x;
+  const float *bias;
+  const uint16_t *h;   // nullable
+  uint16_t *out;
+  int64_t rows;
+  int32_t channels;
+};
+hipError_t launch_epilogue(const EpilogueArgs &a, const DeviceInfo &dev, hipStream_t stream);
+
+// Plain 16-byte copy (measurement utility).
+hipError_t launch_copy(const void *src, void *dst, int64_t bytes, const DeviceInfo &dev,
+                       hipStream_t stream);
+
+// Persistent-grid size: min(work units, CUs x resident blocks per CU).
+template <typename K>
+inline int64_t persistent_grid(K kernel, int block, int64_t units, const DeviceInfo &dev,
+                               int min_per_cu = 1) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess ||
+      per_cu < min_per_cu)
+    per_cu = min_per_cu;
+  const int64_t g = (int64_t)dev.num_cu * per_cu;
+  return units < g ? units : g;
+}
+
+}  // namespace ditnorm

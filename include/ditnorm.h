@@ -1,0 +1,246 @@
+/*
+ * ditnorm -- fused adaLN row normalisation for diffusion transformers on
+ * AMD Instinct MI355X (gfx950).  C ABI of libditnorm.so.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every tensor pointer is a DEVICE pointer owned by the caller.
+ *   The library never allocates, frees or keeps any of them.  bf16 tensors
+ *   are passed as `void*` (2-byte bfloat16 bit patterns); fp32 tensors as
+ *   `float*`.  Every tensor pointer must be 16-byte aligned.
+ *
+ * Layout.  Activations are dense row-major [rows, cols] (row stride == cols
+ *   elements).  For a [B, S, D] activation, rows = B*S and cols = D.
+ *   Modulation rows (scale, shift, gate) are [B, cols] with a row stride of
+ *   `mod_batch_stride` elements (>= cols; a multiple of 8 when B > 1), so a
+ *   chunk view of a [B, k*D] adaLN embedding can be passed directly.
+ *   Activation row r uses modulation row r / rows_per_batch; B is
+ *   rows / rows_per_batch.  The caller picks the (scale, shift) order of its
+ *   embedding's chunks by passing the right pointers.
+ *
+ * Streams.  Calls are asynchronous: the work is enqueued on `stream` (a
+ *   hipStream_t passed as void*; NULL = the null stream) and the call
+ *   returns.  Outputs are valid once the stream has been synchronised.
+ *
+ * Status.  Every entry point returns an int:
+ *   DITNORM_OK (0)
+ *   DITNORM_INVALID_ARGUMENT (1): a required pointer is NULL, a size is
+ *       negative or zero where it must be positive, rows is not a multiple of
+ *       rows_per_batch, mod_batch_stride < cols, eps is negative or not finite,
+ *       or an optional group is given half-way (see each entry point).
+ *   DITNORM_UNSUPPORTED (2): the arguments are valid but outside what the
+ *       kernels implement: cols not a multiple of 8 or above the stated
+ *       maximum, head_dim other than 128, a pointer not 16-byte aligned, a
+ *       modulation row stride that breaks 16-byte alignment, or an output that
+ *       overlaps an input other than in the exact in-place forms allowed.
+ *   DITNORM_DEVICE_ERROR (3): the current device is not gfx950, or a HIP call
+ *       or kernel launch failed (ditnorm_last_hip_error() keeps the code).
+ *   All argument checks run on the host before any HIP call; a call that
+ *   fails them has no effect.  rows == 0 is a valid no-op.  No exception
+ *   crosses the ABI and nothing falls back to another implementation.
+ *
+ * Aliasing.  `out == x` (exactly the same pointer) is allowed: every row is
+ *   read completely before any of it is written.  `residual_out == residual`
+ *   is allowed likewise.  Any other overlap of an output with an input or
+ *   with another output returns DITNORM_UNSUPPORTED.
+ *
+ * Optional outputs.  mean_out / rstd_out (fp32, one value per row), y_out
+ *   (bf16, the normalised value before modulation) and xb_out (bf16, the
+ *   biased input) expose intermediate stages for verification; pass NULL in
+ *   production.  They cost one extra write each.
+ *
+ * Numerics.  Statistics are fp32 values: mean = fp32(sum(x)/N),
+ *   rstd = fp32(1/sqrt(var + eps)) with the biased variance, the sums
+ *   accumulated in binary64 so that they are exact or within 1e-16 of exact.
+ *   Every elementwise stage keeps the eager chain's bf16 round-to-nearest-even
+ *   at each op boundary, with no fused multiply-add.
+ *
+ * Thread safety.  Entry points may be called concurrently from several host
+ *   threads; the library keeps only per-device read-only state and the last
+ *   HIP error code (thread-local).
+ */
+#ifndef DITNORM_H
+#define DITNORM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DITNORM_OK 0
+#define DITNORM_INVALID_ARGUMENT 1
+#define DITNORM_UNSUPPORTED 2
+#define DITNORM_DEVICE_ERROR 3
+
+/* Largest row width of the row kernels (ln_modulate, gated_ln_modulate,
+ * rms_modulate) and the largest channel count of the channels_last kernels. */
+#define DITNORM_MAX_COLS 16384
+#define DITNORM_MAX_CHANNELS 4096
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *ditnorm_status_string(int status);
+
+/* hipError_t of the last failing HIP call on this host thread (0 if none). */
+int ditnorm_last_hip_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int ditnorm_version(void);
+
+/*
+ * ln_modulate -- affine-free LayerNorm of each row, then the adaLN modulate.
+ *
+ * Defined on the GLM-Image page ("[diffusion] GLM-Image bit-exact fused aten
+ * LayerNorm+modulate / qk-LN", Motivation and "What rounding-faithful means
+ * here") and on the FLUX.1 page (fused adaLN modulate, Commit 2):
+ *     y   = bf16( rstd * (x - mean) )                    per row, fp32 stats
+ *     out = bf16( bf16( y * bf16(1 + scale) ) + shift )  per element
+ * x, out: bf16 [rows, cols].  scale, shift: bf16 [B, cols], row stride
+ * mod_batch_stride.  eps: fp32 (1e-6 on the pages' adaLN sites).
+ * cols: multiple of 8, at most DITNORM_MAX_COLS.  out == x allowed.
+ * mean_out, rstd_out (fp32 [rows]) and y_out (bf16 [rows, cols]) optional.
+ */
+int ln_modulate(const void *x, const void *scale, const void *shift, void *out,
+                int64_t rows, int64_t cols, int64_t rows_per_batch,
+                int64_t mod_batch_stride, float eps, float *mean_out, float *rstd_out,
+                void *y_out, void *stream);
+
+/*
+ * gated_ln_modulate -- the pre-norm gated residual, then ln_modulate on it.
+ *
+ * The residual-gate half of the adaLN block (GLM-Image page, ff gate
+ * "hidden + ff_out * gate"; ERNIE-Image page "[diffusion] ERNIE-Image
+ * bit-exact fused RMSNorm+scale/shift", second kernel, which also returns the
+ * residual stream):
+ *     h   = bf16( residual + bf16( gate * update ) )     -> residual_out
+ *     out = ln_modulate(h, scale, shift)
+ * update (x), residual, residual_out, out: bf16 [rows, cols].
+ * gate, scale, shift: bf16 [B, cols], row stride mod_batch_stride.
+ * residual_out == residual allowed; out must not alias anything.
+ * mean_out, rstd_out, y_out optional, as for ln_modulate (statistics of h).
+ */
+int gated_ln_modulate(const void *x, const void *residual, const void *gate,
+                      const void *scale, const void *shift, void *residual_out, void *out,
+                      int64_t rows, int64_t cols, int64_t rows_per_batch,
+                      int64_t mod_batch_stride, float eps, float *mean_out,
+                      float *rstd_out, void *y_out, void *stream);
+
+/*
+ * rms_modulate -- weighted RMSNorm of each row, then the adaLN modulate;
+ * optionally preceded by the gated residual.
+ *
+ * ERNIE-Image page ("[diffusion] ERNIE-Image bit-exact fused
+ * RMSNorm+scale/shift", "What rounding-faithful means here" and
+ * Modifications):
+ *     rstd = fp32( 1 / sqrt( sum(x^2)/cols + eps ) )
+ *     y    = bf16( (x * rstd) * weight )           two fp32 products, left to right
+ *     out  = bf16( bf16( y * bf16(1 + scale) ) + shift )
+ * Gated site (residual, gate and residual_out all non-NULL; all NULL for the
+ * plain site -- anything else is DITNORM_INVALID_ARGUMENT):
+ *     h = bf16( residual + bf16( gate * x ) ) -> residual_out, and the norm
+ *     runs on h.
+ * x, out, residual, residual_out: bf16 [rows, cols]; weight: bf16 [cols];
+ * scale, shift, gate: bf16 [B, cols], row stride mod_batch_stride.
+ * out == x allowed on the plain site; residual_out == residual allowed.
+ * rstd_out (fp32 [rows]) and y_out optional.
+ */
+int rms_modulate(const void *x, const void *weight, const void *scale, const void *shift,
+                 void *out, const void *residual, const void *gate, void *residual_out,
+                 int64_t rows, int64_t cols, int64_t rows_per_batch,
+                 int64_t mod_batch_stride, float eps, float *rstd_out, void *y_out,
+                 void *stream);
+
+/*
+ * qk_layernorm -- per-head affine-free LayerNorm of q and k in one launch.
+ *
+ * GLM-Image page, Motivation (nn.LayerNorm(128) per head on (1, S, 32, 128))
+ * and "What rounding-faithful means here" (q and k in one launch):
+ *     for every head_dim-wide row of q, then of k:
+ *     out = bf16( rstd * (x - mean) ),  fp32 stats, eps (1e-5 on the page's model)
+ * q, q_out: bf16 [rows_q, 128]; k, k_out: bf16 [rows_k, 128] (a (B, S, H, 128)
+ * tensor is rows = B*S*H).  head_dim must be 128.  k and k_out may be NULL only
+ * when rows_k == 0.  q_out == q and k_out == k allowed.
+ * mean_out, rstd_out: optional fp32 [rows_q + rows_k], q rows first.
+ */
+int qk_layernorm(const void *q, const void *k, void *q_out, void *k_out, int64_t rows_q,
+                 int64_t rows_k, int64_t head_dim, float eps, float *mean_out,
+                 float *rstd_out, void *stream);
+
+/*
+ * rmsnorm_silu_bias -- channels_last RMSNorm over the channels of each pixel,
+ * times gamma, then SiLU, with the deferred conv bias folded in first.
+ *
+ * Wan VAE page ("[Diffusion] Fuse the Wan VAE conv bias epilogue and tile the
+ * RMSNorm+SiLU kernel", Modifications, Quality-gated: the [ROWS, C] tiled
+ * kernel and its conv_bias= fold, applied exactly like aten's add_):
+ *     xb   = bf16( x + bf16(bias) )        (xb = x when bias is NULL)
+ *     rstd = fp32( 1 / sqrt( sum(xb^2)/C + eps ) )
+ *     t    = (xb * rstd) * gamma           fp32
+ *     out  = bf16( SiLU(t) )               one rounding, within 1 bf16 ulp
+ * x, out: bf16 channels_last [N, C, D, H, W] = [rows = N*D*H*W, C] dense rows
+ * of C channels.  bias: fp32 [C] or NULL; gamma: fp32 [C].
+ * channels: multiple of 8, at most DITNORM_MAX_CHANNELS.  out == x allowed.
+ * rstd_out (fp32 [rows]) and xb_out (bf16 [rows, C]) optional.
+ */
+int rmsnorm_silu_bias(const void *x, const float *bias, const float *gamma, void *out,
+                      int64_t rows, int64_t channels, float eps, float *rstd_out,
+                      void *xb_out, void *stream);
+
+/*
+ * conv_bias_epilogue -- the channels_last conv-bias add, optionally fused
+ * with the residual add that follows the conv.
+ *
+ * Wan VAE page (same title), Modifications, "New kernel, lossless": the
+ * arithmetic of aten's add_ with an fp32 bias cast to the activation dtype
+ * first, and with the residual the two roundings of the eager conv(x) + h:
+ *     out = bf16( x + bf16(bias) )                      (h == NULL)
+ *     out = bf16( bf16( x + bf16(bias) ) + h )          (h != NULL)
+ * x, h, out: bf16 [rows, channels] (channels_last pixels); bias: fp32 [C].
+ * channels: multiple of 8, at most DITNORM_MAX_CHANNELS.  out == x allowed.
+ */
+int conv_bias_epilogue(const void *x, const float *bias, const void *h, void *out,
+                       int64_t rows, int64_t channels, void *stream);
+
+/*
+ * *_supported -- 1 if the same call would pass every argument check (it may
+ * still fail with DITNORM_DEVICE_ERROR), else 0.  Never fails, never touches
+ * the GPU, never enqueues work.
+ */
+int ln_modulate_supported(const void *x, const void *scale, const void *shift,
+                          const void *out, int64_t rows, int64_t cols,
+                          int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
+                          const float *mean_out, const float *rstd_out, const void *y_out);
+int gated_ln_modulate_supported(const void *x, const void *residual, const void *gate,
+                                const void *scale, const void *shift,
+                                const void *residual_out, const void *out, int64_t rows,
+                                int64_t cols, int64_t rows_per_batch,
+                                int64_t mod_batch_stride, float eps, const float *mean_out,
+                                const float *rstd_out, const void *y_out);
+int rms_modulate_supported(const void *x, const void *weight, const void *scale,
+                           const void *shift, const void *out, const void *residual,
+                           const void *gate, const void *residual_out, int64_t rows,
+                           int64_t cols, int64_t rows_per_batch, int64_t mod_batch_stride,
+                           float eps, const float *rstd_out, const void *y_out);
+int qk_layernorm_supported(const void *q, const void *k, const void *q_out,
+                           const void *k_out, int64_t rows_q, int64_t rows_k,
+                           int64_t head_dim, float eps, const float *mean_out,
+                           const float *rstd_out);
+int rmsnorm_silu_bias_supported(const void *x, const float *bias, const float *gamma,
+                                const void *out, int64_t rows, int64_t channels, float eps,
+                                const float *rstd_out, const void *xb_out);
+int conv_bias_epilogue_supported(const void *x, const float *bias, const void *h,
+                                 const void *out, int64_t rows, int64_t channels);
+
+/*
+ * ditnorm_copy -- measurement utility, not part of the method: a plain
+ * 16-byte-vector device-to-device copy of `bytes` bytes (a multiple of 16,
+ * both pointers 16-byte aligned, no overlap).  Used as the practical HBM
+ * ceiling and to calibrate the FETCH_SIZE / WRITE_SIZE counters.
+ */
+int ditnorm_copy(const void *src, void *dst, int64_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DITNORM_H */

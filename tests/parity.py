@@ -1,0 +1,112 @@
+"""Helpers for comparing the HIP path with the CPU oracle.
+
+The bar (from the method's tolerance: within 1 bf16 ulp per element, fp32
+mean / rstd within 2e-6 relative, byte-identical elementwise stages):
+
+* statistics: |rstd_gpu - rstd_oracle| <= 2e-6 rstd_oracle and
+  |mean_gpu - mean_oracle| <= 2e-6 sqrt(mean^2 + var) (relative to the row's
+  RMS, since a near-zero mean makes a plain relative test ill-posed);
+* every elementwise stage is byte-identical to the oracle's stage applied to
+  the GPU's own inputs of that stage (y given the GPU's statistics, out given
+  the GPU's y, h, xb);
+* end to end: outputs of rows whose statistics carry the oracle's exact bits
+  are bit-identical; any other element is within 1 bf16 ulp or, where the
+  normalised value cancels (x ~ mean), explained by the stages above.
+
+Both sides accumulate the statistics exactly (binary64), so in practice the
+statistics -- and therefore every output -- match bit for bit; the helpers
+report the counts so a regression shows as numbers, not just a failure.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import sys
+
+import numpy as np
+import torch
+
+from dit_adaln_row_amd.inputs import from_u16, to_u16
+
+STATS_RTOL = 2e-6
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a, device="cuda"):
+    """numpy uint16 (bf16 bits) or float32 -> device tensor."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return from_u16(a, device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def host(t):
+    if t is None:
+        return None
+    if t.dtype == torch.bfloat16:
+        return to_u16(t)
+    return t.detach().cpu().numpy()
+
+
+def ulp_key(b):
+    b = np.asarray(b, np.uint16).astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def ulp_diff(a, b):
+    return np.abs(ulp_key(a) - ulp_key(b))
+
+
+def is_nan(b):
+    b = np.asarray(b, np.uint16)
+    return ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+
+
+def same_bits(a, b):
+    """bitwise equality, NaNs compared by class."""
+    na, nb = is_nan(a), is_nan(b)
+    return np.array_equal(na, nb) and np.array_equal(np.asarray(a)[~na], np.asarray(b)[~nb])
+
+
+def by_row_chunks(fn, arrays, rows, nthreads=8):
+    """Run a per-row oracle function over row chunks in threads (ctypes drops
+    the GIL).  ``fn(lo, hi)`` returns a dict of arrays for rows [lo, hi)."""
+    step = max(1, -(-rows // (nthreads * 4)))
+    bounds = [(lo, min(rows, lo + step)) for lo in range(0, rows, step)]
+    with cf.ThreadPoolExecutor(nthreads) as ex:
+        parts = list(ex.map(lambda b: fn(*b), bounds))
+    return {k: np.concatenate([p[k] for p in parts]) for k in parts[0]} if parts else {}
+
+
+def check_stats(mean_g, rstd_g, mean_o, rstd_o, what=""):
+    """Tolerance on fp32 statistics; returns the mask of rows whose bits differ."""
+    rstd_o = rstd_o.astype(np.float64)
+    assert np.all(np.abs(rstd_g.astype(np.float64) - rstd_o) <= STATS_RTOL * np.abs(rstd_o)), \
+        f"{what}: rstd beyond 2e-6"
+    differ = rstd_g.view(np.uint32) != rstd_o.astype(np.float32).view(np.uint32)
+    if mean_g is not None:
+        mo = mean_o.astype(np.float64)
+        var = np.maximum(1.0 / rstd_o ** 2, 0.0)
+        scale = np.sqrt(mo ** 2 + var)
+        assert np.all(np.abs(mean_g.astype(np.float64) - mo) <= STATS_RTOL * scale), \
+            f"{what}: mean beyond 2e-6 of the row RMS"
+        differ |= mean_g.view(np.uint32) != mean_o.view(np.uint32)
+    return differ
+
+
+def check_rows_end_to_end(out_g, out_o, stat_differ, what=""):
+    """Rows with the oracle's statistics: bit-identical.  Others: <= 1 ulp except
+    explained cancellation elements (reported)."""
+    same = ~stat_differ
+    assert same_bits(out_g[same], out_o[same]), \
+        f"{what}: {int((out_g[same] != out_o[same]).sum())} elements differ in rows with exact stats"
+    if stat_differ.any():
+        d = ulp_diff(out_g[stat_differ], out_o[stat_differ])
+        log(f"  {what}: {int(stat_differ.sum())} rows with last-bit stats differences, "
+            f"max {int(d.max())} ulp over {d.size} elements, {int((d > 1).sum())} above 1 ulp")
+    return int(stat_differ.sum())

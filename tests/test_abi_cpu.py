@@ -1,0 +1,142 @@
+"""Host-side tests of the C ABI (no GPU needed, no compute call made).
+
+The library must load on a machine without a GPU, export every function the
+header declares, and reject invalid arguments before any HIP call (every
+case below returns before the library looks for a device).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dit_adaln_row_amd as dn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ditnorm.h")
+
+A = 0x10000        # a 16-byte-aligned fake device address (never dereferenced)
+B = 0x20000000
+C = 0x40000000
+D = 0x60000000
+E = 0x80000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dn.LIB_PATH):
+        import dit_adaln_row_amd.build as b
+        b.build(verbose=False)
+    return dn.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    for must in ("ln_modulate", "gated_ln_modulate", "rms_modulate", "qk_layernorm",
+                 "rmsnorm_silu_bias", "conv_bias_epilogue", "ditnorm_status_string"):
+        assert must in names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.ditnorm_status_string(0) == b"DITNORM_OK"
+    assert lib.ditnorm_status_string(1) == b"DITNORM_INVALID_ARGUMENT"
+    assert lib.ditnorm_status_string(2) == b"DITNORM_UNSUPPORTED"
+    assert lib.ditnorm_status_string(3) == b"DITNORM_DEVICE_ERROR"
+    assert lib.ditnorm_status_string(99) == b"DITNORM_UNKNOWN_STATUS"
+    assert lib.ditnorm_version() >= 100
+
+
+def ln(lib, x=A, sc=B, sh=C, out=D, rows=4, cols=1024, rpb=4, mbs=1024, eps=1e-6, mean=None,
+       rstd=None, y=None):
+    return lib.ln_modulate(x, sc, sh, out, rows, cols, rpb, mbs, eps, mean, rstd, y, None)
+
+
+def test_ln_modulate_validation(lib):
+    assert ln(lib, x=None) == dn.INVALID_ARGUMENT
+    assert ln(lib, rows=-1) == dn.INVALID_ARGUMENT
+    assert ln(lib, cols=0) == dn.INVALID_ARGUMENT
+    assert ln(lib, rows=6, rpb=4) == dn.INVALID_ARGUMENT          # rows % rows_per_batch
+    assert ln(lib, mbs=512) == dn.INVALID_ARGUMENT                # stride < cols
+    assert ln(lib, eps=float("nan")) == dn.INVALID_ARGUMENT
+    assert ln(lib, eps=-1.0) == dn.INVALID_ARGUMENT
+    assert ln(lib, eps=float("inf")) == dn.INVALID_ARGUMENT
+    assert ln(lib, cols=1004, mbs=1004) == dn.UNSUPPORTED          # cols % 8
+    assert ln(lib, cols=16392, mbs=16392) == dn.UNSUPPORTED        # above the maximum
+    assert ln(lib, x=A + 2) == dn.UNSUPPORTED                      # misaligned
+    assert ln(lib, y=A + 8) == dn.UNSUPPORTED
+    assert ln(lib, rows=8, rpb=4, mbs=1028) == dn.UNSUPPORTED      # batch stride breaks alignment
+    assert ln(lib, out=A + 16) == dn.UNSUPPORTED                   # partial overlap with x
+    assert ln(lib, y=D) == dn.UNSUPPORTED                          # two outputs overlap
+    assert ln(lib, out=B) == dn.UNSUPPORTED                        # output over an input
+    assert ln(lib, rows=0, x=None) == dn.OK                        # empty: no-op
+
+
+def test_supported_predicates_never_touch_the_gpu(lib):
+    ok = lib.ln_modulate_supported(A, B, C, D, 4, 1024, 4, 1024, 1e-6, None, None, None)
+    assert ok == 1
+    assert lib.ln_modulate_supported(A, B, C, A, 4, 1024, 4, 1024, 1e-6, None, None, None) == 1  # in place
+    assert lib.ln_modulate_supported(A, B, C, D, 4, 1004, 4, 1004, 1e-6, None, None, None) == 0
+    assert lib.gated_ln_modulate_supported(A, B, C, D, E, C + 0x10, E + 0x100000, 4, 1024, 4,
+                                           1024, 1e-6, None, None, None) == 0  # residual_out over gate
+    assert lib.gated_ln_modulate_supported(A, B, C, C + 0x4000, C + 0x8000, B, D, 4, 1024, 4, 1024,
+                                           1e-6, None, None, None) == 1  # residual_out == residual
+    assert lib.rms_modulate_supported(A, B, C, C + 0x4000, D, None, None, None, 4, 4096, 4, 4096,
+                                      1e-6, None, None) == 1
+    assert lib.rms_modulate_supported(A, B, C, C + 0x4000, D, E, None, None, 4, 4096, 4, 4096,
+                                      1e-6, None, None) == 0   # half a gated group
+    assert lib.qk_layernorm_supported(A, B, C, D, 10, 10, 128, 1e-5, None, None) == 1
+    assert lib.qk_layernorm_supported(A, B, C, D, 10, 10, 64, 1e-5, None, None) == 0
+    assert lib.qk_layernorm_supported(A, None, C, None, 10, 0, 128, 1e-5, None, None) == 1
+    assert lib.qk_layernorm_supported(A, None, C, None, 10, 3, 128, 1e-5, None, None) == 0
+    assert lib.rmsnorm_silu_bias_supported(A, B, C, D, 100, 96, 1e-6, None, None) == 1
+    assert lib.rmsnorm_silu_bias_supported(A, None, C, D, 100, 96, 1e-6, None, None) == 1
+    assert lib.rmsnorm_silu_bias_supported(A, B, C, D, 100, 100, 1e-6, None, None) == 0
+    assert lib.rmsnorm_silu_bias_supported(A, B + 4, C, D, 100, 96, 1e-6, None, None) == 0
+    assert lib.conv_bias_epilogue_supported(A, B, C, D, 100, 96) == 1
+    assert lib.conv_bias_epilogue_supported(A, B, C, A, 100, 96) == 1      # in place
+    assert lib.conv_bias_epilogue_supported(A, B, C, C, 100, 96) == 0      # out over h
+
+
+def test_other_entry_validation(lib):
+    assert lib.gated_ln_modulate(A, None, C, C, C, D, E, 4, 1024, 4, 1024, 1e-6, None, None,
+                                 None, None) == dn.INVALID_ARGUMENT
+    assert lib.rms_modulate(A, B, C, C, D, E, None, None, 4, 1024, 4, 1024, 1e-6, None, None,
+                            None) == dn.INVALID_ARGUMENT
+    assert lib.qk_layernorm(A, B, C, D, 4, 4, 64, 1e-5, None, None, None) == dn.UNSUPPORTED
+    assert lib.qk_layernorm(A, B, C, D, -1, 4, 128, 1e-5, None, None, None) == dn.INVALID_ARGUMENT
+    assert lib.qk_layernorm(A, B, A + 128, D, 4, 4, 128, 1e-5, None, None, None) == dn.UNSUPPORTED
+    assert lib.rmsnorm_silu_bias(A, B, None, D, 10, 96, 1e-6, None, None, None) == dn.INVALID_ARGUMENT
+    assert lib.rmsnorm_silu_bias(A, B, C, D, 10, 4104, 1e-6, None, None, None) == dn.UNSUPPORTED
+    assert lib.conv_bias_epilogue(A, None, None, D, 10, 96, None) == dn.INVALID_ARGUMENT
+    assert lib.ditnorm_copy(A, B, 15, None) == dn.UNSUPPORTED
+    assert lib.ditnorm_copy(A, A + 16, 64, None) == dn.UNSUPPORTED
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    import importlib
+    mod = importlib.reload(dn)
+    mod._lib = None
+    with pytest.raises(RuntimeError):
+        mod.load(str(tmp_path / "nope.so"))
+    importlib.reload(dn)
+
+
+def test_product_never_uses_the_oracle():
+    pkg = os.path.join(ROOT, "dit_adaln_row_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", text, flags=re.M), f
+                assert "ditnorm_oracle" not in text and "libditnorm_oracle" not in text, f
+    osrc = open(os.path.join(ROOT, "oracle", "ditnorm_oracle.c")).read()
+    assert "#include \"" not in osrc   # the oracle includes no project header

@@ -1,0 +1,396 @@
+"""GPU parity: the HIP kernels (called through the C ABI via the binding)
+against the CPU oracle, element by element, on seeded inputs.
+
+Sizes: small and ragged cases (several tiles / workgroups plus a tail, odd
+widths, batched modulation with chunk-view strides, empty launches) and every
+workload at its full size, in the launch configuration the benchmark times
+(no debug outputs) and with the debug outputs on for the stage checks.
+"""
+import numpy as np
+import pytest
+import torch
+
+from dit_adaln_row_amd import inputs as gen
+from dit_adaln_row_amd.workloads import WORKLOADS
+from parity import (by_row_chunks, check_rows_end_to_end, check_stats, dev, host, log,
+                    same_bits, ulp_diff)
+
+pytestmark = pytest.mark.gpu
+F32 = torch.float32
+
+
+def rand(shape, mu, sigma, seed):
+    return gen.to_u16(gen.normal(shape, mu, sigma, seed))
+
+
+def empty_f32(n):
+    return torch.empty(n, dtype=F32, device="cuda")
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm + modulate (plain and gated)
+# ---------------------------------------------------------------------------
+
+def _ln_gpu(dn, x, sc, sh, eps, mod_dev=None, debug=True):
+    rows, cols = x.shape
+    xd = dev(x)
+    scd, shd = mod_dev if mod_dev is not None else (dev(sc), dev(sh))
+    kw = {}
+    if debug:
+        kw = dict(mean_out=empty_f32(rows), rstd_out=empty_f32(rows), y_out=torch.empty_like(xd))
+    out = dn.ln_modulate(xd, scd, shd, eps, **kw)
+    torch.cuda.synchronize()
+    if not debug:
+        return host(out), None, None, None
+    return host(out), host(kw["mean_out"]), host(kw["rstd_out"]), host(kw["y_out"])
+
+
+def _ln_check(orc, what, x, sc, sh, eps, rpb, out_g, mean_g, rstd_g, y_g, ref=None):
+    ref = ref or orc.ln_modulate(x, sc, sh, eps, rows_per_batch=rpb)
+    differ = check_stats(mean_g, rstd_g, ref["mean"], ref["rstd"], what)
+    assert same_bits(y_g, orc.ln_normalize(x, mean_g, rstd_g)), f"{what}: y stage"
+    assert same_bits(out_g, orc.modulate(y_g, sc, sh, rows_per_batch=rpb)), f"{what}: modulate stage"
+    check_rows_end_to_end(out_g, ref["out"], np.repeat(differ[:, None], x.shape[1], 1), what)
+    return ref
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 8), (3, 40), (257, 1024), (100, 3072), (37, 4096),
+                                       (5, 2048), (9, 1536), (3, 16384), (1000, 512), (2, 9000)])
+def test_ln_modulate_shapes(gpu, orc, rows, cols):
+    log(f"ln_modulate rows={rows} cols={cols}")
+    x = rand((rows, cols), 0.3, 1.5, 11 + cols)
+    sc = rand((1, cols), 0, 0.1, 12)
+    sh = rand((1, cols), 0, 0.1, 13)
+    out, mean, rstd, y = _ln_gpu(gpu, x, sc, sh, 1e-6)
+    _ln_check(orc, f"ln {rows}x{cols}", x, sc, sh, 1e-6, rows, out, mean, rstd, y)
+
+
+def test_ln_modulate_batched_chunk_views(gpu, orc):
+    """B = 3 modulation rows taken as chunk views of a [B, 6*D] embedding."""
+    B, S, D = 3, 129, 3072
+    log(f"ln_modulate batched B={B} S={S} D={D}")
+    x = rand((B * S, D), 0, 1.5, 21)
+    emb = rand((B, 6 * D), 0, 0.1, 22)
+    embd = dev(emb)
+    sc_view, sh_view = embd[:, D:2 * D], embd[:, 0:D]
+    out, mean, rstd, y = _ln_gpu(gpu, x, None, None, 1e-6, mod_dev=(sc_view, sh_view))
+    sc = np.concatenate([emb.ravel()[D:], np.zeros(D, np.uint16)]).reshape(B, 6 * D)
+    _ln_check(orc, "ln batched", x, sc, emb, 1e-6, S, out, mean, rstd, y)
+
+
+def test_ln_modulate_empty_and_inplace(gpu, orc):
+    x = torch.empty((0, 1024), dtype=torch.bfloat16, device="cuda")
+    s = torch.zeros((1, 1024), dtype=torch.bfloat16, device="cuda")
+    assert gpu.ln_modulate(x, s, s).numel() == 0
+    xs = rand((65, 1024), 0, 1, 31)
+    sc, sh = rand((1, 1024), 0, 0.1, 32), rand((1, 1024), 0, 0.1, 33)
+    xd = dev(xs)
+    gpu.ln_modulate(xd, dev(sc), dev(sh), 1e-6, out=xd)   # in place
+    torch.cuda.synchronize()
+    assert same_bits(host(xd), orc.ln_modulate(xs, sc, sh, 1e-6)["out"])
+
+
+def test_ln_special_rows(gpu, orc):
+    """Constant rows (variance 0), an all-zero row, a high-offset row, huge and
+    tiny (subnormal) magnitudes, and a NaN row."""
+    cols = 3072
+    x = rand((12, cols), 0, 1, 41)
+    x[0] = 0x3FC0                                           # constant 1.5
+    x[1] = 0                                                # zeros
+    x[2] = rand((1, cols), 64.0, 0.1, 42)                   # offset row
+    x[3] = rand((1, cols), 0, 1e30, 43)                     # huge
+    x[4] = rand((1, cols), 0, 1e-39, 44)                    # subnormal
+    x[5] = rand((1, cols), 0, 3e-38, 45)                    # tiny normal
+    x[6] = np.where(np.arange(cols) % 2 == 0, 0x4040, 0xC040).astype(np.uint16)  # +-3
+    x[7, 17] = 0x7FC0                                       # a NaN in a row
+    sc = rand((1, cols), 0, 0.1, 46)
+    sh = rand((1, cols), 0, 0.1, 47)
+    out, mean, rstd, y = _ln_gpu(gpu, x, sc, sh, 1e-6)
+    ref = orc.ln_modulate(x, sc, sh, 1e-6)
+    fin = np.isfinite(ref["rstd"]) & np.isfinite(ref["mean"])
+    _ln_check(orc, "ln special", x[fin], sc, sh, 1e-6, int(fin.sum()), out[fin], mean[fin],
+              rstd[fin], y[fin])
+    assert np.all(~np.isfinite(rstd[~fin]) | ~np.isfinite(mean[~fin]))
+    assert same_bits(out[7], ref["out"][7])                # NaN row: NaN everywhere
+
+
+def test_gated_ln_modulate_shapes(gpu, orc):
+    for rows, cols, B in [(7, 1024, 1), (300, 3072, 1), (2 * 65, 3072, 2), (33, 4096, 1)]:
+        log(f"gated_ln_modulate rows={rows} cols={cols} B={B}")
+        upd = rand((rows, cols), 0, 1.5, 51)
+        res = rand((rows, cols), 0, 1, 52)
+        gate = rand((B, cols), 0, 0.1, 53)
+        sc = rand((B, cols), 0, 0.1, 54)
+        sh = rand((B, cols), 0, 0.1, 55)
+        kw = dict(mean_out=empty_f32(rows), rstd_out=empty_f32(rows), y_out=torch.empty(
+            (rows, cols), dtype=torch.bfloat16, device="cuda"))
+        h, out = gpu.gated_ln_modulate(dev(upd), dev(res), dev(gate), dev(sc), dev(sh), 1e-6, **kw)
+        torch.cuda.synchronize()
+        h, out = host(h), host(out)
+        rpb = rows // B
+        ref = orc.gated_ln_modulate(upd, res, gate, sc, sh, 1e-6, rows_per_batch=rpb)
+        assert same_bits(h, ref["h"]), "gate stage"
+        _ln_check(orc, "gated", h, sc, sh, 1e-6, rpb, out, host(kw["mean_out"]),
+                  host(kw["rstd_out"]), host(kw["y_out"]), ref=ref)
+
+
+def test_gated_inplace_residual(gpu, orc):
+    rows, cols = 64, 3072
+    upd, res = rand((rows, cols), 0, 1.5, 61), rand((rows, cols), 0, 1, 62)
+    gate, sc, sh = (rand((1, cols), 0, 0.1, s) for s in (63, 64, 65))
+    rd = dev(res)
+    gpu.gated_ln_modulate(dev(upd), rd, dev(gate), dev(sc), dev(sh), 1e-6, residual_out=rd)
+    torch.cuda.synchronize()
+    assert same_bits(host(rd), orc.gate_residual(upd, res, gate))
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm + modulate (plain and gated)
+# ---------------------------------------------------------------------------
+
+def _rms_run_check(gpu, orc, what, x, w, sc, sh, eps, rpb, res=None, gate=None):
+    rows, cols = x.shape
+    kw = dict(rstd_out=empty_f32(rows), y_out=torch.empty((rows, cols), dtype=torch.bfloat16,
+                                                          device="cuda"))
+    if res is not None:
+        h, out = gpu.rms_modulate(dev(x), dev(w), dev(sc), dev(sh), eps, residual=dev(res),
+                                  gate=dev(gate), **kw)
+    else:
+        h, out = None, gpu.rms_modulate(dev(x), dev(w), dev(sc), dev(sh), eps, **kw)
+    torch.cuda.synchronize()
+    out, rstd, y = host(out), host(kw["rstd_out"]), host(kw["y_out"])
+    ref = orc.rms_modulate(x, w, sc, sh, eps, residual=res, gate=gate, rows_per_batch=rpb)
+    src = x
+    if res is not None:
+        h = host(h)
+        assert same_bits(h, ref["h"]), f"{what}: gate stage"
+        src = h
+    differ = check_stats(None, rstd, None, ref["rstd"], what)
+    assert same_bits(y, orc.rms_normalize(src, rstd, w)), f"{what}: y stage"
+    assert same_bits(out, orc.modulate(y, sc, sh, rows_per_batch=rpb)), f"{what}: modulate stage"
+    check_rows_end_to_end(out, ref["out"], np.repeat(differ[:, None], cols, 1), what)
+    assert np.all(ulp_diff(out, ref["out"]) <= 1), f"{what}: beyond 1 ulp"
+
+
+@pytest.mark.parametrize("rows,cols,B,gated", [(1, 4096, 1, False), (128, 2048, 1, False),
+                                               (2 * 1140, 4096, 2, False), (257, 4096, 1, True),
+                                               (2 * 65, 4096, 2, True), (11, 1024, 1, True),
+                                               (5, 24, 1, False), (3, 16384, 1, True)])
+def test_rms_modulate_shapes(gpu, orc, rows, cols, B, gated):
+    log(f"rms_modulate rows={rows} cols={cols} B={B} gated={gated}")
+    x = rand((rows, cols), 0, 1, 71 + cols)
+    w = rand((cols,), 1, 0.05, 72)
+    sc, sh = rand((B, cols), 0, 0.1, 73), rand((B, cols), 0, 0.1, 74)
+    res = rand((rows, cols), 0, 1, 75) if gated else None
+    gate = rand((B, cols), 0, 0.1, 76) if gated else None
+    _rms_run_check(gpu, orc, f"rms {rows}x{cols}", x, w, sc, sh, 1e-6, rows // B, res, gate)
+
+
+# ---------------------------------------------------------------------------
+# qk LayerNorm
+# ---------------------------------------------------------------------------
+
+def _qk_run_check(gpu, orc, what, q, k, eps):
+    rq, rk = q.shape[0], (0 if k is None else k.shape[0])
+    mean, rstd = empty_f32(rq + rk), empty_f32(rq + rk)
+    qo, ko = gpu.qk_layernorm(dev(q), None if k is None else dev(k), eps, mean_out=mean,
+                              rstd_out=rstd)
+    torch.cuda.synchronize()
+    qo = host(qo)
+    ko = host(ko) if k is not None else np.zeros((0, 128), np.uint16)
+    kk = k if k is not None else np.zeros((0, 128), np.uint16)
+    ref = orc.qk_layernorm(q, kk, eps)
+    mean, rstd = host(mean), host(rstd)
+    differ = check_stats(mean, rstd, ref["mean"], ref["rstd"], what)
+    both = np.concatenate([q, kk])
+    got = np.concatenate([qo, ko])
+    assert same_bits(got, orc.ln_normalize(both, mean, rstd)), f"{what}: normalise stage"
+    check_rows_end_to_end(got, np.concatenate([ref["q_out"], ref["k_out"]]),
+                          np.repeat(differ[:, None], 128, 1), what)
+
+
+@pytest.mark.parametrize("rq,rk", [(1, 0), (4, 4), (3, 5), (17, 1), (4360 * 32, 4360 * 32),
+                                   (1000, 37), (16 * 7 + 3, 16 * 5 + 1)])
+def test_qk_layernorm_shapes(gpu, orc, rq, rk):
+    log(f"qk_layernorm rows_q={rq} rows_k={rk}")
+    q = rand((rq, 128), 0, 2, 81)
+    k = rand((rk, 128), 0.1, 2, 82) if rk else None
+    _qk_run_check(gpu, orc, f"qk {rq}+{rk}", q, k, 1e-5)
+
+
+# ---------------------------------------------------------------------------
+# channels_last RMSNorm + SiLU (+ bias) and the conv-bias epilogue
+# ---------------------------------------------------------------------------
+
+def _wan_run_check(gpu, orc, what, x, bias, gamma, eps):
+    rows, c = x.shape
+    rstd, xb = empty_f32(rows), torch.empty((rows, c), dtype=torch.bfloat16, device="cuda")
+    out = gpu.rmsnorm_silu_bias(dev(x), dev(gamma), None if bias is None else dev(bias), eps,
+                                rstd_out=rstd, xb_out=xb)
+    torch.cuda.synchronize()
+    out, rstd, xb = host(out), host(rstd), host(xb)
+    ref = by_row_chunks(lambda lo, hi: orc.rmsnorm_silu_bias(x[lo:hi], bias, gamma, eps), None, rows)
+    assert same_bits(xb, ref["xb"]), f"{what}: bias stage"
+    check_stats(None, rstd, None, ref["rstd"], what)
+    exact = rstd.view(np.uint32) == ref["rstd"].view(np.uint32)
+    d = ulp_diff(out, ref["out"])
+    log(f"  {what}: rstd exact on {exact.mean():.6f} of rows; out exact on "
+        f"{(d == 0).mean():.6f} of elements, max {int(d.max())} ulp")
+    assert np.all(d <= 1), f"{what}: SiLU output beyond 1 ulp"
+    return ref
+
+
+@pytest.mark.parametrize("rows,c,bias", [(1, 96, True), (17, 96, True), (1000, 384, True),
+                                         (333, 96, False), (64, 128, True), (77, 256, True),
+                                         (50, 512, True), (13, 40, True), (9, 1000, False),
+                                         (5, 4096, True), (31, 192, True)])
+def test_rmsnorm_silu_bias_shapes(gpu, orc, rows, c, bias):
+    log(f"rmsnorm_silu_bias rows={rows} C={c} bias={bias}")
+    x = rand((rows, c), 0, 1, 91 + c)
+    b = gen.normal((c,), 0, 0.05, 92, "f32").numpy() if bias else None
+    g = gen.normal((c,), 1, 0.05, 93, "f32_bf16vals").numpy()
+    _wan_run_check(gpu, orc, f"wan {rows}x{c}", x, b, g, 1e-6)
+
+
+def test_rmsnorm_silu_extreme_t(gpu, orc):
+    """Large |t| (gamma up to 120): exp(-|t|) underflows / becomes subnormal."""
+    rows, c = 64, 96
+    x = rand((rows, c), 0, 1, 94)
+    g = np.linspace(-120, 120, c).astype(np.float32)
+    _wan_run_check(gpu, orc, "wan extreme", x, None, g, 1e-6)
+
+
+def test_rmsnorm_silu_channels_last_5d(gpu, orc):
+    n, c, d, h, w = 1, 96, 2, 12, 20
+    xt = gen.normal((n, c, d, h, w), 0, 1, 95).to(memory_format=torch.channels_last_3d)
+    g = gen.normal((c,), 1, 0.05, 96, "f32_bf16vals")
+    b = gen.normal((c,), 0, 0.05, 97, "f32")
+    out = gpu.rmsnorm_silu_bias(xt.cuda(), g.cuda(), b.cuda(), 1e-6)
+    torch.cuda.synchronize()
+    assert out.is_contiguous(memory_format=torch.channels_last_3d)
+    rows = gen.to_u16(xt.permute(0, 2, 3, 4, 1).reshape(-1, c).contiguous())
+    ref = orc.rmsnorm_silu_bias(rows, b.numpy(), g.numpy(), 1e-6)["out"]
+    got = gen.to_u16(out.permute(0, 2, 3, 4, 1).reshape(-1, c).contiguous())
+    assert np.all(ulp_diff(got, ref) <= 1)
+    with pytest.raises(ValueError):
+        gpu.rmsnorm_silu_bias(xt.contiguous().cuda(), g.cuda(), b.cuda())  # NCDHW rejected
+
+
+@pytest.mark.parametrize("rows,c,res", [(1, 96, False), (1000, 96, True), (777, 384, True),
+                                        (3, 8, False), (12345, 40, True)])
+def test_conv_bias_epilogue(gpu, orc, rows, c, res):
+    log(f"conv_bias_epilogue rows={rows} C={c} residual={res}")
+    x = rand((rows, c), 0, 1, 101)
+    h = rand((rows, c), 0, 1, 102) if res else None
+    b = gen.normal((c,), 0, 0.05, 103, "f32").numpy()
+    out = gpu.conv_bias_epilogue(dev(x), dev(b), None if h is None else dev(h))
+    torch.cuda.synchronize()
+    assert same_bits(host(out), orc.conv_bias_epilogue(x, b, h))
+
+
+# ---------------------------------------------------------------------------
+# every workload at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("key", list(WORKLOADS))
+def test_full_workload(gpu, orc, key):
+    w = WORKLOADS[key]
+    log(f"full workload {key}")
+    t = {k: (gen.to_u16(v) if v.dtype == torch.bfloat16 else v.numpy())
+         for k, v in gen.make(w).items()}
+    for l in w.launches:
+        log(f"  launch {l.name} rows={l.rows} cols={l.cols}")
+        if l.entry == "ln_modulate":
+            x, sc, sh = t["x"], t["scale"], t["shift"]
+            out_fast, *_ = _ln_gpu(gpu, x, sc, sh, l.eps, debug=False)
+            out, mean, rstd, y = _ln_gpu(gpu, x, sc, sh, l.eps)
+            assert same_bits(out_fast, out), "debug outputs changed the result"
+            ref = by_row_chunks(lambda lo, hi: orc.ln_modulate(x[lo:hi], sc, sh, l.eps), None,
+                                x.shape[0])
+            _ln_check(orc, f"{key}/{l.name}", x, sc, sh, l.eps, x.shape[0], out, mean, rstd, y,
+                      ref=ref)
+        elif l.entry == "gated_ln_modulate":
+            upd, res, gate, sc, sh = (t[n] for n in ("update", "residual", "gate", "scale", "shift"))
+            rows, cols = upd.shape
+            _, out_fast = gpu.gated_ln_modulate(dev(upd), dev(res), dev(gate), dev(sc), dev(sh),
+                                                l.eps)
+            kw = dict(mean_out=empty_f32(rows), rstd_out=empty_f32(rows),
+                      y_out=torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda"))
+            h, out = gpu.gated_ln_modulate(dev(upd), dev(res), dev(gate), dev(sc), dev(sh), l.eps,
+                                           **kw)
+            torch.cuda.synchronize()
+            h, out = host(h), host(out)
+            assert same_bits(host(out_fast), out), "debug outputs changed the result"
+            ref = by_row_chunks(lambda lo, hi: orc.gated_ln_modulate(
+                upd[lo:hi], res[lo:hi], gate, sc, sh, l.eps), None, rows)
+            assert same_bits(h, ref["h"]), "gate stage"
+            _ln_check(orc, f"{key}/{l.name}", h, sc, sh, l.eps, rows, out, host(kw["mean_out"]),
+                      host(kw["rstd_out"]), host(kw["y_out"]), ref=ref)
+        elif l.entry == "rms_modulate":
+            gated = l.extra.get("gated", False)
+            xn = "update" if gated else "x"
+            _rms_run_check(gpu, orc, f"{key}/{l.name}", t[xn], t["weight"], t["scale"], t["shift"],
+                           l.eps, t[xn].shape[0], t["residual"] if gated else None,
+                           t["gate"] if gated else None)
+        elif l.entry == "qk_layernorm":
+            _qk_run_check(gpu, orc, f"{key}/{l.name}", t["q"], t["k"], l.eps)
+        elif l.entry == "rmsnorm_silu_bias":
+            _wan_run_check(gpu, orc, f"{key}/{l.name}", t["x"], t["bias"], t["gamma"], l.eps)
+
+
+# ---------------------------------------------------------------------------
+# invariance and determinism
+# ---------------------------------------------------------------------------
+
+def test_row_position_batch_and_chunking_invariance(gpu, orc):
+    """A row's result does not depend on where it sits, how many rows are
+    launched with it (grid size), the batch split, or repeated runs."""
+    cols = 3072
+    x = rand((2 * 257, cols), 0, 1.5, 111)
+    sc, sh = rand((1, cols), 0, 0.1, 112), rand((1, cols), 0, 0.1, 113)
+    full, *_ = _ln_gpu(gpu, x, sc, sh, 1e-6, debug=False)
+    again, *_ = _ln_gpu(gpu, x, sc, sh, 1e-6, debug=False)
+    assert np.array_equal(full, again), "not deterministic"
+    for lo, hi in [(0, 1), (5, 6), (513, 514), (31, 32 + 31), (100, 357), (0, 257), (257, 514)]:
+        part, *_ = _ln_gpu(gpu, x[lo:hi], sc, sh, 1e-6, debug=False)
+        assert np.array_equal(part, full[lo:hi]), (lo, hi)
+    # B = 2 with equal modulation rows == B = 1
+    sc2, sh2 = np.repeat(sc, 2, 0), np.repeat(sh, 2, 0)
+    b2, *_ = _ln_gpu(gpu, x, sc2, sh2, 1e-6, debug=False)
+    assert np.array_equal(b2, full)
+    # qk: a head row alone vs inside a large launch
+    q = rand((4096, 128), 0, 2, 114)
+    qa, _ = gpu.qk_layernorm(dev(q), None)
+    q1, _ = gpu.qk_layernorm(dev(q[1234:1235]), None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(qa)[1234:1235], host(q1))
+    # wan: ragged pixel groups
+    xw = rand((1000, 96), 0, 1, 115)
+    g = gen.normal((96,), 1, 0.05, 116, "f32_bf16vals")
+    b = gen.normal((96,), 0, 0.05, 117, "f32")
+    wa = gpu.rmsnorm_silu_bias(dev(xw), g.cuda(), b.cuda())
+    w1 = gpu.rmsnorm_silu_bias(dev(xw[999:1000]), g.cuda(), b.cuda())
+    w7 = gpu.rmsnorm_silu_bias(dev(xw[3:10]), g.cuda(), b.cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(host(wa)[999:1000], host(w1))
+    assert np.array_equal(host(wa)[3:10], host(w7))
+
+
+def test_rejections_raise(gpu):
+    x = torch.zeros((4, 1024), dtype=torch.bfloat16, device="cuda")
+    s = torch.zeros((1, 1024), dtype=torch.bfloat16, device="cuda")
+    x1000 = torch.zeros((4, 1004), dtype=torch.bfloat16, device="cuda")
+    s1000 = torch.zeros((1, 1004), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(gpu.DitnormError) as e:
+        gpu.ln_modulate(x1000, s1000, s1000)                       # cols % 8 != 0
+    assert e.value.status == gpu.UNSUPPORTED
+    with pytest.raises(gpu.DitnormError) as e:
+        gpu.ln_modulate(x, s, s, eps=float("nan"))
+    assert e.value.status == gpu.INVALID_ARGUMENT
+    with pytest.raises(gpu.DitnormError) as e:                      # partial overlap
+        gpu.ln_modulate(x, s, s, out=torch.as_strided(x, (4, 1024), (1024, 1), 8))
+    assert e.value.status == gpu.UNSUPPORTED
+    with pytest.raises(gpu.DitnormError) as e:                      # misaligned
+        gpu.ln_modulate(torch.as_strided(x, (3, 1024), (1024, 1), 4), s, s,
+                        out=torch.empty((3, 1024), dtype=torch.bfloat16, device="cuda"))
+    assert e.value.status == gpu.UNSUPPORTED
