@@ -387,10 +387,12 @@ def test_rejections_raise(gpu):
     with pytest.raises(gpu.DitnormError) as e:
         gpu.ln_modulate(x, s, s, eps=float("nan"))
     assert e.value.status == gpu.INVALID_ARGUMENT
+    buf = torch.zeros(4 * 1024 + 64, dtype=torch.bfloat16, device="cuda")
+    xv = buf[:4096].view(4, 1024)
     with pytest.raises(gpu.DitnormError) as e:                      # partial overlap
-        gpu.ln_modulate(x, s, s, out=torch.as_strided(x, (4, 1024), (1024, 1), 8))
+        gpu.ln_modulate(xv, s, s, out=buf[8:8 + 4096].view(4, 1024))
     assert e.value.status == gpu.UNSUPPORTED
-    with pytest.raises(gpu.DitnormError) as e:                      # misaligned
-        gpu.ln_modulate(torch.as_strided(x, (3, 1024), (1024, 1), 4), s, s,
+    with pytest.raises(gpu.DitnormError) as e:                      # misaligned (4 bytes)
+        gpu.ln_modulate(buf[2:2 + 3072].view(3, 1024), s, s,
                         out=torch.empty((3, 1024), dtype=torch.bfloat16, device="cuda"))
     assert e.value.status == gpu.UNSUPPORTED
