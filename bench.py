@@ -106,48 +106,55 @@ def check_status(st, what):
 # ---------------------------------------------------------------------------
 
 def time_step_loop(calls_per_set, steps, warmup):
-    """calls_per_set[s] = [(fn, args, name), ...] for rotation set s.  Returns
-    (wall seconds for `steps` steps, {name: [event ms per launch]})."""
+    """calls_per_set[s] = [(fn, args, name), ...]: the launches of one step on
+    rotation set s.  Runs `warmup` untimed steps, then `steps` timed steps.
+    Inside the timed region each launch kind runs as one back-to-back burst
+    (the K plain launches, then the K gated launches, every launch on its own
+    rotating buffer set), with a HIP event on the launch stream between
+    bursts: a kind's average launch duration is its burst interval / K, which
+    is what rocprofv3 reports as the kernel's average duration.  Returns
+    (wall seconds for the `steps` steps, {name: average ms per launch})."""
     nsets = len(calls_per_set)
     names = [c[2] for c in calls_per_set[0]]
     for i in range(warmup):
         for fn, args, name in calls_per_set[i % nsets]:
             check_status(fn(*args), name)
-    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)] for n in names}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        for fn, args, name in calls_per_set[(warmup + i) % nsets]:
-            a, b = ev[name][i]
-            a.record()
+    ev[0].record()
+    for j, name in enumerate(names):
+        for i in range(steps):
+            fn, args, _ = calls_per_set[(warmup + i) % nsets][j]
             st = fn(*args)
-            b.record()
             if st != 0:
                 check_status(st, name)
+        ev[j + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    per = {n: [a.elapsed_time(b) for a, b in ev[n]] for n in names}
+    per = {n: ev[j].elapsed_time(ev[j + 1]) / steps for j, n in enumerate(names)}
     return t1 - t0, per
 
 
-def time_kernel(calls, iters=200, warmup=20):
-    """Per-launch event times (ms) of one launch kind over rotating sets; a
-    spin kernel first lets the host queue the launches ahead of the GPU."""
+def time_kernel(calls, iters=100, reps=5, warmup=20):
+    """Median over `reps` bursts of `iters` back-to-back launches (rotating
+    buffer sets) of the per-launch time in ms; also the fastest and slowest
+    burst."""
     for i in range(warmup):
         fn, args = calls[i % len(calls)]
         check_status(fn(*args), "warmup")
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(iters)]
-    torch.cuda.synchronize()
-    torch.cuda._sleep(2_000_000)
-    for i in range(iters):
-        fn, args = calls[i % len(calls)]
-        ev[i][0].record()
-        fn(*args)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    return sorted(a.elapsed_time(b) for a, b in ev)
+    out = []
+    for r in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(iters):
+            fn, args = calls[i % len(calls)]
+            fn(*args)
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / iters)
+    return sorted(out)
 
 
 def kernel_source_hash(entry):
@@ -228,7 +235,18 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-kernels", action="store_true")
     ap.add_argument("--only", default=None, help="time only this workload's kernels (profiling)")
+    ap.add_argument("--calib", action="store_true",
+                    help="also launch the 16-byte copy kernel over 128 MB (counter calibration)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "NAME"),
+                    help="CPU only: summarise a rocprofv3 --kernel-trace --stats run into profiles/NAME.txt")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "NAME"),
+                    help="CPU only: turn FETCH_SIZE / WRITE_SIZE runs into profiles/traffic.json")
+    ap.add_argument("--cmd", default="", help="the profiled command, recorded in the summary")
     args = ap.parse_args()
+    if args.summarize_trace:
+        return summarize_trace(*args.summarize_trace, args.cmd)
+    if args.summarize_pmc:
+        return summarize_pmc(*args.summarize_pmc, args.cmd)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested). Rows are independent; see DESIGN.md for how the "
@@ -265,7 +283,7 @@ def main():
 
     kinfo = {}
     for l in w.launches:
-        ms = sum(per[l.name]) / len(per[l.name])
+        ms = per[l.name]
         kinfo[l.name] = {"avg_ms": ms, "gbps": l.algorithmic_bytes() / (ms * 1e-3) / 1e9,
                          "bytes": l.algorithmic_bytes(), "rows": l.rows}
     dom = max(w.launches, key=lambda l: l.algorithmic_bytes() * kinfo[l.name]["avg_ms"])
@@ -295,6 +313,8 @@ def main():
     }
     del sets, calls, keep
     torch.cuda.empty_cache()
+    if args.calib:
+        copy_calibration(lib, dev, stream)
 
     if not args.no_kernels and args.only is None:
         result["kernels"] = per_kernel_table(lib, dev, stream)
@@ -305,8 +325,9 @@ def main():
 
 
 def per_kernel_table(lib, dev, stream):
-    """Median per-launch GB/s and rows/s of every workload's launches (200
-    timed launches over rotating buffer sets each; copy kernel for context)."""
+    """Per-launch GB/s and rows/s of every workload's launches: the median of
+    5 bursts of 100 back-to-back launches over rotating buffer sets (and the
+    plain 16-byte copy kernel moving 256 MB, for context)."""
     table = {}
     for key, w in WORKLOADS.items():
         log(f"[bench] kernels: {key}")
@@ -321,8 +342,8 @@ def per_kernel_table(lib, dev, stream):
             med = times[len(times) // 2]
             gbps = l.algorithmic_bytes() / (med * 1e-3) / 1e9
             table[f"{key}/{l.name}"] = {
-                "median_us": round(med * 1e3, 2), "p10_us": round(times[len(times) // 10] * 1e3, 2),
-                "p90_us": round(times[9 * len(times) // 10] * 1e3, 2), "gbps": round(gbps, 1),
+                "median_us": round(med * 1e3, 2), "min_us": round(times[0] * 1e3, 2),
+                "max_us": round(times[-1] * 1e3, 2), "gbps": round(gbps, 1),
                 "pct_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
                 "rows_per_s": round(l.rows / (med * 1e-3), 1), "bytes": l.algorithmic_bytes()}
             del keep
@@ -339,6 +360,117 @@ def per_kernel_table(lib, dev, stream):
     table["copy_256MB"] = {"median_us": round(med * 1e3, 2), "gbps": round(gbps, 1),
                            "pct_peak": round(100 * gbps / PEAK_HBM_GBPS, 2), "bytes": 2 * n}
     return table
+
+
+CALIB_BYTES = 128 << 20   # bytes read (and written) by one calibration copy launch
+
+
+def copy_calibration(lib, dev, stream, launches=8):
+    srcs = [torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev) for _ in range(4)]
+    dsts = [torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev) for _ in range(4)]
+    for i in range(launches):
+        check_status(lib.ditnorm_copy(_p(srcs[i % 4]), _p(dsts[i % 4]), CALIB_BYTES, stream), "copy")
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 output -> profiles/ (CPU only)
+# ---------------------------------------------------------------------------
+
+def _kernel_label(name):
+    """Launch kind of a demangled kernel name."""
+    if "ditnorm::row_kernel<" in name or "ditnorm::row_wave_kernel<" in name:
+        # row_kernel<NT, NV, RMS, GATED> / row_wave_kernel<NV, FULL, RMS, GATED, MODLDS>
+        args = name.split("_kernel<", 1)[1].split(">", 1)[0].split(",")
+        rms, gated = args[2].strip() == "true", args[3].strip() == "true"
+        return {(False, False): "ln_modulate", (False, True): "gated_ln_modulate",
+                (True, False): "rms_modulate", (True, True): "gated_rms_modulate"}[(rms, gated)]
+    for key, label in (("qk_kernel", "qk_layernorm"), ("wan_kernel", "rmsnorm_silu_bias"),
+                       ("epilogue_kernel", "conv_bias_epilogue"), ("copy_kernel", "copy")):
+        if f"ditnorm::{key}" in name:
+            return label
+    return None
+
+
+def _csvs(d, suffix):
+    import glob
+    return sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+
+
+def summarize_trace(d, name, cmd):
+    import csv
+    files = _csvs(d, "kernel_stats.csv")
+    if not files:
+        sys.exit(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(files[0])))
+    lines = [f"# rocprofv3 kernel trace summary: {name}", f"# command: {cmd}", "",
+             f"{'kernel':<70} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}"]
+    for r in rows:
+        n = r["Name"]
+        lab = _kernel_label(n)
+        short = (lab + "  " if lab else "") + n[:60]
+        lines.append(f"{short:<70} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>9.2f} "
+                     f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f} "
+                     f"{float(r['Percentage']):>6.2f}")
+    out = os.path.join(ROOT, "profiles", f"{name}.txt")
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(open(out).read())
+
+
+def _pmc_means(d, counter):
+    """{kernel label: mean counter value (KiB) per dispatch} from counter_collection.csv."""
+    import csv
+    files = _csvs(d, "counter_collection.csv")
+    if not files:
+        sys.exit(f"no counter_collection.csv under {d}")
+    acc = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") != counter:
+                continue
+            lab = _kernel_label(r["Kernel_Name"])
+            if lab:
+                acc.setdefault(lab, []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, cmd):
+    fetch = _pmc_means(fetch_dir, "FETCH_SIZE")
+    write = _pmc_means(write_dir, "WRITE_SIZE")
+    w = WORKLOADS[workload]
+    f_cal = CALIB_BYTES / (fetch["copy"][0] * 1024.0)
+    w_cal = CALIB_BYTES / (write["copy"][0] * 1024.0)
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        rec = {"kernels": {}}
+    lines = [f"# HBM traffic per launch from rocprofv3 counters: {workload}",
+             f"# command (two runs, --pmc FETCH_SIZE then --pmc WRITE_SIZE): {cmd}",
+             f"# calibration: a plain 16-byte copy of {CALIB_BYTES} bytes reads "
+             f"{fetch['copy'][0] * 1024:.0f} B by FETCH_SIZE (factor {f_cal:.4f}) and writes "
+             f"{write['copy'][0] * 1024:.0f} B by WRITE_SIZE (factor {w_cal:.4f})", "",
+             f"{'launch':<22} {'dispatches':>10} {'fetch_MB':>10} {'write_MB':>10} {'hbm_MB':>10} "
+             f"{'algo_MB':>10} {'ratio':>7}"]
+    for l in w.launches:
+        lab = "gated_rms_modulate" if (l.entry == "rms_modulate" and l.extra.get("gated")) else l.entry
+        if lab not in fetch or lab not in write:
+            continue
+        fb = fetch[lab][0] * 1024.0 * f_cal
+        wb = write[lab][0] * 1024.0 * w_cal
+        algo = l.algorithmic_bytes()
+        rec["kernels"][f"{workload}/{l.name}"] = {
+            "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+            "hbm_bytes_per_launch": round(fb + wb), "algorithmic_bytes": algo,
+            "ratio": round((fb + wb) / algo, 4), "calibration": {"fetch": f_cal, "write": w_cal},
+            "source_hash": kernel_source_hash(l.entry), "command": cmd}
+        lines.append(f"{l.name:<22} {fetch[lab][1]:>10} {fb / 1e6:>10.2f} {wb / 1e6:>10.2f} "
+                     f"{(fb + wb) / 1e6:>10.2f} {algo / 1e6:>10.2f} {(fb + wb) / algo:>7.3f}")
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+    out = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(open(out).read())
 
 
 if __name__ == "__main__":

@@ -59,6 +59,21 @@ __device__ __forceinline__ uint4 pack8(const float f[8]) {
   return v;
 }
 
+// Opaque to the optimiser: after this the packed value must be re-widened
+// where it is used again, instead of keeping every widened copy live across
+// a reduction (which would multiply the register footprint).
+__device__ __forceinline__ void launder(uint4 &v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
+// Index of this wavefront within its workgroup, as a wave-uniform (scalar)
+// value: the compiler cannot prove threadIdx.x / 64 uniform by itself, and
+// would otherwise keep row indices, batch tests and 64-bit address
+// arithmetic in vector registers behind exec-mask branches.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // --------------------------------------------------------------------------
 // global memory: 16-byte vectors
 // --------------------------------------------------------------------------
@@ -73,6 +88,27 @@ __device__ __forceinline__ float4 ld16f(const float *p) {
   return *reinterpret_cast<const float4 *>(p);
 }
 
+// Streaming variants for data touched exactly once (activations in and out):
+// the nontemporal hint keeps them from displacing reused lines (modulation
+// rows, weights) in the caches.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16s(const uint16_t *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  uint4 r;
+  r.x = v.x; r.y = v.y; r.z = v.z; r.w = v.w;
+  return r;
+}
+__device__ __forceinline__ void st16s(uint16_t *p, uint4 v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
+}
+// streaming (NT) or ordinary load, chosen at compile time
+template <bool NT>
+__device__ __forceinline__ uint4 ld16x(const uint16_t *p) {
+  if constexpr (NT) return ld16s(p);
+  else return ld16(p);
+}
+
 // --------------------------------------------------------------------------
 // DPP reductions in binary64
 // --------------------------------------------------------------------------
@@ -83,11 +119,13 @@ constexpr int DPP_QUAD_XOR2 = 0x4E;      // quad_perm(2,3,0,1)
 constexpr int DPP_ROW_MIRROR = 0x140;    // lane i <- lane 15-i within a row of 16
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <- lane 7-i within 8 lanes
 
+// Every control code used here reads a valid lane of the same row for every
+// lane, so bound_ctrl never applies and no "old" value has to be materialised.
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
   return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
@@ -152,6 +190,22 @@ __device__ __forceinline__ void lds_barrier() {
 // --------------------------------------------------------------------------
 // statistics -> the fp32 values the chain consumes
 // --------------------------------------------------------------------------
+
+// Single-pass moments.  For bf16 inputs S1 = sum(x) and S2 = sum(x^2) are
+// exact in binary64 (a bf16 square has 16 significant bits) unless a row
+// spans more than ~2^37 in magnitude, so the mean S1/N is the correctly
+// rounded binary64 quotient of the exact sum, and the biased variance
+// (S2 - S1*mean)/N loses only the cancellation of S1*mean against S2 (about
+// 1e-16 times (mean^2 + var)/var, relative).
+struct Moments {
+  double s1, s2;
+};
+
+__device__ __forceinline__ void accumulate(Moments &m, float x) {
+  const double d = (double)x;
+  m.s1 += d;
+  m.s2 = __builtin_fma(d, d, m.s2);
+}
 
 // rstd = fp32(1 / sqrt(v)), v = var + eps in binary64 (correctly rounded
 // binary64 square root and division, then one rounding to binary32).

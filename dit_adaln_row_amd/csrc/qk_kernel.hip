@@ -5,13 +5,17 @@
 // out = bf16(rstd * (x - mean)).
 //
 // The eager kernel spends a 128-thread block on each 128-element row (one
-// warp busy, three idle).  Here a 128-element row is 256 bytes = 16 lanes x
-// one 16-byte vector, so one wavefront instruction covers 4 rows and every
-// lane does useful work.  The reduction over a row is a 16-lane DPP
-// butterfly in binary64 (no LDS, no barrier).  Each wavefront keeps G row
-// groups (4G rows) in flight and issues the loads of its next 4G rows before
-// it reduces the current ones.  Rows are numbered q first, then k; a row
-// group may straddle the q/k boundary.
+// warp busy, three idle).  Here a 128-element row (256 bytes) is spread over
+// L lanes holding 16/L 16-byte vectors each (lane p of a row: vectors p,
+// p+L, ...), so one wavefront instruction covers 64/L rows and the per-row
+// finalisation (one binary64 square root and division) is shared by them.
+// L = 8 is used: every load instruction then reads whole 128-byte lines (with
+// L = 4 each instruction reads half lines, and the streaming hint lets the
+// other half be evicted before its turn), the row reduction is three DPP
+// steps.  Statistics are one pass of binary64 moments.  The grid is one-shot:
+// each wavefront owns G groups of 64/L consecutive rows and issues all their
+// loads before it reduces them.  Rows are numbered q first, then k; a group
+// may straddle the q/k boundary.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -20,15 +24,17 @@ namespace ditnorm {
 constexpr int QK_HEAD = 128;
 constexpr int QK_BLOCK = 256;
 
-template <int G>
+template <int L, int G, bool NTL>
 __global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
+  constexpr int VPL = 16 / L;   // 16-byte vectors per lane (a row is 16 vectors)
+  constexpr int RPW = 64 / L;   // rows per wavefront instruction
   const int lane = threadIdx.x & 63;
-  const int sub = lane >> 4;            // row within a group of 4
-  const int col = (lane & 15) * 8;      // first element of this lane's vector
+  const int sub = lane / L;     // row within a group of RPW
+  const int part = lane % L;    // lane within the row
   const int64_t total = a.rows_q + a.rows_k;
-  const int64_t waves = (int64_t)gridDim.x * (QK_BLOCK / 64);
-  const int64_t wave = (int64_t)blockIdx.x * (QK_BLOCK / 64) + (threadIdx.x >> 6);
-  const int64_t step = waves * 4 * G;
+  const int64_t wave = (int64_t)blockIdx.x * (QK_BLOCK / 64) + wave_id();
+  const int64_t base = wave * RPW * G;
+  if (base >= total) return;
 
   auto src = [&](int64_t r) -> const uint16_t * {
     return r < a.rows_q ? a.q + r * QK_HEAD : a.k + (r - a.rows_q) * QK_HEAD;
@@ -37,68 +43,72 @@ __global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
     return r < a.rows_q ? a.q_out + r * QK_HEAD : a.k_out + (r - a.rows_q) * QK_HEAD;
   };
 
-  int64_t base = wave * 4 * G;
-  if (base >= total) return;
-
-  uint4 nx[G];
-  auto load = [&](int64_t b0) {
+  uint4 xv[G][VPL];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int64_t r = b0 + 4 * g + sub;
+  for (int g = 0; g < G; ++g) {
+    const int64_t r = base + RPW * g + sub;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
       const uint4 zero = {0, 0, 0, 0};
-      nx[g] = r < total ? ld16(src(r) + col) : zero;
+      xv[g][k] = r < total ? ld16x<NTL>(src(r) + (part + L * k) * 8) : zero;
     }
-  };
-  load(base);
+  }
 
   const double eps = (double)a.eps;
-  for (; base < total; base += step) {
-    uint4 cx[G];
+  float mean_f[G], rstd_f[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) cx[g] = nx[g];
-    if (base + step < total) load(base + step);
-
+  for (int g = 0; g < G; ++g) {
+    Moments m = {0.0, 0.0};
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int64_t r = base + 4 * g + sub;
+    for (int k = 0; k < VPL; ++k) {
       float v[8];
-      unpack8(cx[g], v);
-      double s = 0.0;
+      unpack8(xv[g][k], v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += (double)v[e];
-      s = sum16(s);
-      const double mean_d = s * (1.0 / QK_HEAD);  // exact: 128 is a power of two
-      double m2 = 0.0;
+      for (int e = 0; e < 8; ++e) accumulate(m, v[e]);
+    }
+    const double s1 = group_sum<L>(m.s1), s2 = group_sum<L>(m.s2);
+    const double mean_d = s1 * (1.0 / QK_HEAD);  // exact: 128 is a power of two
+    const double var_d = __builtin_fmax(__builtin_fma(-s1, mean_d, s2) * (1.0 / QK_HEAD), 0.0);
+    mean_f[g] = (float)mean_d;
+    rstd_f[g] = rstd_from(var_d + eps);
+  }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double d = (double)v[e] - mean_d;
-        m2 = __builtin_fma(d, d, m2);
-      }
-      m2 = sum16(m2);
-      const float mean_f = (float)mean_d;
-      const float rstd_f = rstd_from(m2 * (1.0 / QK_HEAD) + eps);
-      float y[8];
+  for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = rstd_f * (v[e] - mean_f);
-      if (r < total) {
-        st16(dst(r) + col, pack8(y));
-        if ((lane & 15) == 0) {
-          if (a.mean_out) a.mean_out[r] = mean_f;
-          if (a.rstd_out) a.rstd_out[r] = rstd_f;
-        }
-      }
+    for (int k = 0; k < VPL; ++k) launder(xv[g][k]);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int64_t r = base + RPW * g + sub;
+    if (r >= total) continue;
+    uint16_t *d = dst(r);
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      float v[8], y[8];
+      unpack8(xv[g][k], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = rstd_f[g] * (v[e] - mean_f[g]);
+      st16s(d + (part + L * k) * 8, pack8(y));
+    }
+    if (part == 0) {
+      if (a.mean_out) a.mean_out[r] = mean_f[g];
+      if (a.rstd_out) a.rstd_out[r] = rstd_f[g];
     }
   }
 }
 
-hipError_t launch_qk(const QkArgs &a, const DeviceInfo &dev, hipStream_t stream) {
-  constexpr int G = 4;
+template <int L, int G, bool NTL>
+hipError_t launch_qk_cfg(const QkArgs &a, hipStream_t stream) {
   const int64_t total = a.rows_q + a.rows_k;
-  const int64_t groups = (total + 4 * G - 1) / (4 * G);          // wave-iterations
-  const int64_t blocks = (groups + QK_BLOCK / 64 - 1) / (QK_BLOCK / 64);
-  const int64_t grid = persistent_grid(qk_kernel<G>, QK_BLOCK, blocks, dev);
-  hipLaunchKernelGGL(qk_kernel<G>, dim3((unsigned)grid), dim3(QK_BLOCK), 0, stream, a);
+  const int64_t rows_per_block = (QK_BLOCK / 64) * (64 / L) * G;
+  const int64_t grid = (total + rows_per_block - 1) / rows_per_block;
+  hipLaunchKernelGGL((qk_kernel<L, G, NTL>), dim3((unsigned)grid), dim3(QK_BLOCK), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_qk(const QkArgs &a, const DeviceInfo &dev, hipStream_t stream) {
+  (void)dev;
+  // 8 lanes per row: each load instruction reads whole 128-byte lines
+  return launch_qk_cfg<8, 1, true>(a, stream);
 }
 
 }  // namespace ditnorm

@@ -224,6 +224,198 @@ __global__ __launch_bounds__(NT) void row_kernel(const RowArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// One wavefront per row (rows of up to 4096 columns)
+// ---------------------------------------------------------------------------
+//
+// A workgroup of four wavefronts owns four consecutive rows, one per
+// wavefront.  Lane l holds the row's 16-byte vectors l, l+64, ...,
+// l+64*(NV-1) as packed bf16 (NV*4 VGPRs).  The statistics are one pass of
+// binary64 moments (sum and sum of squares, exact for bf16 rows) reduced
+// across the wavefront with DPP, so a row needs no LDS traffic and no
+// barrier of its own.  The grid is one-shot -- rows/4 workgroups -- and the
+// register and LDS budgets are kept low enough that every row of a launch
+// the size of the pages' workloads is resident at once: all loads are issued
+// at the start and the launch streams at the rate HBM delivers.
+//
+// The modulation rows are converted once per workgroup: s1 = bf16(1 + scale)
+// and shift go to LDS as fp32, laid out so that the 64 lanes of a wavefront
+// read 64 consecutive 16-byte words (no bank conflicts).  A row whose batch
+// index differs from the workgroup's first row (batched modulation with a
+// batch boundary inside the workgroup) reads its modulation row directly.
+
+// fp32 slot of element half h (0: elements 0-3, 1: 4-7) of vector j.
+__device__ __forceinline__ int mod_slot(int j, int h) {
+  return (((j >> 6) * 2 + h) * 64 + (j & 63)) * 4;
+}
+
+template <int NV, bool FULL, bool RMS, bool GATED, bool MODLDS = true>
+__global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
+  __shared__ float4 lds_s1[MODLDS ? NV * 128 : 1], lds_sh[MODLDS ? NV * 128 : 1];
+  const int lane = threadIdx.x & 63;
+  const int cols = a.cols;
+  const int nvec = cols >> 3;
+  const int64_t row0 = (int64_t)blockIdx.x * 4;
+  const int64_t row = row0 + wave_id();
+  const bool live = row < a.rows;
+  const int64_t base = row * (int64_t)cols;
+  const uint4 zero = {0, 0, 0, 0};
+  auto ok = [&](int k) { return FULL || lane + 64 * k < nvec; };
+  auto col = [&](int k) { return (lane + 64 * k) * 8; };
+
+  // Modulation rows of the workgroup's first batch (cache-resident).  Issued
+  // before the row loads: loads return in order, so the LDS staging below
+  // waits only for these, while the row is still on its way from HBM.
+  constexpr int FILL = MODLDS ? (NV * 64 + 255) / 256 : 0;
+  const int64_t b0 = row0 / a.rows_per_batch;
+  uint4 fsc[FILL > 0 ? FILL : 1], fsh[FILL > 0 ? FILL : 1];
+#pragma unroll
+  for (int i = 0; i < FILL; ++i) {
+    const int j = threadIdx.x + 256 * i;
+    const bool in = j < nvec;
+    fsc[i] = in ? ld16(a.scale + b0 * a.mod_stride + j * 8) : zero;
+    fsh[i] = in ? ld16(a.shift + b0 * a.mod_stride + j * 8) : zero;
+  }
+
+  // this wavefront's row
+  uint4 xv[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) xv[k] = (live && ok(k)) ? ld16s(a.x + base + col(k)) : zero;
+  uint4 rv[GATED ? NV : 1];
+  if constexpr (GATED) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+      rv[k] = (live && ok(k)) ? ld16s(a.residual + base + col(k)) : zero;
+  }
+
+  // stage s1 = bf16(1 + scale) and shift in LDS as fp32
+#pragma unroll
+  for (int i = 0; i < FILL; ++i) {
+    const int j = threadIdx.x + 256 * i;
+    if (j >= NV * 64) break;
+    float sc[8], sh[8];
+    unpack8(fsc[i], sc);
+    unpack8(fsh[i], sh);
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      sc[e] = 1.0f + sc[e];
+      sc[e + 1] = 1.0f + sc[e + 1];
+      round2(sc[e], sc[e + 1]);
+    }
+    lds_s1[mod_slot(j, 0) / 4] = make_float4(sc[0], sc[1], sc[2], sc[3]);
+    lds_s1[mod_slot(j, 1) / 4] = make_float4(sc[4], sc[5], sc[6], sc[7]);
+    lds_sh[mod_slot(j, 0) / 4] = make_float4(sh[0], sh[1], sh[2], sh[3]);
+    lds_sh[mod_slot(j, 1) / 4] = make_float4(sh[4], sh[5], sh[6], sh[7]);
+  }
+  if constexpr (MODLDS) lds_barrier();
+  if (!live) return;  // whole wavefront; no barrier follows
+  const int64_t mo = (row / a.rows_per_batch) * a.mod_stride;
+  const bool mod_in_lds = MODLDS && (mo == b0 * a.mod_stride);
+
+  // gated residual: h = bf16(residual + bf16(gate * update)), stored
+  if constexpr (GATED) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float u[8], r[8], g[8];
+      unpack8(xv[k], u);
+      unpack8(rv[k], r);
+      unpack8(ok(k) ? ld16(a.gate + mo + col(k)) : zero, g);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float g0 = g[e] * u[e], g1 = g[e + 1] * u[e + 1];
+        round2(g0, g1);
+        u[e] = r[e] + g0;
+        u[e + 1] = r[e + 1] + g1;
+      }
+      xv[k] = pack8(u);
+      if (ok(k)) st16s(a.residual_out + base + col(k), xv[k]);
+    }
+  }
+
+  // statistics: one pass of binary64 moments (padding vectors hold zeros)
+  Moments m = {0.0, 0.0};
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    float v[8];
+    unpack8(xv[k], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) accumulate(m, v[e]);
+  }
+  const double n_d = (double)cols;
+  const double s2 = sum64(m.s2);
+  float mean_f = 0.0f, rstd_f;
+  if constexpr (RMS) {
+    rstd_f = rstd_from(s2 / n_d + (double)a.eps);
+  } else {
+    const double s1 = sum64(m.s1);
+    const double mean_d = s1 / n_d;
+    const double var_d = __builtin_fmax(__builtin_fma(-s1, mean_d, s2) / n_d, 0.0);
+    mean_f = (float)mean_d;
+    rstd_f = rstd_from(var_d + (double)a.eps);
+  }
+  if (lane == 0) {
+    if (a.mean_out) a.mean_out[row] = mean_f;
+    if (a.rstd_out) a.rstd_out[row] = rstd_f;
+  }
+
+  // normalise, modulate, store
+#pragma unroll
+  for (int k = 0; k < NV; ++k) launder(xv[k]);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    if (!ok(k)) continue;
+    float v[8], s1v[8], shv[8], y[8], o[8];
+    unpack8(xv[k], v);
+    if (mod_in_lds) {
+      const int j = lane + 64 * k;
+      const float4 a0 = lds_s1[mod_slot(j, 0) / 4], a1 = lds_s1[mod_slot(j, 1) / 4];
+      const float4 c0 = lds_sh[mod_slot(j, 0) / 4], c1 = lds_sh[mod_slot(j, 1) / 4];
+      s1v[0] = a0.x; s1v[1] = a0.y; s1v[2] = a0.z; s1v[3] = a0.w;
+      s1v[4] = a1.x; s1v[5] = a1.y; s1v[6] = a1.z; s1v[7] = a1.w;
+      shv[0] = c0.x; shv[1] = c0.y; shv[2] = c0.z; shv[3] = c0.w;
+      shv[4] = c1.x; shv[5] = c1.y; shv[6] = c1.z; shv[7] = c1.w;
+    } else {
+      unpack8(ld16(a.scale + mo + col(k)), s1v);
+      unpack8(ld16(a.shift + mo + col(k)), shv);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        s1v[e] = 1.0f + s1v[e];
+        s1v[e + 1] = 1.0f + s1v[e + 1];
+        round2(s1v[e], s1v[e + 1]);
+      }
+    }
+    if constexpr (RMS) {
+      float w[8];
+      unpack8(ld16(a.weight + col(k)), w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = (v[e] * rstd_f) * w[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = rstd_f * (v[e] - mean_f);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      round2(y[e], y[e + 1]);
+      float p0 = y[e] * s1v[e], p1 = y[e + 1] * s1v[e + 1];
+      round2(p0, p1);
+      o[e] = p0 + shv[e];
+      o[e + 1] = p1 + shv[e + 1];
+    }
+    st16s(a.out + base + col(k), pack8(o));
+    if (a.y_out) st16(a.y_out + base + col(k), pack8(y));
+  }
+}
+
+template <int NV, bool FULL, bool MODLDS = true>
+hipError_t launch_wave(const RowArgs &a, bool rms, bool gated, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
+  if (!rms && !gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, false, false, MODLDS>), grid, block, 0, stream, a);
+  if (!rms && gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, false, true, MODLDS>), grid, block, 0, stream, a);
+  if (rms && !gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, true, false, MODLDS>), grid, block, 0, stream, a);
+  if (rms && gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, true, true, MODLDS>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
 
@@ -252,6 +444,33 @@ static hipError_t launch_cfg(const RowArgs &a, bool rms, bool gated, const Devic
 hipError_t launch_row(const RowArgs &a, bool rms, bool gated, const DeviceInfo &dev,
                       hipStream_t stream) {
   const int nvec = a.cols / 8;
+  // Rows up to 4096 columns: one wavefront per row.  The gated sites stage
+  // the modulation rows in LDS (their extra residual stream leaves no
+  // registers for in-flight modulation loads); the plain sites read them per
+  // row from the caches, which measured faster than the workgroup barrier.
+  if (gated) {
+    switch (nvec) {
+      case 128: return launch_wave<2, true, true>(a, rms, gated, stream);
+      case 256: return launch_wave<4, true, true>(a, rms, gated, stream);
+      case 384: return launch_wave<6, true, true>(a, rms, gated, stream);
+      case 512: return launch_wave<8, true, true>(a, rms, gated, stream);
+      default: break;
+    }
+  } else {
+    switch (nvec) {
+      case 128: return launch_wave<2, true, false>(a, rms, gated, stream);
+      case 256: return launch_wave<4, true, false>(a, rms, gated, stream);
+      case 384: return launch_wave<6, true, false>(a, rms, gated, stream);
+      case 512: return launch_wave<8, true, false>(a, rms, gated, stream);
+      default: break;
+    }
+  }
+  if (nvec <= 64) return launch_wave<1, false>(a, rms, gated, stream);
+  if (nvec <= 128) return launch_wave<2, false>(a, rms, gated, stream);
+  if (nvec <= 256) return launch_wave<4, false>(a, rms, gated, stream);
+  if (nvec <= 384) return launch_wave<6, false>(a, rms, gated, stream);
+  if (nvec <= 512) return launch_wave<8, false>(a, rms, gated, stream);
+  // wider rows: one workgroup per row
   // (threads, vectors per thread): the row must fit NT*NV vectors; prefer
   // exact fits and 2-4 vectors (16-32 values) per thread.
   if (nvec <= 64) return launch_cfg<64, 1>(a, rms, gated, dev, stream);

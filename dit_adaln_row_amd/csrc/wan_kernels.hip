@@ -14,16 +14,17 @@
 // l, l+L, ...), so one wavefront instruction covers 64/L pixels and the load
 // of a group of pixels is one contiguous stretch of memory.  C = 96 uses
 // L = 4 (16 pixels per instruction), C = 384 uses L = 16 (4 pixels); other
-// widths use a whole wavefront per pixel.  The channel-indexed bias (already
-// rounded to bf16) and gamma stay in VGPRs for the whole kernel, the sum of
-// squares is a DPP butterfly over the L lanes in binary64, and each
-// wavefront prefetches its next pixel group while it computes the current one.
+// widths use a whole wavefront per pixel.  The sum of squares is a DPP
+// butterfly over the L lanes in binary64, the biased input is kept in fp32
+// registers between the two passes, and the grid is one-shot: each wavefront
+// issues the loads of its G pixel groups first.
 //
-// SiLU(t) = t * sigmoid(t) with sigmoid from e = exp(-|t|) (never overflows):
-// sigmoid = 1/(1+e) for t >= 0 and e/(1+e) for t < 0, using the hardware
-// exp2 and reciprocal.  Its relative error (a few 1e-7) is far below half a
-// bf16 ulp (2^-9), so the rounded result is within one bf16 ulp of the
-// correctly rounded SiLU.
+// SiLU(t) = t / (1 + e^-t) with the hardware exp2 and reciprocal: relative
+// error a few 1e-7, far below half a bf16 ulp (2^-9), so the rounded result is
+// within one bf16 ulp of the correctly rounded SiLU.  That form needs e^-t and
+// its reciprocal to stay normal, i.e. t >= -87; a wavefront that meets a
+// smaller t (never, for normalised activations) redoes its pixels with the
+// sign-split form t * e^t / (1 + e^t) and the denormal-safe exp2.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -31,22 +32,33 @@ namespace ditnorm {
 
 constexpr int WAN_BLOCK = 256;
 
-__device__ __forceinline__ float silu_f32(float t) {
-  const float e = __builtin_exp2f(-__builtin_fabsf(t) * 1.4426950408889634f);
+constexpr float kLog2e = 1.4426950408889634f;
+
+// t >= -87 (e^-t below the binary32 overflow, its reciprocal normal)
+__device__ __forceinline__ float silu_fast(float t) {
+  const float e = __builtin_amdgcn_exp2f(t * -kLog2e);
+  return t * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// any t: e = e^-|t| never overflows; subnormal e^-|t| handled by exp2f
+__device__ __forceinline__ float silu_safe(float t) {
+  const float e = __builtin_exp2f(-__builtin_fabsf(t) * kLog2e);
   const float r = __builtin_amdgcn_rcpf(1.0f + e);
   const float s = t >= 0.0f ? r : e * r;
   return t * s;
 }
 
-template <int L, int VPL, bool BIAS, bool EXACT>
+template <int L, int VPL, bool BIAS, bool EXACT, int G, bool NTL = true>
 __global__ __launch_bounds__(WAN_BLOCK) void wan_kernel(const WanArgs a) {
   constexpr int RPW = 64 / L;  // pixels per wavefront instruction
-  constexpr int G = (RPW >= 16) ? 1 : 2;  // pixel groups in flight per wavefront
   const int lane = threadIdx.x & 63;
   const int sub = lane / L;
   const int part = lane % L;
   const int C = a.channels;
   const int nvec = C >> 3;
+  const int64_t wave = (int64_t)blockIdx.x * (WAN_BLOCK / 64) + wave_id();
+  const int64_t base = wave * RPW * G;
+  if (base >= a.rows) return;
 
   int vch[VPL];
   bool ok[VPL];
@@ -56,129 +68,134 @@ __global__ __launch_bounds__(WAN_BLOCK) void wan_kernel(const WanArgs a) {
     ok[k] = EXACT || (part + k * L) < nvec;
   }
 
-  // per-lane channel constants
-  float bq[BIAS ? VPL : 1][8], gm[VPL][8];
+  // the pixels' loads first
+  uint4 xv[G][VPL];
 #pragma unroll
-  for (int k = 0; k < VPL; ++k) {
+  for (int g = 0; g < G; ++g) {
+    const int64_t r = base + g * RPW + sub;
+    const uint16_t *p = a.x + r * (int64_t)C;
 #pragma unroll
-    for (int e = 0; e < 8; e += 4) {
-      const float4 zero = {0.f, 0.f, 0.f, 0.f};
-      const float4 gv = ok[k] ? ld16f(a.gamma + vch[k] + e) : zero;
-      gm[k][e] = gv.x; gm[k][e + 1] = gv.y; gm[k][e + 2] = gv.z; gm[k][e + 3] = gv.w;
-      if constexpr (BIAS) {
-        const float4 bv = ok[k] ? ld16f(a.bias + vch[k] + e) : zero;
-        bq[k][e] = bv.x; bq[k][e + 1] = bv.y; bq[k][e + 2] = bv.z; bq[k][e + 3] = bv.w;
-        round2(bq[k][e], bq[k][e + 1]);
-        round2(bq[k][e + 2], bq[k][e + 3]);
-      }
+    for (int k = 0; k < VPL; ++k) {
+      const uint4 zero = {0, 0, 0, 0};
+      xv[g][k] = (r < a.rows && ok[k]) ? ld16x<NTL>(p + vch[k]) : zero;
     }
   }
 
-  const int64_t waves = (int64_t)gridDim.x * (WAN_BLOCK / 64);
-  const int64_t wave = (int64_t)blockIdx.x * (WAN_BLOCK / 64) + (threadIdx.x >> 6);
-  const int64_t per_iter = (int64_t)RPW * G;
-  const int64_t step = waves * per_iter;
-  int64_t base = wave * per_iter;
-  if (base >= a.rows) return;
-
-  uint4 nx[G][VPL];
-  auto load = [&](int64_t b0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int64_t r = b0 + g * RPW + sub;
-      const uint16_t *p = a.x + r * (int64_t)C;
-#pragma unroll
-      for (int k = 0; k < VPL; ++k) {
-        const uint4 zero = {0, 0, 0, 0};
-        nx[g][k] = (r < a.rows && ok[k]) ? ld16(p + vch[k]) : zero;
-      }
-    }
-  };
-  load(base);
-
+  // xb = bf16(x + bf16(bias)) in fp32 registers; sum of squares per pixel
   const double n_d = (double)C;
   const double eps = (double)a.eps;
-  for (; base < a.rows; base += step) {
-    uint4 cx[G][VPL];
+  float xb[G][VPL][8];
+  float rstd_f[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+  for (int g = 0; g < G; ++g) {
+    double s2 = 0.0;
 #pragma unroll
-      for (int k = 0; k < VPL; ++k) cx[g][k] = nx[g][k];
-    if (base + step < a.rows) load(base + step);
-
+    for (int k = 0; k < VPL; ++k) {
+      unpack8(xv[g][k], xb[g][k]);
+      if constexpr (BIAS) {
+        const float4 zero = {0.f, 0.f, 0.f, 0.f};
+        const float4 b0 = ok[k] ? ld16f(a.bias + vch[k]) : zero;
+        const float4 b1 = ok[k] ? ld16f(a.bias + vch[k] + 4) : zero;
+        float bq[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int64_t r = base + g * RPW + sub;
-      const bool live = r < a.rows;
-      float v[VPL][8];
-      double s2 = 0.0;
-#pragma unroll
-      for (int k = 0; k < VPL; ++k) {
-        unpack8(cx[g][k], v[k]);
-        if constexpr (BIAS) {
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            float b0 = v[k][e] + bq[k][e], b1 = v[k][e + 1] + bq[k][e + 1];
-            round2(b0, b1);
-            v[k][e] = b0;
-            v[k][e + 1] = b1;
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const double d = (double)v[k][e];
-          s2 = ok[k] ? __builtin_fma(d, d, s2) : s2;
+        for (int e = 0; e < 8; e += 2) {
+          round2(bq[e], bq[e + 1]);
+          xb[g][k][e] = xb[g][k][e] + bq[e];
+          xb[g][k][e + 1] = xb[g][k][e + 1] + bq[e + 1];
+          round2(xb[g][k][e], xb[g][k][e + 1]);
         }
       }
-      s2 = group_sum<L>(s2);
-      const float rstd_f = rstd_from(s2 / n_d + eps);
-      const int64_t off = r * (int64_t)C;
 #pragma unroll
-      for (int k = 0; k < VPL; ++k) {
+      for (int e = 0; e < 8; ++e) {
+        const double d = (double)xb[g][k][e];
+        s2 = __builtin_fma(d, d, s2);  // padding vectors are zero
+      }
+    }
+    rstd_f[g] = rstd_from(group_sum<L>(s2) / n_d + eps);
+  }
+
+  // t = (xb * rstd) * gamma; out = bf16(SiLU(t))
+  float tmin = 0.0f;
+  uint4 ov[G][VPL];
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const float4 zero = {0.f, 0.f, 0.f, 0.f};
+    const float4 g0 = ok[k] ? ld16f(a.gamma + vch[k]) : zero;
+    const float4 g1 = ok[k] ? ld16f(a.gamma + vch[k] + 4) : zero;
+    const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float t = xb[g][k][e] * rstd_f[g];
+        t = t * gm[e];
+        tmin = __builtin_fminf(tmin, t);
+        o[e] = silu_fast(t);
+      }
+      ov[g][k] = pack8(o);
+    }
+  }
+  if (__builtin_expect(__any(tmin < -87.0f), 0)) {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const float4 zero = {0.f, 0.f, 0.f, 0.f};
+      const float4 g0 = ok[k] ? ld16f(a.gamma + vch[k]) : zero;
+      const float4 g1 = ok[k] ? ld16f(a.gamma + vch[k] + 4) : zero;
+      const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float t = v[k][e] * rstd_f;
-          t = t * gm[k][e];
-          o[e] = silu_f32(t);
+          float t = xb[g][k][e] * rstd_f[g];
+          t = t * gm[e];
+          o[e] = silu_safe(t);
         }
-        if (live && ok[k]) {
-          st16(a.out + off + vch[k], pack8(o));
-          if (a.xb_out) st16(a.xb_out + off + vch[k], pack8(v[k]));
-        }
+        ov[g][k] = pack8(o);
       }
-      if (live && part == 0 && a.rstd_out) a.rstd_out[r] = rstd_f;
     }
+  }
+
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int64_t r = base + g * RPW + sub;
+    if (r >= a.rows) continue;
+    const int64_t off = r * (int64_t)C;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      if (!ok[k]) continue;
+      st16s(a.out + off + vch[k], ov[g][k]);
+      if (a.xb_out) st16(a.xb_out + off + vch[k], pack8(xb[g][k]));
+    }
+    if (part == 0 && a.rstd_out) a.rstd_out[r] = rstd_f[g];
   }
 }
 
-template <int L, int VPL, bool EXACT>
-static hipError_t launch_wan_cfg(const WanArgs &a, const DeviceInfo &dev, hipStream_t stream) {
+template <int L, int VPL, bool EXACT, int G, bool NTL = true>
+hipError_t launch_wan_cfg(const WanArgs &a, hipStream_t stream) {
   constexpr int RPW = 64 / L;
-  constexpr int G = (RPW >= 16) ? 1 : 2;
-  const int64_t iters = (a.rows + RPW * G - 1) / (RPW * G);
-  const int64_t blocks = (iters + WAN_BLOCK / 64 - 1) / (WAN_BLOCK / 64);
-  if (a.bias) {
-    const int64_t grid = persistent_grid(wan_kernel<L, VPL, true, EXACT>, WAN_BLOCK, blocks, dev);
-    hipLaunchKernelGGL((wan_kernel<L, VPL, true, EXACT>), dim3((unsigned)grid), dim3(WAN_BLOCK),
-                       0, stream, a);
-  } else {
-    const int64_t grid = persistent_grid(wan_kernel<L, VPL, false, EXACT>, WAN_BLOCK, blocks, dev);
-    hipLaunchKernelGGL((wan_kernel<L, VPL, false, EXACT>), dim3((unsigned)grid), dim3(WAN_BLOCK),
-                       0, stream, a);
-  }
+  const int64_t per_block = (int64_t)(WAN_BLOCK / 64) * RPW * G;
+  const dim3 grid((unsigned)((a.rows + per_block - 1) / per_block)), block(WAN_BLOCK);
+  if (a.bias)
+    hipLaunchKernelGGL((wan_kernel<L, VPL, true, EXACT, G, NTL>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((wan_kernel<L, VPL, false, EXACT, G, NTL>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_wan(const WanArgs &a, const DeviceInfo &dev, hipStream_t stream) {
+  (void)dev;
   switch (a.channels) {
-    case 96: return launch_wan_cfg<4, 3, true>(a, dev, stream);
-    case 128: return launch_wan_cfg<16, 1, true>(a, dev, stream);
-    case 192: return launch_wan_cfg<8, 3, true>(a, dev, stream);
-    case 256: return launch_wan_cfg<16, 2, true>(a, dev, stream);
-    case 384: return launch_wan_cfg<16, 3, true>(a, dev, stream);
-    case 512: return launch_wan_cfg<16, 4, true>(a, dev, stream);
-    default: return launch_wan_cfg<64, 8, false>(a, dev, stream);  // any C <= 4096
+    // C = 96: a load instruction covers 64 of each pixel's 192 bytes; keep
+    // the lines cacheable so the other instructions find them
+    case 96: return launch_wan_cfg<4, 3, true, 2, false>(a, stream);
+    case 128: return launch_wan_cfg<4, 4, true, 1>(a, stream);
+    case 192: return launch_wan_cfg<8, 3, true, 1>(a, stream);
+    case 256: return launch_wan_cfg<8, 4, true, 1>(a, stream);
+    case 384: return launch_wan_cfg<16, 3, true, 2>(a, stream);
+    case 512: return launch_wan_cfg<16, 4, true, 1>(a, stream);
+    default: return launch_wan_cfg<64, 8, false, 1>(a, stream);  // any C <= 4096
   }
 }
 
