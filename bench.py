@@ -256,6 +256,7 @@ def main():
         sys.exit("bench.py needs a GPU")
 
     lib = dn.load()
+    log("[bench] source_hashes " + json.dumps({e: kernel_source_hash(e) for e in KERNEL_SOURCES}))
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev).cuda_stream
 
@@ -435,9 +436,23 @@ def _pmc_means(d, counter):
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
+def _run_hashes(run_dir):
+    """Kernel-source hashes the profiled bench run printed (in <run_dir>.log)."""
+    try:
+        for line in open(run_dir.rstrip("/") + ".log"):
+            if "[bench] source_hashes " in line:
+                return json.loads(line.split("[bench] source_hashes ", 1)[1])
+    except OSError:
+        pass
+    sys.exit(f"{run_dir}.log has no source_hashes line: cannot tell which kernels were measured")
+
+
 def summarize_pmc(fetch_dir, write_dir, workload, cmd):
     fetch = _pmc_means(fetch_dir, "FETCH_SIZE")
     write = _pmc_means(write_dir, "WRITE_SIZE")
+    hashes = _run_hashes(fetch_dir)
+    if hashes != _run_hashes(write_dir):
+        sys.exit("the FETCH and WRITE runs measured different kernel sources")
     w = WORKLOADS[workload]
     f_cal = CALIB_BYTES / (fetch["copy"][0] * 1024.0)
     w_cal = CALIB_BYTES / (write["copy"][0] * 1024.0)
@@ -463,7 +478,7 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd):
             "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
             "hbm_bytes_per_launch": round(fb + wb), "algorithmic_bytes": algo,
             "ratio": round((fb + wb) / algo, 4), "calibration": {"fetch": f_cal, "write": w_cal},
-            "source_hash": kernel_source_hash(l.entry), "command": cmd}
+            "source_hash": hashes[l.entry], "command": cmd}
         lines.append(f"{l.name:<22} {fetch[lab][1]:>10} {fb / 1e6:>10.2f} {wb / 1e6:>10.2f} "
                      f"{(fb + wb) / 1e6:>10.2f} {algo / 1e6:>10.2f} {(fb + wb) / algo:>7.3f}")
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)

@@ -248,8 +248,27 @@ __device__ __forceinline__ int mod_slot(int j, int h) {
   return (((j >> 6) * 2 + h) * 64 + (j & 63)) * 4;
 }
 
-template <int NV, bool FULL, bool RMS, bool GATED, bool MODLDS = true>
+// How a row kernel obtains its modulation operands (s1 = bf16(1+scale),
+// shift, and the RMS weight / the gate where used).
+enum ModMode : int {
+  MOD_SERIAL = 0,  // per 16-byte vector, from the caches, as each is needed
+  MOD_LDS = 1,     // s1 / shift staged per workgroup in LDS (fp32); weight / gate as SERIAL
+  MOD_BATCH = 2,   // all of a row's operands in one batch of loads: the gate with the
+                   // row, scale / shift / weight after the statistics, before any store
+  MOD_EARLY = 3,   // all of a row's operands loaded together with the row
+};
+
+// Pointer the optimiser cannot see through: loads through it stay after
+// this point in program order.
+template <typename T>
+__device__ __forceinline__ const T *pin(const T *p) {
+  asm volatile("" : "+s"(p));
+  return p;
+}
+
+template <int NV, bool FULL, bool RMS, bool GATED, int MODE = MOD_LDS>
 __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
+  constexpr bool MODLDS = MODE == MOD_LDS;
   __shared__ float4 lds_s1[MODLDS ? NV * 128 : 1], lds_sh[MODLDS ? NV * 128 : 1];
   const int lane = threadIdx.x & 63;
   const int cols = a.cols;
@@ -286,6 +305,24 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
     for (int k = 0; k < NV; ++k)
       rv[k] = (live && ok(k)) ? ld16s(a.residual + base + col(k)) : zero;
   }
+  const int64_t mo = (row / a.rows_per_batch) * a.mod_stride;
+
+  // batched / early operand loads
+  constexpr bool HOLD = MODE == MOD_BATCH || MODE == MOD_EARLY;
+  uint4 mg[GATED && HOLD ? NV : 1], ms[HOLD ? NV : 1], mh[HOLD ? NV : 1], mw[RMS && HOLD ? NV : 1];
+  auto load_mod = [&](const uint16_t *sc, const uint16_t *sh, const uint16_t *w) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      ms[k] = ok(k) ? ld16(sc + mo + col(k)) : zero;
+      mh[k] = ok(k) ? ld16(sh + mo + col(k)) : zero;
+      if constexpr (RMS) mw[k] = ok(k) ? ld16(w + col(k)) : zero;
+    }
+  };
+  if constexpr (GATED && HOLD) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) mg[k] = ok(k) ? ld16(a.gate + mo + col(k)) : zero;
+  }
+  if constexpr (MODE == MOD_EARLY) load_mod(a.scale, a.shift, a.weight);
 
   // stage s1 = bf16(1 + scale) and shift in LDS as fp32
 #pragma unroll
@@ -308,7 +345,6 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
   }
   if constexpr (MODLDS) lds_barrier();
   if (!live) return;  // whole wavefront; no barrier follows
-  const int64_t mo = (row / a.rows_per_batch) * a.mod_stride;
   const bool mod_in_lds = MODLDS && (mo == b0 * a.mod_stride);
 
   // gated residual: h = bf16(residual + bf16(gate * update)), stored
@@ -318,7 +354,8 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
       float u[8], r[8], g[8];
       unpack8(xv[k], u);
       unpack8(rv[k], r);
-      unpack8(ok(k) ? ld16(a.gate + mo + col(k)) : zero, g);
+      if constexpr (HOLD) unpack8(mg[k], g);
+      else unpack8(ok(k) ? ld16(a.gate + mo + col(k)) : zero, g);
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         float g0 = g[e] * u[e], g1 = g[e + 1] * u[e + 1];
@@ -356,6 +393,7 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
     if (a.mean_out) a.mean_out[row] = mean_f;
     if (a.rstd_out) a.rstd_out[row] = rstd_f;
   }
+  if constexpr (MODE == MOD_BATCH) load_mod(pin(a.scale), pin(a.shift), pin(a.weight));
 
   // normalise, modulate, store
 #pragma unroll
@@ -374,8 +412,13 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
       shv[0] = c0.x; shv[1] = c0.y; shv[2] = c0.z; shv[3] = c0.w;
       shv[4] = c1.x; shv[5] = c1.y; shv[6] = c1.z; shv[7] = c1.w;
     } else {
-      unpack8(ld16(a.scale + mo + col(k)), s1v);
-      unpack8(ld16(a.shift + mo + col(k)), shv);
+      if constexpr (HOLD) {
+        unpack8(ms[k], s1v);
+        unpack8(mh[k], shv);
+      } else {
+        unpack8(ld16(a.scale + mo + col(k)), s1v);
+        unpack8(ld16(a.shift + mo + col(k)), shv);
+      }
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         s1v[e] = 1.0f + s1v[e];
@@ -385,7 +428,8 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
     }
     if constexpr (RMS) {
       float w[8];
-      unpack8(ld16(a.weight + col(k)), w);
+      if constexpr (HOLD) unpack8(mw[k], w);
+      else unpack8(ld16(a.weight + col(k)), w);
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] = (v[e] * rstd_f) * w[e];
     } else {
@@ -405,13 +449,13 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
   }
 }
 
-template <int NV, bool FULL, bool MODLDS = true>
+template <int NV, bool FULL, int MODE = MOD_LDS>
 hipError_t launch_wave(const RowArgs &a, bool rms, bool gated, hipStream_t stream) {
   const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
-  if (!rms && !gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, false, false, MODLDS>), grid, block, 0, stream, a);
-  if (!rms && gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, false, true, MODLDS>), grid, block, 0, stream, a);
-  if (rms && !gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, true, false, MODLDS>), grid, block, 0, stream, a);
-  if (rms && gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, true, true, MODLDS>), grid, block, 0, stream, a);
+  if (!rms && !gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, false, false, MODE>), grid, block, 0, stream, a);
+  if (!rms && gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, false, true, MODE>), grid, block, 0, stream, a);
+  if (rms && !gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, true, false, MODE>), grid, block, 0, stream, a);
+  if (rms && gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, true, true, MODE>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -450,18 +494,18 @@ hipError_t launch_row(const RowArgs &a, bool rms, bool gated, const DeviceInfo &
   // row from the caches, which measured faster than the workgroup barrier.
   if (gated) {
     switch (nvec) {
-      case 128: return launch_wave<2, true, true>(a, rms, gated, stream);
-      case 256: return launch_wave<4, true, true>(a, rms, gated, stream);
-      case 384: return launch_wave<6, true, true>(a, rms, gated, stream);
-      case 512: return launch_wave<8, true, true>(a, rms, gated, stream);
+      case 128: return launch_wave<2, true, MOD_LDS>(a, rms, gated, stream);
+      case 256: return launch_wave<4, true, MOD_LDS>(a, rms, gated, stream);
+      case 384: return launch_wave<6, true, MOD_LDS>(a, rms, gated, stream);
+      case 512: return launch_wave<8, true, MOD_LDS>(a, rms, gated, stream);
       default: break;
     }
   } else {
     switch (nvec) {
-      case 128: return launch_wave<2, true, false>(a, rms, gated, stream);
-      case 256: return launch_wave<4, true, false>(a, rms, gated, stream);
-      case 384: return launch_wave<6, true, false>(a, rms, gated, stream);
-      case 512: return launch_wave<8, true, false>(a, rms, gated, stream);
+      case 128: return launch_wave<2, true, MOD_SERIAL>(a, rms, gated, stream);
+      case 256: return launch_wave<4, true, MOD_SERIAL>(a, rms, gated, stream);
+      case 384: return launch_wave<6, true, MOD_SERIAL>(a, rms, gated, stream);
+      case 512: return launch_wave<8, true, MOD_SERIAL>(a, rms, gated, stream);
       default: break;
     }
   }

@@ -11,11 +11,13 @@
 //
 // Work layout for rmsnorm_silu_bias: a pixel row of C channels is split over
 // L lanes of a wavefront, each lane holding VPL 16-byte vectors (vectors
-// l, l+L, ...), so one wavefront instruction covers 64/L pixels and the load
-// of a group of pixels is one contiguous stretch of memory.  C = 96 uses
-// L = 4 (16 pixels per instruction), C = 384 uses L = 16 (4 pixels); other
+// l, l+L, ...), so one wavefront instruction covers 64/L pixels.  C = 384
+// uses L = 16 (4 pixels per instruction, 256 contiguous bytes of each); C = 96
+// uses L = 4 (16 pixels per instruction) and moves each 16-pixel group
+// through the wavefront's own LDS slice, so that global loads and stores are
+// three whole contiguous kilobytes instead of a quarter of every line; other
 // widths use a whole wavefront per pixel.  The sum of squares is a DPP
-// butterfly over the L lanes in binary64, the biased input is kept in fp32
+// butterfly over the L lanes in binary64, the biased input stays in fp32
 // registers between the two passes, and the grid is one-shot: each wavefront
 // issues the loads of its G pixel groups first.
 //
@@ -48,9 +50,13 @@ __device__ __forceinline__ float silu_safe(float t) {
   return t * s;
 }
 
-template <int L, int VPL, bool BIAS, bool EXACT, int G, bool NTL = true>
+template <int L, int VPL, bool BIAS, bool EXACT, int G, bool NTL = true, bool TRANS = false>
 __global__ __launch_bounds__(WAN_BLOCK) void wan_kernel(const WanArgs a) {
   constexpr int RPW = 64 / L;  // pixels per wavefront instruction
+  // TRANS: a group of RPW pixels is VPL * 1 KB of contiguous memory; load it
+  // with VPL fully contiguous instructions into this wavefront's LDS slice
+  // and read the per-pixel lane layout back from there.
+  __shared__ uint4 stage[TRANS ? (WAN_BLOCK / 64) * G * VPL * 64 : 1];
   const int lane = threadIdx.x & 63;
   const int sub = lane / L;
   const int part = lane % L;
@@ -70,14 +76,41 @@ __global__ __launch_bounds__(WAN_BLOCK) void wan_kernel(const WanArgs a) {
 
   // the pixels' loads first
   uint4 xv[G][VPL];
+  if constexpr (TRANS) {
+    static_assert(EXACT, "contiguous staging needs C == 8 * L * VPL");
+    uint4 *slice = stage + (threadIdx.x >> 6) * G * VPL * 64;
+    const int64_t vec_end = a.rows * (int64_t)(C >> 3);
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int64_t r = base + g * RPW + sub;
-    const uint16_t *p = a.x + r * (int64_t)C;
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-      const uint4 zero = {0, 0, 0, 0};
-      xv[g][k] = (r < a.rows && ok[k]) ? ld16x<NTL>(p + vch[k]) : zero;
+      for (int k = 0; k < VPL; ++k) {
+        const int64_t v = (base + g * RPW) * (int64_t)(C >> 3) + k * 64 + lane;  // 16-byte vector index
+        const uint4 zero = {0, 0, 0, 0};
+        xv[g][k] = v < vec_end ? ld16x<NTL>(a.x + v * 8) : zero;
+      }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int k = 0; k < VPL; ++k) slice[(g * VPL + k) * 64 + lane] = xv[g][k];
+    // lanes of one wavefront exchange through LDS: order the writes before
+    // the reads for the compiler (the hardware runs them in program order)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int k = 0; k < VPL; ++k) xv[g][k] = slice[g * VPL * 64 + sub * L * VPL + part + L * k];
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int64_t r = base + g * RPW + sub;
+      const uint16_t *p = a.x + r * (int64_t)C;
+#pragma unroll
+      for (int k = 0; k < VPL; ++k) {
+        const uint4 zero = {0, 0, 0, 0};
+        xv[g][k] = (r < a.rows && ok[k]) ? ld16x<NTL>(p + vch[k]) : zero;
+      }
     }
   }
 
@@ -157,6 +190,28 @@ __global__ __launch_bounds__(WAN_BLOCK) void wan_kernel(const WanArgs a) {
     }
   }
 
+  if constexpr (TRANS) {
+    // outputs back through the LDS slice, then VPL contiguous stores per group
+    uint4 *slice = stage + (threadIdx.x >> 6) * G * VPL * 64;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int k = 0; k < VPL; ++k) slice[g * VPL * 64 + sub * L * VPL + part + L * k] = ov[g][k];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    const int64_t vec_end = a.rows * (int64_t)(C >> 3);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int k = 0; k < VPL; ++k) {
+        const int64_t v = (base + g * RPW) * (int64_t)(C >> 3) + k * 64 + lane;
+        if (v < vec_end) st16s(a.out + v * 8, slice[(g * VPL + k) * 64 + lane]);
+      }
+  }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int64_t r = base + g * RPW + sub;
@@ -165,32 +220,33 @@ __global__ __launch_bounds__(WAN_BLOCK) void wan_kernel(const WanArgs a) {
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       if (!ok[k]) continue;
-      st16s(a.out + off + vch[k], ov[g][k]);
+      if constexpr (!TRANS) st16s(a.out + off + vch[k], ov[g][k]);
       if (a.xb_out) st16(a.xb_out + off + vch[k], pack8(xb[g][k]));
     }
     if (part == 0 && a.rstd_out) a.rstd_out[r] = rstd_f[g];
   }
 }
 
-template <int L, int VPL, bool EXACT, int G, bool NTL = true>
+template <int L, int VPL, bool EXACT, int G, bool NTL = true, bool TRANS = false>
 hipError_t launch_wan_cfg(const WanArgs &a, hipStream_t stream) {
   constexpr int RPW = 64 / L;
   const int64_t per_block = (int64_t)(WAN_BLOCK / 64) * RPW * G;
   const dim3 grid((unsigned)((a.rows + per_block - 1) / per_block)), block(WAN_BLOCK);
   if (a.bias)
-    hipLaunchKernelGGL((wan_kernel<L, VPL, true, EXACT, G, NTL>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((wan_kernel<L, VPL, true, EXACT, G, NTL, TRANS>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((wan_kernel<L, VPL, false, EXACT, G, NTL>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((wan_kernel<L, VPL, false, EXACT, G, NTL, TRANS>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_wan(const WanArgs &a, const DeviceInfo &dev, hipStream_t stream) {
   (void)dev;
   switch (a.channels) {
-    // C = 96: a load instruction covers 64 of each pixel's 192 bytes; keep
-    // the lines cacheable so the other instructions find them
-    case 96: return launch_wan_cfg<4, 3, true, 2, false>(a, stream);
-    case 128: return launch_wan_cfg<4, 4, true, 1>(a, stream);
+    // C = 96 / 128: four lanes per pixel would make each instruction touch
+    // part of every cache line of 16 pixels; the group is moved through the
+    // wavefront's LDS slice instead, as whole contiguous lines
+    case 96: return launch_wan_cfg<4, 3, true, 1, true, true>(a, stream);
+    case 128: return launch_wan_cfg<4, 4, true, 1, true, true>(a, stream);
     case 192: return launch_wan_cfg<8, 3, true, 1>(a, stream);
     case 256: return launch_wan_cfg<8, 4, true, 1>(a, stream);
     case 384: return launch_wan_cfg<16, 3, true, 2>(a, stream);

@@ -50,6 +50,11 @@ def _load():
         sig = {
             "oracle_round_f32_to_bf16": [_f32p, _u16p, _i64],
             "oracle_round_f64_to_bf16": [_f64p, _u16p, _i64],
+            "oracle_round_f32_to_f16": [_f32p, _u16p, _i64],
+            "oracle_widen_f16": [_u16p, _f32p, _i64],
+            "oracle_modulate_dt": [_u16p, _u16p, _u16p, _u16p, _i64, _i64, _i64, _i64, ctypes.c_int],
+            "oracle_gate_residual_dt": [_u16p, _u16p, _u16p, _u16p, _i64, _i64, _i64, _i64,
+                                        ctypes.c_int],
             "oracle_silu_bf16": [_f32p, _u16p, _i64],
             "oracle_ln_stats": [_u16p, _i64, _i64, ctypes.c_float, _f32p, _f32p],
             "oracle_rms_stats": [_u16p, _i64, _i64, ctypes.c_float, _f32p],
@@ -75,7 +80,8 @@ def _load():
         for name, args in sig.items():
             fn = getattr(lib, name)
             fn.argtypes = args
-            fn.restype = ctypes.c_int if name.startswith(("oracle_ln", "oracle_rms", "oracle_mod",
+            fn.restype = None if name in ("oracle_round_f32_to_f16", "oracle_widen_f16") else \
+                ctypes.c_int if name.startswith(("oracle_ln", "oracle_rms", "oracle_mod",
                                                           "oracle_gate", "oracle_bias",
                                                           "oracle_silu_norm", "oracle_gated",
                                                           "oracle_qk", "oracle_conv")) else None
@@ -118,6 +124,49 @@ def round_f64_to_bf16(d):
     d = np.ascontiguousarray(d, dtype=np.float64)
     out = np.empty(d.shape, np.uint16)
     _load().oracle_round_f64_to_bf16(_p(d, _f64p), _p(out, _u16p), d.size)
+    return out
+
+
+def round_f32_to_f16(f):
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    out = np.empty(f.shape, np.uint16)
+    _load().oracle_round_f32_to_f16(_p(f, _f32p), _p(out, _u16p), f.size)
+    return out
+
+
+def widen_f16(h):
+    h = _u16(h)
+    out = np.empty(h.shape, np.float32)
+    _load().oracle_widen_f16(_p(h, _u16p), _p(out, _f32p), h.size)
+    return out
+
+
+DTYPES = {"bf16": 0, "f16": 1}
+
+
+def modulate_dt(x, scale, shift, dtype="bf16", rows_per_batch=None):
+    """Standalone modulate in bf16 or fp16 storage (uint16 bit patterns)."""
+    x = _u16(x)
+    rows, cols = x.shape
+    scale, stride = _mod_rows(scale, cols)
+    shift, stride2 = _mod_rows(shift, cols)
+    assert stride == stride2
+    out = np.empty_like(x)
+    _check(_load().oracle_modulate_dt(_p(x, _u16p), _p(scale, _u16p), _p(shift, _u16p),
+                                      _p(out, _u16p), rows, cols, rows_per_batch or max(rows, 1),
+                                      stride, DTYPES[dtype]))
+    return out
+
+
+def gate_residual_dt(update, residual, gate, dtype="bf16", rows_per_batch=None):
+    """Standalone residual-gate add in bf16 or fp16 storage."""
+    update, residual = _u16(update), _u16(residual)
+    rows, cols = update.shape
+    gate, stride = _mod_rows(gate, cols)
+    out = np.empty_like(update)
+    _check(_load().oracle_gate_residual_dt(_p(update, _u16p), _p(residual, _u16p), _p(gate, _u16p),
+                                           _p(out, _u16p), rows, cols,
+                                           rows_per_batch or max(rows, 1), stride, DTYPES[dtype]))
     return out
 
 

@@ -122,6 +122,57 @@ static uint16_t f64_to_bf16(double d)
     return f32_to_bf16(f);
 }
 
+/* binary16 (fp16) storage, for the standalone elementwise sites (the FLUX.1
+ * page's fused modulate is checked on bf16 and fp16). */
+static float f16_to_f32(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+    uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
+    float f;
+    if (e == 0x1Fu) {
+        uint32_t u = sign | 0x7F800000u | (m << 13);
+        memcpy(&f, &u, sizeof f);
+        return f;
+    }
+    if (e == 0) {
+        f = ldexpf((float)m, -24); /* subnormal (or zero): m * 2^-24, exact */
+        return sign ? -f : f;
+    }
+    uint32_t u = sign | ((e + 112u) << 23) | (m << 13);
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Round a binary32 value to binary16, nearest-even; NaN -> 0x7E00 | sign. */
+static uint16_t f32_to_f16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u)
+        return sign | 0x7E00u;
+    if (a >= 0x477FF000u) /* >= 65520: rounds to infinity */
+        return sign | 0x7C00u;
+    int e = (int)(a >> 23) - 127; /* unbiased binary32 exponent */
+    uint32_t sig = (a & 0x7FFFFFu) | (a ? 0x800000u : 0u);
+    if (a < 0x00800000u)
+        return sign; /* binary32 subnormals are far below half the least fp16 step */
+    int shift = e >= -14 ? 13 : 13 + (-14 - e); /* bits dropped from the 24-bit significand */
+    if (shift > 31)
+        return sign;
+    uint32_t q = sig >> shift, rem = sig & ((1u << shift) - 1u), half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1u)))
+        q += 1u;
+    if (e >= -14) /* normal: q holds the implicit bit; rebase the exponent */
+        return sign | (uint16_t)((((uint32_t)(e + 15)) << 10) + (q - 0x400u));
+    return sign | (uint16_t)q; /* subnormal (q may carry into the least normal) */
+}
+
+/* The storage type of an elementwise stage: 0 = bf16, 1 = fp16. */
+static float st_to_f32(uint16_t v, int dtype) { return dtype ? f16_to_f32(v) : bf16_to_f32(v); }
+static uint16_t f32_to_st(float f, int dtype) { return dtype ? f32_to_f16(f) : f32_to_bf16(f); }
+
 /* ------------------------------------------------------------------------- */
 /* Row statistics: the plain definitions                                     */
 /* ------------------------------------------------------------------------- */
@@ -220,6 +271,18 @@ static int mod_args_ok(int64_t rows, int64_t cols, int64_t rows_per_batch,
 /* Exported: conversions (for pinning the rounding helpers)                  */
 /* ------------------------------------------------------------------------- */
 
+void oracle_round_f32_to_f16(const float *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = f32_to_f16(in[i]);
+}
+
+void oracle_widen_f16(const uint16_t *in, float *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = f16_to_f32(in[i]);
+}
+
 void oracle_round_f32_to_bf16(const float *in, uint16_t *out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i)
@@ -313,6 +376,43 @@ int oracle_modulate(const uint16_t *y, const uint16_t *scale, const uint16_t *sh
         for (int64_t c = 0; c < cols; ++c)
             out[r * cols + c] = modulate(y[r * cols + c], scale[b * mod_batch_stride + c],
                                          shift[b * mod_batch_stride + c]);
+    }
+    return OR_OK;
+}
+
+/* Standalone modulate in the storage type `dtype` (0 bf16, 1 fp16):
+ * out = rnd(rnd(x * rnd(1 + scale)) + shift), every op one binary32 op. */
+int oracle_modulate_dt(const uint16_t *x, const uint16_t *scale, const uint16_t *shift,
+                       uint16_t *out, int64_t rows, int64_t cols, int64_t rows_per_batch,
+                       int64_t mod_batch_stride, int dtype)
+{
+    if (!mod_args_ok(rows, cols, rows_per_batch, mod_batch_stride) || (dtype != 0 && dtype != 1))
+        return OR_INVALID;
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / rows_per_batch;
+        for (int64_t c = 0; c < cols; ++c) {
+            float s1 = st_to_f32(f32_to_st(1.0f + st_to_f32(scale[b * mod_batch_stride + c], dtype), dtype), dtype);
+            float p = st_to_f32(f32_to_st(st_to_f32(x[r * cols + c], dtype) * s1, dtype), dtype);
+            out[r * cols + c] = f32_to_st(p + st_to_f32(shift[b * mod_batch_stride + c], dtype), dtype);
+        }
+    }
+    return OR_OK;
+}
+
+/* Standalone residual-gate add in `dtype`: out = rnd(residual + rnd(gate * update)). */
+int oracle_gate_residual_dt(const uint16_t *update, const uint16_t *residual,
+                            const uint16_t *gate, uint16_t *out, int64_t rows, int64_t cols,
+                            int64_t rows_per_batch, int64_t mod_batch_stride, int dtype)
+{
+    if (!mod_args_ok(rows, cols, rows_per_batch, mod_batch_stride) || (dtype != 0 && dtype != 1))
+        return OR_INVALID;
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / rows_per_batch;
+        for (int64_t c = 0; c < cols; ++c) {
+            float g = st_to_f32(f32_to_st(st_to_f32(gate[b * mod_batch_stride + c], dtype) *
+                                              st_to_f32(update[r * cols + c], dtype), dtype), dtype);
+            out[r * cols + c] = f32_to_st(st_to_f32(residual[r * cols + c], dtype) + g, dtype);
+        }
     }
     return OR_OK;
 }

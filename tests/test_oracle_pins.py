@@ -508,3 +508,58 @@ def test_byte_model_reproduces_page_bandwidths():
             l = Launch("e", "rmsnorm_silu_bias", rows, c, (), 1e-6, extra={"bias": False})
         tbps = l.algorithmic_bytes() / (e["ms"] * 1e-3) / 1e12
         assert abs(tbps - e["tbps_printed"]) <= e["printed_precision"], (e["what"], tbps)
+
+
+# ---------------------------------------------------------------------------
+# binary16 storage (standalone elementwise sites)
+# ---------------------------------------------------------------------------
+
+def test_round_f32_to_f16_matches_numpy_on_every_tie_class(orc):
+    """All 2^16 upper halves x the low halves that decide RNE at bit 13 (exact,
+    just below / at / just above the halfway point) + 2M random patterns,
+    against numpy's correctly rounded float32 -> float16 conversion."""
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0FFF, 0x1000, 0x1001, 0x2000, 0x3000, 0x3001, 0xEFFF, 0xF000,
+                     0xFFFF], np.uint32)
+    pats = (hi[:, None] | lows[None, :]).ravel()
+    rng = np.random.default_rng(17)
+    pats = np.concatenate([pats, rng.integers(0, 1 << 32, 2_000_000, dtype=np.uint64).astype(np.uint32)])
+    f = pats.view(np.float32)
+    with np.errstate(over="ignore"):
+        ref = f.astype(np.float16).view(np.uint16)
+    ours = orc.round_f32_to_f16(f)
+    nan_o = ((ours & 0x7C00) == 0x7C00) & ((ours & 0x3FF) != 0)
+    nan_r = ((ref & 0x7C00) == 0x7C00) & ((ref & 0x3FF) != 0)
+    assert np.array_equal(nan_o, nan_r)
+    assert np.array_equal(ours[~nan_o], ref[~nan_r])
+
+
+def test_widen_f16_exact(orc):
+    h = np.arange(1 << 16, dtype=np.uint16)
+    ours = orc.widen_f16(h)
+    ref = h.view(np.float16).astype(np.float32)
+    n = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), n) and np.array_equal(ours[~n], ref[~n])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_standalone_modulate_and_gate_match_eager(orc, dtype):
+    """x * (1 + scale) + shift and residual + gate * update evaluated by torch
+    on CPU tensors of the storage dtype (each op rounds), (B,1,D) broadcast."""
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    B, S, D = 3, 41, 96
+    g = torch.Generator().manual_seed(21)
+    mk = lambda *shape, s=1.0: (torch.randn(*shape, generator=g) * s).to(tdt)
+    x, sc, sh = mk(B, S, D, s=2.0), mk(B, 1, D, s=0.3), mk(B, 1, D, s=0.3)
+    u, res, gate = mk(B, S, D, s=1.5), mk(B, S, D), mk(B, 1, D, s=0.1)
+    x[0, 0, :6] = torch.tensor([0.0, -0.0, 65504.0, 6e-5, -1e-7, 1.0]).to(tdt)
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16).reshape(-1, D)
+    ref = x * (1 + sc) + sh
+    ours = orc.modulate_dt(bits(x), bits(sc), bits(sh), dtype, rows_per_batch=S)
+    assert same_bits(ours, bits(ref)) if dtype == "bf16" else np.array_equal(ours, bits(ref))
+    ref = res + gate * u
+    ours = orc.gate_residual_dt(bits(u), bits(res), bits(gate), dtype, rows_per_batch=S)
+    assert np.array_equal(ours, bits(ref))
+    if dtype == "bf16":   # the same stages as the fused paths use
+        assert np.array_equal(orc.modulate_dt(bits(x), bits(sc), bits(sh), "bf16", S),
+                              orc.modulate(bits(x), bits(sc), bits(sh), rows_per_batch=S))
