@@ -42,7 +42,9 @@ KERNEL_SOURCES = {
     "ln_modulate": "row_kernels.hip", "gated_ln_modulate": "row_kernels.hip",
     "rms_modulate": "row_kernels.hip", "qk_layernorm": "qk_kernel.hip",
     "rmsnorm_silu_bias": "wan_kernels.hip", "conv_bias_epilogue": "wan_kernels.hip",
+    "modulate_scale_shift": "elementwise.hip", "residual_gate_add": "elementwise.hip",
 }
+DTYPE_CODES = {"bf16": 0, "f16": 1}
 
 
 def log(msg):
@@ -86,6 +88,15 @@ def make_call(lib, launch, t, stream):
         out = torch.empty_like(t["x"])
         return lib.rmsnorm_silu_bias, (_p(t["x"]), _p(t["bias"]), _p(t["gamma"]), _p(out), rows,
                                        cols, launch.eps, None, None, stream), out
+    a, b, c = (t[n] for n in launch.inputs)
+    if e == "conv_bias_epilogue":          # inputs: x, bias, h
+        out = torch.empty_like(a)
+        return lib.conv_bias_epilogue, (_p(a), _p(b), _p(c), _p(out), rows, cols, stream), out
+    if e in ("modulate_scale_shift", "residual_gate_add"):
+        # modulate: x, scale, shift; gate add: update, residual, gate
+        out = torch.empty_like(a)
+        return getattr(lib, e), (_p(a), _p(b), _p(c), _p(out), rows, cols, rows, cols,
+                                 DTYPE_CODES[launch.extra["dtype"]], stream), out
     raise KeyError(e)
 
 
@@ -184,7 +195,7 @@ def traffic_for(workload, launch):
 # CPU baseline: the oracle on this host's cores
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(w, min_seconds=8.0):
+def cpu_baseline(w, min_seconds=10.0):
     import concurrent.futures as cf
 
     import oracle
@@ -215,7 +226,7 @@ def cpu_baseline(w, min_seconds=8.0):
                 run_launch(l, ex)
             reps += 1
             el = time.perf_counter() - t0
-            if el >= min_seconds or reps >= 50:
+            if el >= min_seconds or reps >= 5000:
                 break
     gbps = w.algorithmic_bytes() * reps / el / 1e9
     return {"value": round(gbps, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
@@ -386,6 +397,11 @@ def _kernel_label(name):
         rms, gated = args[2].strip() == "true", args[3].strip() == "true"
         return {(False, False): "ln_modulate", (False, True): "gated_ln_modulate",
                 (True, False): "rms_modulate", (True, True): "gated_rms_modulate"}[(rms, gated)]
+    if "ditnorm::elementwise_kernel<" in name:
+        # elementwise_kernel<OP, DT>
+        op, dt = (a.strip() for a in name.split("_kernel<", 1)[1].split(">", 1)[0].split(","))
+        return ("modulate_scale_shift" if op == "0" else "residual_gate_add") + \
+            ("_bf16" if dt == "0" else "_f16")
     for key, label in (("qk_kernel", "qk_layernorm"), ("wan_kernel", "rmsnorm_silu_bias"),
                        ("epilogue_kernel", "conv_bias_epilogue"), ("copy_kernel", "copy")):
         if f"ditnorm::{key}" in name:
@@ -468,7 +484,7 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd):
              f"{'launch':<22} {'dispatches':>10} {'fetch_MB':>10} {'write_MB':>10} {'hbm_MB':>10} "
              f"{'algo_MB':>10} {'ratio':>7}"]
     for l in w.launches:
-        lab = "gated_rms_modulate" if (l.entry == "rms_modulate" and l.extra.get("gated")) else l.entry
+        lab = l.label()
         if lab not in fetch or lab not in write:
             continue
         fb = fetch[lab][0] * 1024.0 * f_cal

@@ -10,7 +10,7 @@ the call raises.
 
 Entry points (same names as the C ABI):
     ln_modulate, gated_ln_modulate, rms_modulate, qk_layernorm,
-    rmsnorm_silu_bias, conv_bias_epilogue, copy
+    rmsnorm_silu_bias, conv_bias_epilogue, modulate_scale_shift, residual_gate_add, copy
 """
 from __future__ import annotations
 
@@ -20,7 +20,8 @@ import os
 import torch
 
 __all__ = ["load", "ln_modulate", "gated_ln_modulate", "rms_modulate", "qk_layernorm",
-           "rmsnorm_silu_bias", "conv_bias_epilogue", "copy", "DitnormError", "LIB_PATH"]
+           "rmsnorm_silu_bias", "conv_bias_epilogue", "modulate_scale_shift",
+           "residual_gate_add", "copy", "DitnormError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditnorm.so")
 
@@ -39,6 +40,10 @@ _lib = None
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _f32 = ctypes.c_float
+_i32 = ctypes.c_int
+
+# storage types of the standalone elementwise entry points (DITNORM_DTYPE_*)
+_DTYPE_CODES = {torch.bfloat16: 0, torch.float16: 1}
 
 _SIGNATURES = {
     "ln_modulate": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp],
@@ -49,6 +54,8 @@ _SIGNATURES = {
     "qk_layernorm": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp, _vp, _vp],
     "rmsnorm_silu_bias": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp, _vp],
     "conv_bias_epilogue": [_vp, _vp, _vp, _vp, _i64, _i64, _vp],
+    "modulate_scale_shift": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp],
+    "residual_gate_add": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp],
     "ditnorm_copy": [_vp, _vp, _i64, _vp],
     "ln_modulate_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp],
     "gated_ln_modulate_supported": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
@@ -58,6 +65,8 @@ _SIGNATURES = {
     "qk_layernorm_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp, _vp],
     "rmsnorm_silu_bias_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp],
     "conv_bias_epilogue_supported": [_vp, _vp, _vp, _vp, _i64, _i64],
+    "modulate_scale_shift_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32],
+    "residual_gate_add_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32],
     "ditnorm_last_hip_error": [],
     "ditnorm_version": [],
 }
@@ -109,12 +118,12 @@ def _act(t, name, dtype=torch.bfloat16):
     return t
 
 
-def _mod(t, name, cols, device):
+def _mod(t, name, cols, device, dtype=torch.bfloat16):
     """Modulation rows: (cols,), (B, cols) or (B, 1, cols), last dim dense; the
     batch stride may exceed cols (a chunk view of an adaLN embedding).
     Returns (tensor, B, batch_stride)."""
-    if t.dtype != torch.bfloat16 or t.device != device:
-        raise TypeError(f"{name} must be bf16 on {device}")
+    if t.dtype != dtype or t.device != device:
+        raise TypeError(f"{name} must be {dtype} on {device}")
     if t.shape[-1] != cols or t.stride(-1) != 1:
         raise ValueError(f"{name}: last dim must be {cols} and dense")
     if t.dim() == 1:
@@ -293,6 +302,50 @@ def conv_bias_epilogue(x, bias, h=None, out=None):
         raise ValueError("h must match x in shape, strides and dtype")
     out = _out_like(x, out)
     _call("conv_bias_epilogue", _p(x), _p(bias), _p(h), _p(out), rows2d.shape[0], c, _stream(x))
+    return out
+
+
+def _ew_dtype(x):
+    if x.dtype not in _DTYPE_CODES:
+        raise TypeError(f"expected bf16 or fp16, got {x.dtype}")
+    return x.dtype
+
+
+def modulate_scale_shift(x, scale, shift, out=None):
+    """out = rnd(rnd(x * rnd(1 + scale)) + shift), rnd the storage type of x
+    (bf16 or fp16); x (..., D), scale / shift (D,), (B, D) or (B, 1, D).
+    out may be x (in place)."""
+    dt = _ew_dtype(x)
+    _act(x, "x", dt)
+    rows, cols = _rows_cols(x)
+    scale, b, stride = _mod(scale, "scale", cols, x.device, dt)
+    shift, b2, stride2 = _mod(shift, "shift", cols, x.device, dt)
+    if (b, stride) != (b2, stride2):
+        raise ValueError("scale and shift must have the same batch count and stride")
+    out = torch.empty_like(x) if out is None else _act(out, "out", dt)
+    if out.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    _call("modulate_scale_shift", _p(x), _p(scale), _p(shift), _p(out), rows, cols,
+          _batch(rows, b), stride, _DTYPE_CODES[dt], _stream(x))
+    return out
+
+
+def residual_gate_add(update, residual, gate, out=None):
+    """out = rnd(residual + rnd(gate * update)), rnd the storage type (bf16 or
+    fp16); update / residual (..., D), gate (D,), (B, D) or (B, 1, D).
+    out may be residual (in place)."""
+    dt = _ew_dtype(update)
+    _act(update, "update", dt)
+    _act(residual, "residual", dt)
+    if residual.shape != update.shape:
+        raise ValueError("residual must have the shape of update")
+    rows, cols = _rows_cols(update)
+    gate, b, stride = _mod(gate, "gate", cols, update.device, dt)
+    out = torch.empty_like(update) if out is None else _act(out, "out", dt)
+    if out.shape != update.shape:
+        raise ValueError("out must have the shape of update")
+    _call("residual_gate_add", _p(update), _p(residual), _p(gate), _p(out), rows, cols,
+          _batch(rows, b), stride, _DTYPE_CODES[dt], _stream(update))
     return out
 
 

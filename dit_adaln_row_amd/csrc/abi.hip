@@ -229,6 +229,41 @@ int validate_epilogue(const void *x, const float *bias, const void *h, const voi
   return aliasing_ok(in, o, alias) ? DITNORM_OK : DITNORM_UNSUPPORTED;
 }
 
+int validate_elementwise(int op, const void *a, const void *b, const void *m0, const void *m1,
+                         const void *out, int64_t rows, int64_t cols, int64_t rpb, int64_t mbs,
+                         int dtype) {
+  if (dtype != DITNORM_DTYPE_BF16 && dtype != DITNORM_DTYPE_F16) return DITNORM_INVALID_ARGUMENT;
+  int st = check_rows(rows, cols, rpb, mbs, 0.0f);
+  if (st != DITNORM_OK || rows == 0) return st;
+  if (!a || !m0 || !out || (op == 0 && !m1) || (op == 1 && !b)) return DITNORM_INVALID_ARGUMENT;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(m0) || !aligned16(m1) || !aligned16(out))
+    return DITNORM_UNSUPPORTED;
+  const int64_t act = rows * cols * 2, mb = mod_bytes(rows / rpb, mbs, cols);
+  const Buf in[] = {{a, act}, {b, op == 1 ? act : 0}, {m0, mb}, {m1, op == 0 ? mb : 0}};
+  const Buf o[] = {{out, act}};
+  const int alias[] = {op == 0 ? 0 : 1};  // modulate: out may be x; gate add: out may be residual
+  return aliasing_ok(in, o, alias) ? DITNORM_OK : DITNORM_UNSUPPORTED;
+}
+
+int launch_ew(int op, const void *a, const void *b, const void *m0, const void *m1, void *out,
+              int64_t rows, int64_t cols, int64_t rpb, int64_t mbs, int dtype, void *stream) {
+  int st = validate_elementwise(op, a, b, m0, m1, out, rows, cols, rpb, mbs, dtype);
+  if (st != DITNORM_OK || rows == 0) return st;
+  DeviceInfo dev;
+  if ((st = current_device(&dev)) != DITNORM_OK) return st;
+  ElementwiseArgs e{};
+  e.a = (const uint16_t *)a;
+  e.b = (const uint16_t *)b;
+  e.m0 = (const uint16_t *)m0;
+  e.m1 = (const uint16_t *)m1;
+  e.out = (uint16_t *)out;
+  e.rows = rows;
+  e.cols = (int32_t)cols;
+  e.rows_per_batch = rpb;
+  e.mod_stride = mbs;
+  return finish(launch_elementwise(e, op, dtype, (hipStream_t)stream));
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -431,6 +466,34 @@ int rmsnorm_silu_bias_supported(const void *x, const float *bias, const float *g
 int conv_bias_epilogue_supported(const void *x, const float *bias, const void *h,
                                  const void *out, int64_t rows, int64_t channels) {
   return validate_epilogue(x, bias, h, out, rows, channels) == DITNORM_OK;
+}
+
+int modulate_scale_shift(const void *x, const void *scale, const void *shift, void *out,
+                         int64_t rows, int64_t cols, int64_t rows_per_batch,
+                         int64_t mod_batch_stride, int dtype, void *stream) {
+  return launch_ew(0, x, nullptr, scale, shift, out, rows, cols, rows_per_batch,
+                   mod_batch_stride, dtype, stream);
+}
+
+int residual_gate_add(const void *update, const void *residual, const void *gate, void *out,
+                      int64_t rows, int64_t cols, int64_t rows_per_batch,
+                      int64_t mod_batch_stride, int dtype, void *stream) {
+  return launch_ew(1, update, residual, gate, nullptr, out, rows, cols, rows_per_batch,
+                   mod_batch_stride, dtype, stream);
+}
+
+int modulate_scale_shift_supported(const void *x, const void *scale, const void *shift,
+                                   const void *out, int64_t rows, int64_t cols,
+                                   int64_t rows_per_batch, int64_t mod_batch_stride, int dtype) {
+  return validate_elementwise(0, x, nullptr, scale, shift, out, rows, cols, rows_per_batch,
+                              mod_batch_stride, dtype) == DITNORM_OK;
+}
+
+int residual_gate_add_supported(const void *update, const void *residual, const void *gate,
+                                const void *out, int64_t rows, int64_t cols,
+                                int64_t rows_per_batch, int64_t mod_batch_stride, int dtype) {
+  return validate_elementwise(1, update, residual, gate, nullptr, out, rows, cols,
+                              rows_per_batch, mod_batch_stride, dtype) == DITNORM_OK;
 }
 
 int ditnorm_copy(const void *src, void *dst, int64_t bytes, void *stream) {

@@ -1,0 +1,143 @@
+// Standalone elementwise adaLN stages, for sites whose norm is not fused.
+//
+// modulate_scale_shift (FLUX.1 page, "Commit 2": a fused modulate kernel
+// whose intermediates are rounded back to the storage dtype exactly like the
+// eager chain's kernel boundaries; bf16 and fp16, batched rows, adaLN chunk
+// views):
+//     out = rnd(rnd(x * rnd(1 + scale)) + shift)
+// residual_gate_add (GLM-Image page, the ff gate reusing residual_gate_add;
+// ERNIE-Image page, the residual variant):
+//     out = rnd(residual + rnd(gate * update))
+// rnd rounds to the storage type (bf16 or fp16) nearest-even; each operation
+// is one binary32 operation on exactly widened operands.  For fp16 the
+// compiler may fuse a widen / operate / round triple into one fp16
+// instruction: a binary32 intermediate has at least 2p+2 significand bits for
+// p = 11, so the correctly rounded fp16 result is the same either way.
+//
+// Work layout: thread t owns the 16-byte column slot t % (cols/8) of U
+// consecutive rows, so its modulation vector (already rounded 1 + scale, and
+// shift; or the gate) is loaded once and reused; consecutive threads touch
+// consecutive 16-byte vectors of a row, and each of the U row accesses is a
+// separate fully coalesced instruction.  One-shot grid.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace ditnorm {
+
+constexpr int EW_BLOCK = 256;
+constexpr int EW_ROWS = 4;  // rows per thread
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+__device__ __forceinline__ void widen8(const uint4 v, float f[8]) {
+  if constexpr (DT == 0) {
+    unpack8(v, f);
+  } else {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 p = __builtin_convertvector(__builtin_bit_cast(f16x2, w[i]), f32x2);
+      f[2 * i] = p.x;
+      f[2 * i + 1] = p.y;
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint4 narrow8(const float f[8]) {
+  if constexpr (DT == 0) {
+    return pack8(f);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 p = {f[2 * i], f[2 * i + 1]};
+      w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, f16x2));
+    }
+    uint4 r;
+    r.x = w[0]; r.y = w[1]; r.z = w[2]; r.w = w[3];
+    return r;
+  }
+}
+
+// the value a storage-type kernel boundary keeps
+template <int DT>
+__device__ __forceinline__ void round8(float f[8]) {
+  const uint4 p = narrow8<DT>(f);
+  widen8<DT>(p, f);
+}
+
+// OP 0: modulate (x, scale, shift); OP 1: gate add (update, residual, gate)
+template <int OP, int DT>
+__global__ __launch_bounds__(EW_BLOCK) void elementwise_kernel(const ElementwiseArgs a) {
+  const int nvec = a.cols >> 3;
+  const int64_t t = (int64_t)blockIdx.x * EW_BLOCK + threadIdx.x;
+  const int64_t rg = t / nvec;
+  const int c8 = (int)(t - rg * nvec) * 8;
+  const int64_t r0 = rg * EW_ROWS;
+  if (r0 >= a.rows) return;
+  const int nr = (int)(a.rows - r0 < EW_ROWS ? a.rows - r0 : EW_ROWS);
+
+  // the rows first
+  uint4 in0[EW_ROWS], in1[EW_ROWS];
+#pragma unroll
+  for (int u = 0; u < EW_ROWS; ++u) {
+    if (u >= nr) break;
+    const int64_t off = (r0 + u) * (int64_t)a.cols + c8;
+    in0[u] = ld16s(a.a + off);
+    if constexpr (OP == 1) in1[u] = ld16s(a.b + off);
+  }
+
+  int64_t cur_b = -1;
+  float m0[8], m1[8];
+#pragma unroll
+  for (int u = 0; u < EW_ROWS; ++u) {
+    if (u >= nr) break;
+    const int64_t r = r0 + u;
+    const int64_t b = r / a.rows_per_batch;
+    if (b != cur_b) {  // the first row, and batch boundaries
+      cur_b = b;
+      const int64_t mo = b * a.mod_stride + c8;
+      widen8<DT>(ld16(a.m0 + mo), m0);
+      if constexpr (OP == 0) {
+        widen8<DT>(ld16(a.m1 + mo), m1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m0[e] = 1.0f + m0[e];
+        round8<DT>(m0);  // s1 = rnd(1 + scale)
+      }
+    }
+    float v[8], w[8], o[8];
+    widen8<DT>(in0[u], v);
+    if constexpr (OP == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = v[e] * m0[e];
+      round8<DT>(w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = w[e] + m1[e];
+    } else {
+      float res[8];
+      widen8<DT>(in1[u], res);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = m0[e] * v[e];
+      round8<DT>(w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = res[e] + w[e];
+    }
+    st16s(a.out + r * (int64_t)a.cols + c8, narrow8<DT>(o));
+  }
+}
+
+hipError_t launch_elementwise(const ElementwiseArgs &a, int op, int dtype, hipStream_t stream) {
+  const int64_t nvec = a.cols >> 3;
+  const int64_t threads = nvec * ((a.rows + EW_ROWS - 1) / EW_ROWS);
+  if (threads > (int64_t)INT32_MAX) return hipErrorInvalidConfiguration;  // > 32 GiB per row slot
+  const dim3 grid((unsigned)((threads + EW_BLOCK - 1) / EW_BLOCK)), block(EW_BLOCK);
+  if (op == 0 && dtype == 0) hipLaunchKernelGGL((elementwise_kernel<0, 0>), grid, block, 0, stream, a);
+  if (op == 0 && dtype == 1) hipLaunchKernelGGL((elementwise_kernel<0, 1>), grid, block, 0, stream, a);
+  if (op == 1 && dtype == 0) hipLaunchKernelGGL((elementwise_kernel<1, 0>), grid, block, 0, stream, a);
+  if (op == 1 && dtype == 1) hipLaunchKernelGGL((elementwise_kernel<1, 1>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace ditnorm

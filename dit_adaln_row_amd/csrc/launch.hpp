@@ -75,6 +75,22 @@ struct EpilogueArgs {
 };
 hipError_t launch_epilogue(const EpilogueArgs &a, const DeviceInfo &dev, hipStream_t stream);
 
+// Standalone elementwise stages: op 0 modulate (a = x, m0 = scale, m1 = shift),
+// op 1 residual-gate add (a = update, b = residual, m0 = gate); dtype 0 bf16,
+// 1 fp16.
+struct ElementwiseArgs {
+  const uint16_t *a;
+  const uint16_t *b;
+  const uint16_t *m0;
+  const uint16_t *m1;
+  uint16_t *out;
+  int64_t rows;
+  int64_t rows_per_batch;
+  int64_t mod_stride;
+  int32_t cols;
+};
+hipError_t launch_elementwise(const ElementwiseArgs &a, int op, int dtype, hipStream_t stream);
+
 // Plain 16-byte copy (measurement utility).
 hipError_t launch_copy(const void *src, void *dst, int64_t bytes, const DeviceInfo &dev,
                        hipStream_t stream);

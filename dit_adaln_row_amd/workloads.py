@@ -29,7 +29,7 @@ class Tensor:
     shape: tuple
     mu: float
     sigma: float
-    kind: str = "bf16"   # "bf16" | "f32" | "f32_bf16vals" (fp32 holding bf16 values)
+    kind: str = "bf16"   # "bf16" | "f16" | "f32" | "f32_bf16vals" (fp32 holding bf16 values)
 
 
 @dataclass(frozen=True)
@@ -63,7 +63,20 @@ class Launch:
         if self.entry == "conv_bias_epilogue":
             act = (3 if self.extra.get("residual", False) else 2) * r * c * BF16
             return act + c * F32
+        # standalone elementwise stages: bf16 and fp16 are both 2-byte types
+        if self.entry == "modulate_scale_shift":
+            return 2 * r * c * BF16 + 2 * self.n_mod_rows * c * BF16
+        if self.entry == "residual_gate_add":
+            return 3 * r * c * BF16 + self.n_mod_rows * c * BF16
         raise KeyError(self.entry)
+
+    def label(self) -> str:
+        """The kernel kind a profiler trace attributes this launch to."""
+        if self.entry == "rms_modulate" and self.extra.get("gated"):
+            return "gated_rms_modulate"
+        if self.entry in ("modulate_scale_shift", "residual_gate_add"):
+            return f"{self.entry}_{self.extra.get('dtype', 'bf16')}"
+        return self.entry
 
 
 def _seed(cfg: int, idx: int) -> int:
@@ -159,6 +172,44 @@ WORKLOADS = {
          Tensor("gamma", (384,), 1.0, 0.05, "f32_bf16vals")),
         (Launch("rmsnorm_silu_bias", "rmsnorm_silu_bias", 4 * 240 * 416, 384,
                 ("x", "bias", "gamma"), 1e-6),),
+    ),
+    "flux_elementwise_1x4608x3072": Workload(
+        "flux_elementwise_1x4608x3072", 7,
+        "FLUX.1-like standalone modulate and residual-gate add on (1,4608,3072), bf16 and "
+        "fp16 storage: x ~N(0,1.5), residual ~N(0,1), scale/shift/gate (1,3072) ~N(0,0.1)",
+        (Tensor("x", (4608, 3072), 0.0, 1.5), Tensor("residual", (4608, 3072), 0.0, 1.0),
+         Tensor("scale", (1, 3072), 0.0, 0.1), Tensor("shift", (1, 3072), 0.0, 0.1),
+         Tensor("gate", (1, 3072), 0.0, 0.1),
+         Tensor("x16", (4608, 3072), 0.0, 1.5, "f16"),
+         Tensor("residual16", (4608, 3072), 0.0, 1.0, "f16"),
+         Tensor("scale16", (1, 3072), 0.0, 0.1, "f16"), Tensor("shift16", (1, 3072), 0.0, 0.1, "f16"),
+         Tensor("gate16", (1, 3072), 0.0, 0.1, "f16")),
+        (Launch("modulate_bf16", "modulate_scale_shift", 4608, 3072, ("x", "scale", "shift"), 0.0,
+                extra={"dtype": "bf16"}),
+         Launch("gate_add_bf16", "residual_gate_add", 4608, 3072, ("x", "residual", "gate"), 0.0,
+                extra={"dtype": "bf16"}),
+         Launch("modulate_f16", "modulate_scale_shift", 4608, 3072, ("x16", "scale16", "shift16"),
+                0.0, extra={"dtype": "f16"}),
+         Launch("gate_add_f16", "residual_gate_add", 4608, 3072, ("x16", "residual16", "gate16"),
+                0.0, extra={"dtype": "f16"})),
+    ),
+    "wan_epilogue_1x96x4x480x832": Workload(
+        "wan_epilogue_1x96x4x480x832", 8,
+        "Wan-VAE-like conv-bias epilogue with residual, channels_last [1,96,4,480,832]: "
+        "x, h ~N(0,1), bias (96) fp32 ~N(0,0.05)",
+        (Tensor("x", (4 * 480 * 832, 96), 0.0, 1.0), Tensor("bias", (96,), 0.0, 0.05, "f32"),
+         Tensor("h", (4 * 480 * 832, 96), 0.0, 1.0)),
+        (Launch("conv_bias_epilogue", "conv_bias_epilogue", 4 * 480 * 832, 96,
+                ("x", "bias", "h"), 0.0, extra={"residual": True}),),
+    ),
+    "wan_epilogue_1x384x4x240x416": Workload(
+        "wan_epilogue_1x384x4x240x416", 9,
+        "Wan-VAE-like conv-bias epilogue with residual, channels_last [1,384,4,240,416]: "
+        "x, h ~N(0,1), bias (384) fp32 ~N(0,0.05)",
+        (Tensor("x", (4 * 240 * 416, 384), 0.0, 1.0), Tensor("bias", (384,), 0.0, 0.05, "f32"),
+         Tensor("h", (4 * 240 * 416, 384), 0.0, 1.0)),
+        (Launch("conv_bias_epilogue", "conv_bias_epilogue", 4 * 240 * 416, 384,
+                ("x", "bias", "h"), 0.0, extra={"residual": True}),),
     ),
 }
 

@@ -73,6 +73,10 @@ extern "C" {
 #define DITNORM_UNSUPPORTED 2
 #define DITNORM_DEVICE_ERROR 3
 
+/* Storage types of the standalone elementwise entry points. */
+#define DITNORM_DTYPE_BF16 0
+#define DITNORM_DTYPE_F16 1
+
 /* Largest row width of the row kernels (ln_modulate, gated_ln_modulate,
  * rms_modulate) and the largest channel count of the channels_last kernels. */
 #define DITNORM_MAX_COLS 16384
@@ -202,6 +206,38 @@ int conv_bias_epilogue(const void *x, const float *bias, const void *h, void *ou
                        int64_t rows, int64_t channels, void *stream);
 
 /*
+ * modulate_scale_shift -- the adaLN modulate alone, for sites whose norm is
+ * not fused into it.
+ *
+ * FLUX.1 page ("[diffusion] FLUX.1 fused adaLN modulate (bit-exact) + RoPE
+ * cache hoist, LN-affine folding behind quality=high", Commit 2): each
+ * intermediate rounded back to the storage dtype exactly like the eager
+ * chain's kernel boundaries, bf16 and fp16, batched rows, adaLN chunk views:
+ *     out = rnd( rnd( x * rnd(1 + scale) ) + shift )
+ * dtype: DITNORM_DTYPE_BF16 or DITNORM_DTYPE_F16 -- x, scale, shift and out
+ * all of that type, rnd rounding to it nearest-even.  x, out: [rows, cols];
+ * scale, shift: [B, cols], row stride mod_batch_stride.  cols: multiple of 8,
+ * at most DITNORM_MAX_COLS.  out == x allowed.
+ */
+int modulate_scale_shift(const void *x, const void *scale, const void *shift, void *out,
+                         int64_t rows, int64_t cols, int64_t rows_per_batch,
+                         int64_t mod_batch_stride, int dtype, void *stream);
+
+/*
+ * residual_gate_add -- the gated residual alone.
+ *
+ * GLM-Image page (the ff gate reuses the residual-gate-add kernel) and
+ * ERNIE-Image page ("What rounding-faithful means here": the residual
+ * variant's eager pair round(gate*update), round(residual+...)):
+ *     out = rnd( residual + rnd( gate * update ) )
+ * dtype as for modulate_scale_shift.  update, residual, out: [rows, cols];
+ * gate: [B, cols], row stride mod_batch_stride.  out == residual allowed.
+ */
+int residual_gate_add(const void *update, const void *residual, const void *gate, void *out,
+                      int64_t rows, int64_t cols, int64_t rows_per_batch,
+                      int64_t mod_batch_stride, int dtype, void *stream);
+
+/*
  * *_supported -- 1 if the same call would pass every argument check (it may
  * still fail with DITNORM_DEVICE_ERROR), else 0.  Never fails, never touches
  * the GPU, never enqueues work.
@@ -230,6 +266,12 @@ int rmsnorm_silu_bias_supported(const void *x, const float *bias, const float *g
                                 const float *rstd_out, const void *xb_out);
 int conv_bias_epilogue_supported(const void *x, const float *bias, const void *h,
                                  const void *out, int64_t rows, int64_t channels);
+int modulate_scale_shift_supported(const void *x, const void *scale, const void *shift,
+                                   const void *out, int64_t rows, int64_t cols,
+                                   int64_t rows_per_batch, int64_t mod_batch_stride, int dtype);
+int residual_gate_add_supported(const void *update, const void *residual, const void *gate,
+                                const void *out, int64_t rows, int64_t cols,
+                                int64_t rows_per_batch, int64_t mod_batch_stride, int dtype);
 
 /*
  * ditnorm_copy -- measurement utility, not part of the method: a plain

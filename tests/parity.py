@@ -35,19 +35,20 @@ def log(msg):
     sys.stdout.flush()
 
 
-def dev(a, device="cuda"):
-    """numpy uint16 (bf16 bits) or float32 -> device tensor."""
+def dev(a, device="cuda", dtype=torch.bfloat16):
+    """numpy uint16 (bf16 bits, or fp16 bits with dtype=float16) or float32 ->
+    device tensor."""
     if a is None:
         return None
     if a.dtype == np.uint16:
-        return from_u16(a, device)
+        return from_u16(a, device, dtype)
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
 def host(t):
     if t is None:
         return None
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return to_u16(t)
     return t.detach().cpu().numpy()
 
@@ -62,14 +63,16 @@ def ulp_diff(a, b):
     return np.abs(ulp_key(a) - ulp_key(b))
 
 
-def is_nan(b):
+def is_nan(b, dtype="bf16"):
     b = np.asarray(b, np.uint16)
+    if dtype == "f16":
+        return ((b & 0x7C00) == 0x7C00) & ((b & 0x3FF) != 0)
     return ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
 
 
-def same_bits(a, b):
+def same_bits(a, b, dtype="bf16"):
     """bitwise equality, NaNs compared by class."""
-    na, nb = is_nan(a), is_nan(b)
+    na, nb = is_nan(a, dtype), is_nan(b, dtype)
     return np.array_equal(na, nb) and np.array_equal(np.asarray(a)[~na], np.asarray(b)[~nb])
 
 

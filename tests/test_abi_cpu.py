@@ -40,7 +40,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     for must in ("ln_modulate", "gated_ln_modulate", "rms_modulate", "qk_layernorm",
-                 "rmsnorm_silu_bias", "conv_bias_epilogue", "ditnorm_status_string"):
+                 "rmsnorm_silu_bias", "conv_bias_epilogue", "modulate_scale_shift",
+                 "residual_gate_add", "ditnorm_status_string"):
         assert must in names
     for n in names:
         assert hasattr(lib, n), n
@@ -104,6 +105,16 @@ def test_supported_predicates_never_touch_the_gpu(lib):
     assert lib.conv_bias_epilogue_supported(A, B, C, D, 100, 96) == 1
     assert lib.conv_bias_epilogue_supported(A, B, C, A, 100, 96) == 1      # in place
     assert lib.conv_bias_epilogue_supported(A, B, C, C, 100, 96) == 0      # out over h
+    for dt in (0, 1):
+        assert lib.modulate_scale_shift_supported(A, B, C, D, 8, 3072, 4, 6 * 3072, dt) == 1
+        assert lib.modulate_scale_shift_supported(A, B, C, A, 8, 3072, 4, 3072, dt) == 1  # in place
+        assert lib.modulate_scale_shift_supported(A, B, C, B, 8, 3072, 4, 3072, dt) == 0  # out over scale
+        assert lib.modulate_scale_shift_supported(A, B, C, D, 8, 3076, 8, 3076, dt) == 0
+        assert lib.modulate_scale_shift_supported(A, B, C, D, 8, 3072, 4, 3076, dt) == 0  # stride
+        assert lib.residual_gate_add_supported(A, B, C, B, 8, 3072, 8, 3072, dt) == 1     # out == residual
+        assert lib.residual_gate_add_supported(A, B, C, A, 8, 3072, 8, 3072, dt) == 0     # out == update
+        assert lib.residual_gate_add_supported(A, B, C + 8, D, 8, 3072, 8, 3072, dt) == 0  # misaligned
+    assert lib.modulate_scale_shift_supported(A, B, C, D, 8, 3072, 8, 3072, 2) == 0
 
 
 def test_other_entry_validation(lib):
@@ -117,6 +128,13 @@ def test_other_entry_validation(lib):
     assert lib.rmsnorm_silu_bias(A, B, None, D, 10, 96, 1e-6, None, None, None) == dn.INVALID_ARGUMENT
     assert lib.rmsnorm_silu_bias(A, B, C, D, 10, 4104, 1e-6, None, None, None) == dn.UNSUPPORTED
     assert lib.conv_bias_epilogue(A, None, None, D, 10, 96, None) == dn.INVALID_ARGUMENT
+    assert lib.modulate_scale_shift(A, B, C, D, 8, 3072, 8, 3072, 7, None) == dn.INVALID_ARGUMENT
+    assert lib.modulate_scale_shift(A, B, None, D, 8, 3072, 8, 3072, 0, None) == dn.INVALID_ARGUMENT
+    assert lib.modulate_scale_shift(A, B, C, D, 8, 3072, 3, 3072, 1, None) == dn.INVALID_ARGUMENT
+    assert lib.modulate_scale_shift(A, B, C, D, 8, 3072, 8, 3000, 0, None) == dn.INVALID_ARGUMENT
+    assert lib.modulate_scale_shift(A, B, C, D, 0, 3072, 8, 3072, 0, None) == dn.OK   # no-op
+    assert lib.residual_gate_add(A, None, C, D, 8, 3072, 8, 3072, 0, None) == dn.INVALID_ARGUMENT
+    assert lib.residual_gate_add(A, B, C, D, 8, 16392, 8, 16392, 0, None) == dn.UNSUPPORTED
     assert lib.ditnorm_copy(A, B, 15, None) == dn.UNSUPPORTED
     assert lib.ditnorm_copy(A, A + 16, 64, None) == dn.UNSUPPORTED
 

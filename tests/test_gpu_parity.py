@@ -296,7 +296,7 @@ def test_conv_bias_epilogue(gpu, orc, rows, c, res):
 def test_full_workload(gpu, orc, key):
     w = WORKLOADS[key]
     log(f"full workload {key}")
-    t = {k: (gen.to_u16(v) if v.dtype == torch.bfloat16 else v.numpy())
+    t = {k: (gen.to_u16(v) if v.dtype in (torch.bfloat16, torch.float16) else v.numpy())
          for k, v in gen.make(w).items()}
     for l in w.launches:
         log(f"  launch {l.name} rows={l.rows} cols={l.cols}")
@@ -336,6 +336,25 @@ def test_full_workload(gpu, orc, key):
             _qk_run_check(gpu, orc, f"{key}/{l.name}", t["q"], t["k"], l.eps)
         elif l.entry == "rmsnorm_silu_bias":
             _wan_run_check(gpu, orc, f"{key}/{l.name}", t["x"], t["bias"], t["gamma"], l.eps)
+        elif l.entry == "conv_bias_epilogue":
+            x, b, h = (t[n] for n in l.inputs)
+            out = gpu.conv_bias_epilogue(dev(x), dev(b), dev(h))
+            torch.cuda.synchronize()
+            assert same_bits(host(out), orc.conv_bias_epilogue(x, b, h)), l.name
+        elif l.entry in ("modulate_scale_shift", "residual_gate_add"):
+            dt = l.extra["dtype"]
+            td = torch.float16 if dt == "f16" else torch.bfloat16
+            a, b, c = (t[n] for n in l.inputs)
+            if l.entry == "modulate_scale_shift":
+                out = gpu.modulate_scale_shift(dev(a, dtype=td), dev(b, dtype=td), dev(c, dtype=td))
+                ref = orc.modulate_dt(a, b, c, dt)
+            else:
+                out = gpu.residual_gate_add(dev(a, dtype=td), dev(b, dtype=td), dev(c, dtype=td))
+                ref = orc.gate_residual_dt(a, b, c, dt)
+            torch.cuda.synchronize()
+            assert same_bits(host(out), ref, dt), l.name
+        else:
+            raise KeyError(l.entry)
 
 
 # ---------------------------------------------------------------------------
