@@ -40,6 +40,7 @@ METRIC = "achieved HBM GB/s (% of MI355X peak) and rows/s per fused norm+modulat
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "ln_modulate": "row_kernels.hip", "gated_ln_modulate": "row_kernels.hip",
+    "ln_modulate_folded": "row_kernels.hip",
     "rms_modulate": "row_kernels.hip", "qk_layernorm": "qk_kernel.hip",
     "rmsnorm_silu_bias": "wan_kernels.hip", "conv_bias_epilogue": "wan_kernels.hip",
     "modulate_scale_shift": "elementwise.hip", "residual_gate_add": "elementwise.hip",
@@ -66,6 +67,10 @@ def make_call(lib, launch, t, stream):
         out = torch.empty_like(t["x"])
         return lib.ln_modulate, (_p(t["x"]), _p(t["scale"]), _p(t["shift"]), _p(out), rows, cols,
                                  rows, cols, launch.eps, None, None, None, stream), out
+    if e == "ln_modulate_folded":
+        out = torch.empty_like(t["x"])
+        return lib.ln_modulate_folded, (_p(t["x"]), _p(t["scale"]), _p(t["shift"]), _p(out), rows,
+                                        cols, rows, cols, launch.eps, None, None, stream), out
     if e == "gated_ln_modulate":
         h, out = torch.empty_like(t["update"]), torch.empty_like(t["update"])
         return lib.gated_ln_modulate, (_p(t["update"]), _p(t["residual"]), _p(t["gate"]),
@@ -392,14 +397,16 @@ def copy_calibration(lib, dev, stream, launches=8):
 def _kernel_label(name):
     """Launch kind of a demangled kernel name."""
     if "ditnorm::row_kernel<" in name or "ditnorm::row_wave_kernel<" in name:
-        # row_kernel<NT, NV, RMS, GATED> / row_wave_kernel<NV, FULL, RMS, GATED, MODLDS>
-        args = name.split("_kernel<", 1)[1].split(">", 1)[0].split(",")
-        rms, gated = args[2].strip() == "true", args[3].strip() == "true"
+        # row_kernel<NT, NV, RMS, GATED, FOLD> / row_wave_kernel<NV, FULL, RMS, GATED, MODE, FOLD>
+        args = [a.strip() for a in name.split("_kernel<", 1)[1].split(">", 1)[0].split(",")]
+        rms, gated = args[2] == "true", args[3] == "true"
+        if args[-1] == "true" and len(args) in (5, 6):
+            return "ln_modulate_folded"
         return {(False, False): "ln_modulate", (False, True): "gated_ln_modulate",
                 (True, False): "rms_modulate", (True, True): "gated_rms_modulate"}[(rms, gated)]
     if "ditnorm::elementwise_kernel<" in name:
-        # elementwise_kernel<OP, DT>
-        op, dt = (a.strip() for a in name.split("_kernel<", 1)[1].split(">", 1)[0].split(","))
+        # elementwise_kernel<OP, DT, U>
+        op, dt = (a.strip() for a in name.split("_kernel<", 1)[1].split(">", 1)[0].split(",")[:2])
         return ("modulate_scale_shift" if op == "0" else "residual_gate_add") + \
             ("_bf16" if dt == "0" else "_f16")
     for key, label in (("qk_kernel", "qk_layernorm"), ("wan_kernel", "rmsnorm_silu_bias"),

@@ -9,7 +9,7 @@ implementation to fall back to -- if the library is missing or rejects a call,
 the call raises.
 
 Entry points (same names as the C ABI):
-    ln_modulate, gated_ln_modulate, rms_modulate, qk_layernorm,
+    ln_modulate, ln_modulate_folded, gated_ln_modulate, rms_modulate, qk_layernorm,
     rmsnorm_silu_bias, conv_bias_epilogue, modulate_scale_shift, residual_gate_add, copy
 """
 from __future__ import annotations
@@ -19,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["load", "ln_modulate", "gated_ln_modulate", "rms_modulate", "qk_layernorm",
+__all__ = ["load", "ln_modulate", "ln_modulate_folded", "gated_ln_modulate", "rms_modulate", "qk_layernorm",
            "rmsnorm_silu_bias", "conv_bias_epilogue", "modulate_scale_shift",
            "residual_gate_add", "copy", "DitnormError", "LIB_PATH"]
 
@@ -47,6 +47,7 @@ _DTYPE_CODES = {torch.bfloat16: 0, torch.float16: 1}
 
 _SIGNATURES = {
     "ln_modulate": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp],
+    "ln_modulate_folded": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp],
     "gated_ln_modulate": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32,
                           _vp, _vp, _vp, _vp],
     "rms_modulate": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32,
@@ -58,6 +59,8 @@ _SIGNATURES = {
     "residual_gate_add": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp],
     "ditnorm_copy": [_vp, _vp, _i64, _vp],
     "ln_modulate_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp],
+    "ln_modulate_folded_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp,
+                                     _vp],
     "gated_ln_modulate_supported": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                     _f32, _vp, _vp, _vp],
     "rms_modulate_supported": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
@@ -176,6 +179,22 @@ def ln_modulate(x, scale, shift, eps=1e-6, out=None, *, mean_out=None, rstd_out=
           stride, eps, _p(_f32_out(mean_out, rows, "mean_out")),
           _p(_f32_out(rstd_out, rows, "rstd_out")),
           _p(None if y_out is None else _act(y_out, "y_out")), _stream(x))
+    return out
+
+
+def ln_modulate_folded(x, scale, shift, eps=1e-6, out=None, *, mean_out=None, rstd_out=None):
+    """The lossy one-pass form: out = bf16((rstd*(x-mean)) * bf16(1+scale) + shift),
+    fp32 ops on the unrounded normalised value; x (..., D) bf16."""
+    _act(x, "x")
+    rows, cols = _rows_cols(x)
+    scale, b, stride = _mod(scale, "scale", cols, x.device)
+    shift, b2, stride2 = _mod(shift, "shift", cols, x.device)
+    if (b, stride) != (b2, stride2):
+        raise ValueError("scale and shift must have the same batch count and stride")
+    out = torch.empty_like(x) if out is None else _act(out, "out")
+    _call("ln_modulate_folded", _p(x), _p(scale), _p(shift), _p(out), rows, cols,
+          _batch(rows, b), stride, eps, _p(_f32_out(mean_out, rows, "mean_out")),
+          _p(_f32_out(rstd_out, rows, "rstd_out")), _stream(x))
     return out
 
 

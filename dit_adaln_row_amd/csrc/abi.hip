@@ -286,9 +286,10 @@ int ditnorm_last_hip_error(void) { return g_last_hip_error; }
 
 int ditnorm_version(void) { return 100; }
 
-int ln_modulate(const void *x, const void *scale, const void *shift, void *out, int64_t rows,
-                int64_t cols, int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
-                float *mean_out, float *rstd_out, void *y_out, void *stream) {
+namespace {
+int ln_common(const void *x, const void *scale, const void *shift, void *out, int64_t rows,
+              int64_t cols, int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
+              float *mean_out, float *rstd_out, void *y_out, bool fold, void *stream) {
   int st = validate_ln(x, scale, shift, out, rows, cols, rows_per_batch, mod_batch_stride, eps,
                        mean_out, rstd_out, y_out);
   if (st != DITNORM_OK || rows == 0) return st;
@@ -307,7 +308,23 @@ int ln_modulate(const void *x, const void *scale, const void *shift, void *out, 
   a.rows_per_batch = rows_per_batch;
   a.mod_stride = mod_batch_stride;
   a.eps = eps;
-  return finish(launch_row(a, false, false, dev, (hipStream_t)stream));
+  return finish(launch_row(a, false, false, fold, dev, (hipStream_t)stream));
+}
+}  // namespace
+
+int ln_modulate(const void *x, const void *scale, const void *shift, void *out, int64_t rows,
+                int64_t cols, int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
+                float *mean_out, float *rstd_out, void *y_out, void *stream) {
+  return ln_common(x, scale, shift, out, rows, cols, rows_per_batch, mod_batch_stride, eps,
+                   mean_out, rstd_out, y_out, false, stream);
+}
+
+int ln_modulate_folded(const void *x, const void *scale, const void *shift, void *out,
+                       int64_t rows, int64_t cols, int64_t rows_per_batch,
+                       int64_t mod_batch_stride, float eps, float *mean_out, float *rstd_out,
+                       void *stream) {
+  return ln_common(x, scale, shift, out, rows, cols, rows_per_batch, mod_batch_stride, eps,
+                   mean_out, rstd_out, nullptr, true, stream);
 }
 
 int gated_ln_modulate(const void *x, const void *residual, const void *gate, const void *scale,
@@ -335,7 +352,7 @@ int gated_ln_modulate(const void *x, const void *residual, const void *gate, con
   a.rows_per_batch = rows_per_batch;
   a.mod_stride = mod_batch_stride;
   a.eps = eps;
-  return finish(launch_row(a, false, true, dev, (hipStream_t)stream));
+  return finish(launch_row(a, false, true, false, dev, (hipStream_t)stream));
 }
 
 int rms_modulate(const void *x, const void *weight, const void *scale, const void *shift,
@@ -363,7 +380,7 @@ int rms_modulate(const void *x, const void *weight, const void *scale, const voi
   a.rows_per_batch = rows_per_batch;
   a.mod_stride = mod_batch_stride;
   a.eps = eps;
-  return finish(launch_row(a, true, residual != nullptr, dev, (hipStream_t)stream));
+  return finish(launch_row(a, true, residual != nullptr, false, dev, (hipStream_t)stream));
 }
 
 int qk_layernorm(const void *q, const void *k, void *q_out, void *k_out, int64_t rows_q,
@@ -428,6 +445,14 @@ int ln_modulate_supported(const void *x, const void *scale, const void *shift, c
                           const float *rstd_out, const void *y_out) {
   return validate_ln(x, scale, shift, out, rows, cols, rows_per_batch, mod_batch_stride, eps,
                      mean_out, rstd_out, y_out) == DITNORM_OK;
+}
+
+int ln_modulate_folded_supported(const void *x, const void *scale, const void *shift,
+                                 const void *out, int64_t rows, int64_t cols,
+                                 int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
+                                 const float *mean_out, const float *rstd_out) {
+  return validate_ln(x, scale, shift, out, rows, cols, rows_per_batch, mod_batch_stride, eps,
+                     mean_out, rstd_out, nullptr) == DITNORM_OK;
 }
 
 int gated_ln_modulate_supported(const void *x, const void *residual, const void *gate,

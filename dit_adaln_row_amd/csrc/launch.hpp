@@ -33,7 +33,8 @@ struct RowArgs {
   int32_t cols;
   float eps;
 };
-hipError_t launch_row(const RowArgs &a, bool rms, bool gated, const DeviceInfo &dev,
+// fold: the affine-folded LN form (LN only: rms and gated false)
+hipError_t launch_row(const RowArgs &a, bool rms, bool gated, bool fold, const DeviceInfo &dev,
                       hipStream_t stream);
 
 // Per-head LayerNorm over 128-wide rows of q then k.

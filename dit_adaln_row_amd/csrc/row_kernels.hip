@@ -12,6 +12,9 @@
 //           (ERNIE-Image page, "What rounding-faithful means here")
 //   out = bf16(bf16(y * bf16(1 + scale)) + shift)   (the eager modulate's
 //           three rounded kernels; FLUX.1 page, Commit 2)
+//   FOLD (LN only, the lossy affine-folded form of the FLUX.1 page, Commit 3):
+//           out = bf16((rstd * (x - mean)) * bf16(1 + scale) + shift), every
+//           op in fp32 on the unrounded normalised value, one rounding
 //
 // Layout of the work on gfx950.  One workgroup of NT threads (NT/64
 // wavefronts) owns one row at a time; thread t holds the 16-byte vectors
@@ -27,7 +30,7 @@
 
 namespace ditnorm {
 
-template <int NT, int NV, bool RMS, bool GATED>
+template <int NT, int NV, bool RMS, bool GATED, bool FOLD = false>
 __global__ __launch_bounds__(NT) void row_kernel(const RowArgs a) {
   constexpr int NW = NT / 64;
   __shared__ double red[2][2][NW];  // [row parity][pass][wave]
@@ -199,6 +202,13 @@ __global__ __launch_bounds__(NT) void row_kernel(const RowArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         float y0, y1;
+        if constexpr (FOLD) {
+          const float t0 = rstd_f * (v[k][e] - mean_f), t1 = rstd_f * (v[k][e + 1] - mean_f);
+          const float p0 = t0 * s1[k][e], p1 = t1 * s1[k][e + 1];
+          o[e] = p0 + sh[k][e];
+          o[e + 1] = p1 + sh[k][e + 1];
+          continue;
+        }
         if constexpr (RMS) {
           y0 = (v[k][e] * rstd_f) * wt[k][e];
           y1 = (v[k][e + 1] * rstd_f) * wt[k][e + 1];
@@ -217,7 +227,7 @@ __global__ __launch_bounds__(NT) void row_kernel(const RowArgs a) {
       if (ok[k]) {
         const int64_t off = row * (int64_t)cols + vcol[k];
         st16(a.out + off, pack8(o));
-        if (a.y_out) st16(a.y_out + off, pack8(y));
+        if (!FOLD && a.y_out) st16(a.y_out + off, pack8(y));
       }
     }
   }
@@ -266,7 +276,7 @@ __device__ __forceinline__ const T *pin(const T *p) {
   return p;
 }
 
-template <int NV, bool FULL, bool RMS, bool GATED, int MODE = MOD_LDS>
+template <int NV, bool FULL, bool RMS, bool GATED, int MODE = MOD_LDS, bool FOLD = false>
 __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
   constexpr bool MODLDS = MODE == MOD_LDS;
   __shared__ float4 lds_s1[MODLDS ? NV * 128 : 1], lds_sh[MODLDS ? NV * 128 : 1];
@@ -426,6 +436,16 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
         round2(s1v[e], s1v[e + 1]);
       }
     }
+    if constexpr (FOLD) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = rstd_f * (v[e] - mean_f);
+        const float p = t * s1v[e];
+        o[e] = p + shv[e];
+      }
+      st16s(a.out + base + col(k), pack8(o));
+      continue;
+    }
     if constexpr (RMS) {
       float w[8];
       if constexpr (HOLD) unpack8(mw[k], w);
@@ -450,8 +470,12 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
 }
 
 template <int NV, bool FULL, int MODE = MOD_LDS>
-hipError_t launch_wave(const RowArgs &a, bool rms, bool gated, hipStream_t stream) {
+hipError_t launch_wave(const RowArgs &a, bool rms, bool gated, bool fold, hipStream_t stream) {
   const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
+  if (fold) {  // LN only
+    hipLaunchKernelGGL((row_wave_kernel<NV, FULL, false, false, MODE, true>), grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
   if (!rms && !gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, false, false, MODE>), grid, block, 0, stream, a);
   if (!rms && gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, false, true, MODE>), grid, block, 0, stream, a);
   if (rms && !gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, true, false, MODE>), grid, block, 0, stream, a);
@@ -464,8 +488,8 @@ hipError_t launch_wave(const RowArgs &a, bool rms, bool gated, hipStream_t strea
 // ---------------------------------------------------------------------------
 
 template <int NT, int NV>
-static hipError_t launch_cfg(const RowArgs &a, bool rms, bool gated, const DeviceInfo &dev,
-                             hipStream_t stream) {
+static hipError_t launch_cfg(const RowArgs &a, bool rms, bool gated, bool fold,
+                             const DeviceInfo &dev, hipStream_t stream) {
   const void *kfn;
 #define DITNORM_PICK(R, G) \
   if (rms == R && gated == G) kfn = (const void *)row_kernel<NT, NV, R, G>;
@@ -475,6 +499,7 @@ static hipError_t launch_cfg(const RowArgs &a, bool rms, bool gated, const Devic
   DITNORM_PICK(true, false)
   DITNORM_PICK(true, true)
 #undef DITNORM_PICK
+  if (fold) kfn = (const void *)row_kernel<NT, NV, false, false, true>;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, NT, 0) != hipSuccess ||
       per_cu < 1)
@@ -485,7 +510,7 @@ static hipError_t launch_cfg(const RowArgs &a, bool rms, bool gated, const Devic
   return hipLaunchKernel(kfn, dim3((unsigned)grid), dim3(NT), args, 0, stream);
 }
 
-hipError_t launch_row(const RowArgs &a, bool rms, bool gated, const DeviceInfo &dev,
+hipError_t launch_row(const RowArgs &a, bool rms, bool gated, bool fold, const DeviceInfo &dev,
                       hipStream_t stream) {
   const int nvec = a.cols / 8;
   // Rows up to 4096 columns: one wavefront per row.  The gated sites stage
@@ -494,38 +519,38 @@ hipError_t launch_row(const RowArgs &a, bool rms, bool gated, const DeviceInfo &
   // row from the caches, which measured faster than the workgroup barrier.
   if (gated) {
     switch (nvec) {
-      case 128: return launch_wave<2, true, MOD_LDS>(a, rms, gated, stream);
-      case 256: return launch_wave<4, true, MOD_LDS>(a, rms, gated, stream);
-      case 384: return launch_wave<6, true, MOD_LDS>(a, rms, gated, stream);
-      case 512: return launch_wave<8, true, MOD_LDS>(a, rms, gated, stream);
+      case 128: return launch_wave<2, true, MOD_LDS>(a, rms, gated, fold, stream);
+      case 256: return launch_wave<4, true, MOD_LDS>(a, rms, gated, fold, stream);
+      case 384: return launch_wave<6, true, MOD_LDS>(a, rms, gated, fold, stream);
+      case 512: return launch_wave<8, true, MOD_LDS>(a, rms, gated, fold, stream);
       default: break;
     }
   } else {
     switch (nvec) {
-      case 128: return launch_wave<2, true, MOD_SERIAL>(a, rms, gated, stream);
-      case 256: return launch_wave<4, true, MOD_SERIAL>(a, rms, gated, stream);
-      case 384: return launch_wave<6, true, MOD_SERIAL>(a, rms, gated, stream);
-      case 512: return launch_wave<8, true, MOD_SERIAL>(a, rms, gated, stream);
+      case 128: return launch_wave<2, true, MOD_SERIAL>(a, rms, gated, fold, stream);
+      case 256: return launch_wave<4, true, MOD_SERIAL>(a, rms, gated, fold, stream);
+      case 384: return launch_wave<6, true, MOD_SERIAL>(a, rms, gated, fold, stream);
+      case 512: return launch_wave<8, true, MOD_SERIAL>(a, rms, gated, fold, stream);
       default: break;
     }
   }
-  if (nvec <= 64) return launch_wave<1, false>(a, rms, gated, stream);
-  if (nvec <= 128) return launch_wave<2, false>(a, rms, gated, stream);
-  if (nvec <= 256) return launch_wave<4, false>(a, rms, gated, stream);
-  if (nvec <= 384) return launch_wave<6, false>(a, rms, gated, stream);
-  if (nvec <= 512) return launch_wave<8, false>(a, rms, gated, stream);
+  if (nvec <= 64) return launch_wave<1, false>(a, rms, gated, fold, stream);
+  if (nvec <= 128) return launch_wave<2, false>(a, rms, gated, fold, stream);
+  if (nvec <= 256) return launch_wave<4, false>(a, rms, gated, fold, stream);
+  if (nvec <= 384) return launch_wave<6, false>(a, rms, gated, fold, stream);
+  if (nvec <= 512) return launch_wave<8, false>(a, rms, gated, fold, stream);
   // wider rows: one workgroup per row
   // (threads, vectors per thread): the row must fit NT*NV vectors; prefer
   // exact fits and 2-4 vectors (16-32 values) per thread.
-  if (nvec <= 64) return launch_cfg<64, 1>(a, rms, gated, dev, stream);
-  if (nvec <= 128) return launch_cfg<64, 2>(a, rms, gated, dev, stream);
-  if (nvec <= 192) return launch_cfg<64, 3>(a, rms, gated, dev, stream);
-  if (nvec <= 256) return launch_cfg<128, 2>(a, rms, gated, dev, stream);
-  if (nvec <= 384) return launch_cfg<128, 3>(a, rms, gated, dev, stream);
-  if (nvec <= 512) return launch_cfg<128, 4>(a, rms, gated, dev, stream);
-  if (nvec <= 768) return launch_cfg<256, 3>(a, rms, gated, dev, stream);
-  if (nvec <= 1024) return launch_cfg<256, 4>(a, rms, gated, dev, stream);
-  return launch_cfg<512, 4>(a, rms, gated, dev, stream);  // up to 16384 columns
+  if (nvec <= 64) return launch_cfg<64, 1>(a, rms, gated, fold, dev, stream);
+  if (nvec <= 128) return launch_cfg<64, 2>(a, rms, gated, fold, dev, stream);
+  if (nvec <= 192) return launch_cfg<64, 3>(a, rms, gated, fold, dev, stream);
+  if (nvec <= 256) return launch_cfg<128, 2>(a, rms, gated, fold, dev, stream);
+  if (nvec <= 384) return launch_cfg<128, 3>(a, rms, gated, fold, dev, stream);
+  if (nvec <= 512) return launch_cfg<128, 4>(a, rms, gated, fold, dev, stream);
+  if (nvec <= 768) return launch_cfg<256, 3>(a, rms, gated, fold, dev, stream);
+  if (nvec <= 1024) return launch_cfg<256, 4>(a, rms, gated, fold, dev, stream);
+  return launch_cfg<512, 4>(a, rms, gated, fold, dev, stream);  // up to 16384 columns
 }
 
 }  // namespace ditnorm

@@ -46,7 +46,7 @@ class Launch:
 
     def algorithmic_bytes(self) -> int:
         r, c = self.rows, self.cols
-        if self.entry == "ln_modulate":
+        if self.entry in ("ln_modulate", "ln_modulate_folded"):
             return 2 * r * c * BF16 + 2 * self.n_mod_rows * c * BF16
         if self.entry == "gated_ln_modulate":
             return 4 * r * c * BF16 + 3 * self.n_mod_rows * c * BF16
@@ -172,6 +172,15 @@ WORKLOADS = {
          Tensor("gamma", (384,), 1.0, 0.05, "f32_bf16vals")),
         (Launch("rmsnorm_silu_bias", "rmsnorm_silu_bias", 4 * 240 * 416, 384,
                 ("x", "bias", "gamma"), 1e-6),),
+    ),
+    "flux_folded_1x4608x3072": Workload(
+        "flux_folded_1x4608x3072", 10,
+        "FLUX.1-like LN with the modulate folded into its affine (lossy form), (1,4608,3072): "
+        "x ~N(0,1.5), scale/shift (1,3072) ~N(0,0.1)",
+        (Tensor("x", (4608, 3072), 0.0, 1.5), Tensor("scale", (1, 3072), 0.0, 0.1),
+         Tensor("shift", (1, 3072), 0.0, 0.1)),
+        (Launch("ln_modulate_folded", "ln_modulate_folded", 4608, 3072, ("x", "scale", "shift"),
+                1e-6),),
     ),
     "flux_elementwise_1x4608x3072": Workload(
         "flux_elementwise_1x4608x3072", 7,

@@ -110,6 +110,28 @@ int ln_modulate(const void *x, const void *scale, const void *shift, void *out,
                 void *y_out, void *stream);
 
 /*
+ * ln_modulate_folded -- the lossy one-pass form of ln_modulate: the modulate
+ * folded into the LayerNorm's elementwise affine.
+ *
+ * FLUX.1 page ("[diffusion] FLUX.1 fused adaLN modulate (bit-exact) + RoPE
+ * cache hoist, LN-affine folding behind quality=high", Commit 3): LayerNorm
+ * with weight = bf16(1 + scale) (the [D] row keeps its eager rounding) and
+ * bias = shift, so scale and shift act in fp32 on the unrounded normalised
+ * value and the result is rounded once:
+ *     t   = rstd * (x - mean)                           fp32, not rounded
+ *     out = bf16( (t * bf16(1 + scale)) + shift )      fp32 ops, no FMA
+ * Not bit-exact with ln_modulate (the pages report a max abs difference of
+ * about 0.05 on FLUX.1 shapes); for callers that accept that, as the pages'
+ * quality tier does.  Statistics as for ln_modulate (mean_out, rstd_out
+ * optional).  Arguments, layout, batching and aliasing as for ln_modulate;
+ * unlike the pages' per-call guard, B > 1 modulation rows are supported.
+ */
+int ln_modulate_folded(const void *x, const void *scale, const void *shift, void *out,
+                       int64_t rows, int64_t cols, int64_t rows_per_batch,
+                       int64_t mod_batch_stride, float eps, float *mean_out, float *rstd_out,
+                       void *stream);
+
+/*
  * gated_ln_modulate -- the pre-norm gated residual, then ln_modulate on it.
  *
  * The residual-gate half of the adaLN block (GLM-Image page, ff gate
@@ -246,6 +268,10 @@ int ln_modulate_supported(const void *x, const void *scale, const void *shift,
                           const void *out, int64_t rows, int64_t cols,
                           int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
                           const float *mean_out, const float *rstd_out, const void *y_out);
+int ln_modulate_folded_supported(const void *x, const void *scale, const void *shift,
+                                 const void *out, int64_t rows, int64_t cols,
+                                 int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
+                                 const float *mean_out, const float *rstd_out);
 int gated_ln_modulate_supported(const void *x, const void *residual, const void *gate,
                                 const void *scale, const void *shift,
                                 const void *residual_out, const void *out, int64_t rows,

@@ -66,6 +66,8 @@ def _load():
             "oracle_silu_normalize": [_u16p, _f32p, _f32p, _u16p, _i64, _i64],
             "oracle_ln_modulate": [_u16p, _u16p, _u16p, _u16p, _i64, _i64, _i64, _i64,
                                    ctypes.c_float, _f32p, _f32p, _u16p],
+            "oracle_ln_modulate_folded": [_u16p, _u16p, _u16p, _u16p, _i64, _i64, _i64, _i64,
+                                          ctypes.c_float, _f32p, _f32p],
             "oracle_gated_ln_modulate": [_u16p, _u16p, _u16p, _u16p, _u16p, _u16p, _u16p,
                                          _i64, _i64, _i64, _i64, ctypes.c_float,
                                          _f32p, _f32p, _u16p],
@@ -285,6 +287,23 @@ def ln_modulate(x, scale, shift, eps, rows_per_batch=None, row_slice=None):
                                       _p(out, _u16p), rows, cols, rpb, stride, eps,
                                       _p(mean, _f32p), _p(rstd, _f32p), _p(y, _u16p)))
     return dict(out=out, mean=mean, rstd=rstd, y=y)
+
+
+def ln_modulate_folded(x, scale, shift, eps, rows_per_batch=None):
+    """LN with the modulate folded into its affine (lossy one-pass form).
+    Returns dict(out, mean, rstd)."""
+    x = _u16(x)
+    rows, cols = x.shape
+    scale, stride = _mod_rows(scale, cols)
+    shift, _ = _mod_rows(shift, cols)
+    rpb = rows_per_batch or max(rows, 1)
+    out = np.empty_like(x)
+    mean = np.empty(rows, np.float32)
+    rstd = np.empty(rows, np.float32)
+    _check(_load().oracle_ln_modulate_folded(_p(x, _u16p), _p(scale, _u16p), _p(shift, _u16p),
+                                             _p(out, _u16p), rows, cols, rpb, stride, eps,
+                                             _p(mean, _f32p), _p(rstd, _f32p)))
+    return dict(out=out, mean=mean, rstd=rstd)
 
 
 def gated_ln_modulate(update, residual, gate, scale, shift, eps, rows_per_batch=None):

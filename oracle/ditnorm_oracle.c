@@ -42,6 +42,16 @@
  *    H columns (no mean subtraction), rstd = 1/sqrt(ms + eps) in fp32, and one
  *    rounding of the product x * rstd * w evaluated left to right.
  *
+ *  - LN-affine folding, the lossy one-pass form ("FLUX.1 fused adaLN
+ *    modulate (bit-exact) + RoPE cache hoist, LN-affine folding behind
+ *    quality=high", Commit 3): the modulate becomes the LayerNorm's affine,
+ *    weight = bf16(1 + scale) (the [D] row keeps its eager rounding) and
+ *    bias = shift, applied in fp32 to the unrounded normalised value and
+ *    rounded once: out = bf16((rstd * (x - mean)) * w + shift).  The page
+ *    leaves the fp32 order of the affine open; the order written here (the
+ *    normalise's subtract-then-multiply, then the weight, then the bias, no
+ *    FMA) is the plain reading.
+ *
  *  - Gated residual (pre-norm; same ERNIE page, second kernel, and the GLM
  *    page's ff-gate):  h = bf16(residual + bf16(gate * update)); the norm
  *    then runs on h, and h is returned as the residual stream.
@@ -227,6 +237,15 @@ static uint16_t modulate(uint16_t y, uint16_t scale, uint16_t shift)
     uint16_t s1 = f32_to_bf16(1.0f + bf16_to_f32(scale));
     uint16_t p = f32_to_bf16(bf16_to_f32(y) * bf16_to_f32(s1));
     return f32_to_bf16(bf16_to_f32(p) + bf16_to_f32(shift));
+}
+
+static uint16_t ln_modulate_folded(float x, float mean, float rstd, uint16_t scale,
+                                   uint16_t shift)
+{
+    float t = rstd * (x - mean);
+    float w = bf16_to_f32(f32_to_bf16(1.0f + bf16_to_f32(scale)));
+    float p = t * w;
+    return f32_to_bf16(p + bf16_to_f32(shift));
 }
 
 static uint16_t gate_residual(uint16_t residual, uint16_t gate, uint16_t update)
@@ -491,6 +510,34 @@ int oracle_ln_modulate(const uint16_t *x, const uint16_t *scale, const uint16_t 
             out[r * cols + c] = modulate(y, scale[b * mod_batch_stride + c],
                                          shift[b * mod_batch_stride + c]);
         }
+    }
+    return OR_OK;
+}
+
+/* LN with the modulate folded into its affine (lossy form).  mean_out /
+ * rstd_out may be NULL. */
+int oracle_ln_modulate_folded(const uint16_t *x, const uint16_t *scale, const uint16_t *shift,
+                              uint16_t *out, int64_t rows, int64_t cols, int64_t rows_per_batch,
+                              int64_t mod_batch_stride, float eps, float *mean_out,
+                              float *rstd_out)
+{
+    if (!mod_args_ok(rows, cols, rows_per_batch, mod_batch_stride))
+        return OR_INVALID;
+    if (cols > OR_MAX_COLS)
+        return OR_INVALID;
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *xr = widen_row(x + r * cols, cols);
+        int64_t b = r / rows_per_batch;
+        float mean, rstd;
+        ln_stats(xr, cols, eps, &mean, &rstd);
+        if (mean_out)
+            mean_out[r] = mean;
+        if (rstd_out)
+            rstd_out[r] = rstd;
+        for (int64_t c = 0; c < cols; ++c)
+            out[r * cols + c] = ln_modulate_folded(xr[c], mean, rstd,
+                                                   scale[b * mod_batch_stride + c],
+                                                   shift[b * mod_batch_stride + c]);
     }
     return OR_OK;
 }

@@ -39,7 +39,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    for must in ("ln_modulate", "gated_ln_modulate", "rms_modulate", "qk_layernorm",
+    for must in ("ln_modulate", "ln_modulate_folded", "gated_ln_modulate", "rms_modulate", "qk_layernorm",
                  "rmsnorm_silu_bias", "conv_bias_epilogue", "modulate_scale_shift",
                  "residual_gate_add", "ditnorm_status_string"):
         assert must in names
@@ -105,6 +105,10 @@ def test_supported_predicates_never_touch_the_gpu(lib):
     assert lib.conv_bias_epilogue_supported(A, B, C, D, 100, 96) == 1
     assert lib.conv_bias_epilogue_supported(A, B, C, A, 100, 96) == 1      # in place
     assert lib.conv_bias_epilogue_supported(A, B, C, C, 100, 96) == 0      # out over h
+    assert lib.ln_modulate_folded_supported(A, B, C, D, 4, 3072, 4, 3072, 1e-6, None, None) == 1
+    assert lib.ln_modulate_folded_supported(A, B, C, A, 4, 3072, 4, 3072, 1e-6, None, None) == 1
+    assert lib.ln_modulate_folded_supported(A, B, C, D, 4, 3076, 4, 3076, 1e-6, None, None) == 0
+    assert lib.ln_modulate_folded_supported(A, B, C, D, 4, 3072, 4, 3072, -1.0, None, None) == 0
     for dt in (0, 1):
         assert lib.modulate_scale_shift_supported(A, B, C, D, 8, 3072, 4, 6 * 3072, dt) == 1
         assert lib.modulate_scale_shift_supported(A, B, C, A, 8, 3072, 4, 3072, dt) == 1  # in place
@@ -128,6 +132,10 @@ def test_other_entry_validation(lib):
     assert lib.rmsnorm_silu_bias(A, B, None, D, 10, 96, 1e-6, None, None, None) == dn.INVALID_ARGUMENT
     assert lib.rmsnorm_silu_bias(A, B, C, D, 10, 4104, 1e-6, None, None, None) == dn.UNSUPPORTED
     assert lib.conv_bias_epilogue(A, None, None, D, 10, 96, None) == dn.INVALID_ARGUMENT
+    assert lib.ln_modulate_folded(A, B, None, D, 4, 3072, 4, 3072, 1e-6, None, None,
+                                  None) == dn.INVALID_ARGUMENT
+    assert lib.ln_modulate_folded(A, B, C, D, 4, 3072, 3, 3072, 1e-6, None, None,
+                                  None) == dn.INVALID_ARGUMENT
     assert lib.modulate_scale_shift(A, B, C, D, 8, 3072, 8, 3072, 7, None) == dn.INVALID_ARGUMENT
     assert lib.modulate_scale_shift(A, B, None, D, 8, 3072, 8, 3072, 0, None) == dn.INVALID_ARGUMENT
     assert lib.modulate_scale_shift(A, B, C, D, 8, 3072, 3, 3072, 1, None) == dn.INVALID_ARGUMENT

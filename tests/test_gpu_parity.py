@@ -114,6 +114,28 @@ def test_ln_special_rows(gpu, orc):
     assert same_bits(out[7], ref["out"][7])                # NaN row: NaN everywhere
 
 
+@pytest.mark.parametrize("rows,cols,B", [(1, 8, 1), (257, 1024, 1), (100, 3072, 2), (37, 4096, 1),
+                                         (3, 16384, 1), (2, 9000, 2), (5, 2048, 5), (9, 1536, 3)])
+def test_ln_modulate_folded(gpu, orc, rows, cols, B):
+    """The lossy affine-folded LN: same statistics, one fp32 chain per element."""
+    log(f"ln_modulate_folded rows={rows} cols={cols} B={B}")
+    x = rand((rows, cols), 0.1, 1.5, 71 + cols)
+    emb = rand((B, 6 * cols), 0, 0.1, 72 + B)
+    embd = dev(emb)
+    sc_view, sh_view = embd[:, cols:2 * cols], embd[:, 0:cols]
+    mean, rstd = empty_f32(rows), empty_f32(rows)
+    xd = dev(x)
+    out = gpu.ln_modulate_folded(xd, sc_view, sh_view, 1e-6, mean_out=mean, rstd_out=rstd)
+    fast = gpu.ln_modulate_folded(xd, sc_view, sh_view, 1e-6)
+    torch.cuda.synchronize()
+    out, fast, mean, rstd = host(out), host(fast), host(mean), host(rstd)
+    assert same_bits(out, fast), "statistics outputs changed the result"
+    sc = np.concatenate([emb.ravel()[cols:], np.zeros(cols, np.uint16)]).reshape(B, 6 * cols)
+    ref = orc.ln_modulate_folded(x, sc, emb, 1e-6, rows_per_batch=rows // B)
+    differ = check_stats(mean, rstd, ref["mean"], ref["rstd"], "folded")
+    check_rows_end_to_end(out, ref["out"], np.repeat(differ[:, None], cols, 1), "folded")
+
+
 def test_gated_ln_modulate_shapes(gpu, orc):
     for rows, cols, B in [(7, 1024, 1), (300, 3072, 1), (2 * 65, 3072, 2), (33, 4096, 1)]:
         log(f"gated_ln_modulate rows={rows} cols={cols} B={B}")
@@ -309,6 +331,17 @@ def test_full_workload(gpu, orc, key):
                                 x.shape[0])
             _ln_check(orc, f"{key}/{l.name}", x, sc, sh, l.eps, x.shape[0], out, mean, rstd, y,
                       ref=ref)
+        elif l.entry == "ln_modulate_folded":
+            x, sc, sh = t["x"], t["scale"], t["shift"]
+            rows = x.shape[0]
+            mean, rstd = empty_f32(rows), empty_f32(rows)
+            out = host(gpu.ln_modulate_folded(dev(x), dev(sc), dev(sh), l.eps, mean_out=mean,
+                                              rstd_out=rstd))
+            torch.cuda.synchronize()
+            ref = by_row_chunks(lambda lo, hi: orc.ln_modulate_folded(x[lo:hi], sc, sh, l.eps),
+                                None, rows)
+            differ = check_stats(host(mean), host(rstd), ref["mean"], ref["rstd"], l.name)
+            check_rows_end_to_end(out, ref["out"], np.repeat(differ[:, None], x.shape[1], 1), l.name)
         elif l.entry == "gated_ln_modulate":
             upd, res, gate, sc, sh = (t[n] for n in ("update", "residual", "gate", "scale", "shift"))
             rows, cols = upd.shape

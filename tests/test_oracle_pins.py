@@ -563,3 +563,58 @@ def test_standalone_modulate_and_gate_match_eager(orc, dtype):
     if dtype == "bf16":   # the same stages as the fused paths use
         assert np.array_equal(orc.modulate_dt(bits(x), bits(sc), bits(sh), "bf16", S),
                               orc.modulate(bits(x), bits(sc), bits(sh), rows_per_batch=S))
+
+
+# ---------------------------------------------------------------------------
+# LN-affine folding (the lossy one-pass form; FLUX.1 page, Commit 3)
+# ---------------------------------------------------------------------------
+
+def test_folded_ln_pins(orc):
+    rows, cols = 64, 3072
+    x = rand_bf16((rows, cols), 0.0, 1.5, 700)
+    sc = rand_bf16((1, cols), 0, 0.1, 701)
+    sh = rand_bf16((1, cols), 0, 0.1, 702)
+    f = orc.ln_modulate_folded(x, sc, sh, 1e-6)
+    lossless = orc.ln_modulate(x, sc, sh, 1e-6)
+    # the statistics are the lossless LayerNorm's
+    assert np.array_equal(f["mean"].view(np.uint32), lossless["mean"].view(np.uint32))
+    assert np.array_equal(f["rstd"].view(np.uint32), lossless["rstd"].view(np.uint32))
+
+    # weight 1, bias 0: the unrounded normalised value rounded once, i.e. the
+    # lossless chain's y (equal up to the sign of zero)
+    z = np.zeros((1, cols), np.uint16)
+    f0 = orc.ln_modulate_folded(x, z, z, 1e-6)
+    assert np.array_equal(f32_from_u16(f0["out"]), f32_from_u16(lossless["y"]))
+
+    # scale = -1: the weight bf16(1 + scale) is 0, so out == shift exactly
+    m1 = np.full((1, cols), 0xBF80, np.uint16)
+    fm = orc.ln_modulate_folded(x, m1, sh, 1e-6)
+    assert np.array_equal(f32_from_u16(fm["out"]), np.broadcast_to(f32_from_u16(sh), (rows, cols)))
+
+    # library: torch's LayerNorm with weight = (1 + scale) in bf16 eager and
+    # bias = shift, evaluated in float64 (the page's layer_norm(x, weight=1+scale,
+    # bias=shift)); one rounding of an fp32 chain on fp32 statistics lands
+    # within half a bf16 ulp plus the chain's fp32 error
+    w = to_u16(torch.ones(cols, dtype=torch.bfloat16) + t_bf16(sc[0]))      # eager bf16 add
+    x64 = torch.from_numpy(f32_from_u16(x).astype(np.float64))
+    w64 = torch.from_numpy(f32_from_u16(w).astype(np.float64))
+    b64 = torch.from_numpy(f32_from_u16(sh[0]).astype(np.float64))
+    ref = torch.nn.functional.layer_norm(x64, (cols,), weight=w64, bias=b64, eps=1e-6).numpy()
+    tw = torch.nn.functional.layer_norm(x64, (cols,), eps=1e-6).numpy() * w64.numpy()
+    out = f32_from_u16(f["out"]).astype(np.float64)
+    chain = 2.0 ** -21 * (np.abs(tw) + np.abs(b64.numpy())) + \
+        f["rstd"][:, None].astype(np.float64) * np.abs(f["mean"][:, None]) * np.abs(w64.numpy()) * 2.0 ** -23
+    slack = 0.5 * ulp_bf16(np.abs(ref) + chain) + chain + 1e-30
+    assert np.all(np.abs(out - ref) <= slack)
+    assert np.mean(out == ref.astype(np.float32).astype(np.float64)) < 1.0  # it is rounded
+
+    # against the lossless three-rounding chain: the two extra roundings (y,
+    # then y * s1) and the two final ones differ by at most
+    # |s1| ulp(y)/2 + ulp(p)/2 + ulp(out) -- at this scale a few hundredths
+    # (the page reports a max abs difference of about 0.05 on FLUX.1 shapes)
+    y = f32_from_u16(lossless["y"]).astype(np.float64)
+    p = y * w64.numpy()
+    bound = np.abs(w64.numpy()) * 0.5 * ulp_bf16(y) + 0.5 * ulp_bf16(p) + ulp_bf16(np.abs(p) + np.abs(b64.numpy()))
+    diff = np.abs(out - f32_from_u16(lossless["out"]).astype(np.float64))
+    assert np.all(diff <= bound + 1e-30)
+    assert 0 < diff.max() <= 0.0625
