@@ -260,6 +260,11 @@ __device__ __forceinline__ int mod_slot(int j, int h) {
 
 // How a row kernel obtains its modulation operands (s1 = bf16(1+scale),
 // shift, and the RMS weight / the gate where used).
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 enum ModMode : int {
   MOD_SERIAL = 0,  // per 16-byte vector, from the caches, as each is needed
   MOD_LDS = 1,     // s1 / shift staged per workgroup in LDS (fp32); weight / gate as SERIAL
@@ -278,12 +283,16 @@ __device__ __forceinline__ const T *pin(const T *p) {
 
 template <int NV, bool FULL, bool RMS, bool GATED, int MODE = MOD_LDS, bool FOLD = false>
 __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
+  constexpr int WPB = 4;  // wavefronts (rows) per workgroup
+  constexpr int NT = 64 * WPB;
   constexpr bool MODLDS = MODE == MOD_LDS;
+  constexpr bool WLDS = MODLDS && RMS;  // the RMS weight staged too
   __shared__ float4 lds_s1[MODLDS ? NV * 128 : 1], lds_sh[MODLDS ? NV * 128 : 1];
+  __shared__ float4 lds_w[WLDS ? NV * 128 : 1];
   const int lane = threadIdx.x & 63;
   const int cols = a.cols;
   const int nvec = cols >> 3;
-  const int64_t row0 = (int64_t)blockIdx.x * 4;
+  const int64_t row0 = (int64_t)blockIdx.x * WPB;
   const int64_t row = row0 + wave_id();
   const bool live = row < a.rows;
   const int64_t base = row * (int64_t)cols;
@@ -294,15 +303,16 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
   // Modulation rows of the workgroup's first batch (cache-resident).  Issued
   // before the row loads: loads return in order, so the LDS staging below
   // waits only for these, while the row is still on its way from HBM.
-  constexpr int FILL = MODLDS ? (NV * 64 + 255) / 256 : 0;
+  constexpr int FILL = MODLDS ? (NV * 64 + NT - 1) / NT : 0;
   const int64_t b0 = row0 / a.rows_per_batch;
-  uint4 fsc[FILL > 0 ? FILL : 1], fsh[FILL > 0 ? FILL : 1];
+  uint4 fsc[FILL > 0 ? FILL : 1], fsh[FILL > 0 ? FILL : 1], fw[WLDS ? FILL : 1];
 #pragma unroll
   for (int i = 0; i < FILL; ++i) {
-    const int j = threadIdx.x + 256 * i;
+    const int j = threadIdx.x + NT * i;
     const bool in = j < nvec;
     fsc[i] = in ? ld16(a.scale + b0 * a.mod_stride + j * 8) : zero;
     fsh[i] = in ? ld16(a.shift + b0 * a.mod_stride + j * 8) : zero;
+    if constexpr (WLDS) fw[i] = in ? ld16(a.weight + j * 8) : zero;
   }
 
   // this wavefront's row
@@ -337,7 +347,7 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
   // stage s1 = bf16(1 + scale) and shift in LDS as fp32
 #pragma unroll
   for (int i = 0; i < FILL; ++i) {
-    const int j = threadIdx.x + 256 * i;
+    const int j = threadIdx.x + NT * i;
     if (j >= NV * 64) break;
     float sc[8], sh[8];
     unpack8(fsc[i], sc);
@@ -352,6 +362,12 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
     lds_s1[mod_slot(j, 1) / 4] = make_float4(sc[4], sc[5], sc[6], sc[7]);
     lds_sh[mod_slot(j, 0) / 4] = make_float4(sh[0], sh[1], sh[2], sh[3]);
     lds_sh[mod_slot(j, 1) / 4] = make_float4(sh[4], sh[5], sh[6], sh[7]);
+    if constexpr (WLDS) {
+      float w[8];
+      unpack8(fw[i], w);
+      lds_w[mod_slot(j, 0) / 4] = make_float4(w[0], w[1], w[2], w[3]);
+      lds_w[mod_slot(j, 1) / 4] = make_float4(w[4], w[5], w[6], w[7]);
+    }
   }
   if constexpr (MODLDS) lds_barrier();
   if (!live) return;  // whole wavefront; no barrier follows
@@ -378,14 +394,15 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
     }
   }
 
-  // statistics: one pass of binary64 moments (padding vectors hold zeros)
+  // statistics: one pass of binary64 moments (padding vectors hold zeros).
+  // The widened row stays in registers for the normalise pass.
   Moments m = {0.0, 0.0};
+  float xf[NV][8];
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    float v[8];
-    unpack8(xv[k], v);
+    unpack8(xv[k], xf[k]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) accumulate(m, v[e]);
+    for (int e = 0; e < 8; ++e) accumulate(m, xf[k][e]);
   }
   const double n_d = (double)cols;
   const double s2 = sum64(m.s2);
@@ -405,81 +422,103 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
   }
   if constexpr (MODE == MOD_BATCH) load_mod(pin(a.scale), pin(a.shift), pin(a.weight));
 
-  // normalise, modulate, store
+  // normalise, modulate, store.  The two run-time choices (debug output,
+  // modulation source) are taken once, outside the loop, so the unrolled
+  // loop is one basic block the scheduler can interleave freely.
+  auto normalise = [&](auto with_y, auto from_lds) {
+    constexpr bool WY = decltype(with_y)::value, FROM_LDS = decltype(from_lds)::value;
 #pragma unroll
-  for (int k = 0; k < NV; ++k) launder(xv[k]);
-#pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    if (!ok(k)) continue;
-    float v[8], s1v[8], shv[8], y[8], o[8];
-    unpack8(xv[k], v);
-    if (mod_in_lds) {
-      const int j = lane + 64 * k;
-      const float4 a0 = lds_s1[mod_slot(j, 0) / 4], a1 = lds_s1[mod_slot(j, 1) / 4];
-      const float4 c0 = lds_sh[mod_slot(j, 0) / 4], c1 = lds_sh[mod_slot(j, 1) / 4];
-      s1v[0] = a0.x; s1v[1] = a0.y; s1v[2] = a0.z; s1v[3] = a0.w;
-      s1v[4] = a1.x; s1v[5] = a1.y; s1v[6] = a1.z; s1v[7] = a1.w;
-      shv[0] = c0.x; shv[1] = c0.y; shv[2] = c0.z; shv[3] = c0.w;
-      shv[4] = c1.x; shv[5] = c1.y; shv[6] = c1.z; shv[7] = c1.w;
-    } else {
-      if constexpr (HOLD) {
-        unpack8(ms[k], s1v);
-        unpack8(mh[k], shv);
+    for (int k = 0; k < NV; ++k) {
+      if (!ok(k)) continue;
+      float s1v[8], shv[8], y[8], o[8];
+      const float *v = xf[k];
+      if constexpr (FROM_LDS) {
+        const int j = lane + 64 * k;
+        const float4 a0 = lds_s1[mod_slot(j, 0) / 4], a1 = lds_s1[mod_slot(j, 1) / 4];
+        const float4 c0 = lds_sh[mod_slot(j, 0) / 4], c1 = lds_sh[mod_slot(j, 1) / 4];
+        s1v[0] = a0.x; s1v[1] = a0.y; s1v[2] = a0.z; s1v[3] = a0.w;
+        s1v[4] = a1.x; s1v[5] = a1.y; s1v[6] = a1.z; s1v[7] = a1.w;
+        shv[0] = c0.x; shv[1] = c0.y; shv[2] = c0.z; shv[3] = c0.w;
+        shv[4] = c1.x; shv[5] = c1.y; shv[6] = c1.z; shv[7] = c1.w;
       } else {
-        unpack8(ld16(a.scale + mo + col(k)), s1v);
-        unpack8(ld16(a.shift + mo + col(k)), shv);
+        if constexpr (HOLD) {
+          unpack8(ms[k], s1v);
+          unpack8(mh[k], shv);
+        } else {
+          unpack8(ld16(a.scale + mo + col(k)), s1v);
+          unpack8(ld16(a.shift + mo + col(k)), shv);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          s1v[e] = 1.0f + s1v[e];
+          s1v[e + 1] = 1.0f + s1v[e + 1];
+          round2(s1v[e], s1v[e + 1]);
+        }
       }
+      if constexpr (FOLD) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float t = rstd_f * (v[e] - mean_f);
+          const float p = t * s1v[e];
+          o[e] = p + shv[e];
+        }
+        st16s(a.out + base + col(k), pack8(o));
+        continue;
+      }
+      if constexpr (RMS) {
+        float w[8];
+        if constexpr (WLDS) {
+          const int j = lane + 64 * k;
+          const float4 w0 = lds_w[mod_slot(j, 0) / 4], w1 = lds_w[mod_slot(j, 1) / 4];
+          w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+          w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+        } else if constexpr (HOLD) {
+          unpack8(mw[k], w);
+        } else {
+          unpack8(ld16(a.weight + col(k)), w);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (v[e] * rstd_f) * w[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = rstd_f * (v[e] - mean_f);
+      }
+      uint4 yq;  // y as stored bf16 (the rounding is the packing)
+      yq = pack8(y);
+      unpack8(yq, y);
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        s1v[e] = 1.0f + s1v[e];
-        s1v[e + 1] = 1.0f + s1v[e + 1];
-        round2(s1v[e], s1v[e + 1]);
-      }
-    }
-    if constexpr (FOLD) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float t = rstd_f * (v[e] - mean_f);
-        const float p = t * s1v[e];
-        o[e] = p + shv[e];
+        float p0 = y[e] * s1v[e], p1 = y[e + 1] * s1v[e + 1];
+        round2(p0, p1);
+        o[e] = p0 + shv[e];
+        o[e + 1] = p1 + shv[e + 1];
       }
       st16s(a.out + base + col(k), pack8(o));
-      continue;
+      if constexpr (WY) st16(a.y_out + base + col(k), yq);
     }
-    if constexpr (RMS) {
-      float w[8];
-      if constexpr (HOLD) unpack8(mw[k], w);
-      else unpack8(ld16(a.weight + col(k)), w);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = (v[e] * rstd_f) * w[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = rstd_f * (v[e] - mean_f);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      round2(y[e], y[e + 1]);
-      float p0 = y[e] * s1v[e], p1 = y[e + 1] * s1v[e + 1];
-      round2(p0, p1);
-      o[e] = p0 + shv[e];
-      o[e + 1] = p1 + shv[e + 1];
-    }
-    st16s(a.out + base + col(k), pack8(o));
-    if (a.y_out) st16(a.y_out + base + col(k), pack8(y));
+  };
+  using T = BoolC<true>;
+  using F = BoolC<false>;
+  if (a.y_out) {
+    if (mod_in_lds) normalise(T{}, T{});
+    else normalise(T{}, F{});
+  } else {
+    if (mod_in_lds) normalise(F{}, T{});
+    else normalise(F{}, F{});
   }
 }
 
 template <int NV, bool FULL, int MODE = MOD_LDS>
 hipError_t launch_wave(const RowArgs &a, bool rms, bool gated, bool fold, hipStream_t stream) {
   const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
-  if (fold) {  // LN only
-    hipLaunchKernelGGL((row_wave_kernel<NV, FULL, false, false, MODE, true>), grid, block, 0, stream, a);
-    return hipGetLastError();
-  }
-  if (!rms && !gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, false, false, MODE>), grid, block, 0, stream, a);
-  if (!rms && gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, false, true, MODE>), grid, block, 0, stream, a);
-  if (rms && !gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, true, false, MODE>), grid, block, 0, stream, a);
-  if (rms && gated) hipLaunchKernelGGL((row_wave_kernel<NV, FULL, true, true, MODE>), grid, block, 0, stream, a);
+#define DITNORM_WAVE(R, G, F) \
+  hipLaunchKernelGGL((row_wave_kernel<NV, FULL, R, G, MODE, F>), grid, block, 0, stream, a)
+  if (fold) DITNORM_WAVE(false, false, true);  // LN only
+  else if (!rms && !gated) DITNORM_WAVE(false, false, false);
+  else if (!rms && gated) DITNORM_WAVE(false, true, false);
+  else if (rms && !gated) DITNORM_WAVE(true, false, false);
+  else DITNORM_WAVE(true, true, false);
+#undef DITNORM_WAVE
   return hipGetLastError();
 }
 
@@ -513,19 +552,10 @@ static hipError_t launch_cfg(const RowArgs &a, bool rms, bool gated, bool fold,
 hipError_t launch_row(const RowArgs &a, bool rms, bool gated, bool fold, const DeviceInfo &dev,
                       hipStream_t stream) {
   const int nvec = a.cols / 8;
-  // Rows up to 4096 columns: one wavefront per row.  The gated sites stage
-  // the modulation rows in LDS (their extra residual stream leaves no
-  // registers for in-flight modulation loads); the plain sites read them per
-  // row from the caches, which measured faster than the workgroup barrier.
-  if (gated) {
-    switch (nvec) {
-      case 128: return launch_wave<2, true, MOD_LDS>(a, rms, gated, fold, stream);
-      case 256: return launch_wave<4, true, MOD_LDS>(a, rms, gated, fold, stream);
-      case 384: return launch_wave<6, true, MOD_LDS>(a, rms, gated, fold, stream);
-      case 512: return launch_wave<8, true, MOD_LDS>(a, rms, gated, fold, stream);
-      default: break;
-    }
-  } else {
+  // Rows up to 4096 columns: one wavefront per row, the modulation rows (and
+  // the RMS weight) staged in LDS once per workgroup -- except for the folded
+  // form, whose lighter chain measured faster reading them per row.
+  if (fold) {
     switch (nvec) {
       case 128: return launch_wave<2, true, MOD_SERIAL>(a, rms, gated, fold, stream);
       case 256: return launch_wave<4, true, MOD_SERIAL>(a, rms, gated, fold, stream);
@@ -533,6 +563,13 @@ hipError_t launch_row(const RowArgs &a, bool rms, bool gated, bool fold, const D
       case 512: return launch_wave<8, true, MOD_SERIAL>(a, rms, gated, fold, stream);
       default: break;
     }
+  }
+  switch (nvec) {
+    case 128: return launch_wave<2, true, MOD_LDS>(a, rms, gated, fold, stream);
+    case 256: return launch_wave<4, true, MOD_LDS>(a, rms, gated, fold, stream);
+    case 384: return launch_wave<6, true, MOD_LDS>(a, rms, gated, fold, stream);
+    case 512: return launch_wave<8, true, MOD_LDS>(a, rms, gated, fold, stream);
+    default: break;
   }
   if (nvec <= 64) return launch_wave<1, false>(a, rms, gated, fold, stream);
   if (nvec <= 128) return launch_wave<2, false>(a, rms, gated, fold, stream);
