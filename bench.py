@@ -106,9 +106,10 @@ def make_call(lib, launch, t, stream):
 
 
 def rotation_sets(w, device):
-    """Enough independent input/output sets that their total is >= 1 GiB."""
+    """Enough independent input/output sets that their total is >= 1 GiB (at
+    most 64: the 1 MB workload stays cache-resident, and is launch-bound)."""
     per_set = w.algorithmic_bytes()
-    n = max(2, -(-ROTATE_BYTES // per_set))
+    n = min(64, max(2, -(-ROTATE_BYTES // per_set)))
     return [gen.make(w, device=device, seed_offset=i) for i in range(n)]
 
 
