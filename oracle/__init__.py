@@ -68,6 +68,9 @@ def _load():
                                    ctypes.c_float, _f32p, _f32p, _u16p],
             "oracle_ln_modulate_folded": [_u16p, _u16p, _u16p, _u16p, _i64, _i64, _i64, _i64,
                                           ctypes.c_float, _f32p, _f32p],
+            "oracle_tree32_sum": [_f32p, _i64],
+            "oracle_ln_modulate_backward": [_u16p, _u16p, _u16p, _i64, _i64, _i64, _i64,
+                                            ctypes.c_float, _u16p, _f32p, _f32p, _f32p, _f32p],
             "oracle_gated_ln_modulate": [_u16p, _u16p, _u16p, _u16p, _u16p, _u16p, _u16p,
                                          _i64, _i64, _i64, _i64, ctypes.c_float,
                                          _f32p, _f32p, _u16p],
@@ -82,6 +85,9 @@ def _load():
         for name, args in sig.items():
             fn = getattr(lib, name)
             fn.argtypes = args
+            if name == "oracle_tree32_sum":
+                fn.restype = ctypes.c_float
+                continue
             fn.restype = None if name in ("oracle_round_f32_to_f16", "oracle_widen_f16") else \
                 ctypes.c_int if name.startswith(("oracle_ln", "oracle_rms", "oracle_mod",
                                                           "oracle_gate", "oracle_bias",
@@ -304,6 +310,32 @@ def ln_modulate_folded(x, scale, shift, eps, rows_per_batch=None):
                                              _p(out, _u16p), rows, cols, rpb, stride, eps,
                                              _p(mean, _f32p), _p(rstd, _f32p)))
     return dict(out=out, mean=mean, rstd=rstd)
+
+
+def tree32_sum(values):
+    """The fixed fp32 token-sum tree over a 1-D array of fp32 values."""
+    v = np.array(values, dtype=np.float32, copy=True)
+    return np.float32(_load().oracle_tree32_sum(_p(v, _f32p), v.size))
+
+
+def ln_modulate_backward(x, scale, d_out, eps, rows_per_batch=None):
+    """Backward of LN (no affine) + modulate.  Returns dict(d_x (bf16 bits),
+    d_scale, d_shift (fp32 [B, cols]), mean, rstd)."""
+    x, d_out = _u16(x), _u16(d_out)
+    rows, cols = x.shape
+    scale, stride = _mod_rows(scale, cols)
+    rpb = rows_per_batch or max(rows, 1)
+    nb = rows // rpb if rows else 0
+    d_x = np.empty_like(x)
+    d_scale = np.empty((nb, cols), np.float32)
+    d_shift = np.empty((nb, cols), np.float32)
+    mean = np.empty(rows, np.float32)
+    rstd = np.empty(rows, np.float32)
+    _check(_load().oracle_ln_modulate_backward(
+        _p(x, _u16p), _p(scale, _u16p), _p(d_out, _u16p), rows, cols, rpb, stride, eps,
+        _p(d_x, _u16p), _p(d_scale, _f32p), _p(d_shift, _f32p), _p(mean, _f32p),
+        _p(rstd, _f32p)))
+    return dict(d_x=d_x, d_scale=d_scale, d_shift=d_shift, mean=mean, rstd=rstd)
 
 
 def gated_ln_modulate(update, residual, gate, scale, shift, eps, rows_per_batch=None):

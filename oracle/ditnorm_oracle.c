@@ -52,6 +52,23 @@
  *    normalise's subtract-then-multiply, then the weight, then the bias, no
  *    FMA) is the plain reading.
  *
+ *  - Backward of LN (no affine) + modulate ("[WS1][Qwen-Image][CUDA] Final
+ *    AdaLN output (final_adaln_out)", What): the forward
+ *    out = LN(x) * (1 + scale) + shift executed in fp32 on widened inputs,
+ *    with fp32 statistics kept from the forward.  With x_hat the normalised
+ *    value and g = d_out * (1 + scale):
+ *      d_x     = rstd * (g - mean_row(g) - x_hat * mean_row(g * x_hat)),
+ *                evaluated here in binary64 and rounded once to bf16 (the
+ *                execution-dtype store);
+ *      d_shift = sum over a batch's tokens of d_out,
+ *      d_scale = sum over a batch's tokens of d_out * x_hat,
+ *    the two token sums in fp32 by the page's fixed balanced trees: adjacent
+ *    pairs within groups of 32 consecutive values (5 levels), the group sums
+ *    again in groups of 32, until one value remains; a short group is padded
+ *    with +0.  The tree depends only on the batch's token count.  The fp32
+ *    terms are d_out (exact) and d_out * x_hat with x_hat = rstd * (x - mean)
+ *    in fp32 (the normalise's subtract-then-multiply, unrounded).
+ *
  *  - Gated residual (pre-norm; same ERNIE page, second kernel, and the GLM
  *    page's ff-gate):  h = bf16(residual + bf16(gate * update)); the norm
  *    then runs on h, and h is returned as the residual stream.
@@ -77,6 +94,7 @@
  */
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -539,6 +557,104 @@ int oracle_ln_modulate_folded(const uint16_t *x, const uint16_t *scale, const ui
                                                    scale[b * mod_batch_stride + c],
                                                    shift[b * mod_batch_stride + c]);
     }
+    return OR_OK;
+}
+
+/* The fixed fp32 token-sum tree: v[0..n-1] is reduced in place by adjacent
+ * pairs within groups of 32 (a short group padded with +0), group by group,
+ * level after level, until one value remains.  n == 0 gives +0. */
+static float tree32_sum(float *v, int64_t n)
+{
+    if (n == 0)
+        return 0.0f;
+    while (n > 1) {
+        int64_t groups = (n + 31) / 32;
+        for (int64_t g = 0; g < groups; ++g) {
+            float t[32];
+            for (int i = 0; i < 32; ++i) {
+                int64_t k = g * 32 + i;
+                t[i] = k < n ? v[k] : 0.0f;
+            }
+            for (int width = 16; width >= 1; width /= 2)
+                for (int i = 0; i < width; ++i)
+                    t[i] = t[2 * i] + t[2 * i + 1];
+            v[g] = t[0];
+        }
+        n = groups;
+    }
+    return v[0];
+}
+
+/* Exposed for the tests: the fixed tree over n fp32 values (v is clobbered). */
+float oracle_tree32_sum(float *v, int64_t n)
+{
+    return tree32_sum(v, n);
+}
+
+/* Backward of LN (no affine) + modulate.  x, d_out: [rows, cols] bf16;
+ * scale: [B, cols] bf16 at row stride mod_batch_stride; d_x: bf16 [rows,
+ * cols]; d_scale, d_shift: fp32 [B, cols] (dense).  mean_out / rstd_out may be
+ * NULL. */
+int oracle_ln_modulate_backward(const uint16_t *x, const uint16_t *scale, const uint16_t *d_out,
+                                int64_t rows, int64_t cols, int64_t rows_per_batch,
+                                int64_t mod_batch_stride, float eps, uint16_t *d_x,
+                                float *d_scale, float *d_shift, float *mean_out,
+                                float *rstd_out)
+{
+    if (!mod_args_ok(rows, cols, rows_per_batch, mod_batch_stride))
+        return OR_INVALID;
+    if (cols > OR_MAX_COLS)
+        return OR_INVALID;
+    int64_t nb = rows / rows_per_batch;
+    float *mean = (float *)malloc(sizeof(float) * (size_t)(rows > 0 ? rows : 1));
+    float *rstd = (float *)malloc(sizeof(float) * (size_t)(rows > 0 ? rows : 1));
+    float *ts = (float *)malloc(sizeof(float) * (size_t)(rows_per_batch > 0 ? rows_per_batch : 1));
+    float *tc = (float *)malloc(sizeof(float) * (size_t)(rows_per_batch > 0 ? rows_per_batch : 1));
+    if (!mean || !rstd || !ts || !tc) {
+        free(mean); free(rstd); free(ts); free(tc);
+        return OR_INVALID;
+    }
+    /* per row: statistics and d_x */
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *xr = widen_row(x + r * cols, cols);
+        const uint16_t *sr = scale + (r / rows_per_batch) * mod_batch_stride;
+        const uint16_t *gr = d_out + r * cols;
+        ln_stats(xr, cols, eps, &mean[r], &rstd[r]);
+        if (mean_out)
+            mean_out[r] = mean[r];
+        if (rstd_out)
+            rstd_out[r] = rstd[r];
+        double m = (double)mean[r], rs = (double)rstd[r];
+        double c1 = 0.0, c2 = 0.0;
+        for (int64_t c = 0; c < cols; ++c) {
+            double xh = ((double)xr[c] - m) * rs;
+            double g = (double)bf16_to_f32(gr[c]) * (double)(1.0f + bf16_to_f32(sr[c]));
+            c1 += g;
+            c2 += g * xh;
+        }
+        c1 /= (double)cols;
+        c2 /= (double)cols;
+        for (int64_t c = 0; c < cols; ++c) {
+            double xh = ((double)xr[c] - m) * rs;
+            double g = (double)bf16_to_f32(gr[c]) * (double)(1.0f + bf16_to_f32(sr[c]));
+            d_x[r * cols + c] = f64_to_bf16(rs * (g - c1 - xh * c2));
+        }
+    }
+    /* per batch and column: the two token sums */
+    for (int64_t b = 0; b < nb; ++b) {
+        for (int64_t c = 0; c < cols; ++c) {
+            for (int64_t s = 0; s < rows_per_batch; ++s) {
+                int64_t r = b * rows_per_batch + s;
+                float dout = bf16_to_f32(d_out[r * cols + c]);
+                float xh = rstd[r] * (bf16_to_f32(x[r * cols + c]) - mean[r]);
+                ts[s] = dout;
+                tc[s] = dout * xh;
+            }
+            d_shift[b * cols + c] = tree32_sum(ts, rows_per_batch);
+            d_scale[b * cols + c] = tree32_sum(tc, rows_per_batch);
+        }
+    }
+    free(mean); free(rstd); free(ts); free(tc);
     return OR_OK;
 }
 

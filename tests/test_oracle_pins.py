@@ -618,3 +618,115 @@ def test_folded_ln_pins(orc):
     diff = np.abs(out - f32_from_u16(lossless["out"]).astype(np.float64))
     assert np.all(diff <= bound + 1e-30)
     assert 0 < diff.max() <= 0.0625
+
+
+# ---------------------------------------------------------------------------
+# backward of LN + modulate (Qwen-Image final AdaLN output page): the fixed
+# fp32 token-sum tree and the gradients
+# ---------------------------------------------------------------------------
+
+U24 = 2.0 ** -24
+
+
+def test_tree32_shape_by_hand(orc):
+    """Hand-derived results that tell the page's tree (adjacent pairs in
+    groups of 32, recursively, +0 padding) from its plausible neighbours."""
+    f = lambda v: float(orc.tree32_sum(np.array(v, np.float32)))
+    # adjacent pairs: (1 + u) + (u + u) = 1 + 2u; a sequential sum gives 1
+    assert f([1, U24, U24, U24]) == 1 + 2 * U24
+    # adjacent pairs: (1 + -1) + (u + u) = 2u; pairing i with i+2 first gives u
+    assert f([1, -1, U24, U24]) == 2 * U24
+    # 33 values: group 0 = 1 + 15*2u exactly, group 1 = u; their sum is a tie
+    # rounded to even: 1 + 32u
+    assert f([1] + [U24] * 32) == 1 + 32 * U24
+    # four groups whose sums are 1, u, u, u: the second level pairs them as
+    # ((1 + u) + (u + u)) = 1 + 2u; adding the group sums in order gives 1
+    v = np.zeros(128, np.float32)
+    v[0], v[32], v[64], v[96] = 1, U24, U24, U24
+    assert f(v) == 1 + 2 * U24
+    # +0 padding: two -0 terms meet a padded +0, so the sum is +0
+    r = orc.tree32_sum(np.array([-0.0, -0.0], np.float32))
+    assert r == 0 and not np.signbit(r)
+    assert orc.tree32_sum(np.array([], np.float32)) == 0
+    # n equal bf16 values sum to n*c exactly
+    c = np.float32(0.10009765625)
+    for n in (1, 2, 3, 31, 32, 33, 100, 1000, 4096):
+        assert orc.tree32_sum(np.full(n, c, np.float32)) == np.float32(n * float(c))
+
+
+def test_tree32_error_bound(orc):
+    rng = np.random.default_rng(5)
+    for n in (7, 32, 1000, 6889):
+        v = rng.standard_normal(n).astype(np.float32)
+        exact = sum(Fraction(float(t)) for t in v)
+        depth = 5 * max(1, math.ceil(math.log(n, 32)))
+        got = Fraction(float(orc.tree32_sum(v)))
+        assert abs(got - exact) <= Fraction(depth) * Fraction(U24) * sum(abs(Fraction(float(t))) for t in v)
+
+
+def _torch_backward(x, sc, dout, eps, rpb):
+    """Gradients of LN(x) * (1 + scale) + shift by torch autograd in float64."""
+    rows, cols = x.shape
+    xt = torch.from_numpy(f32_from_u16(x).astype(np.float64)).requires_grad_()
+    st = torch.from_numpy(f32_from_u16(sc).astype(np.float64)).requires_grad_()
+    ht = torch.zeros_like(st, requires_grad=True)
+    b = torch.arange(rows) // rpb
+    out = torch.nn.functional.layer_norm(xt, (cols,), eps=eps) * (1 + st[b]) + ht[b]
+    out.backward(torch.from_numpy(f32_from_u16(dout).astype(np.float64)))
+    xh = torch.nn.functional.layer_norm(xt.detach(), (cols,), eps=eps).numpy()
+    return xt.grad.numpy(), st.grad.numpy(), ht.grad.numpy(), xh
+
+
+def test_backward_vs_torch_autograd(orc):
+    B, S, D = 2, 77, 1024
+    x = rand_bf16((B * S, D), 0.3, 1.5, 800)
+    sc = rand_bf16((B, D), 0, 0.1, 801)
+    dout = rand_bf16((B * S, D), 0, 1.0, 802)
+    r = orc.ln_modulate_backward(x, sc, dout, 1e-6, rows_per_batch=S)
+    gx, gs, gh, xh = _torch_backward(x, sc, dout, 1e-6, S)
+    # d_x: one rounding of a binary64 evaluation on fp32 statistics
+    g = f32_from_u16(dout).astype(np.float64) * (1 + np.repeat(f32_from_u16(sc), S, 0))
+    rstd = r["rstd"].astype(np.float64)[:, None]
+    c1 = g.mean(1, keepdims=True)
+    c2 = (g * xh).mean(1, keepdims=True)
+    slack = 1e-6 * rstd * (np.abs(g) + np.abs(c1) + np.abs(xh * c2))
+    dx = f32_from_u16(r["d_x"]).astype(np.float64)
+    assert np.all(np.abs(dx - gx) <= 0.5 * ulp_bf16(np.abs(gx) + slack) + slack + 1e-30)
+    assert np.mean(r["d_x"] == bf16_bits_from_f32(gx.astype(np.float32))) > 0.99
+    # token sums: the fixed tree's error bound over the exact sums
+    depth = 5 * 2
+    tsh = np.abs(f32_from_u16(dout).astype(np.float64)).reshape(B, S, D).sum(1)
+    assert np.all(np.abs(r["d_shift"] - gh) <= depth * U24 * tsh + 1e-30)
+    tsc = np.abs(f32_from_u16(dout).astype(np.float64) * xh).reshape(B, S, D).sum(1)
+    assert np.all(np.abs(r["d_scale"] - gs) <= (depth + 4) * U24 * tsc + 1e-30)
+
+
+def test_backward_batch_invariance_and_closed_forms(orc):
+    S, D = 45, 256
+    xs = [rand_bf16((S, D), 0, 1, 810 + i) for i in range(3)]
+    scs = [rand_bf16((1, D), 0, 0.1, 820 + i) for i in range(3)]
+    ds = [rand_bf16((S, D), 0, 1, 830 + i) for i in range(3)]
+    whole = orc.ln_modulate_backward(np.concatenate(xs), np.concatenate(scs), np.concatenate(ds),
+                                     1e-6, rows_per_batch=S)
+    for i in range(3):
+        alone = orc.ln_modulate_backward(xs[i], scs[i], ds[i], 1e-6)
+        assert np.array_equal(alone["d_x"], whole["d_x"][i * S:(i + 1) * S])
+        assert np.array_equal(alone["d_scale"][0].view(np.uint32), whole["d_scale"][i].view(np.uint32))
+        assert np.array_equal(alone["d_shift"][0].view(np.uint32), whole["d_shift"][i].view(np.uint32))
+    # d_out constant c: d_shift = S*c exactly, whatever x and scale are
+    c = np.full((S, D), 0x3DCD, np.uint16)                     # 0.10009765625
+    r = orc.ln_modulate_backward(xs[0], scs[0], c, 1e-6)
+    assert np.all(r["d_shift"] == np.float32(S * 0.10009765625))
+    # scale = -1: no gradient reaches x (g = 0), the token sums do not see scale
+    m1 = np.full((1, D), 0xBF80, np.uint16)
+    r1 = orc.ln_modulate_backward(xs[0], m1, ds[0], 1e-6)
+    r0 = orc.ln_modulate_backward(xs[0], scs[0], ds[0], 1e-6)
+    assert np.all(f32_from_u16(r1["d_x"]) == 0)
+    assert np.array_equal(r1["d_shift"], r0["d_shift"]) and np.array_equal(r1["d_scale"], r0["d_scale"])
+    # the LN backward is orthogonal to shifts and scalings of the row: the
+    # row sums of d_x and of d_x * x_hat vanish up to the bf16 rounding of d_x
+    _, _, _, xh = _torch_backward(xs[0], scs[0], ds[0], 1e-6, S)
+    dx = f32_from_u16(r0["d_x"]).astype(np.float64)
+    half = 0.5 * ulp_bf16(dx)
+    assert np.all(np.abs(dx.sum(1)) <= half.sum(1) * 1.01)
+    assert np.all(np.abs((dx * xh).sum(1)) <= (half * np.abs(xh)).sum(1) * 1.01 + 1e-3 * np.abs(dx * xh).sum(1) * 2 ** -10)
