@@ -44,6 +44,7 @@ KERNEL_SOURCES = {
     "rms_modulate": "row_kernels.hip", "qk_layernorm": "qk_kernel.hip",
     "rmsnorm_silu_bias": "wan_kernels.hip", "conv_bias_epilogue": "wan_kernels.hip",
     "modulate_scale_shift": "elementwise.hip", "residual_gate_add": "elementwise.hip",
+    "ln_modulate_backward": "backward.hip",
 }
 DTYPE_CODES = {"bf16": 0, "f16": 1}
 
@@ -94,6 +95,17 @@ def make_call(lib, launch, t, stream):
         return lib.rmsnorm_silu_bias, (_p(t["x"]), _p(t["bias"]), _p(t["gamma"]), _p(out), rows,
                                        cols, launch.eps, None, None, stream), out
     a, b, c = (t[n] for n in launch.inputs)
+    if e == "ln_modulate_backward":        # inputs: x, scale, d_out
+        rpb = launch.extra["rows_per_batch"]
+        nb = rows // rpb
+        d_x = torch.empty_like(a)
+        d_scale = torch.empty((nb, cols), dtype=torch.float32, device=a.device)
+        d_shift = torch.empty((nb, cols), dtype=torch.float32, device=a.device)
+        ws_bytes = lib.ln_modulate_backward_workspace_bytes(rows, cols, rpb)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a.device)
+        return lib.ln_modulate_backward, (_p(a), _p(b), _p(c), _p(d_x), _p(d_scale), _p(d_shift),
+                                          rows, cols, rpb, cols, launch.eps, _p(ws), ws_bytes,
+                                          None, None, stream), (d_x, d_scale, d_shift, ws)
     if e == "conv_bias_epilogue":          # inputs: x, bias, h
         out = torch.empty_like(a)
         return lib.conv_bias_epilogue, (_p(a), _p(b), _p(c), _p(out), rows, cols, stream), out
@@ -405,6 +417,9 @@ def _kernel_label(name):
             return "ln_modulate_folded"
         return {(False, False): "ln_modulate", (False, True): "gated_ln_modulate",
                 (True, False): "rms_modulate", (True, True): "gated_rms_modulate"}[(rms, gated)]
+    for key in ("bwd_row_kernel", "bwd_token_kernel", "bwd_tree_kernel"):
+        if f"ditnorm::{key}" in name:
+            return key
     if "ditnorm::elementwise_kernel<" in name:
         # elementwise_kernel<OP, DT, U>
         op, dt = (a.strip() for a in name.split("_kernel<", 1)[1].split(">", 1)[0].split(",")[:2])

@@ -10,7 +10,8 @@ the call raises.
 
 Entry points (same names as the C ABI):
     ln_modulate, ln_modulate_folded, gated_ln_modulate, rms_modulate, qk_layernorm,
-    rmsnorm_silu_bias, conv_bias_epilogue, modulate_scale_shift, residual_gate_add, copy
+    rmsnorm_silu_bias, conv_bias_epilogue, modulate_scale_shift, residual_gate_add,
+    ln_modulate_backward (+ ln_modulate_backward_workspace_bytes), copy
 """
 from __future__ import annotations
 
@@ -21,7 +22,8 @@ import torch
 
 __all__ = ["load", "ln_modulate", "ln_modulate_folded", "gated_ln_modulate", "rms_modulate", "qk_layernorm",
            "rmsnorm_silu_bias", "conv_bias_epilogue", "modulate_scale_shift",
-           "residual_gate_add", "copy", "DitnormError", "LIB_PATH"]
+           "residual_gate_add", "ln_modulate_backward", "ln_modulate_backward_workspace_bytes",
+           "copy", "DitnormError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditnorm.so")
 
@@ -57,6 +59,8 @@ _SIGNATURES = {
     "conv_bias_epilogue": [_vp, _vp, _vp, _vp, _i64, _i64, _vp],
     "modulate_scale_shift": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp],
     "residual_gate_add": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp],
+    "ln_modulate_backward": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp,
+                             _i64, _vp, _vp, _vp],
     "ditnorm_copy": [_vp, _vp, _i64, _vp],
     "ln_modulate_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp],
     "ln_modulate_folded_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp,
@@ -70,6 +74,8 @@ _SIGNATURES = {
     "conv_bias_epilogue_supported": [_vp, _vp, _vp, _vp, _i64, _i64],
     "modulate_scale_shift_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32],
     "residual_gate_add_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32],
+    "ln_modulate_backward_supported": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                       _f32, _vp, _i64, _vp, _vp],
     "ditnorm_last_hip_error": [],
     "ditnorm_version": [],
 }
@@ -86,6 +92,8 @@ def load(path: str = LIB_PATH):
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        lib.ln_modulate_backward_workspace_bytes.argtypes = [_i64, _i64, _i64]
+        lib.ln_modulate_backward_workspace_bytes.restype = _i64
         lib.ditnorm_status_string.argtypes = [ctypes.c_int]
         lib.ditnorm_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -366,6 +374,44 @@ def residual_gate_add(update, residual, gate, out=None):
     _call("residual_gate_add", _p(update), _p(residual), _p(gate), _p(out), rows, cols,
           _batch(rows, b), stride, _DTYPE_CODES[dt], _stream(update))
     return out
+
+
+def ln_modulate_backward_workspace_bytes(rows, cols, rows_per_batch):
+    """Bytes of device workspace ln_modulate_backward needs (host-only)."""
+    n = load().ln_modulate_backward_workspace_bytes(rows, cols, rows_per_batch)
+    if n < 0:
+        raise ValueError("invalid sizes")
+    return n
+
+
+def ln_modulate_backward(x, scale, d_out, eps=1e-6, *, d_x=None, d_scale=None, d_shift=None,
+                         workspace=None, mean_out=None, rstd_out=None):
+    """Gradients of LN(x) * (1 + scale) + shift: returns (d_x bf16 like x,
+    d_scale fp32 [B, D], d_shift fp32 [B, D]).  x, d_out (..., D) bf16; scale
+    (D,), (B, D) or (B, 1, D) bf16.  The workspace (uint8 device tensor) is
+    allocated here when not given."""
+    _act(x, "x")
+    _act(d_out, "d_out")
+    if d_out.shape != x.shape:
+        raise ValueError("d_out must have the shape of x")
+    rows, cols = _rows_cols(x)
+    scale, b, stride = _mod(scale, "scale", cols, x.device)
+    rpb = _batch(rows, b)
+    d_x = torch.empty_like(x) if d_x is None else _act(d_x, "d_x")
+    f32 = dict(dtype=torch.float32, device=x.device)
+    d_scale = torch.empty((b, cols), **f32) if d_scale is None else d_scale
+    d_shift = torch.empty((b, cols), **f32) if d_shift is None else d_shift
+    for t, nm in ((d_scale, "d_scale"), (d_shift, "d_shift")):
+        if t.dtype != torch.float32 or t.numel() != b * cols or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous fp32 tensor of {b}x{cols}")
+    need = ln_modulate_backward_workspace_bytes(rows, cols, rpb) if rows else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _call("ln_modulate_backward", _p(x), _p(scale), _p(d_out), _p(d_x), _p(d_scale), _p(d_shift),
+          rows, cols, rpb, stride, eps, _p(workspace), workspace.numel() * workspace.element_size(),
+          _p(_f32_out(mean_out, rows, "mean_out")), _p(_f32_out(rstd_out, rows, "rstd_out")),
+          _stream(x))
+    return d_x, d_scale, d_shift
 
 
 def copy(src, dst):

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libditnorm.so")
-SOURCES = ["abi.hip", "row_kernels.hip", "qk_kernel.hip", "wan_kernels.hip", "elementwise.hip"]
+SOURCES = ["abi.hip", "row_kernels.hip", "qk_kernel.hip", "wan_kernels.hip", "elementwise.hip",
+           "backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

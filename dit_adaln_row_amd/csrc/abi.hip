@@ -229,6 +229,28 @@ int validate_epilogue(const void *x, const float *bias, const void *h, const voi
   return aliasing_ok(in, o, alias) ? DITNORM_OK : DITNORM_UNSUPPORTED;
 }
 
+int validate_backward(const void *x, const void *scale, const void *d_out, const void *d_x,
+                      const float *d_scale, const float *d_shift, int64_t rows, int64_t cols,
+                      int64_t rpb, int64_t mbs, float eps, const void *ws, int64_t ws_bytes,
+                      const float *mean_out, const float *rstd_out) {
+  int st = check_rows(rows, cols, rpb, mbs, eps);
+  if (st != DITNORM_OK || rows == 0) return st;
+  if (cols > DITNORM_MAX_BACKWARD_COLS) return DITNORM_UNSUPPORTED;
+  if (!x || !scale || !d_out || !d_x || !d_scale || !d_shift || !ws)
+    return DITNORM_INVALID_ARGUMENT;
+  if (ws_bytes < bwd_layout(rows, cols, rpb).bytes) return DITNORM_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(scale) || !aligned16(d_out) || !aligned16(d_x) ||
+      !aligned16(d_scale) || !aligned16(d_shift) || ((uintptr_t)ws & 255u) != 0 ||
+      !aligned4(mean_out) || !aligned4(rstd_out))
+    return DITNORM_UNSUPPORTED;
+  const int64_t act = rows * cols * 2, nb = rows / rpb;
+  const Buf in[] = {{x, act}, {scale, mod_bytes(nb, mbs, cols)}, {d_out, act}};
+  const Buf o[] = {{d_x, act}, {d_scale, nb * cols * 4}, {d_shift, nb * cols * 4},
+                   {ws, ws_bytes}, {mean_out, rows * 4}, {rstd_out, rows * 4}};
+  const int alias[] = {-1, -1, -1, -1, -1, -1};
+  return aliasing_ok(in, o, alias) ? DITNORM_OK : DITNORM_UNSUPPORTED;
+}
+
 int validate_elementwise(int op, const void *a, const void *b, const void *m0, const void *m1,
                          const void *out, int64_t rows, int64_t cols, int64_t rpb, int64_t mbs,
                          int dtype) {
@@ -519,6 +541,57 @@ int residual_gate_add_supported(const void *update, const void *residual, const 
                                 int64_t rows_per_batch, int64_t mod_batch_stride, int dtype) {
   return validate_elementwise(1, update, residual, gate, nullptr, out, rows, cols,
                               rows_per_batch, mod_batch_stride, dtype) == DITNORM_OK;
+}
+
+int64_t ln_modulate_backward_workspace_bytes(int64_t rows, int64_t cols,
+                                             int64_t rows_per_batch) {
+  if (rows < 0 || cols <= 0 || rows_per_batch <= 0 || rows % rows_per_batch != 0) return -1;
+  if (rows == 0) return 0;
+  return bwd_layout(rows, cols, rows_per_batch).bytes;
+}
+
+int ln_modulate_backward(const void *x, const void *scale, const void *d_out, void *d_x,
+                         float *d_scale, float *d_shift, int64_t rows, int64_t cols,
+                         int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
+                         void *workspace, int64_t workspace_bytes, float *mean_out,
+                         float *rstd_out, void *stream) {
+  int st = validate_backward(x, scale, d_out, d_x, d_scale, d_shift, rows, cols, rows_per_batch,
+                             mod_batch_stride, eps, workspace, workspace_bytes, mean_out,
+                             rstd_out);
+  if (st != DITNORM_OK || rows == 0) return st;
+  DeviceInfo dev;
+  if ((st = current_device(&dev)) != DITNORM_OK) return st;
+  const BwdLayout L = bwd_layout(rows, cols, rows_per_batch);
+  char *ws = (char *)workspace;
+  BwdArgs a{};
+  a.x = (const uint16_t *)x;
+  a.scale = (const uint16_t *)scale;
+  a.d_out = (const uint16_t *)d_out;
+  a.d_x = (uint16_t *)d_x;
+  a.d_scale = d_scale;
+  a.d_shift = d_shift;
+  a.ws_mean = (float *)(ws + L.mean_off);
+  a.ws_rstd = (float *)(ws + L.rstd_off);
+  a.mean_out = mean_out;
+  a.rstd_out = rstd_out;
+  a.rows = rows;
+  a.rows_per_batch = rows_per_batch;
+  a.mod_stride = mod_batch_stride;
+  a.cols = (int32_t)cols;
+  a.eps = eps;
+  return finish(launch_backward(a, (float *)(ws + L.part0_off), (float *)(ws + L.part1_off),
+                                L.groups, (hipStream_t)stream));
+}
+
+int ln_modulate_backward_supported(const void *x, const void *scale, const void *d_out,
+                                   const void *d_x, const float *d_scale, const float *d_shift,
+                                   int64_t rows, int64_t cols, int64_t rows_per_batch,
+                                   int64_t mod_batch_stride, float eps, const void *workspace,
+                                   int64_t workspace_bytes, const float *mean_out,
+                                   const float *rstd_out) {
+  return validate_backward(x, scale, d_out, d_x, d_scale, d_shift, rows, cols, rows_per_batch,
+                           mod_batch_stride, eps, workspace, workspace_bytes, mean_out,
+                           rstd_out) == DITNORM_OK;
 }
 
 int ditnorm_copy(const void *src, void *dst, int64_t bytes, void *stream) {

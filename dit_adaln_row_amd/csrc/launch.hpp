@@ -92,6 +92,37 @@ struct ElementwiseArgs {
 };
 hipError_t launch_elementwise(const ElementwiseArgs &a, int op, int dtype, hipStream_t stream);
 
+// Backward of LN (no affine) + modulate: d_x, and the token sums d_scale,
+// d_shift by fixed balanced trees.
+struct BwdArgs {
+  const uint16_t *x;      // [rows, cols]
+  const uint16_t *scale;  // [B, mod_stride]
+  const uint16_t *d_out;  // [rows, cols]
+  uint16_t *d_x;          // [rows, cols]
+  float *d_scale;         // [B, cols]
+  float *d_shift;         // [B, cols]
+  float *ws_mean;         // workspace [rows]
+  float *ws_rstd;         // workspace [rows]
+  float *mean_out;        // optional [rows]
+  float *rstd_out;        // optional [rows]
+  int64_t rows;
+  int64_t rows_per_batch;
+  int64_t mod_stride;
+  int32_t cols;
+  float eps;
+};
+// Workspace layout (byte offsets; every region 256-byte aligned).
+struct BwdLayout {
+  int64_t groups;        // first-level token groups per batch, ceil(rows_per_batch / 32)
+  int64_t mean_off, rstd_off;
+  int64_t part0_off, part0_floats;  // per sum: B * groups * cols
+  int64_t part1_off, part1_floats;  // per sum: B * ceil(groups / 32) * cols (0 if groups == 1)
+  int64_t bytes;
+};
+BwdLayout bwd_layout(int64_t rows, int64_t cols, int64_t rows_per_batch);
+hipError_t launch_backward(const BwdArgs &a, float *part0, float *part1, int64_t groups,
+                           hipStream_t stream);
+
 // Plain 16-byte copy (measurement utility).
 hipError_t launch_copy(const void *src, void *dst, int64_t bytes, const DeviceInfo &dev,
                        hipStream_t stream);

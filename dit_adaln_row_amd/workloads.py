@@ -68,6 +68,9 @@ class Launch:
             return 2 * r * c * BF16 + 2 * self.n_mod_rows * c * BF16
         if self.entry == "residual_gate_add":
             return 3 * r * c * BF16 + self.n_mod_rows * c * BF16
+        if self.entry == "ln_modulate_backward":
+            # x and d_out read, d_x written, scale read, d_scale and d_shift written
+            return 3 * r * c * BF16 + self.n_mod_rows * c * (BF16 + 2 * F32)
         raise KeyError(self.entry)
 
     def label(self) -> str:
@@ -181,6 +184,25 @@ WORKLOADS = {
          Tensor("shift", (1, 3072), 0.0, 0.1)),
         (Launch("ln_modulate_folded", "ln_modulate_folded", 4608, 3072, ("x", "scale", "shift"),
                 1e-6),),
+    ),
+    "qwen_bwd_1x6889x3072": Workload(
+        "qwen_bwd_1x6889x3072", 11,
+        "Qwen-Image-like final adaLN output backward, (1,6889,3072): x ~N(0,1.5), "
+        "d_out ~N(0,1), scale (1,3072) ~N(0,0.1); d_x, and d_scale/d_shift by the fixed "
+        "32-way fp32 token trees",
+        (Tensor("x", (6889, 3072), 0.0, 1.5), Tensor("d_out", (6889, 3072), 0.0, 1.0),
+         Tensor("scale", (1, 3072), 0.0, 0.1)),
+        (Launch("ln_modulate_backward", "ln_modulate_backward", 6889, 3072,
+                ("x", "scale", "d_out"), 1e-6, n_mod_rows=1, extra={"rows_per_batch": 6889}),),
+    ),
+    "qwen_bwd_2048x3x3072": Workload(
+        "qwen_bwd_2048x3x3072", 12,
+        "Qwen-Image-like final adaLN output backward at a large conditioning batch, "
+        "(2048,3,3072): x ~N(0,1.5), d_out ~N(0,1), scale (2048,3072) ~N(0,0.1)",
+        (Tensor("x", (2048 * 3, 3072), 0.0, 1.5), Tensor("d_out", (2048 * 3, 3072), 0.0, 1.0),
+         Tensor("scale", (2048, 3072), 0.0, 0.1)),
+        (Launch("ln_modulate_backward", "ln_modulate_backward", 2048 * 3, 3072,
+                ("x", "scale", "d_out"), 1e-6, n_mod_rows=2048, extra={"rows_per_batch": 3}),),
     ),
     "flux_elementwise_1x4608x3072": Workload(
         "flux_elementwise_1x4608x3072", 7,

@@ -81,6 +81,8 @@ extern "C" {
  * rms_modulate) and the largest channel count of the channels_last kernels. */
 #define DITNORM_MAX_COLS 16384
 #define DITNORM_MAX_CHANNELS 4096
+/* Largest row width of ln_modulate_backward. */
+#define DITNORM_MAX_BACKWARD_COLS 4096
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *ditnorm_status_string(int status);
@@ -260,6 +262,45 @@ int residual_gate_add(const void *update, const void *residual, const void *gate
                       int64_t mod_batch_stride, int dtype, void *stream);
 
 /*
+ * ln_modulate_backward -- gradients of out = LN(x) * (1 + scale) + shift.
+ *
+ * Qwen-Image page ("[WS1][Qwen-Image][CUDA] Final AdaLN output
+ * (final_adaln_out)", What): the forward and backward of the final adaLN
+ * output, the LayerNorm (no affine, fp32 statistics) run in fp32 on widened
+ * inputs, the modulation-parameter gradients as token sums reduced by fixed
+ * fp32 balanced trees that depend only on the token count:
+ *     x_hat   = (x - mean) * rstd,   g = d_out * (1 + scale)   (1 + scale in fp32)
+ *     d_x     = bf16( rstd * (g - mean_row(g) - x_hat * mean_row(g * x_hat)) )
+ *               (evaluated in binary64, one rounding to bf16)
+ *     d_shift = sum over the batch's tokens of d_out
+ *     d_scale = sum over the batch's tokens of d_out * x_hat   (terms in fp32,
+ *               x_hat = rstd * (x - mean) in fp32)
+ * The token sums: adjacent pairs within groups of 32 consecutive tokens, then
+ * the group sums again in groups of 32, until one value remains; a short
+ * group is padded with +0.  The result for a batch depends only on its own
+ * rows and its token count (bitwise batch-invariant).
+ * x, d_out, d_x: bf16 [rows, cols]; scale: bf16 [B, cols], row stride
+ * mod_batch_stride; d_scale, d_shift: fp32 [B, cols] dense.  cols: multiple
+ * of 8, at most DITNORM_MAX_BACKWARD_COLS.  No output may overlap an input or
+ * another output.
+ * workspace: device memory of at least
+ * ln_modulate_backward_workspace_bytes(rows, cols, rows_per_batch) bytes,
+ * 256-byte aligned, owned by the caller, clobbered by the call (it holds the
+ * per-row statistics and the partial tree sums).  mean_out, rstd_out (fp32
+ * [rows]) optional.  The work is three to five kernel launches on `stream`.
+ */
+int ln_modulate_backward(const void *x, const void *scale, const void *d_out, void *d_x,
+                         float *d_scale, float *d_shift, int64_t rows, int64_t cols,
+                         int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
+                         void *workspace, int64_t workspace_bytes, float *mean_out,
+                         float *rstd_out, void *stream);
+
+/* Workspace bytes ln_modulate_backward needs (0 for rows == 0, -1 for invalid
+ * sizes).  Host-only, never touches the GPU. */
+int64_t ln_modulate_backward_workspace_bytes(int64_t rows, int64_t cols,
+                                             int64_t rows_per_batch);
+
+/*
  * *_supported -- 1 if the same call would pass every argument check (it may
  * still fail with DITNORM_DEVICE_ERROR), else 0.  Never fails, never touches
  * the GPU, never enqueues work.
@@ -292,6 +333,12 @@ int rmsnorm_silu_bias_supported(const void *x, const float *bias, const float *g
                                 const float *rstd_out, const void *xb_out);
 int conv_bias_epilogue_supported(const void *x, const float *bias, const void *h,
                                  const void *out, int64_t rows, int64_t channels);
+int ln_modulate_backward_supported(const void *x, const void *scale, const void *d_out,
+                                   const void *d_x, const float *d_scale, const float *d_shift,
+                                   int64_t rows, int64_t cols, int64_t rows_per_batch,
+                                   int64_t mod_batch_stride, float eps, const void *workspace,
+                                   int64_t workspace_bytes, const float *mean_out,
+                                   const float *rstd_out);
 int modulate_scale_shift_supported(const void *x, const void *scale, const void *shift,
                                    const void *out, int64_t rows, int64_t cols,
                                    int64_t rows_per_batch, int64_t mod_batch_stride, int dtype);

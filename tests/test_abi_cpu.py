@@ -25,7 +25,7 @@ E = 0x80000000
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int64_t|int|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
                                  text, flags=re.M)))
 
 
@@ -41,7 +41,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     for must in ("ln_modulate", "ln_modulate_folded", "gated_ln_modulate", "rms_modulate", "qk_layernorm",
                  "rmsnorm_silu_bias", "conv_bias_epilogue", "modulate_scale_shift",
-                 "residual_gate_add", "ditnorm_status_string"):
+                 "residual_gate_add", "ln_modulate_backward",
+                 "ln_modulate_backward_workspace_bytes", "ditnorm_status_string"):
         assert must in names
     for n in names:
         assert hasattr(lib, n), n
@@ -143,6 +144,24 @@ def test_other_entry_validation(lib):
     assert lib.modulate_scale_shift(A, B, C, D, 0, 3072, 8, 3072, 0, None) == dn.OK   # no-op
     assert lib.residual_gate_add(A, None, C, D, 8, 3072, 8, 3072, 0, None) == dn.INVALID_ARGUMENT
     assert lib.residual_gate_add(A, B, C, D, 8, 16392, 8, 16392, 0, None) == dn.UNSUPPORTED
+    # backward: workspace size, validation before any HIP call
+    ws = dn.ln_modulate_backward_workspace_bytes(6889, 3072, 6889)
+    assert ws >= 2 * 6889 * 4 + 2 * 216 * 3072 * 4 + 2 * 7 * 3072 * 4
+    assert dn.ln_modulate_backward_workspace_bytes(0, 3072, 1) == 0
+    assert lib.ln_modulate_backward_workspace_bytes(10, 3072, 3) == -1
+    W = 0xA0000000
+    bw = lambda **k: lib.ln_modulate_backward(
+        k.get("x", A), k.get("sc", B), k.get("do", C), k.get("dx", D), k.get("ds", E),
+        k.get("dh", E + 0x100000), k.get("rows", 64), k.get("cols", 3072), k.get("rpb", 64),
+        k.get("mbs", 3072), 1e-6, k.get("ws", W), k.get("wsb", 1 << 24), None, None, None)
+    assert bw(wsb=100) == dn.INVALID_ARGUMENT                  # workspace too small
+    assert bw(ws=W + 16) == dn.UNSUPPORTED                     # workspace not 256-aligned
+    assert bw(cols=4104, mbs=4104) == dn.UNSUPPORTED           # wider than the backward serves
+    assert bw(dx=C) == dn.UNSUPPORTED                          # d_x over d_out
+    assert bw(do=None) == dn.INVALID_ARGUMENT
+    assert bw(rows=0) == dn.OK
+    assert lib.ln_modulate_backward_supported(A, B, C, D, E, E + 0x100000, 64, 3072, 64, 3072,
+                                              1e-6, W, 1 << 24, None, None) == 1
     assert lib.ditnorm_copy(A, B, 15, None) == dn.UNSUPPORTED
     assert lib.ditnorm_copy(A, A + 16, 64, None) == dn.UNSUPPORTED
 

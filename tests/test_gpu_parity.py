@@ -386,6 +386,21 @@ def test_full_workload(gpu, orc, key):
                 ref = orc.gate_residual_dt(a, b, c, dt)
             torch.cuda.synchronize()
             assert same_bits(host(out), ref, dt), l.name
+        elif l.entry == "ln_modulate_backward":
+            x, sc, dout = (t[n] for n in l.inputs)
+            rpb = l.extra["rows_per_batch"]
+            rows, cols = x.shape
+            mean, rstd = empty_f32(rows), empty_f32(rows)
+            d_x, d_scale, d_shift = gpu.ln_modulate_backward(dev(x), dev(sc), dev(dout), l.eps,
+                                                             mean_out=mean, rstd_out=rstd)
+            torch.cuda.synchronize()
+            ref = orc.ln_modulate_backward(x, sc, dout, l.eps, rows_per_batch=rpb)
+            differ = check_stats(host(mean), host(rstd), ref["mean"], ref["rstd"], l.name)
+            d = ulp_diff(host(d_x), ref["d_x"])
+            assert d.max() <= 1 and (d == 0).mean() >= 0.9999, l.name
+            if not differ.any():
+                assert np.array_equal(host(d_scale), ref["d_scale"]), l.name
+                assert np.array_equal(host(d_shift), ref["d_shift"]), l.name
         else:
             raise KeyError(l.entry)
 
