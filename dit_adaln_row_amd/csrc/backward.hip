@@ -6,14 +6,16 @@
 //
 // Three kernels, all on the caller's stream:
 //
-//  bwd_row_kernel     one wavefront per row (as the forward): the fp32 row
-//                     statistics from exact binary64 moments, then
-//                       x_hat = (x - mean) * rstd,  g = d_out * (1 + scale),
+//  bwd_row_kernel     one wavefront per row (as the forward): one pass of
+//                     binary64 sums over the raw row (sum x, sum x^2, sum g,
+//                     sum g x with g = d_out * (1 + scale)) gives the fp32
+//                     statistics and both row means the gradient needs, so
 //                       d_x = rstd * (g - mean(g) - x_hat * mean(g * x_hat))
-//                     evaluated in binary64 and rounded once to bf16 (round to
-//                     odd into binary32, then nearest-even into bf16: a single
-//                     correct rounding); the row's mean and rstd go to the
-//                     workspace for the next kernel.
+//                     becomes A g + B x + C with per-row binary64 constants,
+//                     rounded once to bf16 (round to odd into binary32, then
+//                     nearest-even into bf16: a single correct rounding); the
+//                     row's mean and rstd go to the workspace for the next
+//                     kernel.
 //  bwd_token_kernel   the first level of the token trees: a wavefront owns 32
 //                     consecutive tokens of one batch and 256 columns; each
 //                     lane walks the 32 rows of its 4 columns, 8 rows at a
@@ -72,29 +74,11 @@ __global__ __launch_bounds__(256) void bwd_row_kernel(const BwdArgs a) {
 #pragma unroll
   for (int k = 0; k < NV; ++k) sv[k] = ok(k) ? ld16(a.scale + mo + col(k)) : zero;
 
-  // statistics (padding vectors hold zeros)
+  // one pass of binary64 sums over the raw inputs (padding contributes
+  // zeros): S1 = sum x, S2 = sum x^2 (the statistics), G = sum g and
+  // GX = sum g x with g = d_out * (1 + scale)
   Moments m = {0.0, 0.0};
-#pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    float v[8];
-    unpack8(xv[k], v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) accumulate(m, v[e]);
-  }
-  const double n_d = (double)cols;
-  const double s1 = sum64(m.s1), s2 = sum64(m.s2);
-  const double mean_d = s1 / n_d;
-  const double var_d = __builtin_fmax(__builtin_fma(-s1, mean_d, s2) / n_d, 0.0);
-  const float mean_f = (float)mean_d;
-  const float rstd_f = rstd_from(var_d + (double)a.eps);
-  const double mean64 = (double)mean_f, rstd64 = (double)rstd_f;
-
-  // row sums of g and g * x_hat (binary64; padding contributes zeros).  The
-  // packed rows are re-widened in each pass (launder) rather than kept as
-  // binary64 values across the reductions.
-#pragma unroll
-  for (int k = 0; k < NV; ++k) launder(xv[k]);
-  double c1 = 0.0, c2 = 0.0;
+  double sg = 0.0, sgx = 0.0;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     float v[8], d[8], sc[8];
@@ -103,14 +87,29 @@ __global__ __launch_bounds__(256) void bwd_row_kernel(const BwdArgs a) {
     unpack8(sv[k], sc);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double xh = ((double)v[e] - mean64) * rstd64;
+      const double xd = (double)v[e];
+      m.s1 += xd;
+      m.s2 = __builtin_fma(xd, xd, m.s2);
       const double g = (double)d[e] * (double)(1.0f + sc[e]);
-      c1 += g;
-      c2 = __builtin_fma(g, xh, c2);
+      sg += g;
+      sgx = __builtin_fma(g, xd, sgx);
     }
   }
-  c1 = sum64(c1) / n_d;
-  c2 = sum64(c2) / n_d;
+  const double n_d = (double)cols;
+  const double s1 = sum64(m.s1), s2 = sum64(m.s2);
+  const double mean_d = s1 / n_d;
+  const double var_d = __builtin_fmax(__builtin_fma(-s1, mean_d, s2) / n_d, 0.0);
+  const float mean_f = (float)mean_d;
+  const float rstd_f = rstd_from(var_d + (double)a.eps);
+  const double mu = (double)mean_f, rs = (double)rstd_f;
+  // with x_hat = (x - mu) rs:  c1 = mean(g),  c2 = mean(g x_hat) = rs (GX - mu G) / N,
+  // and d_x = rs (g - c1 - x_hat c2) = A g + B x + C for per-row constants
+  const double G = sum64(sg), GX = sum64(sgx);
+  const double c1 = G / n_d;
+  const double c2 = rs * __builtin_fma(-mu, G, GX) / n_d;
+  const double A = rs;
+  const double B = -rs * rs * c2;
+  const double C = __builtin_fma(rs * rs * c2, mu, -rs * c1);
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     launder(xv[k]);
@@ -126,12 +125,22 @@ __global__ __launch_bounds__(256) void bwd_row_kernel(const BwdArgs a) {
     unpack8(xv[k], v);
     unpack8(dv[k], d);
     unpack8(sv[k], sc);
+    // Nearest-even into binary32 and then into bf16 rounds once, correctly,
+    // unless the binary32 value is inexact and lands exactly on a bf16
+    // halfway point (low 16 bits 0x8000): only then, and only for the
+    // wavefront that meets one, the rounding goes through round-to-odd.
+    double t[8];
+    bool tie = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double xh = ((double)v[e] - mean64) * rstd64;
       const double g = (double)d[e] * (double)(1.0f + sc[e]);
-      const double t = (g - c1) - xh * c2;
-      o[e] = f64_round_odd_f32(rstd64 * t);
+      t[e] = __builtin_fma(B, (double)v[e], __builtin_fma(A, g, C));
+      o[e] = (float)t[e];
+      tie |= (__float_as_uint(o[e]) & 0xFFFFu) == 0x8000u;
+    }
+    if (__builtin_amdgcn_ballot_w64(tie) != 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = f64_round_odd_f32(t[e]);
     }
     st16s(a.d_x + base + col(k), pack8(o));
   }
@@ -203,6 +212,12 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(const BwdArgs a, int64_t 
   float ls[4], hs[4], os[4], lc[4], hc[4], oc[4];
 #pragma unroll 1
   for (int c = 0; c < 4; ++c) {
+    if (c * 8 >= n) {  // a chunk wholly past the group folds to +0
+      float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      fold_chunk(c, z, ls, hs, os);
+      fold_chunk(c, z, lc, hc, oc);
+      continue;
+    }
     // this chunk's 8 rows: loads with clamped rows, then +0 for rows past
     // the group (the tree's padding)
     uint2 xq[8], dq[8];
@@ -261,6 +276,12 @@ __global__ __launch_bounds__(64) void bwd_tree_kernel(const float *in_shift, con
   float ls[4], hs[4], os[4], lc[4], hc[4], oc[4];
 #pragma unroll 1
   for (int c = 0; c < 4; ++c) {
+    if (c * 8 >= n) {  // a chunk wholly past the last value folds to +0
+      float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      fold_chunk(c, z, ls, hs, os);
+      fold_chunk(c, z, lc, hc, oc);
+      continue;
+    }
     float ts[8][4], tc[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
