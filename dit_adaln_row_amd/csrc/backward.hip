@@ -258,53 +258,50 @@ __global__ __launch_bounds__(64) void bwd_token_kernel(const BwdArgs a, int64_t 
 
 // ---------------------------------------------------------------------------
 // kernel C: one further tree level.  in: [B * n_in, cols] (both sums), out:
-// [B * n_out, cols], n_out = ceil(n_in / 32).  A thread folds 4 columns;
-// grid.x: batch * n_out, grid.y: column blocks.
+// [B * n_out, cols], n_out = ceil(n_in / 32).  A lane folds one column (the
+// data is small and latency-bound: more lanes, more loads in flight);
+// grid.x: batch * n_out, grid.y: column blocks of 64.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void bwd_tree_kernel(const float *in_shift, const float *in_scale,
                                                       float *out_shift, float *out_scale,
                                                       int64_t n_in, int64_t n_out, int32_t cols) {
-  const int q = blockIdx.y * 64 + threadIdx.x;  // column quad
+  const int cidx = blockIdx.y * 64 + threadIdx.x;  // column
   const int64_t bo = blockIdx.x;
   const int64_t b = bo / n_out, go = bo - b * n_out;
   const int64_t first = go * 32;
   const int64_t left_vals = n_in - first;
   const int n = (int)(left_vals < 32 ? left_vals : 32);
-  const bool live = q * 4 < cols;
-  const int qc = live ? q : cols / 4 - 1;  // clamped: every load is valid
+  const bool live = cidx < cols;
+  const int cc = live ? cidx : cols - 1;  // clamped: every load is valid
 
-  float ls[4], hs[4], os[4], lc[4], hc[4], oc[4];
+  float ls[1], hs[1], os[1], lc[1], hc[1], oc[1];
 #pragma unroll 1
   for (int c = 0; c < 4; ++c) {
     if (c * 8 >= n) {  // a chunk wholly past the last value folds to +0
-      float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      float z[1] = {0.0f};
       fold_chunk(c, z, ls, hs, os);
       fold_chunk(c, z, lc, hc, oc);
       continue;
     }
-    float ts[8][4], tc[8][4];
+    float ts[8][1], tc[8][1];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int s = c * 8 + i;
-      const int64_t off = (b * n_in + first + (s < n ? s : n - 1)) * cols + qc * 4;
-      const float4 vs = *reinterpret_cast<const float4 *>(in_shift + off);
-      const float4 vc = *reinterpret_cast<const float4 *>(in_scale + off);
+      const int64_t off = (b * n_in + first + (s < n ? s : n - 1)) * cols + cc;
+      const float vs = in_shift[off], vc = in_scale[off];
       const bool in = s < n;  // +0 padding past the last value
-      ts[i][0] = in ? vs.x : 0.0f; ts[i][1] = in ? vs.y : 0.0f;
-      ts[i][2] = in ? vs.z : 0.0f; ts[i][3] = in ? vs.w : 0.0f;
-      tc[i][0] = in ? vc.x : 0.0f; tc[i][1] = in ? vc.y : 0.0f;
-      tc[i][2] = in ? vc.z : 0.0f; tc[i][3] = in ? vc.w : 0.0f;
+      ts[i][0] = in ? vs : 0.0f;
+      tc[i][0] = in ? vc : 0.0f;
     }
-    float o[4];
+    float o[1];
     fold8(ts, o);
     fold_chunk(c, o, ls, hs, os);
     fold8(tc, o);
     fold_chunk(c, o, lc, hc, oc);
   }
   if (!live) return;
-  const int64_t o = bo * cols + q * 4;
-  *reinterpret_cast<float4 *>(out_shift + o) = make_float4(os[0], os[1], os[2], os[3]);
-  *reinterpret_cast<float4 *>(out_scale + o) = make_float4(oc[0], oc[1], oc[2], oc[3]);
+  out_shift[bo * cols + cidx] = os[0];
+  out_scale[bo * cols + cidx] = oc[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -370,7 +367,7 @@ hipError_t launch_backward(const BwdArgs &a, float *part0, float *part1, int64_t
     const int64_t dst_f = nb * n_out * a.cols;
     float *os = n_out == 1 ? a.d_shift : dst;
     float *oc = n_out == 1 ? a.d_scale : dst + dst_f;
-    hipLaunchKernelGGL(bwd_tree_kernel, dim3((unsigned)(nb * n_out), (unsigned)((quads + 63) / 64)),
+    hipLaunchKernelGGL(bwd_tree_kernel, dim3((unsigned)(nb * n_out), (unsigned)((a.cols + 63) / 64)),
                        dim3(64), 0, stream, src, src + src_f, os, oc, n, n_out, a.cols);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     n = n_out;
