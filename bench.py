@@ -508,10 +508,21 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd):
              f"{'algo_MB':>10} {'ratio':>7}"]
     for l in w.launches:
         lab = l.label()
-        if lab not in fetch or lab not in write:
+        if l.entry == "ln_modulate_backward":
+            # one call = the row pass, the token pass and the tree levels:
+            # every kernel's bytes over the number of calls
+            parts = ("bwd_row_kernel", "bwd_token_kernel", "bwd_tree_kernel")
+            if "bwd_row_kernel" not in fetch or "bwd_row_kernel" not in write:
+                continue
+            calls_f, calls_w = fetch["bwd_row_kernel"][1], write["bwd_row_kernel"][1]
+            fb = sum(fetch[k][0] * fetch[k][1] for k in parts if k in fetch) / calls_f * 1024.0 * f_cal
+            wb = sum(write[k][0] * write[k][1] for k in parts if k in write) / calls_w * 1024.0 * w_cal
+            lab = "bwd_row_kernel"
+        elif lab not in fetch or lab not in write:
             continue
-        fb = fetch[lab][0] * 1024.0 * f_cal
-        wb = write[lab][0] * 1024.0 * w_cal
+        else:
+            fb = fetch[lab][0] * 1024.0 * f_cal
+            wb = write[lab][0] * 1024.0 * w_cal
         algo = l.algorithmic_bytes()
         rec["kernels"][f"{workload}/{l.name}"] = {
             "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
