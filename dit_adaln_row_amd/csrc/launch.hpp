@@ -32,6 +32,7 @@ struct RowArgs {
   int64_t mod_stride;
   int32_t cols;
   float eps;
+  int64_t full_blocks;       // balanced kernel: workgroups of 4 whole rows (set by the launcher)
 };
 // fold: the affine-folded LN form (LN only: rms and gated false)
 hipError_t launch_row(const RowArgs &a, bool rms, bool gated, bool fold, const DeviceInfo &dev,

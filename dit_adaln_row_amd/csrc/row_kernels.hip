@@ -508,6 +508,255 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Balanced variant: whole rows for whole rounds, half rows for the remainder
+// ---------------------------------------------------------------------------
+//
+// A launch lasts as long as its busiest SIMD.  With one wavefront per row,
+// 4608 rows put 5 rows on half of the 1024 SIMDs and 4 on the rest, and the
+// launch takes as long as 5120 rows would (measured: 4096 rows of 3072 in
+// 9.7 us, 4608 and 5120 rows both 13.5 us).  Here the first rows go one per
+// wavefront in whole rounds (full_blocks workgroups of 4 rows) and the
+// remaining rows are split in two halves, a workgroup of 4 wavefronts taking
+// 2 rows, so 4608 rows are 4 whole rows plus one half row per SIMD.  The two
+// halves' binary64 moments meet through LDS; the sums are exact, so the
+// statistics carry the same bits either way.  Everything else is the
+// wavefront-per-row kernel's MOD_LDS path (rows of NV * 512 columns).
+template <int NVW, int NV, bool RMS, bool GATED, bool FOLD>
+__device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, float4 *lds_sh,
+                                            float4 *lds_w, double (*red)[2], int64_t row0,
+                                            int64_t row, int seg) {
+  constexpr bool SPLIT = NVW != NV;
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const int cols = a.cols;
+  const bool live = row < a.rows;
+  const int64_t base = (live ? row : row0) * (int64_t)cols;
+  const uint4 zero = {0, 0, 0, 0};
+  auto vid = [&](int k) { return seg * (NVW * 64) + lane + 64 * k; };
+  auto col = [&](int k) { return vid(k) * 8; };
+
+  // modulation rows of the workgroup's first batch, then this segment
+  constexpr int FILL = (NV * 64 + 255) / 256;
+  const int64_t b0 = row0 / a.rows_per_batch;
+  uint4 fsc[FILL], fsh[FILL], fw[RMS ? FILL : 1];
+#pragma unroll
+  for (int i = 0; i < FILL; ++i) {
+    const int j = threadIdx.x + 256 * i;
+    const bool in = j < NV * 64;
+    fsc[i] = in ? ld16(a.scale + b0 * a.mod_stride + j * 8) : zero;
+    fsh[i] = in ? ld16(a.shift + b0 * a.mod_stride + j * 8) : zero;
+    if constexpr (RMS) fw[i] = in ? ld16(a.weight + j * 8) : zero;
+  }
+  uint4 xv[NVW], rv[GATED ? NVW : 1];
+#pragma unroll
+  for (int k = 0; k < NVW; ++k) xv[k] = live ? ld16s(a.x + base + col(k)) : zero;
+  if constexpr (GATED) {
+#pragma unroll
+    for (int k = 0; k < NVW; ++k) rv[k] = live ? ld16s(a.residual + base + col(k)) : zero;
+  }
+  const int64_t mo = ((live ? row : row0) / a.rows_per_batch) * a.mod_stride;
+#pragma unroll
+  for (int i = 0; i < FILL; ++i) {
+    const int j = threadIdx.x + 256 * i;
+    if (j >= NV * 64) break;
+    float sc[8], sh[8];
+    unpack8(fsc[i], sc);
+    unpack8(fsh[i], sh);
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      sc[e] = 1.0f + sc[e];
+      sc[e + 1] = 1.0f + sc[e + 1];
+      round2(sc[e], sc[e + 1]);
+    }
+    lds_s1[mod_slot(j, 0) / 4] = make_float4(sc[0], sc[1], sc[2], sc[3]);
+    lds_s1[mod_slot(j, 1) / 4] = make_float4(sc[4], sc[5], sc[6], sc[7]);
+    lds_sh[mod_slot(j, 0) / 4] = make_float4(sh[0], sh[1], sh[2], sh[3]);
+    lds_sh[mod_slot(j, 1) / 4] = make_float4(sh[4], sh[5], sh[6], sh[7]);
+    if constexpr (RMS) {
+      float wt[8];
+      unpack8(fw[i], wt);
+      lds_w[mod_slot(j, 0) / 4] = make_float4(wt[0], wt[1], wt[2], wt[3]);
+      lds_w[mod_slot(j, 1) / 4] = make_float4(wt[4], wt[5], wt[6], wt[7]);
+    }
+  }
+  if constexpr (!SPLIT) {
+    lds_barrier();
+    if (!live) return;  // whole wavefront; no barrier follows
+  }
+
+  // gated residual: h = bf16(residual + bf16(gate * update)), stored
+  if constexpr (GATED) {
+#pragma unroll
+    for (int k = 0; k < NVW; ++k) {
+      float u[8], r[8], g[8];
+      unpack8(xv[k], u);
+      unpack8(rv[k], r);
+      unpack8(ld16(a.gate + mo + col(k)), g);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float g0 = g[e] * u[e], g1 = g[e + 1] * u[e + 1];
+        round2(g0, g1);
+        u[e] = r[e] + g0;
+        u[e + 1] = r[e + 1] + g1;
+      }
+      xv[k] = pack8(u);
+      if (live) st16s(a.residual_out + base + col(k), xv[k]);
+    }
+  }
+
+  // binary64 moments of the segment; the widened segment stays in registers
+  Moments m = {0.0, 0.0};
+  float xf[NVW][8];
+#pragma unroll
+  for (int k = 0; k < NVW; ++k) {
+    unpack8(xv[k], xf[k]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) accumulate(m, xf[k][e]);
+  }
+  double s2 = sum64(m.s2);
+  double s1 = RMS ? 0.0 : sum64(m.s1);
+  if constexpr (SPLIT) {
+    if (lane == 0) {
+      red[w][0] = s1;
+      red[w][1] = s2;
+    }
+    lds_barrier();  // the staged modulation rows and both halves' moments
+    if (!live) return;  // whole wavefront; no barrier follows
+    const int pw = w & ~1;
+    s1 = red[pw][0] + red[pw + 1][0];
+    s2 = red[pw][1] + red[pw + 1][1];
+  }
+  const double n_d = (double)cols;
+  float mean_f = 0.0f, rstd_f;
+  if constexpr (RMS) {
+    rstd_f = rstd_from(s2 / n_d + (double)a.eps);
+  } else {
+    const double mean_d = s1 / n_d;
+    const double var_d = __builtin_fmax(__builtin_fma(-s1, mean_d, s2) / n_d, 0.0);
+    mean_f = (float)mean_d;
+    rstd_f = rstd_from(var_d + (double)a.eps);
+  }
+  if (lane == 0 && seg == 0) {
+    if (a.mean_out) a.mean_out[row] = mean_f;
+    if (a.rstd_out) a.rstd_out[row] = rstd_f;
+  }
+  const bool mod_in_lds = mo == b0 * a.mod_stride;
+
+  // normalise, modulate, store (the run-time choices taken outside the loop)
+  auto normalise = [&](auto with_y, auto from_lds) {
+    constexpr bool WY = decltype(with_y)::value, FROM_LDS = decltype(from_lds)::value;
+#pragma unroll
+    for (int k = 0; k < NVW; ++k) {
+      float s1v[8], shv[8], y[8], o[8];
+      const float *v = xf[k];
+      const int j = vid(k);
+      if constexpr (FROM_LDS) {
+        const float4 a0 = lds_s1[mod_slot(j, 0) / 4], a1 = lds_s1[mod_slot(j, 1) / 4];
+        const float4 c0 = lds_sh[mod_slot(j, 0) / 4], c1 = lds_sh[mod_slot(j, 1) / 4];
+        s1v[0] = a0.x; s1v[1] = a0.y; s1v[2] = a0.z; s1v[3] = a0.w;
+        s1v[4] = a1.x; s1v[5] = a1.y; s1v[6] = a1.z; s1v[7] = a1.w;
+        shv[0] = c0.x; shv[1] = c0.y; shv[2] = c0.z; shv[3] = c0.w;
+        shv[4] = c1.x; shv[5] = c1.y; shv[6] = c1.z; shv[7] = c1.w;
+      } else {
+        unpack8(ld16(a.scale + mo + col(k)), s1v);
+        unpack8(ld16(a.shift + mo + col(k)), shv);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          s1v[e] = 1.0f + s1v[e];
+          s1v[e + 1] = 1.0f + s1v[e + 1];
+          round2(s1v[e], s1v[e + 1]);
+        }
+      }
+      if constexpr (FOLD) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float t = rstd_f * (v[e] - mean_f);
+          const float p = t * s1v[e];
+          o[e] = p + shv[e];
+        }
+        st16s(a.out + base + col(k), pack8(o));
+        continue;
+      }
+      if constexpr (RMS) {
+        const float4 w0 = lds_w[mod_slot(j, 0) / 4], w1 = lds_w[mod_slot(j, 1) / 4];
+        const float wt[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (v[e] * rstd_f) * wt[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = rstd_f * (v[e] - mean_f);
+      }
+      const uint4 yq = pack8(y);  // y as stored bf16 (the rounding is the packing)
+      unpack8(yq, y);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float q0 = y[e] * s1v[e], q1 = y[e + 1] * s1v[e + 1];
+        round2(q0, q1);
+        o[e] = q0 + shv[e];
+        o[e + 1] = q1 + shv[e + 1];
+      }
+      st16s(a.out + base + col(k), pack8(o));
+      if constexpr (WY) st16(a.y_out + base + col(k), yq);
+    }
+  };
+  using T = BoolC<true>;
+  using F = BoolC<false>;
+  if (a.y_out && !FOLD) {
+    if (mod_in_lds) normalise(T{}, T{});
+    else normalise(T{}, F{});
+  } else {
+    if (mod_in_lds) normalise(F{}, T{});
+    else normalise(F{}, F{});
+  }
+}
+
+template <int NV, bool RMS, bool GATED, bool FOLD>
+__global__ __launch_bounds__(256) void row_mixed_kernel(const RowArgs a) {
+  __shared__ float4 lds_s1[NV * 128], lds_sh[NV * 128];
+  __shared__ float4 lds_w[RMS ? NV * 128 : 1];
+  __shared__ double red[4][2];
+  const int w = wave_id();
+  if ((int64_t)blockIdx.x < a.full_blocks) {
+    const int64_t row0 = (int64_t)blockIdx.x * 4;
+    row_segment<NV, NV, RMS, GATED, FOLD>(a, lds_s1, lds_sh, lds_w, red, row0, row0 + w, 0);
+  } else {
+    const int64_t row0 = a.full_blocks * 4 + ((int64_t)blockIdx.x - a.full_blocks) * 2;
+    row_segment<NV / 2, NV, RMS, GATED, FOLD>(a, lds_s1, lds_sh, lds_w, red, row0,
+                                               row0 + (w >> 1), w & 1);
+  }
+}
+
+// Whole rounds of rows (one row per wavefront, one wavefront per SIMD per
+// round) and the remainder in halves when it is at most half a round; else
+// every row whole.
+template <int NV>
+static hipError_t launch_mixed(const RowArgs &a0, bool rms, bool gated, bool fold,
+                               const DeviceInfo &dev, hipStream_t stream) {
+  RowArgs a = a0;
+  const int64_t simds = (int64_t)dev.num_cu * 4;
+  const int64_t whole = a.rows / simds * simds;
+  const int64_t rem = a.rows - whole;
+  int64_t blocks;
+  if (whole > 0 && rem > 0 && 2 * rem <= simds) {
+    a.full_blocks = whole / 4;
+    blocks = a.full_blocks + (rem + 1) / 2;
+  } else {
+    a.full_blocks = (a.rows + 3) / 4;
+    blocks = a.full_blocks;
+  }
+  const dim3 grid((unsigned)blocks), block(256);
+#define DITNORM_MIXED(R, G, F) \
+  hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, F>), grid, block, 0, stream, a)
+  if (fold) DITNORM_MIXED(false, false, true);
+  else if (!rms && !gated) DITNORM_MIXED(false, false, false);
+  else if (!rms && gated) DITNORM_MIXED(false, true, false);
+  else if (rms && !gated) DITNORM_MIXED(true, false, false);
+  else DITNORM_MIXED(true, true, false);
+#undef DITNORM_MIXED
+  return hipGetLastError();
+}
+
 template <int NV, bool FULL, int MODE = MOD_LDS>
 hipError_t launch_wave(const RowArgs &a, bool rms, bool gated, bool fold, hipStream_t stream) {
   const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
@@ -552,9 +801,10 @@ static hipError_t launch_cfg(const RowArgs &a, bool rms, bool gated, bool fold,
 hipError_t launch_row(const RowArgs &a, bool rms, bool gated, bool fold, const DeviceInfo &dev,
                       hipStream_t stream) {
   const int nvec = a.cols / 8;
-  // Rows up to 4096 columns: one wavefront per row, the modulation rows (and
-  // the RMS weight) staged in LDS once per workgroup -- except for the folded
-  // form, whose lighter chain measured faster reading them per row.
+  // Rows of 1024-4096 columns (multiples of 1024): the balanced kernel, the
+  // modulation rows (and the RMS weight) staged in LDS once per workgroup --
+  // except for the folded form, whose lighter chain measured faster reading
+  // them per row.  Other widths up to 4096: one wavefront per row.
   if (fold) {
     switch (nvec) {
       case 128: return launch_wave<2, true, MOD_SERIAL>(a, rms, gated, fold, stream);
@@ -565,10 +815,10 @@ hipError_t launch_row(const RowArgs &a, bool rms, bool gated, bool fold, const D
     }
   }
   switch (nvec) {
-    case 128: return launch_wave<2, true, MOD_LDS>(a, rms, gated, fold, stream);
-    case 256: return launch_wave<4, true, MOD_LDS>(a, rms, gated, fold, stream);
-    case 384: return launch_wave<6, true, MOD_LDS>(a, rms, gated, fold, stream);
-    case 512: return launch_wave<8, true, MOD_LDS>(a, rms, gated, fold, stream);
+    case 128: return launch_mixed<2>(a, rms, gated, fold, dev, stream);
+    case 256: return launch_mixed<4>(a, rms, gated, fold, dev, stream);
+    case 384: return launch_mixed<6>(a, rms, gated, fold, dev, stream);
+    case 512: return launch_mixed<8>(a, rms, gated, fold, dev, stream);
     default: break;
   }
   if (nvec <= 64) return launch_wave<1, false>(a, rms, gated, fold, stream);

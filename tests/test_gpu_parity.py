@@ -170,15 +170,17 @@ def test_gated_inplace_residual(gpu, orc):
 # RMSNorm + modulate (plain and gated)
 # ---------------------------------------------------------------------------
 
-def _rms_run_check(gpu, orc, what, x, w, sc, sh, eps, rpb, res=None, gate=None):
+def _rms_run_check(gpu, orc, what, x, w, sc, sh, eps, rpb, res=None, gate=None, mod_dev=None):
+    """mod_dev: device (scale, shift, gate) views to pass instead of sc, sh, gate
+    (chunk views); the host arrays then describe the same memory for the oracle."""
     rows, cols = x.shape
     kw = dict(rstd_out=empty_f32(rows), y_out=torch.empty((rows, cols), dtype=torch.bfloat16,
                                                           device="cuda"))
+    scd, shd, gd = mod_dev if mod_dev is not None else (dev(sc), dev(sh), dev(gate))
     if res is not None:
-        h, out = gpu.rms_modulate(dev(x), dev(w), dev(sc), dev(sh), eps, residual=dev(res),
-                                  gate=dev(gate), **kw)
+        h, out = gpu.rms_modulate(dev(x), dev(w), scd, shd, eps, residual=dev(res), gate=gd, **kw)
     else:
-        h, out = None, gpu.rms_modulate(dev(x), dev(w), dev(sc), dev(sh), eps, **kw)
+        h, out = None, gpu.rms_modulate(dev(x), dev(w), scd, shd, eps, **kw)
     torch.cuda.synchronize()
     out, rstd, y = host(out), host(kw["rstd_out"]), host(kw["y_out"])
     ref = orc.rms_modulate(x, w, sc, sh, eps, residual=res, gate=gate, rows_per_batch=rpb)
@@ -463,3 +465,49 @@ def test_rejections_raise(gpu):
         gpu.ln_modulate(buf[2:2 + 3072].view(3, 1024), s, s,
                         out=torch.empty((3, 1024), dtype=torch.bfloat16, device="cuda"))
     assert e.value.status == gpu.UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# the balanced launch: whole rows for whole rounds of the 1024 SIMDs, the
+# remainder as half rows (two wavefronts per row, moments through LDS)
+# ---------------------------------------------------------------------------
+
+SPLIT_CASES = [(3072, 4096 + 512, 4096 + 512), (3072, 1024 + 1, 1025), (4096, 2048 + 257, 2305),
+               (1024, 4096 + 3, 4099), (2048, 3072 + 511, 3583), (3072, 4096 + 256, 17)]
+
+
+@pytest.mark.parametrize("cols,rows,rpb", SPLIT_CASES)
+@pytest.mark.parametrize("kind", ["ln", "gated_ln", "rms", "gated_rms"])
+def test_balanced_split_rows(gpu, orc, cols, rows, rpb, kind):
+    """Row counts with a remainder of at most half a round take the half-row
+    path; batch boundaries fall inside half-row workgroups in the last case."""
+    log(f"balanced {kind} rows={rows} cols={cols} rpb={rpb}")
+    B = rows // rpb
+    x = rand((rows, cols), 0.2, 1.5, 1100 + cols + rows)
+    emb = rand((B, 6 * cols), 0, 0.1, 1101 + B)
+    embd = dev(emb)
+    sc_d, sh_d, g_d = embd[:, cols:2 * cols], embd[:, 0:cols], embd[:, 2 * cols:3 * cols]
+    sc = np.concatenate([emb.ravel()[cols:], np.zeros(cols, np.uint16)]).reshape(B, 6 * cols)
+    gt = np.concatenate([emb.ravel()[2 * cols:], np.zeros(2 * cols, np.uint16)]).reshape(B, 6 * cols)
+    mean, rstd = empty_f32(rows), empty_f32(rows)
+    y = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    if kind in ("ln", "gated_ln"):
+        if kind == "ln":
+            xin = x
+            out = gpu.ln_modulate(dev(x), sc_d, sh_d, 1e-6, mean_out=mean, rstd_out=rstd, y_out=y)
+        else:
+            res = rand((rows, cols), 0, 1, 1102)
+            h, out = gpu.gated_ln_modulate(dev(x), dev(res), g_d, sc_d, sh_d, 1e-6, mean_out=mean,
+                                           rstd_out=rstd, y_out=y)
+            torch.cuda.synchronize()
+            xin = orc.gate_residual(x, res, gt, rows_per_batch=rpb)
+            assert same_bits(host(h), xin), "gate stage"
+        torch.cuda.synchronize()
+        ref = orc.ln_modulate(xin, sc, emb, 1e-6, rows_per_batch=rpb)
+        _ln_check(orc, f"balanced {kind}", xin, sc, emb, 1e-6, rpb, host(out), host(mean),
+                  host(rstd), host(y), ref=ref)
+    else:
+        w = rand((cols,), 1, 0.05, 1103)
+        res = rand((rows, cols), 0, 1, 1104) if kind == "gated_rms" else None
+        _rms_run_check(gpu, orc, f"balanced {kind}", x, w, sc, emb, 1e-6, rpb, res,
+                       gt if res is not None else None, mod_dev=(sc_d, sh_d, g_d))
