@@ -409,6 +409,14 @@ def copy_calibration(lib, dev, stream, launches=8):
 
 def _kernel_label(name):
     """Launch kind of a demangled kernel name."""
+    if "ditnorm::row_mixed_kernel<" in name:
+        # row_mixed_kernel<NV, RMS, GATED, FOLD>
+        args = [a.strip() for a in name.split("_kernel<", 1)[1].split(">", 1)[0].split(",")]
+        rms, gated, fold = args[1] == "true", args[2] == "true", args[3] == "true"
+        if fold:
+            return "ln_modulate_folded"
+        return {(False, False): "ln_modulate", (False, True): "gated_ln_modulate",
+                (True, False): "rms_modulate", (True, True): "gated_rms_modulate"}[(rms, gated)]
     if "ditnorm::row_kernel<" in name or "ditnorm::row_wave_kernel<" in name:
         # row_kernel<NT, NV, RMS, GATED, FOLD> / row_wave_kernel<NV, FULL, RMS, GATED, MODE, FOLD>
         args = [a.strip() for a in name.split("_kernel<", 1)[1].split(">", 1)[0].split(",")]
