@@ -267,19 +267,9 @@ struct BoolC {
 
 enum ModMode : int {
   MOD_SERIAL = 0,  // per 16-byte vector, from the caches, as each is needed
-  MOD_LDS = 1,     // s1 / shift staged per workgroup in LDS (fp32); weight / gate as SERIAL
-  MOD_BATCH = 2,   // all of a row's operands in one batch of loads: the gate with the
-                   // row, scale / shift / weight after the statistics, before any store
-  MOD_EARLY = 3,   // all of a row's operands loaded together with the row
+  MOD_LDS = 1,     // s1 / shift (and the RMS weight) staged per workgroup in LDS (fp32);
+                   // the gate as SERIAL
 };
-
-// Pointer the optimiser cannot see through: loads through it stay after
-// this point in program order.
-template <typename T>
-__device__ __forceinline__ const T *pin(const T *p) {
-  asm volatile("" : "+s"(p));
-  return p;
-}
 
 template <int NV, bool FULL, bool RMS, bool GATED, int MODE = MOD_LDS, bool FOLD = false>
 __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
@@ -327,23 +317,6 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
   }
   const int64_t mo = (row / a.rows_per_batch) * a.mod_stride;
 
-  // batched / early operand loads
-  constexpr bool HOLD = MODE == MOD_BATCH || MODE == MOD_EARLY;
-  uint4 mg[GATED && HOLD ? NV : 1], ms[HOLD ? NV : 1], mh[HOLD ? NV : 1], mw[RMS && HOLD ? NV : 1];
-  auto load_mod = [&](const uint16_t *sc, const uint16_t *sh, const uint16_t *w) {
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      ms[k] = ok(k) ? ld16(sc + mo + col(k)) : zero;
-      mh[k] = ok(k) ? ld16(sh + mo + col(k)) : zero;
-      if constexpr (RMS) mw[k] = ok(k) ? ld16(w + col(k)) : zero;
-    }
-  };
-  if constexpr (GATED && HOLD) {
-#pragma unroll
-    for (int k = 0; k < NV; ++k) mg[k] = ok(k) ? ld16(a.gate + mo + col(k)) : zero;
-  }
-  if constexpr (MODE == MOD_EARLY) load_mod(a.scale, a.shift, a.weight);
-
   // stage s1 = bf16(1 + scale) and shift in LDS as fp32
 #pragma unroll
   for (int i = 0; i < FILL; ++i) {
@@ -380,8 +353,7 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
       float u[8], r[8], g[8];
       unpack8(xv[k], u);
       unpack8(rv[k], r);
-      if constexpr (HOLD) unpack8(mg[k], g);
-      else unpack8(ok(k) ? ld16(a.gate + mo + col(k)) : zero, g);
+      unpack8(ok(k) ? ld16(a.gate + mo + col(k)) : zero, g);
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         float g0 = g[e] * u[e], g1 = g[e + 1] * u[e + 1];
@@ -420,7 +392,6 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
     if (a.mean_out) a.mean_out[row] = mean_f;
     if (a.rstd_out) a.rstd_out[row] = rstd_f;
   }
-  if constexpr (MODE == MOD_BATCH) load_mod(pin(a.scale), pin(a.shift), pin(a.weight));
 
   // normalise, modulate, store.  The two run-time choices (debug output,
   // modulation source) are taken once, outside the loop, so the unrolled
@@ -441,13 +412,8 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
         shv[0] = c0.x; shv[1] = c0.y; shv[2] = c0.z; shv[3] = c0.w;
         shv[4] = c1.x; shv[5] = c1.y; shv[6] = c1.z; shv[7] = c1.w;
       } else {
-        if constexpr (HOLD) {
-          unpack8(ms[k], s1v);
-          unpack8(mh[k], shv);
-        } else {
-          unpack8(ld16(a.scale + mo + col(k)), s1v);
-          unpack8(ld16(a.shift + mo + col(k)), shv);
-        }
+        unpack8(ld16(a.scale + mo + col(k)), s1v);
+        unpack8(ld16(a.shift + mo + col(k)), shv);
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           s1v[e] = 1.0f + s1v[e];
@@ -472,8 +438,6 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
           const float4 w0 = lds_w[mod_slot(j, 0) / 4], w1 = lds_w[mod_slot(j, 1) / 4];
           w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
           w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
-        } else if constexpr (HOLD) {
-          unpack8(mw[k], w);
         } else {
           unpack8(ld16(a.weight + col(k)), w);
         }
