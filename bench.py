@@ -425,7 +425,7 @@ def _kernel_label(name):
             return "ln_modulate_folded"
         return {(False, False): "ln_modulate", (False, True): "gated_ln_modulate",
                 (True, False): "rms_modulate", (True, True): "gated_rms_modulate"}[(rms, gated)]
-    for key in ("bwd_row_kernel", "bwd_token_kernel", "bwd_tree_kernel"):
+    for key in ("bwd_fused_kernel", "bwd_tree_kernel"):
         if f"ditnorm::{key}" in name:
             return key
     if "ditnorm::elementwise_kernel<" in name:
@@ -517,15 +517,15 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd):
     for l in w.launches:
         lab = l.label()
         if l.entry == "ln_modulate_backward":
-            # one call = the row pass, the token pass and the tree levels:
+            # one call = the fused row / token pass and the tree levels:
             # every kernel's bytes over the number of calls
-            parts = ("bwd_row_kernel", "bwd_token_kernel", "bwd_tree_kernel")
-            if "bwd_row_kernel" not in fetch or "bwd_row_kernel" not in write:
+            parts = ("bwd_fused_kernel", "bwd_tree_kernel")
+            if "bwd_fused_kernel" not in fetch or "bwd_fused_kernel" not in write:
                 continue
-            calls_f, calls_w = fetch["bwd_row_kernel"][1], write["bwd_row_kernel"][1]
+            calls_f, calls_w = fetch["bwd_fused_kernel"][1], write["bwd_fused_kernel"][1]
             fb = sum(fetch[k][0] * fetch[k][1] for k in parts if k in fetch) / calls_f * 1024.0 * f_cal
             wb = sum(write[k][0] * write[k][1] for k in parts if k in write) / calls_w * 1024.0 * w_cal
-            lab = "bwd_row_kernel"
+            lab = "bwd_fused_kernel"
         elif lab not in fetch or lab not in write:
             continue
         else:

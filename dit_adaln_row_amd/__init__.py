@@ -389,7 +389,7 @@ def ln_modulate_backward(x, scale, d_out, eps=1e-6, *, d_x=None, d_scale=None, d
     """Gradients of LN(x) * (1 + scale) + shift: returns (d_x bf16 like x,
     d_scale fp32 [B, D], d_shift fp32 [B, D]).  x, d_out (..., D) bf16; scale
     (D,), (B, D) or (B, 1, D) bf16.  The workspace (uint8 device tensor) is
-    allocated here when not given."""
+    allocated here when the call needs one and none is given."""
     _act(x, "x")
     _act(d_out, "d_out")
     if d_out.shape != x.shape:
@@ -405,10 +405,11 @@ def ln_modulate_backward(x, scale, d_out, eps=1e-6, *, d_x=None, d_scale=None, d
         if t.dtype != torch.float32 or t.numel() != b * cols or not t.is_contiguous():
             raise ValueError(f"{nm} must be a contiguous fp32 tensor of {b}x{cols}")
     need = ln_modulate_backward_workspace_bytes(rows, cols, rpb) if rows else 0
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _call("ln_modulate_backward", _p(x), _p(scale), _p(d_out), _p(d_x), _p(d_scale), _p(d_shift),
-          rows, cols, rpb, stride, eps, _p(workspace), workspace.numel() * workspace.element_size(),
+          rows, cols, rpb, stride, eps, _p(workspace), ws_bytes,
           _p(_f32_out(mean_out, rows, "mean_out")), _p(_f32_out(rstd_out, rows, "rstd_out")),
           _stream(x))
     return d_x, d_scale, d_shift

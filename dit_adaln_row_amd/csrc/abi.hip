@@ -236,9 +236,9 @@ int validate_backward(const void *x, const void *scale, const void *d_out, const
   int st = check_rows(rows, cols, rpb, mbs, eps);
   if (st != DITNORM_OK || rows == 0) return st;
   if (cols > DITNORM_MAX_BACKWARD_COLS) return DITNORM_UNSUPPORTED;
-  if (!x || !scale || !d_out || !d_x || !d_scale || !d_shift || !ws)
-    return DITNORM_INVALID_ARGUMENT;
-  if (ws_bytes < bwd_layout(rows, cols, rpb).bytes) return DITNORM_INVALID_ARGUMENT;
+  if (!x || !scale || !d_out || !d_x || !d_scale || !d_shift) return DITNORM_INVALID_ARGUMENT;
+  const int64_t need = bwd_layout(rows, cols, rpb).bytes;
+  if (need > 0 && (!ws || ws_bytes < need)) return DITNORM_INVALID_ARGUMENT;
   if (!aligned16(x) || !aligned16(scale) || !aligned16(d_out) || !aligned16(d_x) ||
       !aligned16(d_scale) || !aligned16(d_shift) || ((uintptr_t)ws & 255u) != 0 ||
       !aligned4(mean_out) || !aligned4(rstd_out))
@@ -246,7 +246,7 @@ int validate_backward(const void *x, const void *scale, const void *d_out, const
   const int64_t act = rows * cols * 2, nb = rows / rpb;
   const Buf in[] = {{x, act}, {scale, mod_bytes(nb, mbs, cols)}, {d_out, act}};
   const Buf o[] = {{d_x, act}, {d_scale, nb * cols * 4}, {d_shift, nb * cols * 4},
-                   {ws, ws_bytes}, {mean_out, rows * 4}, {rstd_out, rows * 4}};
+                   {ws, need}, {mean_out, rows * 4}, {rstd_out, rows * 4}};
   const int alias[] = {-1, -1, -1, -1, -1, -1};
   return aliasing_ok(in, o, alias) ? DITNORM_OK : DITNORM_UNSUPPORTED;
 }
@@ -570,8 +570,6 @@ int ln_modulate_backward(const void *x, const void *scale, const void *d_out, vo
   a.d_x = (uint16_t *)d_x;
   a.d_scale = d_scale;
   a.d_shift = d_shift;
-  a.ws_mean = (float *)(ws + L.mean_off);
-  a.ws_rstd = (float *)(ws + L.rstd_off);
   a.mean_out = mean_out;
   a.rstd_out = rstd_out;
   a.rows = rows;
@@ -579,8 +577,8 @@ int ln_modulate_backward(const void *x, const void *scale, const void *d_out, vo
   a.mod_stride = mod_batch_stride;
   a.cols = (int32_t)cols;
   a.eps = eps;
-  return finish(launch_backward(a, (float *)(ws + L.part0_off), (float *)(ws + L.part1_off),
-                                L.groups, (hipStream_t)stream));
+  return finish(launch_backward(a, L, (float *)(ws + L.part0_off), (float *)(ws + L.part1_off),
+                                (hipStream_t)stream));
 }
 
 int ln_modulate_backward_supported(const void *x, const void *scale, const void *d_out,

@@ -4,27 +4,31 @@
 // modulation-parameter gradients as token sums over fixed fp32 balanced
 // trees that depend only on the token count).
 //
-// Three kernels, all on the caller's stream:
+// The token trees fold groups of 32 consecutive tokens by adjacent pairs, then
+// the group sums in groups of 32 again, +0 padding a short group.  Every
+// aligned run of 8 (or 4) tokens inside a group is a complete subtree of it,
+// and the 32 * (32 / R) runs of R tokens in 32 consecutive groups are the
+// leaves of one value of the second level; the kernels follow those subtrees:
 //
-//  bwd_row_kernel     one wavefront per row (as the forward): one pass of
-//                     binary64 sums over the raw row (sum x, sum x^2, sum g,
-//                     sum g x with g = d_out * (1 + scale)) gives the fp32
-//                     statistics and both row means the gradient needs, so
-//                       d_x = rstd * (g - mean(g) - x_hat * mean(g * x_hat))
-//                     becomes A g + B x + C with per-row binary64 constants,
-//                     rounded once to bf16 (round to odd into binary32, then
-//                     nearest-even into bf16: a single correct rounding); the
-//                     row's mean and rstd go to the workspace for the next
-//                     kernel.
-//  bwd_token_kernel   the first level of the token trees: a wavefront owns 32
-//                     consecutive tokens of one batch and 256 columns; each
-//                     lane walks the 32 rows of its 4 columns, 8 rows at a
-//                     time, and folds the fp32 terms d_out and d_out * x_hat
-//                     (x_hat in fp32: rstd * (x - mean)) by adjacent pairs --
-//                     the balanced tree of the 32 values, 8 at a time; rows
-//                     past the batch contribute +0 (the tree's padding).
-//  bwd_tree_kernel    every further level: groups of 32 partial sums folded
-//                     the same way, until one value per batch and column.
+//  bwd_fused_kernel  a workgroup of R wavefronts owns R consecutive tokens of
+//                    one batch (R = 8; 4 for batches of at most 4 tokens and
+//                    rows over 3072 columns), one row per wavefront.  One
+//                    pass of binary64 sums over the raw row (sum x, sum x^2,
+//                    sum g, sum g x with g = d_out * (1 + scale)) gives the
+//                    fp32 statistics and
+//                    both row means the gradient needs, so
+//                      d_x = rstd * (g - mean(g) - x_hat * mean(g * x_hat))
+//                    becomes A g + B x + C with per-row binary64 constants,
+//                    rounded once to bf16.  Then the rows' raw x and d_out
+//                    pass through LDS, column-major: each thread takes two
+//                    columns and folds the fp32 terms d_out and
+//                    d_out * x_hat (x_hat = rstd * (x - mean) in fp32) of the
+//                    R rows by adjacent pairs -- the subtree of those R
+//                    tokens.  x and d_out are read from HBM once.
+//  bwd_tree_kernel   one or more levels at once: out = the balanced fold of
+//                    L consecutive partial sums (L = 4, 8, 32, 128 or 256), T
+//                    wavefronts folding 4, 8 or 16 each, their sums combined
+//                    through LDS.
 //
 // The result depends only on the batch's token count: no atomics, no order
 // chosen at run time, bitwise equal for any batch size or batch position.
@@ -50,23 +54,31 @@ __device__ __forceinline__ float f64_round_odd_f32(double d) {
   return f;
 }
 
+// The balanced fold of N values by adjacent pairs (N a power of two).
+template <int N>
+__device__ __forceinline__ float tree_fold(const float *v) {
+  if constexpr (N == 1) {
+    return v[0];
+  } else {
+    return tree_fold<N / 2>(v) + tree_fold<N / 2>(v + N / 2);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// kernel A: statistics and d_x, one wavefront per row
+// one row: statistics and d_x.  xv / dv keep the raw row for the token sums.
 // ---------------------------------------------------------------------------
 template <int NV, bool FULL>
-__global__ __launch_bounds__(256) void bwd_row_kernel(const BwdArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
-  if (row >= a.rows) return;  // whole wavefront; the kernel has no barrier
+__device__ __forceinline__ void bwd_row(const BwdArgs &a, int64_t row, int64_t mo, int lane,
+                                        uint4 (&xv)[NV], uint4 (&dv)[NV], float &mean_f,
+                                        float &rstd_f) {
   const int cols = a.cols;
   const int nvec = cols >> 3;
   const int64_t base = row * (int64_t)cols;
-  const int64_t mo = (row / a.rows_per_batch) * a.mod_stride;
   const uint4 zero = {0, 0, 0, 0};
   auto ok = [&](int k) { return FULL || lane + 64 * k < nvec; };
   auto col = [&](int k) { return (lane + 64 * k) * 8; };
 
-  uint4 xv[NV], dv[NV], sv[NV];
+  uint4 sv[NV];
 #pragma unroll
   for (int k = 0; k < NV; ++k) xv[k] = ok(k) ? ld16s(a.x + base + col(k)) : zero;
 #pragma unroll
@@ -99,8 +111,8 @@ __global__ __launch_bounds__(256) void bwd_row_kernel(const BwdArgs a) {
   const double s1 = sum64(m.s1), s2 = sum64(m.s2);
   const double mean_d = s1 / n_d;
   const double var_d = __builtin_fmax(__builtin_fma(-s1, mean_d, s2) / n_d, 0.0);
-  const float mean_f = (float)mean_d;
-  const float rstd_f = rstd_from(var_d + (double)a.eps);
+  mean_f = (float)mean_d;
+  rstd_f = rstd_from(var_d + (double)a.eps);
   const double mu = (double)mean_f, rs = (double)rstd_f;
   // with x_hat = (x - mu) rs:  c1 = mean(g),  c2 = mean(g x_hat) = rs (GX - mu G) / N,
   // and d_x = rs (g - c1 - x_hat c2) = A g + B x + C for per-row constants
@@ -144,233 +156,272 @@ __global__ __launch_bounds__(256) void bwd_row_kernel(const BwdArgs a) {
     }
     st16s(a.d_x + base + col(k), pack8(o));
   }
-  if (lane == 0) {
-    a.ws_mean[row] = mean_f;
-    a.ws_rstd[row] = rstd_f;
-    if (a.mean_out) a.mean_out[row] = mean_f;
-    if (a.rstd_out) a.rstd_out[row] = rstd_f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    launder(xv[k]);
+    launder(dv[k]);
   }
 }
 
 // ---------------------------------------------------------------------------
-// The balanced fold of 32 values, in 4 chunks of 8: a chunk's 8 values are
-// folded by adjacent pairs (3 levels, in registers), and the chunk sums
-// o0..o3 combine as (o0 + o1) + (o2 + o3) -- together the adjacent-pairs tree
-// of the 32 values.  W floats per lane.
+// the fused kernel.  grid.x: batch * chunks (chunk = R consecutive tokens of a
+// batch); block: R wavefronts.  out_*: [B * chunks, cols] per sum, the chunk
+// subtree sums; with a single chunk per batch they are the final sums, and
+// the +0 padding of the rest of the 32-token group is added here.
 // ---------------------------------------------------------------------------
-template <int W>
-__device__ __forceinline__ void fold8(float (&t)[8][W], float (&o)[W]) {
-#pragma unroll
-  for (int e = 0; e < W; ++e) {
-    const float p0 = t[0][e] + t[1][e], p1 = t[2][e] + t[3][e];
-    const float p2 = t[4][e] + t[5][e], p3 = t[6][e] + t[7][e];
-    o[e] = (p0 + p1) + (p2 + p3);
-  }
-}
+template <int NV, bool FULL, int R>
+__global__ __launch_bounds__(64 * R) void bwd_fused_kernel(const BwdArgs a, int64_t chunks,
+                                                           float *out_shift, float *out_scale,
+                                                           int final_level) {
+  // a step moves VS 16-byte vectors per lane (VS * 512 columns) through LDS,
+  // and every thread folds one column pair of them
+  constexpr int VS = R / 4;
+  constexpr int STEPS = (NV + VS - 1) / VS;
+  __shared__ float stat[R][2];
+  __shared__ __attribute__((aligned(16))) uint32_t tile[2][R][2][VS * 256];  // [buffer][row][x | d_out][dword]
 
-// chunk c's sum o enters the fold: chunk 0 and 2 wait as left operands,
-// chunk 1 forms (o0 + o1), chunk 3 forms (o2 + o3) and the group sum.
-template <int W>
-__device__ __forceinline__ void fold_chunk(int c, float (&o)[W], float (&left)[W],
-                                           float (&half)[W], float (&out)[W]) {
-#pragma unroll
-  for (int e = 0; e < W; ++e) {
-    if ((c & 1) == 0) {
-      left[e] = o[e];
-    } else {
-      const float pair = left[e] + o[e];
-      if (c == 1) half[e] = pair;
-      else out[e] = half[e] + pair;
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const int64_t b = blockIdx.x / chunks, j = blockIdx.x - b * chunks;
+  const int64_t left = a.rows_per_batch - j * R;
+  const int nrow = (int)(left < R ? left : R);  // tokens of this chunk
+  const int64_t row = b * a.rows_per_batch + j * R + w;
+  const int nvec = a.cols >> 3;
+
+  uint4 xv[NV], dv[NV];
+  if (w < nrow) {
+    float mean_f, rstd_f;
+    bwd_row<NV, FULL>(a, row, b * a.mod_stride, lane, xv, dv, mean_f, rstd_f);
+    if (lane == 0) {
+      stat[w][0] = mean_f;
+      stat[w][1] = rstd_f;
+      if (a.mean_out) a.mean_out[row] = mean_f;
+      if (a.rstd_out) a.rstd_out[row] = rstd_f;
     }
   }
-}
 
-// ---------------------------------------------------------------------------
-// kernel B: first tree level over tokens.  grid.x: batch * groups-per-batch,
-// grid.y: column blocks of 256 columns (one wavefront, 4 columns = 8 bytes per
-// lane, so each row access is 512 contiguous bytes).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint2 ld8s(const uint16_t *p) {
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
-  return make_uint2(v.x, v.y);
-}
-
-__global__ __launch_bounds__(64) void bwd_token_kernel(const BwdArgs a, int64_t groups,
-                                                       float *out_shift, float *out_scale) {
-  const int nq = a.cols >> 2;
-  const int q = blockIdx.y * 64 + threadIdx.x;  // column quad
-  const int64_t bg = blockIdx.x;
-  const int64_t b = bg / groups, g = bg - b * groups;
-  const int64_t first = g * 32;                           // token index within the batch
-  const int64_t left_tokens = a.rows_per_batch - first;
-  const int n = (int)(left_tokens < 32 ? left_tokens : 32);  // tokens in this group
-  const int64_t r0 = b * a.rows_per_batch + first;
-  const bool live = q < nq;
-  const int qc = live ? q : nq - 1;  // clamped: every load is valid
-
-  float ls[4], hs[4], os[4], lc[4], hc[4], oc[4];
-#pragma unroll 1
-  for (int c = 0; c < 4; ++c) {
-    if (c * 8 >= n) {  // a chunk wholly past the group folds to +0
-      float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      fold_chunk(c, z, ls, hs, os);
-      fold_chunk(c, z, lc, hc, oc);
-      continue;
-    }
-    // this chunk's 8 rows: loads with clamped rows, then +0 for rows past
-    // the group (the tree's padding)
-    uint2 xq[8], dq[8];
-    float mu[8], rs[8];
+  // token sums of the chunk
+  const int vk = (int)(threadIdx.x >> 8);  // vector of the step this thread folds
+  const int pr = (int)(threadIdx.x & 255);  // its column pair within that vector
+  float mu[R], rs[R];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int s = c * 8 + i;
-      const int64_t r = r0 + (s < n ? s : n - 1);
-      xq[i] = ld8s(a.x + r * a.cols + qc * 4);
-      dq[i] = ld8s(a.d_out + r * a.cols + qc * 4);
-      mu[i] = a.ws_mean[r];
-      rs[i] = a.ws_rstd[r];
-    }
-    float ts[8][4], tc[8][4];
+  for (int s = 0; s < STEPS; ++s) {
+    const int buf = s & 1;
+    if (w < nrow) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool in = c * 8 + i < n;
-      const float v[4] = {bf_lo(xq[i].x), bf_hi(xq[i].x), bf_lo(xq[i].y), bf_hi(xq[i].y)};
-      const float d[4] = {bf_lo(dq[i].x), bf_hi(dq[i].x), bf_lo(dq[i].y), bf_hi(dq[i].y)};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float t = d[e] * (rs[i] * (v[e] - mu[i]));
-        ts[i][e] = in ? d[e] : 0.0f;
-        tc[i][e] = in ? t : 0.0f;
+      for (int v = 0; v < VS; ++v) {
+        const int k = s * VS + v;
+        if (k < NV && (FULL || lane + 64 * k < nvec)) {
+          *reinterpret_cast<uint4 *>(&tile[buf][w][0][v * 256 + lane * 4]) = xv[k];
+          *reinterpret_cast<uint4 *>(&tile[buf][w][1][v * 256 + lane * 4]) = dv[k];
+        }
       }
     }
-    float o[4];
-    fold8(ts, o);
-    fold_chunk(c, o, ls, hs, os);
-    fold8(tc, o);
-    fold_chunk(c, o, lc, hc, oc);
+    lds_barrier();
+    if (s == 0) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        mu[i] = stat[i][0];
+        rs[i] = stat[i][1];
+      }
+    }
+    const int k = s * VS + vk;
+    const int c = k * 512 + 2 * pr;
+    if (k < NV && (FULL || c < a.cols)) {
+      float s0[R], s1[R], c0[R], c1[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        if (i < nrow) {
+          const uint32_t xw = tile[buf][i][0][vk * 256 + pr];
+          const uint32_t dw = tile[buf][i][1][vk * 256 + pr];
+          const float x0 = bf_lo(xw), x1 = bf_hi(xw), d0 = bf_lo(dw), d1 = bf_hi(dw);
+          s0[i] = d0;
+          s1[i] = d1;
+          c0[i] = d0 * (rs[i] * (x0 - mu[i]));
+          c1[i] = d1 * (rs[i] * (x1 - mu[i]));
+        } else {  // the tree's padding
+          s0[i] = s1[i] = c0[i] = c1[i] = 0.0f;
+        }
+      }
+      float2 hs = make_float2(tree_fold<R>(s0), tree_fold<R>(s1));
+      float2 hc = make_float2(tree_fold<R>(c0), tree_fold<R>(c1));
+      if (final_level) {  // the rest of the 32-token group is +0
+        hs.x += 0.0f;
+        hs.y += 0.0f;
+        hc.x += 0.0f;
+        hc.y += 0.0f;
+      }
+      const int64_t o = (int64_t)blockIdx.x * a.cols + c;
+      *reinterpret_cast<float2 *>(out_shift + o) = hs;
+      *reinterpret_cast<float2 *>(out_scale + o) = hc;
+    }
   }
-  if (!live) return;
-  const int64_t o = bg * a.cols + q * 4;
-  *reinterpret_cast<float4 *>(out_shift + o) = make_float4(os[0], os[1], os[2], os[3]);
-  *reinterpret_cast<float4 *>(out_scale + o) = make_float4(oc[0], oc[1], oc[2], oc[3]);
 }
 
 // ---------------------------------------------------------------------------
-// kernel C: one further tree level.  in: [B * n_in, cols] (both sums), out:
-// [B * n_out, cols], n_out = ceil(n_in / 32).  A lane folds one column (the
-// data is small and latency-bound: more lanes, more loads in flight);
-// grid.x: batch * n_out, grid.y: column blocks of 64.
+// tree levels.  in: [B * n_in, cols] per sum, out: [B * n_out, cols],
+// n_out = ceil(n_in / L), L = CH * T.  Wavefront p folds values
+// [o L + p CH, o L + (p + 1) CH) of 64 columns (+0 past n_in); wavefront 0
+// folds the T chunk sums.  grid.x: batch * n_out, grid.y: column blocks of 64.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void bwd_tree_kernel(const float *in_shift, const float *in_scale,
-                                                      float *out_shift, float *out_scale,
-                                                      int64_t n_in, int64_t n_out, int32_t cols) {
-  const int cidx = blockIdx.y * 64 + threadIdx.x;  // column
+template <int CH, int T>
+__global__ __launch_bounds__(64 * T) void bwd_tree_kernel(const float *in_shift,
+                                                          const float *in_scale, float *out_shift,
+                                                          float *out_scale, int64_t n_in,
+                                                          int64_t n_out, int32_t cols) {
+  const int lane = threadIdx.x & 63;
+  const int p = T == 1 ? 0 : wave_id();
+  const int cidx = blockIdx.y * 64 + lane;  // column
   const int64_t bo = blockIdx.x;
   const int64_t b = bo / n_out, go = bo - b * n_out;
-  const int64_t first = go * 32;
-  const int64_t left_vals = n_in - first;
-  const int n = (int)(left_vals < 32 ? left_vals : 32);
+  const int64_t first = go * (CH * T) + p * CH;
   const bool live = cidx < cols;
   const int cc = live ? cidx : cols - 1;  // clamped: every load is valid
 
-  float ls[1], hs[1], os[1], lc[1], hc[1], oc[1];
-#pragma unroll 1
-  for (int c = 0; c < 4; ++c) {
-    if (c * 8 >= n) {  // a chunk wholly past the last value folds to +0
-      float z[1] = {0.0f};
-      fold_chunk(c, z, ls, hs, os);
-      fold_chunk(c, z, lc, hc, oc);
-      continue;
-    }
-    float ts[8][1], tc[8][1];
+  float vs[CH], vc[CH];
+  if (first < n_in) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int s = c * 8 + i;
-      const int64_t off = (b * n_in + first + (s < n ? s : n - 1)) * cols + cc;
-      const float vs = in_shift[off], vc = in_scale[off];
-      const bool in = s < n;  // +0 padding past the last value
-      ts[i][0] = in ? vs : 0.0f;
-      tc[i][0] = in ? vc : 0.0f;
+    for (int i = 0; i < CH; ++i) {
+      const int64_t s = first + i;
+      const int64_t off = (b * n_in + (s < n_in ? s : n_in - 1)) * cols + cc;
+      const float ls = in_shift[off], lc = in_scale[off];
+      vs[i] = s < n_in ? ls : 0.0f;  // +0 padding past the last value
+      vc[i] = s < n_in ? lc : 0.0f;
     }
-    float o[1];
-    fold8(ts, o);
-    fold_chunk(c, o, ls, hs, os);
-    fold8(tc, o);
-    fold_chunk(c, o, lc, hc, oc);
+  } else {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) vs[i] = vc[i] = 0.0f;
+  }
+  float hs = tree_fold<CH>(vs), hc = tree_fold<CH>(vc);
+  if constexpr (T > 1) {
+    __shared__ float red[T][2][64];
+    red[p][0][lane] = hs;
+    red[p][1][lane] = hc;
+    lds_barrier();
+    if (p != 0) return;
+    float ts[T], tc[T];
+#pragma unroll
+    for (int q = 0; q < T; ++q) {
+      ts[q] = red[q][0][lane];
+      tc[q] = red[q][1][lane];
+    }
+    hs = tree_fold<T>(ts);
+    hc = tree_fold<T>(tc);
   }
   if (!live) return;
-  out_shift[bo * cols + cidx] = os[0];
-  out_scale[bo * cols + cidx] = oc[0];
+  out_shift[bo * cols + cidx] = hs;
+  out_scale[bo * cols + cidx] = hc;
 }
 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 
+// Leaves per value of the first tree level after the fused kernel: the rest
+// of a 32-token group (32 / R chunk sums), and with more than one group per
+// batch, the 32 groups of the next level too.
+static int64_t first_fanin(int64_t rows_per_batch, int rows_per_chunk) {
+  const int64_t per_group = 32 / rows_per_chunk;
+  return rows_per_batch <= 32 ? per_group : 32 * per_group;
+}
+
 BwdLayout bwd_layout(int64_t rows, int64_t cols, int64_t rows_per_batch) {
   BwdLayout L{};
   const int64_t nb = rows / rows_per_batch;
-  const int64_t g = (rows_per_batch + 31) / 32;
-  const int64_t g1 = (g + 31) / 32;
   auto up = [](int64_t v) { return (v + 255) / 256 * 256; };
-  L.groups = g;
-  L.mean_off = 0;
-  L.rstd_off = up(rows * 4);
-  L.part0_off = L.rstd_off + up(rows * 4);
-  L.part0_floats = nb * g * cols;                        // per sum
-  L.part1_off = L.part0_off + up(2 * L.part0_floats * 4);
-  L.part1_floats = g > 1 ? nb * g1 * cols : 0;
+  // 8 tokens per workgroup; 4 for short batches, and for rows over 3072
+  // columns, whose register footprint leaves room for one 8-wavefront
+  // workgroup per compute unit but three of 4
+  L.rows_per_chunk = (rows_per_batch <= 4 || cols > 3072) ? 4 : 8;
+  L.chunks = (rows_per_batch + L.rows_per_chunk - 1) / L.rows_per_chunk;
+  int64_t n1 = 1;
+  if (L.chunks > 1) {
+    const int64_t f = first_fanin(rows_per_batch, L.rows_per_chunk);
+    n1 = (L.chunks + f - 1) / f;
+  }
+  L.part0_off = 0;
+  L.part0_floats = L.chunks > 1 ? nb * L.chunks * cols : 0;  // per sum
+  L.part1_off = up(2 * L.part0_floats * 4);
+  L.part1_floats = n1 > 1 ? nb * n1 * cols : 0;
   L.bytes = L.part1_off + up(2 * L.part1_floats * 4);
   return L;
 }
 
-template <int NV, bool FULL>
-static void launch_bwd_row(const BwdArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_row_kernel<NV, FULL>), dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0,
-                     stream, a);
+template <int NV, bool FULL, int R>
+static void launch_fused(const BwdArgs &a, int64_t nb, int64_t chunks, float *os, float *oc,
+                         hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_fused_kernel<NV, FULL, R>), dim3((unsigned)(nb * chunks)), dim3(64 * R),
+                     0, stream, a, chunks, os, oc, chunks == 1 ? 1 : 0);
 }
 
-hipError_t launch_backward(const BwdArgs &a, float *part0, float *part1, int64_t groups,
+template <int R>
+static void launch_fused_r(const BwdArgs &a, int64_t nb, int64_t chunks, float *os, float *oc,
                            hipStream_t stream) {
-  const int nvec = a.cols >> 3;
-  switch (nvec) {
-    case 128: launch_bwd_row<2, true>(a, stream); break;
-    case 256: launch_bwd_row<4, true>(a, stream); break;
-    case 384: launch_bwd_row<6, true>(a, stream); break;
-    case 512: launch_bwd_row<8, true>(a, stream); break;
-    default:
-      if (nvec <= 64) launch_bwd_row<1, false>(a, stream);
-      else if (nvec <= 128) launch_bwd_row<2, false>(a, stream);
-      else if (nvec <= 256) launch_bwd_row<4, false>(a, stream);
-      else if (nvec <= 384) launch_bwd_row<6, false>(a, stream);
-      else launch_bwd_row<8, false>(a, stream);
+  switch (a.cols >> 3) {
+    case 128: launch_fused<2, true, R>(a, nb, chunks, os, oc, stream); return;
+    case 256: launch_fused<4, true, R>(a, nb, chunks, os, oc, stream); return;
+    case 384: launch_fused<6, true, R>(a, nb, chunks, os, oc, stream); return;
+    case 512: launch_fused<8, true, R>(a, nb, chunks, os, oc, stream); return;
+    default: break;
   }
+  const int nvec = a.cols >> 3;
+  if (nvec <= 64) launch_fused<1, false, R>(a, nb, chunks, os, oc, stream);
+  else if (nvec <= 128) launch_fused<2, false, R>(a, nb, chunks, os, oc, stream);
+  else if (nvec <= 256) launch_fused<4, false, R>(a, nb, chunks, os, oc, stream);
+  else if (nvec <= 384) launch_fused<6, false, R>(a, nb, chunks, os, oc, stream);
+  else launch_fused<8, false, R>(a, nb, chunks, os, oc, stream);
+}
+
+hipError_t launch_backward(const BwdArgs &a, const BwdLayout &L, float *part0, float *part1,
+                           hipStream_t stream) {
+  const int64_t nb = a.rows / a.rows_per_batch;
+  const int64_t pf = L.part0_floats;
+  float *s_out = L.chunks == 1 ? a.d_shift : part0;
+  float *c_out = L.chunks == 1 ? a.d_scale : part0 + pf;
+  if (nb * L.chunks * 64 * L.rows_per_chunk > (int64_t)INT32_MAX) return hipErrorInvalidConfiguration;
+  if (L.rows_per_chunk == 4) launch_fused_r<4>(a, nb, L.chunks, s_out, c_out, stream);
+  else launch_fused_r<8>(a, nb, L.chunks, s_out, c_out, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int64_t nb = a.rows / a.rows_per_batch;
-  const int64_t pf = nb * groups * a.cols;  // floats per sum in part0
-  float *s_out = groups == 1 ? a.d_shift : part0;
-  float *c_out = groups == 1 ? a.d_scale : part0 + pf;
-  const int quads = a.cols / 4;
-  hipLaunchKernelGGL(bwd_token_kernel, dim3((unsigned)(nb * groups), (unsigned)((quads + 63) / 64)),
-                     dim3(64), 0, stream, a, groups, s_out, c_out);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  int64_t n = L.chunks, f = first_fanin(a.rows_per_batch, L.rows_per_chunk);
 
-  // further levels, ping-ponging between the two partial regions
-  int64_t n = groups;
+  // tree levels, ping-ponging between the two partial regions
   float *src = part0, *dst = part1;
   int64_t src_f = pf;
+  const unsigned cblocks = (unsigned)((a.cols + 63) / 64);
   while (n > 1) {
-    const int64_t n_out = (n + 31) / 32;
+    const int64_t n_out = (n + f - 1) / f;
     const int64_t dst_f = nb * n_out * a.cols;
     float *os = n_out == 1 ? a.d_shift : dst;
     float *oc = n_out == 1 ? a.d_scale : dst + dst_f;
-    hipLaunchKernelGGL(bwd_tree_kernel, dim3((unsigned)(nb * n_out), (unsigned)((a.cols + 63) / 64)),
-                       dim3(64), 0, stream, src, src + src_f, os, oc, n, n_out, a.cols);
+    const dim3 grid((unsigned)(nb * n_out), cblocks);
+    const float *is = src, *ic = src + src_f;
+    switch (f) {
+      case 4:
+        hipLaunchKernelGGL((bwd_tree_kernel<4, 1>), grid, dim3(64), 0, stream, is, ic, os, oc, n,
+                           n_out, a.cols);
+        break;
+      case 8:
+        hipLaunchKernelGGL((bwd_tree_kernel<8, 1>), grid, dim3(64), 0, stream, is, ic, os, oc, n,
+                           n_out, a.cols);
+        break;
+      case 32:
+        hipLaunchKernelGGL((bwd_tree_kernel<8, 4>), grid, dim3(256), 0, stream, is, ic, os, oc, n,
+                           n_out, a.cols);
+        break;
+      case 128:
+        hipLaunchKernelGGL((bwd_tree_kernel<8, 16>), grid, dim3(1024), 0, stream, is, ic, os, oc,
+                           n, n_out, a.cols);
+        break;
+      default:  // 256
+        hipLaunchKernelGGL((bwd_tree_kernel<16, 16>), grid, dim3(1024), 0, stream, is, ic, os, oc,
+                           n, n_out, a.cols);
+        break;
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     n = n_out;
+    f = 32;
     float *t = src;
     src = dst;
     dst = t;

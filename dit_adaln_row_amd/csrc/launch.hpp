@@ -102,8 +102,6 @@ struct BwdArgs {
   uint16_t *d_x;          // [rows, cols]
   float *d_scale;         // [B, cols]
   float *d_shift;         // [B, cols]
-  float *ws_mean;         // workspace [rows]
-  float *ws_rstd;         // workspace [rows]
   float *mean_out;        // optional [rows]
   float *rstd_out;        // optional [rows]
   int64_t rows;
@@ -112,16 +110,18 @@ struct BwdArgs {
   int32_t cols;
   float eps;
 };
-// Workspace layout (byte offsets; every region 256-byte aligned).
+// Workspace layout (byte offsets; every region 256-byte aligned): the
+// partial tree sums.  None when a batch has at most rows_per_chunk tokens.
 struct BwdLayout {
-  int64_t groups;        // first-level token groups per batch, ceil(rows_per_batch / 32)
-  int64_t mean_off, rstd_off;
-  int64_t part0_off, part0_floats;  // per sum: B * groups * cols
-  int64_t part1_off, part1_floats;  // per sum: B * ceil(groups / 32) * cols (0 if groups == 1)
+  int rows_per_chunk;               // tokens per workgroup of the fused kernel (4 or 8)
+  int64_t chunks;                   // per batch: ceil(rows_per_batch / rows_per_chunk)
+  int64_t part0_off, part0_floats;  // per sum: B * chunks * cols (0 if chunks == 1)
+  int64_t part1_off, part1_floats;  // per sum: B * (first tree level's count) * cols,
+                                    // 0 if that level is the last
   int64_t bytes;
 };
 BwdLayout bwd_layout(int64_t rows, int64_t cols, int64_t rows_per_batch);
-hipError_t launch_backward(const BwdArgs &a, float *part0, float *part1, int64_t groups,
+hipError_t launch_backward(const BwdArgs &a, const BwdLayout &L, float *part0, float *part1,
                            hipStream_t stream);
 
 // Plain 16-byte copy (measurement utility).

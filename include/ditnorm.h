@@ -286,8 +286,10 @@ int residual_gate_add(const void *update, const void *residual, const void *gate
  * workspace: device memory of at least
  * ln_modulate_backward_workspace_bytes(rows, cols, rows_per_batch) bytes,
  * 256-byte aligned, owned by the caller, clobbered by the call (it holds the
- * per-row statistics and the partial tree sums).  mean_out, rstd_out (fp32
- * [rows]) optional.  The work is three to five kernel launches on `stream`.
+ * partial tree sums); when that size is 0 (batches of at most 8 tokens, 4
+ * for rows over 3072 columns) workspace may be NULL.  mean_out, rstd_out
+ * (fp32 [rows]) optional.  The work is one kernel launch on `stream` when the
+ * workspace size is 0, else two to four.
  */
 int ln_modulate_backward(const void *x, const void *scale, const void *d_out, void *d_x,
                          float *d_scale, float *d_shift, int64_t rows, int64_t cols,

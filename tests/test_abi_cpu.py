@@ -145,9 +145,14 @@ def test_other_entry_validation(lib):
     assert lib.residual_gate_add(A, None, C, D, 8, 3072, 8, 3072, 0, None) == dn.INVALID_ARGUMENT
     assert lib.residual_gate_add(A, B, C, D, 8, 16392, 8, 16392, 0, None) == dn.UNSUPPORTED
     # backward: workspace size, validation before any HIP call
+    # the partial sums of 862 runs of 8 tokens, then of 7 values of the second level
     ws = dn.ln_modulate_backward_workspace_bytes(6889, 3072, 6889)
-    assert ws >= 2 * 6889 * 4 + 2 * 216 * 3072 * 4 + 2 * 7 * 3072 * 4
+    assert ws >= 2 * 862 * 3072 * 4 + 2 * 7 * 3072 * 4
     assert dn.ln_modulate_backward_workspace_bytes(0, 3072, 1) == 0
+    # a batch of at most 8 tokens (4 over 3072 columns) is summed in one workgroup
+    assert dn.ln_modulate_backward_workspace_bytes(2048 * 3, 3072, 3) == 0
+    assert dn.ln_modulate_backward_workspace_bytes(4 * 8, 3072, 8) == 0
+    assert dn.ln_modulate_backward_workspace_bytes(4 * 8, 4096, 8) > 0
     assert lib.ln_modulate_backward_workspace_bytes(10, 3072, 3) == -1
     W = 0xA0000000
     bw = lambda **k: lib.ln_modulate_backward(
