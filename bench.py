@@ -213,45 +213,186 @@ def traffic_for(workload, launch):
 # CPU baseline: the oracle on this host's cores
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(w, min_seconds=10.0):
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_call(oracle, l, t, lo, hi):
+    """The oracle on rows [lo, hi) of launch l (whole batches for the backward)."""
+    e = l.entry
+    x = t[l.inputs[0]]
+    if e == "ln_modulate":
+        return oracle.ln_modulate(x[lo:hi], t["scale"], t["shift"], l.eps)
+    if e == "ln_modulate_folded":
+        return oracle.ln_modulate_folded(x[lo:hi], t["scale"], t["shift"], l.eps)
+    if e == "gated_ln_modulate":
+        return oracle.gated_ln_modulate(x[lo:hi], t["residual"][lo:hi], t["gate"], t["scale"],
+                                        t["shift"], l.eps)
+    if e == "rms_modulate":
+        if l.extra.get("gated"):
+            return oracle.rms_modulate(x[lo:hi], t["weight"], t["scale"], t["shift"], l.eps,
+                                       residual=t["residual"][lo:hi], gate=t["gate"])
+        return oracle.rms_modulate(x[lo:hi], t["weight"], t["scale"], t["shift"], l.eps)
+    if e == "qk_layernorm":  # rows are q rows then k rows: half of the slice from each
+        return oracle.qk_layernorm(t["q"][lo // 2:hi // 2], t["k"][lo // 2:hi // 2], l.eps)
+    if e == "rmsnorm_silu_bias":
+        return oracle.rmsnorm_silu_bias(x[lo:hi], t["bias"], t["gamma"], l.eps)
+    if e == "conv_bias_epilogue":
+        return oracle.conv_bias_epilogue(x[lo:hi], t["bias"], t["h"][lo:hi])
+    if e == "modulate_scale_shift":
+        return oracle.modulate_dt(x[lo:hi], t[l.inputs[1]], t[l.inputs[2]], l.extra["dtype"])
+    if e == "residual_gate_add":
+        return oracle.gate_residual_dt(x[lo:hi], t[l.inputs[1]][lo:hi], t[l.inputs[2]],
+                                       l.extra["dtype"])
+    if e == "ln_modulate_backward":
+        rpb = l.extra["rows_per_batch"]
+        if hi - lo <= rpb:  # part of one batch: a batch of that many tokens
+            return oracle.ln_modulate_backward(x[lo:hi], t["scale"][:1], t["d_out"][lo:hi], l.eps,
+                                               rows_per_batch=hi - lo)
+        return oracle.ln_modulate_backward(x[lo:hi], t["scale"][lo // rpb:hi // rpb],
+                                           t["d_out"][lo:hi], l.eps, rows_per_batch=rpb)
+    raise KeyError(e)
+
+
+def _keep_freed_memory():
+    """glibc: serve large allocations from the heap and keep freed memory, so
+    that the oracle's fresh output arrays do not page-fault on every call and
+    the CPU timings measure its arithmetic."""
+    try:
+        libc = ctypes.CDLL("libc.so.6")
+        libc.mallopt(-1, 1 << 30)  # M_TRIM_THRESHOLD
+        libc.mallopt(-3, 1 << 30)  # M_MMAP_THRESHOLD
+    except (OSError, AttributeError):
+        pass
+
+
+def _host_tensors(w, cap=None):
+    """Host copies of a workload's inputs; with cap, 2-D tensors hold only
+    their first cap rows (same distributions and seeds; a timing sample)."""
+    if cap is None:
+        return {k: (gen.to_u16(v) if v.dtype in (torch.bfloat16, torch.float16) else v.numpy())
+                for k, v in gen.make(w).items()}
+    out = {}
+    for tt in w.tensors:
+        shape = tt.shape if len(tt.shape) < 2 else (min(tt.shape[0], cap),) + tuple(tt.shape[1:])
+        v = gen.normal(shape, tt.mu, tt.sigma, w.seed(tt.name), tt.kind)
+        out[tt.name] = gen.to_u16(v) if v.dtype in (torch.bfloat16, torch.float16) else v.numpy()
+    return out
+
+
+def cpu_baseline(w, min_seconds=10.0, single_seconds=3.0):
+    """The oracle on the host's cores: the whole headline step, rows split
+    over threads, repeated for about min_seconds; and single-threaded on a
+    row sample for about single_seconds."""
     import concurrent.futures as cf
 
     import oracle
     oracle.build()
+    _keep_freed_memory()
     threads = max(1, min(16, os.cpu_count() or 1))
-    t = {k: (gen.to_u16(v) if v.dtype == torch.bfloat16 else v.numpy())
-         for k, v in gen.make(w).items()}
+    t = _host_tensors(w)
 
     def chunks(rows):
         step = -(-rows // (threads * 4))
         return [(lo, min(rows, lo + step)) for lo in range(0, rows, step)]
-
-    def run_launch(l, ex):
-        if l.entry == "ln_modulate":
-            f = lambda b: oracle.ln_modulate(t["x"][b[0]:b[1]], t["scale"], t["shift"], l.eps)
-        elif l.entry == "gated_ln_modulate":
-            f = lambda b: oracle.gated_ln_modulate(t["update"][b[0]:b[1]], t["residual"][b[0]:b[1]],
-                                                   t["gate"], t["scale"], t["shift"], l.eps)
-        else:
-            raise KeyError(l.entry)
-        list(ex.map(f, chunks(l.rows)))
 
     reps = 0
     with cf.ThreadPoolExecutor(threads) as ex:
         t0 = time.perf_counter()
         while True:
             for l in w.launches:
-                run_launch(l, ex)
+                list(ex.map(lambda b, l=l: _oracle_call(oracle, l, t, b[0], b[1]),
+                            chunks(l.rows)))
             reps += 1
             el = time.perf_counter() - t0
             if el >= min_seconds or reps >= 5000:
                 break
     gbps = w.algorithmic_bytes() * reps / el / 1e9
+    # single thread: every launch on its first 1/8 of the rows
+    n1, el1, b1, r1 = 0, 0.0, 0, 0
+    t0 = time.perf_counter()
+    while el1 < single_seconds and n1 < 5000:
+        for l in w.launches:
+            n = max(1, l.rows // 8)
+            _oracle_call(oracle, l, t, 0, n)
+            b1 += l.algorithmic_bytes() * n / l.rows
+            r1 += n
+        n1 += 1
+        el1 = time.perf_counter() - t0
     return {"value": round(gbps, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"the full {w.key} step ({' + '.join(l.name for l in w.launches)}, "
                       f"{w.rows()} rows) x {reps} repetitions, {el:.1f} s wall, rows split over "
                       f"{threads} threads; the oracle is single-threaded C, unchanged",
-            "rows_per_s": round(w.rows() * reps / el, 1)}
+            "rows_per_s": round(w.rows() * reps / el, 1),
+            "single_thread": {"value": round(b1 / el1 / 1e9, 3), "unit": "GB/s",
+                              "rows_per_s": round(r1 / el1, 1),
+                              "sample": f"the first 1/8 of each launch's rows x {n1}, "
+                                        f"{el1:.1f} s"},
+            "cpu_model": _cpu_model()}
+
+
+def cpu_oracle_table(seconds=0.5, skip=()):
+    """The oracle beside every workload's launches: GB/s-equivalent (the
+    launch's algorithmic bytes per row) on a row sample, single-threaded and
+    over the host's threads, each timed for about `seconds`."""
+    import concurrent.futures as cf
+
+    import oracle
+    oracle.build()
+    _keep_freed_memory()
+    threads = max(1, min(16, os.cpu_count() or 1))
+    table = {}
+    with cf.ThreadPoolExecutor(threads) as ex:
+        for key, w in WORKLOADS.items():
+            if key in skip:
+                continue
+            log(f"[bench] oracle: {key}")
+
+            def sample_rows(l):
+                rpb = l.extra.get("rows_per_batch", 1)
+                n = max(1, l.rows // 16)
+                if 1 < rpb <= n:  # whole batches (else one batch's first n tokens)
+                    n -= n % rpb
+                return n
+
+            t = _host_tensors(w, cap=max(sample_rows(l) for l in w.launches))
+            for l in w.launches:
+                rpb = l.extra.get("rows_per_batch", 1)
+                n = sample_rows(l)
+                per_row = l.algorithmic_bytes() / l.rows
+                row = {}
+                for mode in ("single", "threads"):
+                    if mode == "single":
+                        parts = [(0, n)]
+                    elif rpb > 1 and n <= rpb:  # one batch: not split
+                        continue
+                    else:
+                        step = -(-n // threads)
+                        if rpb > 1:
+                            step = -(-step // rpb) * rpb
+                        parts = [(lo, min(n, lo + step)) for lo in range(0, n, step)]
+                    run = lambda l=l, parts=parts: list(
+                        ex.map(lambda b: _oracle_call(oracle, l, t, b[0], b[1]), parts))
+                    run()  # untimed: first-touch of the outputs
+                    reps, t0 = 0, time.perf_counter()
+                    while True:
+                        run()
+                        reps += 1
+                        el = time.perf_counter() - t0
+                        if el >= seconds:
+                            break
+                    row[mode] = {"gbps": round(per_row * n * reps / el / 1e9, 3),
+                                 "rows_per_s": round(n * reps / el, 1)}
+                row["sample_rows"] = n
+                table[f"{key}/{l.name}"] = row
+            del t
+    return {"threads": threads, "cpu_model": _cpu_model(), "launches": table}
 
 
 # ---------------------------------------------------------------------------
@@ -351,6 +492,7 @@ def main():
     if not args.no_cpu and args.only is None:
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_oracle"] = cpu_oracle_table()
     print(json.dumps(result), flush=True)
 
 
