@@ -109,7 +109,8 @@ int check_rows(int64_t rows, int64_t cols, int64_t rows_per_batch, int64_t mod_b
   if (rows < 0 || cols <= 0 || rows_per_batch <= 0 || mod_batch_stride < cols || !eps_ok(eps))
     return DITNORM_INVALID_ARGUMENT;
   if (rows % rows_per_batch != 0) return DITNORM_INVALID_ARGUMENT;
-  if (cols % 8 != 0 || cols > DITNORM_MAX_COLS) return DITNORM_UNSUPPORTED;
+  if (cols % 8 != 0 || cols > DITNORM_MAX_COLS || rows > DITNORM_MAX_ROWS)
+    return DITNORM_UNSUPPORTED;
   const int64_t nb = rows / rows_per_batch;
   if (nb > 1 && mod_batch_stride % 8 != 0) return DITNORM_UNSUPPORTED;
   return DITNORM_OK;
@@ -182,7 +183,7 @@ int validate_qk(const void *q, const void *k, const void *q_out, const void *k_o
                 int64_t rows_q, int64_t rows_k, int64_t head_dim, float eps,
                 const float *mean_out, const float *rstd_out) {
   if (rows_q < 0 || rows_k < 0 || head_dim <= 0 || !eps_ok(eps)) return DITNORM_INVALID_ARGUMENT;
-  if (head_dim != 128) return DITNORM_UNSUPPORTED;
+  if (head_dim != 128 || rows_q + rows_k > DITNORM_MAX_ROWS) return DITNORM_UNSUPPORTED;
   if (rows_q + rows_k == 0) return DITNORM_OK;
   if (rows_q > 0 && (!q || !q_out)) return DITNORM_INVALID_ARGUMENT;
   if (rows_k > 0 && (!k || !k_out)) return DITNORM_INVALID_ARGUMENT;
@@ -201,7 +202,8 @@ int validate_wan(const void *x, const float *bias, const float *gamma, const voi
                  int64_t rows, int64_t channels, float eps, const float *rstd_out,
                  const void *xb_out) {
   if (rows < 0 || channels <= 0 || !eps_ok(eps)) return DITNORM_INVALID_ARGUMENT;
-  if (channels % 8 != 0 || channels > DITNORM_MAX_CHANNELS) return DITNORM_UNSUPPORTED;
+  if (channels % 8 != 0 || channels > DITNORM_MAX_CHANNELS || rows > DITNORM_MAX_ROWS)
+    return DITNORM_UNSUPPORTED;
   if (rows == 0) return DITNORM_OK;
   if (!x || !gamma || !out) return DITNORM_INVALID_ARGUMENT;
   if (!aligned16(x) || !aligned16(bias) || !aligned16(gamma) || !aligned16(out) ||
@@ -217,7 +219,9 @@ int validate_wan(const void *x, const float *bias, const float *gamma, const voi
 int validate_epilogue(const void *x, const float *bias, const void *h, const void *out,
                       int64_t rows, int64_t channels) {
   if (rows < 0 || channels <= 0) return DITNORM_INVALID_ARGUMENT;
-  if (channels % 8 != 0 || channels > DITNORM_MAX_CHANNELS) return DITNORM_UNSUPPORTED;
+  if (channels % 8 != 0 || channels > DITNORM_MAX_CHANNELS || rows > DITNORM_MAX_ROWS ||
+      rows * (channels / 8) > DITNORM_MAX_VECTORS)
+    return DITNORM_UNSUPPORTED;
   if (rows == 0) return DITNORM_OK;
   if (!x || !bias || !out) return DITNORM_INVALID_ARGUMENT;
   if (!aligned16(x) || !aligned16(bias) || !aligned16(h) || !aligned16(out))
@@ -237,7 +241,10 @@ int validate_backward(const void *x, const void *scale, const void *d_out, const
   if (st != DITNORM_OK || rows == 0) return st;
   if (cols > DITNORM_MAX_BACKWARD_COLS) return DITNORM_UNSUPPORTED;
   if (!x || !scale || !d_out || !d_x || !d_scale || !d_shift) return DITNORM_INVALID_ARGUMENT;
-  const int64_t need = bwd_layout(rows, cols, rpb).bytes;
+  const BwdLayout L = bwd_layout(rows, cols, rpb);
+  // one wavefront per row slot of the fused kernel's workgroups
+  if ((rows / rpb) * L.chunks * L.rows_per_chunk > DITNORM_MAX_ROWS) return DITNORM_UNSUPPORTED;
+  const int64_t need = L.bytes;
   if (need > 0 && (!ws || ws_bytes < need)) return DITNORM_INVALID_ARGUMENT;
   if (!aligned16(x) || !aligned16(scale) || !aligned16(d_out) || !aligned16(d_x) ||
       !aligned16(d_scale) || !aligned16(d_shift) || ((uintptr_t)ws & 255u) != 0 ||
@@ -257,6 +264,7 @@ int validate_elementwise(int op, const void *a, const void *b, const void *m0, c
   if (dtype != DITNORM_DTYPE_BF16 && dtype != DITNORM_DTYPE_F16) return DITNORM_INVALID_ARGUMENT;
   int st = check_rows(rows, cols, rpb, mbs, 0.0f);
   if (st != DITNORM_OK || rows == 0) return st;
+  if (rows * (cols / 8) > DITNORM_MAX_VECTORS) return DITNORM_UNSUPPORTED;
   if (!a || !m0 || !out || (op == 0 && !m1) || (op == 1 && !b)) return DITNORM_INVALID_ARGUMENT;
   if (!aligned16(a) || !aligned16(b) || !aligned16(m0) || !aligned16(m1) || !aligned16(out))
     return DITNORM_UNSUPPORTED;

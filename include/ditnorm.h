@@ -30,9 +30,12 @@
  *       or an optional group is given half-way (see each entry point).
  *   DITNORM_UNSUPPORTED (2): the arguments are valid but outside what the
  *       kernels implement: cols not a multiple of 8 or above the stated
- *       maximum, head_dim other than 128, a pointer not 16-byte aligned, a
- *       modulation row stride that breaks 16-byte alignment, or an output that
- *       overlaps an input other than in the exact in-place forms allowed.
+ *       maximum, more than DITNORM_MAX_ROWS rows (rows_q + rows_k for
+ *       qk_layernorm), more than DITNORM_MAX_VECTORS 16-byte vectors in an
+ *       activation of the elementwise entry points, head_dim other than 128,
+ *       a pointer not 16-byte aligned, a modulation row stride that breaks
+ *       16-byte alignment, or an output that overlaps an input other than in
+ *       the exact in-place forms allowed.
  *   DITNORM_DEVICE_ERROR (3): the current device is not gfx950, or a HIP call
  *       or kernel launch failed (ditnorm_last_hip_error() keeps the code).
  *   All argument checks run on the host before any HIP call; a call that
@@ -83,6 +86,12 @@ extern "C" {
 #define DITNORM_MAX_CHANNELS 4096
 /* Largest row width of ln_modulate_backward. */
 #define DITNORM_MAX_BACKWARD_COLS 4096
+/* Most rows of one call (a row has up to one 64-lane wavefront, and a launch
+ * at most 2^31 - 1 work-items), and most 16-byte vectors in one activation of
+ * modulate_scale_shift, residual_gate_add and conv_bias_epilogue (one
+ * work-item per vector). */
+#define DITNORM_MAX_ROWS 33554431LL
+#define DITNORM_MAX_VECTORS 2147483647LL
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *ditnorm_status_string(int status);
@@ -281,7 +290,9 @@ int residual_gate_add(const void *update, const void *residual, const void *gate
  * rows and its token count (bitwise batch-invariant).
  * x, d_out, d_x: bf16 [rows, cols]; scale: bf16 [B, cols], row stride
  * mod_batch_stride; d_scale, d_shift: fp32 [B, cols] dense.  cols: multiple
- * of 8, at most DITNORM_MAX_BACKWARD_COLS.  No output may overlap an input or
+ * of 8, at most DITNORM_MAX_BACKWARD_COLS.  B times rows_per_batch rounded up
+ * to a multiple of 4 (of 8 when rows_per_batch > 4 and cols <= 3072) at most
+ * DITNORM_MAX_ROWS.  No output may overlap an input or
  * another output.
  * workspace: device memory of at least
  * ln_modulate_backward_workspace_bytes(rows, cols, rows_per_batch) bytes,

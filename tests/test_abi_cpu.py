@@ -167,6 +167,27 @@ def test_other_entry_validation(lib):
     assert bw(rows=0) == dn.OK
     assert lib.ln_modulate_backward_supported(A, B, C, D, E, E + 0x100000, 64, 3072, 64, 3072,
                                               1e-6, W, 1 << 24, None, None) == 1
+    # size limits: rows (one wavefront per row) and 16-byte vectors per launch
+    MR = 33554431
+    assert lib.ln_modulate(A, B, C, D, MR + 1, 8, MR + 1, 8, 1e-6, None, None, None, None) \
+        == dn.UNSUPPORTED
+    assert lib.ln_modulate_supported(A, B, C, D, MR, 8, MR, 8, 1e-6, None, None, None) == 1
+    assert lib.qk_layernorm(A, B, C, D, MR, 1, 128, 1e-5, None, None, None) == dn.UNSUPPORTED
+    assert lib.rmsnorm_silu_bias(A, E, E + 4096, D, MR + 1, 96, 1e-6, None, None, None) \
+        == dn.UNSUPPORTED
+    # 2^31 - 1 vectors of 512 per row: 4194303 rows fit, 4194304 do not (buffers 64 GB apart)
+    G = 1 << 36
+    for rows, ok in ((4194303, 1), (4194304, 0)):
+        assert lib.conv_bias_epilogue_supported(G, E, None, 2 * G, rows, 4096) == ok
+        assert lib.modulate_scale_shift_supported(G, B, C, 2 * G, rows, 4096, rows, 4096,
+                                                  0) == ok
+    # (fake buffers spaced so that only the size decides: d_scale / d_shift
+    # of 8.4M batches span 268 MB each)
+    bw3 = lambda rows: lib.ln_modulate_backward(A, B, C, D, E, E + 0x20000000, rows, 8, 3, 8,
+                                                1e-6, None, 0, None, None, None)
+    assert bw3(3 * (MR // 4) + 3) == dn.UNSUPPORTED    # 3-token batches take 4 row slots each
+    assert lib.ln_modulate_backward_supported(A, B, C, D, E, E + 0x20000000, 3 * (MR // 4), 8,
+                                              3, 8, 1e-6, None, 0, None, None) == 1
     assert lib.ditnorm_copy(A, B, 15, None) == dn.UNSUPPORTED
     assert lib.ditnorm_copy(A, A + 16, 64, None) == dn.UNSUPPORTED
 
