@@ -267,7 +267,8 @@ struct BoolC {
 
 enum ModMode : int {
   MOD_SERIAL = 0,  // per 16-byte vector, from the caches, as each is needed
-  MOD_LDS = 1,     // s1 / shift (and the RMS weight) staged per workgroup in LDS (fp32);
+  MOD_LDS = 1,     // s1 / shift staged per workgroup in LDS (fp32; for RMS the shift and
+                   // the weight as bf16);
                    // the gate as SERIAL
 };
 
@@ -276,9 +277,9 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
   constexpr int WPB = 4;  // wavefronts (rows) per workgroup
   constexpr int NT = 64 * WPB;
   constexpr bool MODLDS = MODE == MOD_LDS;
-  constexpr bool WLDS = MODLDS && RMS;  // the RMS weight staged too
+  constexpr bool WLDS = MODLDS && RMS;  // the RMS weight staged too (as bf16)
   __shared__ float4 lds_s1[MODLDS ? NV * 128 : 1], lds_sh[MODLDS ? NV * 128 : 1];
-  __shared__ float4 lds_w[WLDS ? NV * 128 : 1];
+  __shared__ uint4 lds_w[WLDS ? NV * 64 : 1];
   const int lane = threadIdx.x & 63;
   const int cols = a.cols;
   const int nvec = cols >> 3;
@@ -335,12 +336,7 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
     lds_s1[mod_slot(j, 1) / 4] = make_float4(sc[4], sc[5], sc[6], sc[7]);
     lds_sh[mod_slot(j, 0) / 4] = make_float4(sh[0], sh[1], sh[2], sh[3]);
     lds_sh[mod_slot(j, 1) / 4] = make_float4(sh[4], sh[5], sh[6], sh[7]);
-    if constexpr (WLDS) {
-      float w[8];
-      unpack8(fw[i], w);
-      lds_w[mod_slot(j, 0) / 4] = make_float4(w[0], w[1], w[2], w[3]);
-      lds_w[mod_slot(j, 1) / 4] = make_float4(w[4], w[5], w[6], w[7]);
-    }
+    if constexpr (WLDS) lds_w[j] = fw[i];
   }
   if constexpr (MODLDS) lds_barrier();
   if (!live) return;  // whole wavefront; no barrier follows
@@ -434,10 +430,7 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
       if constexpr (RMS) {
         float w[8];
         if constexpr (WLDS) {
-          const int j = lane + 64 * k;
-          const float4 w0 = lds_w[mod_slot(j, 0) / 4], w1 = lds_w[mod_slot(j, 1) / 4];
-          w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
-          w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+          unpack8(lds_w[lane + 64 * k], w);
         } else {
           unpack8(ld16(a.weight + col(k)), w);
         }
@@ -488,8 +481,8 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
 // wavefront-per-row kernel's MOD_LDS path (rows of NV * 512 columns).
 template <int NVW, int NV, bool RMS, bool GATED, bool FOLD>
 __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, float4 *lds_sh,
-                                            float4 *lds_w, double (*red)[2], int64_t row0,
-                                            int64_t row, int seg) {
+                                            uint4 *lds_sh16, uint4 *lds_w, double (*red)[2],
+                                            int64_t row0, int64_t row, int seg) {
   constexpr bool SPLIT = NVW != NV;
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
@@ -524,9 +517,8 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
   for (int i = 0; i < FILL; ++i) {
     const int j = threadIdx.x + 256 * i;
     if (j >= NV * 64) break;
-    float sc[8], sh[8];
+    float sc[8];
     unpack8(fsc[i], sc);
-    unpack8(fsh[i], sh);
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       sc[e] = 1.0f + sc[e];
@@ -535,13 +527,16 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
     }
     lds_s1[mod_slot(j, 0) / 4] = make_float4(sc[0], sc[1], sc[2], sc[3]);
     lds_s1[mod_slot(j, 1) / 4] = make_float4(sc[4], sc[5], sc[6], sc[7]);
-    lds_sh[mod_slot(j, 0) / 4] = make_float4(sh[0], sh[1], sh[2], sh[3]);
-    lds_sh[mod_slot(j, 1) / 4] = make_float4(sh[4], sh[5], sh[6], sh[7]);
     if constexpr (RMS) {
-      float wt[8];
-      unpack8(fw[i], wt);
-      lds_w[mod_slot(j, 0) / 4] = make_float4(wt[0], wt[1], wt[2], wt[3]);
-      lds_w[mod_slot(j, 1) / 4] = make_float4(wt[4], wt[5], wt[6], wt[7]);
+      // shift and weight as bf16, widened where they are used: with the
+      // weight staged too, fp32 copies would cost a workgroup of occupancy
+      lds_sh16[j] = fsh[i];
+      lds_w[j] = fw[i];
+    } else {
+      float sh[8];
+      unpack8(fsh[i], sh);
+      lds_sh[mod_slot(j, 0) / 4] = make_float4(sh[0], sh[1], sh[2], sh[3]);
+      lds_sh[mod_slot(j, 1) / 4] = make_float4(sh[4], sh[5], sh[6], sh[7]);
     }
   }
   if constexpr (!SPLIT) {
@@ -617,11 +612,15 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
       const int j = vid(k);
       if constexpr (FROM_LDS) {
         const float4 a0 = lds_s1[mod_slot(j, 0) / 4], a1 = lds_s1[mod_slot(j, 1) / 4];
-        const float4 c0 = lds_sh[mod_slot(j, 0) / 4], c1 = lds_sh[mod_slot(j, 1) / 4];
         s1v[0] = a0.x; s1v[1] = a0.y; s1v[2] = a0.z; s1v[3] = a0.w;
         s1v[4] = a1.x; s1v[5] = a1.y; s1v[6] = a1.z; s1v[7] = a1.w;
-        shv[0] = c0.x; shv[1] = c0.y; shv[2] = c0.z; shv[3] = c0.w;
-        shv[4] = c1.x; shv[5] = c1.y; shv[6] = c1.z; shv[7] = c1.w;
+        if constexpr (RMS) {
+          unpack8(lds_sh16[j], shv);
+        } else {
+          const float4 c0 = lds_sh[mod_slot(j, 0) / 4], c1 = lds_sh[mod_slot(j, 1) / 4];
+          shv[0] = c0.x; shv[1] = c0.y; shv[2] = c0.z; shv[3] = c0.w;
+          shv[4] = c1.x; shv[5] = c1.y; shv[6] = c1.z; shv[7] = c1.w;
+        }
       } else {
         unpack8(ld16(a.scale + mo + col(k)), s1v);
         unpack8(ld16(a.shift + mo + col(k)), shv);
@@ -643,8 +642,8 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
         continue;
       }
       if constexpr (RMS) {
-        const float4 w0 = lds_w[mod_slot(j, 0) / 4], w1 = lds_w[mod_slot(j, 1) / 4];
-        const float wt[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        float wt[8];
+        unpack8(lds_w[j], wt);
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = (v[e] * rstd_f) * wt[e];
       } else {
@@ -677,16 +676,17 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
 
 template <int NV, bool RMS, bool GATED, bool FOLD>
 __global__ __launch_bounds__(256) void row_mixed_kernel(const RowArgs a) {
-  __shared__ float4 lds_s1[NV * 128], lds_sh[NV * 128];
-  __shared__ float4 lds_w[RMS ? NV * 128 : 1];
+  __shared__ float4 lds_s1[NV * 128], lds_sh[RMS ? 1 : NV * 128];
+  __shared__ uint4 lds_sh16[RMS ? NV * 64 : 1], lds_w[RMS ? NV * 64 : 1];
   __shared__ double red[4][2];
   const int w = wave_id();
   if ((int64_t)blockIdx.x < a.full_blocks) {
     const int64_t row0 = (int64_t)blockIdx.x * 4;
-    row_segment<NV, NV, RMS, GATED, FOLD>(a, lds_s1, lds_sh, lds_w, red, row0, row0 + w, 0);
+    row_segment<NV, NV, RMS, GATED, FOLD>(a, lds_s1, lds_sh, lds_sh16, lds_w, red, row0, row0 + w,
+                                          0);
   } else {
     const int64_t row0 = a.full_blocks * 4 + ((int64_t)blockIdx.x - a.full_blocks) * 2;
-    row_segment<NV / 2, NV, RMS, GATED, FOLD>(a, lds_s1, lds_sh, lds_w, red, row0,
+    row_segment<NV / 2, NV, RMS, GATED, FOLD>(a, lds_s1, lds_sh, lds_sh16, lds_w, red, row0,
                                                row0 + (w >> 1), w & 1);
   }
 }
