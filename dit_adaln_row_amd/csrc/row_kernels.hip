@@ -248,28 +248,30 @@ __global__ __launch_bounds__(NT) void row_kernel(const RowArgs a) {
 // at the start and the launch streams at the rate HBM delivers.
 //
 // The modulation rows are converted once per workgroup: s1 = bf16(1 + scale)
-// and shift go to LDS as fp32, laid out so that the 64 lanes of a wavefront
-// read 64 consecutive 16-byte words (no bank conflicts).  A row whose batch
-// index differs from the workgroup's first row (batched modulation with a
-// batch boundary inside the workgroup) reads its modulation row directly.
+// goes to LDS as fp32, laid out so that the 64 lanes of a wavefront read 64
+// consecutive 16-byte words (no bank conflicts); the shift likewise (fp32)
+// for LN and as its bf16 bits for RMS, whose weight is staged as bf16 too --
+// 16-byte words, one per lane, again consecutive.  A row whose batch index
+// differs from the workgroup's first row (batched modulation with a batch
+// boundary inside the workgroup) reads its modulation row directly.
 
 // fp32 slot of element half h (0: elements 0-3, 1: 4-7) of vector j.
 __device__ __forceinline__ int mod_slot(int j, int h) {
   return (((j >> 6) * 2 + h) * 64 + (j & 63)) * 4;
 }
 
-// How a row kernel obtains its modulation operands (s1 = bf16(1+scale),
-// shift, and the RMS weight / the gate where used).
+// A compile-time bool as a type: run-time choices dispatched to generic
+// lambdas, so that they are taken once outside the unrolled loops.
 template <bool B>
 struct BoolC {
   static constexpr bool value = B;
 };
 
+// How a row kernel obtains its modulation operands (s1 = bf16(1+scale),
+// shift, the RMS weight; the gate always per vector from the caches).
 enum ModMode : int {
   MOD_SERIAL = 0,  // per 16-byte vector, from the caches, as each is needed
-  MOD_LDS = 1,     // s1 / shift staged per workgroup in LDS (fp32; for RMS the shift and
-                   // the weight as bf16);
-                   // the gate as SERIAL
+  MOD_LDS = 1,     // staged once per workgroup in LDS (see above)
 };
 
 template <int NV, bool FULL, bool RMS, bool GATED, int MODE = MOD_LDS, bool FOLD = false>
@@ -277,9 +279,9 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
   constexpr int WPB = 4;  // wavefronts (rows) per workgroup
   constexpr int NT = 64 * WPB;
   constexpr bool MODLDS = MODE == MOD_LDS;
-  constexpr bool WLDS = MODLDS && RMS;  // the RMS weight staged too (as bf16)
-  __shared__ float4 lds_s1[MODLDS ? NV * 128 : 1], lds_sh[MODLDS ? NV * 128 : 1];
-  __shared__ uint4 lds_w[WLDS ? NV * 64 : 1];
+  constexpr bool WLDS = MODLDS && RMS;  // RMS: the shift and the weight staged as bf16
+  __shared__ float4 lds_s1[MODLDS ? NV * 128 : 1], lds_sh[(MODLDS && !RMS) ? NV * 128 : 1];
+  __shared__ uint4 lds_sh16[WLDS ? NV * 64 : 1], lds_w[WLDS ? NV * 64 : 1];
   const int lane = threadIdx.x & 63;
   const int cols = a.cols;
   const int nvec = cols >> 3;
@@ -318,14 +320,14 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
   }
   const int64_t mo = (row / a.rows_per_batch) * a.mod_stride;
 
-  // stage s1 = bf16(1 + scale) and shift in LDS as fp32
+  // stage s1 = bf16(1 + scale) in LDS as fp32, the shift as fp32 (LN) or as
+  // bf16 with the weight (RMS)
 #pragma unroll
   for (int i = 0; i < FILL; ++i) {
     const int j = threadIdx.x + NT * i;
     if (j >= NV * 64) break;
-    float sc[8], sh[8];
+    float sc[8];
     unpack8(fsc[i], sc);
-    unpack8(fsh[i], sh);
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       sc[e] = 1.0f + sc[e];
@@ -334,9 +336,15 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
     }
     lds_s1[mod_slot(j, 0) / 4] = make_float4(sc[0], sc[1], sc[2], sc[3]);
     lds_s1[mod_slot(j, 1) / 4] = make_float4(sc[4], sc[5], sc[6], sc[7]);
-    lds_sh[mod_slot(j, 0) / 4] = make_float4(sh[0], sh[1], sh[2], sh[3]);
-    lds_sh[mod_slot(j, 1) / 4] = make_float4(sh[4], sh[5], sh[6], sh[7]);
-    if constexpr (WLDS) lds_w[j] = fw[i];
+    if constexpr (WLDS) {
+      lds_sh16[j] = fsh[i];
+      lds_w[j] = fw[i];
+    } else {
+      float sh[8];
+      unpack8(fsh[i], sh);
+      lds_sh[mod_slot(j, 0) / 4] = make_float4(sh[0], sh[1], sh[2], sh[3]);
+      lds_sh[mod_slot(j, 1) / 4] = make_float4(sh[4], sh[5], sh[6], sh[7]);
+    }
   }
   if constexpr (MODLDS) lds_barrier();
   if (!live) return;  // whole wavefront; no barrier follows
@@ -402,11 +410,15 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
       if constexpr (FROM_LDS) {
         const int j = lane + 64 * k;
         const float4 a0 = lds_s1[mod_slot(j, 0) / 4], a1 = lds_s1[mod_slot(j, 1) / 4];
-        const float4 c0 = lds_sh[mod_slot(j, 0) / 4], c1 = lds_sh[mod_slot(j, 1) / 4];
         s1v[0] = a0.x; s1v[1] = a0.y; s1v[2] = a0.z; s1v[3] = a0.w;
         s1v[4] = a1.x; s1v[5] = a1.y; s1v[6] = a1.z; s1v[7] = a1.w;
-        shv[0] = c0.x; shv[1] = c0.y; shv[2] = c0.z; shv[3] = c0.w;
-        shv[4] = c1.x; shv[5] = c1.y; shv[6] = c1.z; shv[7] = c1.w;
+        if constexpr (WLDS) {
+          unpack8(lds_sh16[j], shv);
+        } else {
+          const float4 c0 = lds_sh[mod_slot(j, 0) / 4], c1 = lds_sh[mod_slot(j, 1) / 4];
+          shv[0] = c0.x; shv[1] = c0.y; shv[2] = c0.z; shv[3] = c0.w;
+          shv[4] = c1.x; shv[5] = c1.y; shv[6] = c1.z; shv[7] = c1.w;
+        }
       } else {
         unpack8(ld16(a.scale + mo + col(k)), s1v);
         unpack8(ld16(a.shift + mo + col(k)), shv);
@@ -790,15 +802,9 @@ hipError_t launch_row(const RowArgs &a, bool rms, bool gated, bool fold, const D
   if (nvec <= 256) return launch_wave<4, false>(a, rms, gated, fold, stream);
   if (nvec <= 384) return launch_wave<6, false>(a, rms, gated, fold, stream);
   if (nvec <= 512) return launch_wave<8, false>(a, rms, gated, fold, stream);
-  // wider rows: one workgroup per row
-  // (threads, vectors per thread): the row must fit NT*NV vectors; prefer
-  // exact fits and 2-4 vectors (16-32 values) per thread.
-  if (nvec <= 64) return launch_cfg<64, 1>(a, rms, gated, fold, dev, stream);
-  if (nvec <= 128) return launch_cfg<64, 2>(a, rms, gated, fold, dev, stream);
-  if (nvec <= 192) return launch_cfg<64, 3>(a, rms, gated, fold, dev, stream);
-  if (nvec <= 256) return launch_cfg<128, 2>(a, rms, gated, fold, dev, stream);
-  if (nvec <= 384) return launch_cfg<128, 3>(a, rms, gated, fold, dev, stream);
-  if (nvec <= 512) return launch_cfg<128, 4>(a, rms, gated, fold, dev, stream);
+  // wider rows (4104-16384 columns): one workgroup per row, (threads,
+  // vectors per thread) such that NT*NV vectors hold the row with 3-4
+  // vectors (24-32 values) per thread
   if (nvec <= 768) return launch_cfg<256, 3>(a, rms, gated, fold, dev, stream);
   if (nvec <= 1024) return launch_cfg<256, 4>(a, rms, gated, fold, dev, stream);
   return launch_cfg<512, 4>(a, rms, gated, fold, dev, stream);  // up to 16384 columns
