@@ -3,7 +3,8 @@
 // Every entry point validates its arguments on the host first -- sizes,
 // alignment, aliasing -- and only then touches HIP: it looks up the current
 // device (checked once per device to be gfx950), fills the kernel argument
-// block and enqueues one kernel on the caller's stream.  There is no
+// block and enqueues the work on the caller's stream (one kernel; the
+// backward one kernel per tree level more).  There is no
 // fallback path: anything the kernels do not implement is reported as
 // DITNORM_UNSUPPORTED.
 #include <atomic>
