@@ -492,7 +492,7 @@ def main():
     if not args.no_cpu and args.only is None:
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w)
-        result["cpu_oracle"] = cpu_oracle_table()
+        result["cpu_baseline"]["per_launch"] = cpu_oracle_table()
     print(json.dumps(result), flush=True)
 
 
