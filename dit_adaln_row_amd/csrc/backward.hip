@@ -110,7 +110,7 @@ __device__ __forceinline__ void bwd_row(const BwdArgs &a, int64_t row, int64_t m
   const double n_d = (double)cols;
   const double s1 = sum64(m.s1), s2 = sum64(m.s2);
   const double mean_d = s1 / n_d;
-  const double var_d = __builtin_fmax(__builtin_fma(-s1, mean_d, s2) / n_d, 0.0);
+  const double var_d = clamp_var(__builtin_fma(-s1, mean_d, s2) / n_d);
   mean_f = (float)mean_d;
   rstd_f = rstd_from(var_d + (double)a.eps);
   const double mu = (double)mean_f, rs = (double)rstd_f;

@@ -207,6 +207,11 @@ __device__ __forceinline__ void accumulate(Moments &m, float x) {
   m.s2 = __builtin_fma(d, d, m.s2);
 }
 
+// The variance S2/N - mean*S1/N clamped at 0 against its last-bit rounding
+// on near-constant rows.  A comparison, not fmax: a row holding an infinity
+// or a NaN has a NaN variance (inf - inf), and fmax would turn it into 0.
+__device__ __forceinline__ double clamp_var(double v) { return v < 0.0 ? 0.0 : v; }
+
 // rstd = fp32(1 / sqrt(v)), v = var + eps in binary64 (correctly rounded
 // binary64 square root and division, then one rounding to binary32).
 __device__ __forceinline__ float rstd_from(double v) {

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
     }
     const double s1 = group_sum<L>(m.s1), s2 = group_sum<L>(m.s2);
     const double mean_d = s1 * (1.0 / QK_HEAD);  // exact: 128 is a power of two
-    const double var_d = __builtin_fmax(__builtin_fma(-s1, mean_d, s2) * (1.0 / QK_HEAD), 0.0);
+    const double var_d = clamp_var(__builtin_fma(-s1, mean_d, s2) * (1.0 / QK_HEAD));
     mean_f[g] = (float)mean_d;
     rstd_f[g] = rstd_from(var_d + eps);
   }

@@ -388,7 +388,7 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
   } else {
     const double s1 = sum64(m.s1);
     const double mean_d = s1 / n_d;
-    const double var_d = __builtin_fmax(__builtin_fma(-s1, mean_d, s2) / n_d, 0.0);
+    const double var_d = clamp_var(__builtin_fma(-s1, mean_d, s2) / n_d);
     mean_f = (float)mean_d;
     rstd_f = rstd_from(var_d + (double)a.eps);
   }
@@ -604,7 +604,7 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
     rstd_f = rstd_from(s2 / n_d + (double)a.eps);
   } else {
     const double mean_d = s1 / n_d;
-    const double var_d = __builtin_fmax(__builtin_fma(-s1, mean_d, s2) / n_d, 0.0);
+    const double var_d = clamp_var(__builtin_fma(-s1, mean_d, s2) / n_d);
     mean_f = (float)mean_d;
     rstd_f = rstd_from(var_d + (double)a.eps);
   }
