@@ -300,7 +300,8 @@ int residual_gate_add(const void *update, const void *residual, const void *gate
  * partial tree sums); when that size is 0 (batches of at most 8 tokens, 4
  * for rows over 3072 columns) workspace may be NULL.  mean_out, rstd_out
  * (fp32 [rows]) optional.  The work is one kernel launch on `stream` when the
- * workspace size is 0, else two to four.
+ * workspace size is 0, else one more per level of the token tree: two for
+ * batches of up to 1024 tokens, three up to 32768, four up to 2^20.
  */
 int ln_modulate_backward(const void *x, const void *scale, const void *d_out, void *d_x,
                          float *d_scale, float *d_shift, int64_t rows, int64_t cols,
