@@ -40,7 +40,15 @@
  *  - Weighted RMSNorm ("ERNIE-Image bit-exact fused RMSNorm+scale/shift",
  *    section "What rounding-faithful means here"): mean of squares over the
  *    H columns (no mean subtraction), rstd = 1/sqrt(ms + eps) in fp32, and one
- *    rounding of the product x * rstd * w evaluated left to right.
+ *    rounding of the product x * rstd * w evaluated left to right.  That
+ *    order is a reading no independent pin fixes: parity unpinned for the
+ *    last bit of the RMS normalise order ((x * rstd) * w against
+ *    x * (rstd * w), which differ on rare elements).
+ *
+ *  - fp16 storage of the standalone modulate and residual-gate add (FLUX.1
+ *    page, Commit 2: bf16 and fp16): the same binary32 operations, each
+ *    result rounded to IEEE half precision, nearest-even, overflow to
+ *    infinity, subnormals kept.
  *
  *  - LN-affine folding, the lossy one-pass form ("FLUX.1 fused adaLN
  *    modulate (bit-exact) + RoPE cache hoist, LN-affine folding behind
