@@ -1,0 +1,99 @@
+"""Seeded random shapes across the entry points (a fixed list, so failures
+reproduce): widths that are any multiple of 8 up to 4096 (a wavefront per
+row, the balanced launch, ragged last vectors), several modulation batches
+with chunk-view strides, row counts that leave remainders of every size
+against the 1024 SIMDs, and token counts across the backward's tree levels.
+Every output is compared with the oracle at the parity bar."""
+import numpy as np
+import pytest
+import torch
+
+from dit_adaln_row_amd import inputs as gen
+from parity import check_rows_end_to_end, check_stats, dev, host, log, same_bits, ulp_diff
+
+pytestmark = pytest.mark.gpu
+
+
+def rand(shape, mu, sigma, seed):
+    return gen.to_u16(gen.normal(shape, mu, sigma, seed))
+
+
+def _configs(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        cols = int(rng.choice([8 * int(rng.integers(1, 513)), 1024 * int(rng.integers(1, 5))]))
+        B = int(rng.choice([1, 1, 2, 3, 7]))
+        S = int(rng.integers(1, 1400 // B + 2))
+        extra = int(rng.choice([0, 0, 8, 8 * int(rng.integers(1, 64))]))  # chunk-view stride pad
+        out.append((i, B, S, cols, extra))
+    return out
+
+
+CONFIGS = _configs(32, 20261202)
+KINDS = ["ln", "gated", "rms", "gated_rms", "folded", "backward"]
+
+
+def _mod(B, cols, extra, seed):
+    """B modulation rows of `cols` inside rows of cols + extra (a chunk view)."""
+    full = rand((B, cols + extra), 0, 0.1, seed)
+    return full, dev(full)[:, :cols], np.ascontiguousarray(full[:, :cols])
+
+
+@pytest.mark.parametrize("i,B,S,cols,extra", CONFIGS)
+def test_random_shape(gpu, orc, i, B, S, cols, extra):
+    kind = KINDS[i % len(KINDS)]
+    rows = B * S
+    log(f"random shape {i}: {kind} B={B} S={S} cols={cols} stride pad={extra}")
+    x = rand((rows, cols), 0.1 * (i % 3), 1.0 + 0.3 * (i % 4), 700 + i)
+    _, scd, sc = _mod(B, cols, extra, 800 + i)
+    _, shd, sh = _mod(B, cols, extra, 900 + i)
+    mean, rstd = (torch.empty(rows, dtype=torch.float32, device="cuda") for _ in range(2))
+    if kind in ("ln", "folded"):
+        fn = gpu.ln_modulate if kind == "ln" else gpu.ln_modulate_folded
+        out = host(fn(dev(x), scd, shd, 1e-6, mean_out=mean, rstd_out=rstd))
+        torch.cuda.synchronize()
+        ref = (orc.ln_modulate if kind == "ln" else orc.ln_modulate_folded)(
+            x, sc, sh, 1e-6, rows_per_batch=S)
+        differ = check_stats(host(mean), host(rstd), ref["mean"], ref["rstd"], kind)
+        check_rows_end_to_end(out, ref["out"], np.repeat(differ[:, None], cols, 1), kind)
+    elif kind == "gated":
+        res = rand((rows, cols), 0, 1, 1000 + i)
+        _, gd, g = _mod(B, cols, extra, 1100 + i)
+        h, out = gpu.gated_ln_modulate(dev(x), dev(res), gd, scd, shd, 1e-6, mean_out=mean,
+                                       rstd_out=rstd)
+        torch.cuda.synchronize()
+        ref = orc.gated_ln_modulate(x, res, g, sc, sh, 1e-6, rows_per_batch=S)
+        assert same_bits(host(h), ref["h"])
+        differ = check_stats(host(mean), host(rstd), ref["mean"], ref["rstd"], kind)
+        check_rows_end_to_end(host(out), ref["out"], np.repeat(differ[:, None], cols, 1), kind)
+    elif kind in ("rms", "gated_rms"):
+        w = rand((cols,), 1, 0.05, 1200 + i)
+        kw, res, g = {}, None, None
+        if kind == "gated_rms":
+            res = rand((rows, cols), 0, 1, 1300 + i)
+            _, gd, g = _mod(B, cols, extra, 1400 + i)
+            kw = dict(residual=dev(res), gate=gd)
+        r = gpu.rms_modulate(dev(x), dev(w), scd, shd, 1e-6, rstd_out=rstd, **kw)
+        torch.cuda.synchronize()
+        ref = orc.rms_modulate(x, w, sc, sh, 1e-6, residual=res, gate=g, rows_per_batch=S)
+        out = r
+        if kind == "gated_rms":
+            h, out = r
+            assert same_bits(host(h), ref["h"])
+        differ = check_stats(None, host(rstd), None, ref["rstd"], kind)
+        check_rows_end_to_end(host(out), ref["out"], np.repeat(differ[:, None], cols, 1), kind)
+    else:
+        if cols > 4096:
+            pytest.skip("the backward serves rows up to 4096 columns")
+        dout = rand((rows, cols), 0, 1, 1500 + i)
+        d_x, d_scale, d_shift = gpu.ln_modulate_backward(dev(x), scd, dev(dout), 1e-6,
+                                                         mean_out=mean, rstd_out=rstd)
+        torch.cuda.synchronize()
+        ref = orc.ln_modulate_backward(x, sc, dout, 1e-6, rows_per_batch=S)
+        differ = check_stats(host(mean), host(rstd), ref["mean"], ref["rstd"], kind)
+        d = ulp_diff(host(d_x), ref["d_x"])
+        assert d.max() <= 1 and (d == 0).mean() >= 0.9999
+        if not differ.any():
+            assert np.array_equal(host(d_scale), ref["d_scale"])
+            assert np.array_equal(host(d_shift), ref["d_shift"])
