@@ -603,7 +603,9 @@ int ln_modulate_backward_supported(const void *x, const void *scale, const void 
 
 int ditnorm_copy(const void *src, void *dst, int64_t bytes, void *stream) {
   if (bytes < 0 || (bytes > 0 && (!src || !dst))) return DITNORM_INVALID_ARGUMENT;
-  if (bytes % 16 != 0 || !aligned16(src) || !aligned16(dst)) return DITNORM_UNSUPPORTED;
+  if (bytes % 16 != 0 || bytes / 16 > DITNORM_MAX_VECTORS - 255 || !aligned16(src) ||
+      !aligned16(dst))
+    return DITNORM_UNSUPPORTED;
   if (overlap(Buf{src, bytes}, Buf{dst, bytes})) return DITNORM_UNSUPPORTED;
   if (bytes == 0) return DITNORM_OK;
   DeviceInfo dev;

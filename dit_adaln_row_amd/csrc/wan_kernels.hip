@@ -346,19 +346,24 @@ hipError_t launch_epilogue(const EpilogueArgs &a, const DeviceInfo &dev, hipStre
 // plain 16-byte copy (measurement utility)
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(WAN_BLOCK) void copy_kernel(const uint4 *src, uint4 *dst, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * WAN_BLOCK;
-  for (int64_t i = (int64_t)blockIdx.x * WAN_BLOCK + threadIdx.x; i < n; i += stride)
-    dst[i] = src[i];
+// One-shot, one 16-byte vector per thread, streaming hints: the fastest copy
+// form measured on this chip (more vectors per thread, a grid-stride loop or
+// plain loads and stores are all slower), so the ceiling the kernels are
+// compared with is a fair one.
+__global__ __launch_bounds__(WAN_BLOCK) void copy_kernel(const uint16_t *src, uint16_t *dst,
+                                                         int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * WAN_BLOCK + threadIdx.x;
+  if (i < n) st16s(dst + i * 8, ld16s(src + i * 8));
 }
 
 hipError_t launch_copy(const void *src, void *dst, int64_t bytes, const DeviceInfo &dev,
                        hipStream_t stream) {
+  (void)dev;
   const int64_t n = bytes / 16;
   const int64_t blocks = (n + WAN_BLOCK - 1) / WAN_BLOCK;
-  const int64_t grid = persistent_grid(copy_kernel, WAN_BLOCK, blocks, dev);
-  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(WAN_BLOCK), 0, stream,
-                     (const uint4 *)src, (uint4 *)dst, n);
+  if (blocks * WAN_BLOCK > (int64_t)INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(WAN_BLOCK), 0, stream,
+                     (const uint16_t *)src, (uint16_t *)dst, n);
   return hipGetLastError();
 }
 
