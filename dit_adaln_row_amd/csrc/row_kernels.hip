@@ -452,9 +452,14 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = rstd_f * (v[e] - mean_f);
       }
-      uint4 yq;  // y as stored bf16 (the rounding is the packing)
-      yq = pack8(y);
-      unpack8(yq, y);
+      uint4 yq;  // y as stored bf16
+      if constexpr (WY) {
+        yq = pack8(y);
+        unpack8(yq, y);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = round1(y[e]);
+      }
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         float p0 = y[e] * s1v[e], p1 = y[e + 1] * s1v[e + 1];
@@ -662,8 +667,14 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = rstd_f * (v[e] - mean_f);
       }
-      const uint4 yq = pack8(y);  // y as stored bf16 (the rounding is the packing)
-      unpack8(yq, y);
+      uint4 yq;  // y as stored bf16
+      if constexpr (WY) {
+        yq = pack8(y);
+        unpack8(yq, y);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = round1(y[e]);
+      }
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         float q0 = y[e] * s1v[e], q1 = y[e + 1] * s1v[e + 1];
