@@ -6,9 +6,10 @@ A step is one pass of the hot path over the FLUX.1-like adaLN workload
 (1, 4608, 3072): the plain LayerNorm + modulate site and the gated-residual
 site, two launches through the C ABI.  W untimed steps, then K timed steps
 bracketed by torch.cuda.synchronize(); inputs are resident in HBM and rotate
-over enough independent buffer sets (>= 1 GiB in total) that no launch finds
-its data in the 256 MB Infinity Cache.  Every launch is bracketed by HIP
-events on the stream it runs on, which gives each kernel's average duration.
+over enough independent buffer sets (>= 1 GiB for every launch) that no
+launch finds its data in the 256 MB Infinity Cache.  Each launch kind runs as
+a burst between HIP events on the stream it runs on, which gives each
+kernel's average duration.
 
 Prints ONE JSON line: the step's throughput (algorithmic GB/s = bytes every
 launch must move / time), the roofline of the dominant kernel, the CPU oracle
