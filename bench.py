@@ -421,9 +421,9 @@ def main():
     if args.summarize_pmc:
         return summarize_pmc(*args.summarize_pmc, args.cmd)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
-              f"(--gpus {args.gpus} requested). Rows are independent; see DESIGN.md for how the "
-              f"path would shard.", file=sys.stderr)
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
+              f"(--gpus {args.gpus} requested). Rows are independent, so the path shards by rows "
+              f"across GPUs with no communication in the forward.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")

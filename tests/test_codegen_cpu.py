@@ -1,5 +1,5 @@
-"""The built library's gfx950 machine code (this build's own, disassembled on
-the CPU): no packed fp32 arithmetic anywhere, and no fp32 multiply-add in the
+"""The library's gfx950 machine code (built here from its sources and
+disassembled on the CPU): no packed fp32 arithmetic anywhere, and no fp32 multiply-add in the
 numeric chains.
 
 Every elementwise stage is one rounded fp32 operation per eager op, so a
