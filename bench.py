@@ -5,7 +5,11 @@
 A step is one pass of the hot path over the FLUX.1-like adaLN workload
 (1, 4608, 3072): the plain LayerNorm + modulate site and the gated-residual
 site, two launches through the C ABI.  W untimed steps, then K timed steps
-bracketed by torch.cuda.synchronize(); inputs are resident in HBM and rotate
+bracketed by torch.cuda.synchronize().  The default W = 2000 (~65 ms of GPU
+work) is what the GPU needs to settle: in a fresh process the first ~60 ms of
+back-to-back launches run up to 7% slower (the gated launch measured
+21.5 us after 20 warmup steps, 20.4 after 200, 20.1 after 2000 and in every
+later loop).  Inputs are resident in HBM and rotate
 over enough independent buffer sets (>= 1 GiB for every launch) that no
 launch finds its data in the 256 MB Infinity Cache.  Each launch kind runs as
 a burst between HIP events on the stream it runs on, which gives each
@@ -403,8 +407,8 @@ def cpu_oracle_table(seconds=0.5, skip=()):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-kernels", action="store_true")
     ap.add_argument("--only", default=None, help="time only this workload's kernels (profiling)")
