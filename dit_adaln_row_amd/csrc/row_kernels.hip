@@ -483,7 +483,7 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Balanced variant: whole rows for whole rounds, half rows for the remainder
+// Balanced variant: whole rows for whole rounds, split rows for the remainder
 // ---------------------------------------------------------------------------
 //
 // A launch lasts as long as its busiest SIMD.  With one wavefront per row,
@@ -491,10 +491,13 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
 // launch takes as long as 5120 rows would (measured: 4096 rows of 3072 in
 // 9.7 us, 4608 and 5120 rows both 13.5 us).  Here the first rows go one per
 // wavefront in whole rounds (full_blocks workgroups of 4 rows) and the
-// remaining rows are split in two halves, a workgroup of 4 wavefronts taking
-// 2 rows, so 4608 rows are 4 whole rows plus one half row per SIMD.  The two
-// halves' binary64 moments meet through LDS; the sums are exact, so the
-// statistics carry the same bits either way.  Everything else is the
+// remaining rows are split into P segments, one wavefront each: halves (P =
+// 2, a workgroup of 4 wavefronts taking 2 rows), so 4608 rows are 4 whole
+// rows plus one half row per SIMD; or, when the remainder is at most a
+// quarter round, quarters (P = 4, a workgroup per row), so 4216 rows of 4096
+// are 4 whole rows plus a quarter row on 480 SIMDs instead of a half row on
+// 240.  The segments' binary64 moments meet through LDS; the sums are exact,
+// so the statistics carry the same bits either way.  Everything else is the
 // wavefront-per-row kernel's MOD_LDS path (rows of NV * 512 columns).
 template <int NVW, int NV, bool RMS, bool GATED, bool FOLD>
 __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, float4 *lds_sh,
@@ -597,11 +600,17 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
       red[w][0] = s1;
       red[w][1] = s2;
     }
-    lds_barrier();  // the staged modulation rows and both halves' moments
+    lds_barrier();  // the staged modulation rows and every segment's moments
     if (!live) return;  // whole wavefront; no barrier follows
-    const int pw = w & ~1;
-    s1 = red[pw][0] + red[pw + 1][0];
-    s2 = red[pw][1] + red[pw + 1][1];
+    constexpr int P = NV / NVW;  // segments per row: 2 or 4
+    const int pw = w & ~(P - 1);
+    if constexpr (P == 2) {
+      s1 = red[pw][0] + red[pw + 1][0];
+      s2 = red[pw][1] + red[pw + 1][1];
+    } else {
+      s1 = (red[pw][0] + red[pw + 1][0]) + (red[pw + 2][0] + red[pw + 3][0]);
+      s2 = (red[pw][1] + red[pw + 1][1]) + (red[pw + 2][1] + red[pw + 3][1]);
+    }
   }
   const double n_d = (double)cols;
   float mean_f = 0.0f, rstd_f;
@@ -697,7 +706,7 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
   }
 }
 
-template <int NV, bool RMS, bool GATED, bool FOLD>
+template <int NV, bool RMS, bool GATED, bool FOLD, int P>
 __global__ __launch_bounds__(256) void row_mixed_kernel(const RowArgs a) {
   __shared__ float4 lds_s1[NV * 128], lds_sh[RMS ? 1 : NV * 128];
   __shared__ uint4 lds_sh16[RMS ? NV * 64 : 1], lds_w[RMS ? NV * 64 : 1];
@@ -707,16 +716,21 @@ __global__ __launch_bounds__(256) void row_mixed_kernel(const RowArgs a) {
     const int64_t row0 = (int64_t)blockIdx.x * 4;
     row_segment<NV, NV, RMS, GATED, FOLD>(a, lds_s1, lds_sh, lds_sh16, lds_w, red, row0, row0 + w,
                                           0);
-  } else {
+  } else if constexpr (P == 2) {
     const int64_t row0 = a.full_blocks * 4 + ((int64_t)blockIdx.x - a.full_blocks) * 2;
     row_segment<NV / 2, NV, RMS, GATED, FOLD>(a, lds_s1, lds_sh, lds_sh16, lds_w, red, row0,
                                                row0 + (w >> 1), w & 1);
+  } else {  // a row per workgroup, a quarter per wavefront
+    const int64_t row0 = a.full_blocks * 4 + ((int64_t)blockIdx.x - a.full_blocks);
+    row_segment<NV / 4, NV, RMS, GATED, FOLD>(a, lds_s1, lds_sh, lds_sh16, lds_w, red, row0,
+                                               row0, w);
   }
 }
 
 // Whole rounds of rows (one row per wavefront, one wavefront per SIMD per
-// round) and the remainder in halves when it is at most half a round; else
-// every row whole.
+// round) and the remainder in quarters when it is at most a quarter round
+// (rows of 2048 or 4096 columns), in halves when it is at most half a round;
+// else every row whole.
 template <int NV>
 static hipError_t launch_mixed(const RowArgs &a0, bool rms, bool gated, bool fold,
                                const DeviceInfo &dev, hipStream_t stream) {
@@ -725,7 +739,12 @@ static hipError_t launch_mixed(const RowArgs &a0, bool rms, bool gated, bool fol
   const int64_t whole = a.rows / simds * simds;
   const int64_t rem = a.rows - whole;
   int64_t blocks;
-  if (whole > 0 && rem > 0 && 2 * rem <= simds) {
+  int P = 2;
+  if (whole > 0 && rem > 0 && 4 * rem <= simds && NV % 4 == 0) {
+    a.full_blocks = whole / 4;
+    blocks = a.full_blocks + rem;
+    P = 4;
+  } else if (whole > 0 && rem > 0 && 2 * rem <= simds) {
     a.full_blocks = whole / 4;
     blocks = a.full_blocks + (rem + 1) / 2;
   } else {
@@ -733,8 +752,14 @@ static hipError_t launch_mixed(const RowArgs &a0, bool rms, bool gated, bool fol
     blocks = a.full_blocks;
   }
   const dim3 grid((unsigned)blocks), block(256);
-#define DITNORM_MIXED(R, G, F) \
-  hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, F>), grid, block, 0, stream, a)
+#define DITNORM_MIXED(R, G, F)                                                        \
+  do {                                                                                \
+    if (P == 4)                                                                       \
+      hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, F, (NV % 4 == 0 ? 4 : 2)>), grid, \
+                         block, 0, stream, a);                                        \
+    else                                                                              \
+      hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, F, 2>), grid, block, 0, stream, a); \
+  } while (0)
   if (fold) DITNORM_MIXED(false, false, true);
   else if (!rms && !gated) DITNORM_MIXED(false, false, false);
   else if (!rms && gated) DITNORM_MIXED(false, true, false);

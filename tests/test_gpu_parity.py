@@ -469,18 +469,24 @@ def test_rejections_raise(gpu):
 
 # ---------------------------------------------------------------------------
 # the balanced launch: whole rows for whole rounds of the 1024 SIMDs, the
-# remainder as half rows (two wavefronts per row, moments through LDS)
+# remainder as half rows (two wavefronts per row, moments through LDS) or, for
+# rows of 2048 or 4096 columns and a remainder of at most a quarter round, as
+# quarter rows (a workgroup per row)
 # ---------------------------------------------------------------------------
 
 SPLIT_CASES = [(3072, 4096 + 512, 4096 + 512), (3072, 1024 + 1, 1025), (4096, 2048 + 257, 2305),
-               (1024, 4096 + 3, 4099), (2048, 3072 + 511, 3583), (3072, 4096 + 256, 17)]
+               (1024, 4096 + 3, 4099), (2048, 3072 + 511, 3583), (3072, 4096 + 256, 17),
+               # quarters
+               (4096, 1024 + 120, 1144), (2048, 2048 + 256, 2304), (4096, 1024 + 16, 13),
+               (4096, 4096 + 1, 4097)]
 
 
 @pytest.mark.parametrize("cols,rows,rpb", SPLIT_CASES)
 @pytest.mark.parametrize("kind", ["ln", "gated_ln", "rms", "gated_rms"])
 def test_balanced_split_rows(gpu, orc, cols, rows, rpb, kind):
     """Row counts with a remainder of at most half a round take the half-row
-    path; batch boundaries fall inside half-row workgroups in the last case."""
+    path (batch boundaries fall inside half-row workgroups at rpb = 17), at
+    most a quarter round of 2048 or 4096 columns the quarter-row path."""
     log(f"balanced {kind} rows={rows} cols={cols} rpb={rpb}")
     B = rows // rpb
     x = rand((rows, cols), 0.2, 1.5, 1100 + cols + rows)
