@@ -19,7 +19,9 @@
 // widths use a whole wavefront per pixel.  The sum of squares is a DPP
 // butterfly over the L lanes in binary64, the biased input stays in fp32
 // registers between the two passes, and the grid is one-shot: each wavefront
-// issues the loads of its G pixel groups first.
+// issues the loads of its G pixel groups first.  With two groups (C = 96 and
+// 384) the lanes of a pixel split the per-pixel square root and divisions
+// between the groups instead of each lane evaluating them for both.
 //
 // SiLU(t) = t / (1 + e^-t) with the hardware exp2 and reciprocal: relative
 // error a few 1e-7, far below half a bf16 ulp (2^-9), so the rounded result is
@@ -34,6 +36,11 @@
 namespace ditnorm {
 
 constexpr int WAN_BLOCK = 256;
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -120,6 +127,7 @@ __global__ __launch_bounds__(WAN_BLOCK) void wan_kernel(const WanArgs a) {
   const double eps = (double)a.eps;
   float xb[G][VPL][8];
   float rstd_f[G];
+  double tot[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     double s2 = 0.0;
@@ -145,7 +153,33 @@ __global__ __launch_bounds__(WAN_BLOCK) void wan_kernel(const WanArgs a) {
         s2 = __builtin_fma(d, d, s2);  // padding vectors are zero
       }
     }
-    rstd_f[g] = rstd_from(group_sum<L>(s2) / n_d + eps);
+    tot[g] = group_sum<L>(s2);
+  }
+  // Every lane of a pixel holds its sum; the statistics' square root and
+  // divisions are long, so with G groups lane `part` evaluates them for
+  // group part % G only and a quad permutation hands each lane the
+  // values of all G groups (L is a multiple of 4: quads hold 4 / G lanes of
+  // each group, at positions congruent to the group mod G).
+  if constexpr (G > 1 && L % 4 == 0 && (G == 2 || G == 4)) {
+    double mine = tot[0];
+#pragma unroll
+    for (int g = 1; g < G; ++g) mine = (part % G == g) ? tot[g] : mine;
+    const int r = __float_as_int(rstd_from(mine / n_d + eps));
+    auto from = [&](auto ctrl) {
+      return __int_as_float(__builtin_amdgcn_mov_dpp(r, decltype(ctrl)::value, 0xF, 0xF, true));
+    };
+    if constexpr (G == 2) {
+      rstd_f[0] = from(IntC<0xA0>{});  // quad_perm(0,0,2,2)
+      rstd_f[1] = from(IntC<0xF5>{});  // quad_perm(1,1,3,3)
+    } else {
+      rstd_f[0] = from(IntC<0x00>{});  // quad_perm(g,g,g,g)
+      rstd_f[1] = from(IntC<0x55>{});
+      rstd_f[2] = from(IntC<0xAA>{});
+      rstd_f[3] = from(IntC<0xFF>{});
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) rstd_f[g] = rstd_from(tot[g] / n_d + eps);
   }
 
   // t = (xb * rstd) * gamma; out = bf16(SiLU(t))
@@ -246,7 +280,7 @@ hipError_t launch_wan(const WanArgs &a, const DeviceInfo &dev, hipStream_t strea
     // C = 96 / 128: four lanes per pixel would make each instruction touch
     // part of every cache line of 16 pixels; the group is moved through the
     // wavefront's LDS slice instead, as whole contiguous lines
-    case 96: return launch_wan_cfg<4, 3, true, 1, true, true>(a, stream);
+    case 96: return launch_wan_cfg<4, 3, true, 2, true, true>(a, stream);
     case 128: return launch_wan_cfg<4, 4, true, 1, true, true>(a, stream);
     case 192: return launch_wan_cfg<8, 3, true, 1>(a, stream);
     case 256: return launch_wan_cfg<8, 4, true, 1>(a, stream);
