@@ -448,6 +448,48 @@ def test_row_position_batch_and_chunking_invariance(gpu, orc):
     assert np.array_equal(host(wa)[3:10], host(w7))
 
 
+@pytest.mark.parametrize("cols,rows,lo", [(3072, 1024 + 300, 1024),   # halves
+                                           (4096, 1024 + 16, 1024),    # quarters
+                                           (2048, 2048 + 200, 2048)])  # quarters
+@pytest.mark.parametrize("kind", ["ln", "gated_ln", "rms", "gated_rms"])
+def test_split_rows_equal_whole_rows(gpu, kind, cols, rows, lo):
+    """The balanced launch computes the rows past the whole rounds as half or
+    quarter rows; launched on their own (fewer rows than SIMDs) the same rows
+    run whole, one wavefront each.  Every output and statistic is bitwise
+    the same either way (the segments' binary64 moment sums are exact)."""
+    log(f"split vs whole {kind} rows={rows} cols={cols}")
+    x = rand((rows, cols), 0.1, 1.5, 1300 + cols)
+    res = rand((rows, cols), 0, 1, 1301 + cols)
+    sc, sh, gt = (dev(rand((1, cols), 0, 0.1, 1302 + i)) for i in range(3))
+    w = dev(rand((cols,), 1, 0.05, 1305))
+
+    def run(a, b):
+        n = b - a
+        rstd = empty_f32(n)
+        xd, rd = dev(x[a:b]), dev(res[a:b])
+        if kind == "ln":
+            mean = empty_f32(n)
+            outs = [gpu.ln_modulate(xd, sc, sh, 1e-6, mean_out=mean, rstd_out=rstd), mean]
+        elif kind == "gated_ln":
+            mean = empty_f32(n)
+            outs = [*gpu.gated_ln_modulate(xd, rd, gt, sc, sh, 1e-6, mean_out=mean,
+                                           rstd_out=rstd), mean]
+        elif kind == "rms":
+            outs = [gpu.rms_modulate(xd, w, sc, sh, 1e-6, rstd_out=rstd)]
+        else:
+            outs = list(gpu.rms_modulate(xd, w, sc, sh, 1e-6, residual=rd, gate=gt,
+                                         rstd_out=rstd))
+        torch.cuda.synchronize()
+        return [host(t) for t in outs + [rstd]]
+
+    full = run(0, rows)
+    for a, b in [(lo, rows), (rows - 1, rows), (lo - 3, lo + 5)]:
+        part = run(a, b)
+        for f, p_ in zip(full, part):
+            assert np.array_equal(np.asarray(f)[a:b].view(np.uint8), np.asarray(p_).view(np.uint8)), \
+                f"{kind}: rows {a}:{b} differ between the split and the whole-row launch"
+
+
 def test_rejections_raise(gpu):
     x = torch.zeros((4, 1024), dtype=torch.bfloat16, device="cuda")
     s = torch.zeros((1, 1024), dtype=torch.bfloat16, device="cuda")
