@@ -2,7 +2,8 @@
 reproduce): widths that are any multiple of 8 up to 4096 (a wavefront per
 row, the balanced launch, ragged last vectors), several modulation batches
 with chunk-view strides, row counts that leave remainders of every size
-against the 1024 SIMDs, and token counts across the backward's tree levels.
+against the 1024 SIMDs, token counts across the backward's tree levels, and
+Wan pixel counts and qk head-row counts that leave ragged last groups.
 Every output is compared with the oracle at the parity bar."""
 import numpy as np
 import pytest
@@ -32,6 +33,50 @@ def _configs(n, seed):
 
 CONFIGS = _configs(32, 20261202)
 KINDS = ["ln", "gated", "rms", "gated_rms", "folded", "backward"]
+
+
+def _pixel_configs(n, seed):
+    """Wan channel counts (the two tuned widths, the other LDS-staged and
+    lane-split widths, any multiple of 8) with pixel counts that leave every
+    kind of ragged last group; qk head-row counts split between q and k."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        c = int(rng.choice([96, 96, 384, 384, 128, 192, 256, 512, 8 * int(rng.integers(1, 513))]))
+        pixels = int(rng.integers(1, 3000))
+        rq, rk = int(rng.integers(0, 2500)), int(rng.integers(0, 2500))
+        out.append((i, c, pixels, bool(rng.integers(0, 2)), max(rq, 1), rk))
+    return out
+
+
+@pytest.mark.parametrize("i,c,pixels,bias,rq,rk", _pixel_configs(16, 20261203))
+def test_random_pixels_and_heads(gpu, orc, i, c, pixels, bias, rq, rk):
+    log(f"random pixels {i}: C={c} pixels={pixels} bias={bias}; qk rows {rq}+{rk}")
+    x = rand((pixels, c), 0, 1, 1600 + i)
+    b = gen.normal((c,), 0, 0.05, 1700 + i, "f32").numpy() if bias else None
+    g = gen.normal((c,), 1, 0.05, 1800 + i, "f32_bf16vals").numpy()
+    rstd = torch.empty(pixels, dtype=torch.float32, device="cuda")
+    xb = torch.empty((pixels, c), dtype=torch.bfloat16, device="cuda")
+    out = gpu.rmsnorm_silu_bias(dev(x), torch.from_numpy(g).cuda(),
+                                torch.from_numpy(b).cuda() if bias else None, 1e-6,
+                                rstd_out=rstd, xb_out=xb)
+    torch.cuda.synchronize()
+    ref = orc.rmsnorm_silu_bias(x, b, g, 1e-6)
+    assert same_bits(host(xb), ref["xb"])
+    assert np.array_equal(host(rstd).view(np.uint32), ref["rstd"].view(np.uint32))
+    assert ulp_diff(host(out), ref["out"]).max() <= 1
+
+    q = rand((rq, 128), 0, 2, 1900 + i)
+    k = rand((rk, 128), 0.5, 2, 2000 + i) if rk else None
+    mean = torch.empty(rq + rk, dtype=torch.float32, device="cuda")
+    rs = torch.empty(rq + rk, dtype=torch.float32, device="cuda")
+    qo, ko = gpu.qk_layernorm(dev(q), dev(k) if rk else None, 1e-5, mean_out=mean, rstd_out=rs)
+    torch.cuda.synchronize()
+    qref = orc.qk_layernorm(q, k if rk else np.zeros((0, 128), np.uint16), 1e-5)
+    differ = check_stats(host(mean), host(rs), qref["mean"], qref["rstd"], "qk")
+    got = np.concatenate([host(qo)] + ([host(ko)] if rk else []))
+    want = np.concatenate([qref["q_out"]] + ([qref["k_out"]] if rk else []))
+    check_rows_end_to_end(got, want, np.repeat(differ[:, None], 128, 1), "qk")
 
 
 def _mod(B, cols, extra, seed):
