@@ -172,13 +172,20 @@ def time_step_loop(calls_per_set, steps, warmup):
     return t1 - t0, per
 
 
-def time_kernel(calls, iters=100, reps=5, warmup=20):
+def time_kernel(calls, iters=100, reps=5, warmup=20, warm_ms=50.0):
     """Median over `reps` bursts of `iters` back-to-back launches (rotating
     buffer sets) of the per-launch time in ms; also the fastest and slowest
-    burst."""
-    for i in range(warmup):
-        fn, args = calls[i % len(calls)]
-        check_status(fn(*args), "warmup")
+    burst.  The warm-up runs at least `warmup` launches and `warm_ms` of
+    wall time, so that each kernel is timed on a settled GPU (the table
+    follows the CPU baseline, which leaves the GPU idle for seconds)."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t0 < warm_ms * 1e-3:
+        for _ in range(20):
+            fn, args = calls[i % len(calls)]
+            check_status(fn(*args), "warmup")
+            i += 1
+        torch.cuda.synchronize()
     out = []
     for r in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
