@@ -499,7 +499,7 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
 // 240.  The segments' binary64 moments meet through LDS; the sums are exact,
 // so the statistics carry the same bits either way.  Everything else is the
 // wavefront-per-row kernel's MOD_LDS path (rows of NV * 512 columns).
-template <int NVW, int NV, bool RMS, bool GATED, bool FOLD>
+template <int NVW, int NV, bool RMS, bool GATED>
 __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, float4 *lds_sh,
                                             uint4 *lds_sh16, uint4 *lds_w, double (*red)[2],
                                             int64_t row0, int64_t row, int seg) {
@@ -657,16 +657,6 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
           round2(s1v[e], s1v[e + 1]);
         }
       }
-      if constexpr (FOLD) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float t = rstd_f * (v[e] - mean_f);
-          const float p = t * s1v[e];
-          o[e] = p + shv[e];
-        }
-        st16s(a.out + base + col(k), pack8(o));
-        continue;
-      }
       if constexpr (RMS) {
         float wt[8];
         unpack8(lds_w[j], wt);
@@ -697,7 +687,7 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
   };
   using T = BoolC<true>;
   using F = BoolC<false>;
-  if (a.y_out && !FOLD) {
+  if (a.y_out) {
     if (mod_in_lds) normalise(T{}, T{});
     else normalise(T{}, F{});
   } else {
@@ -706,7 +696,7 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
   }
 }
 
-template <int NV, bool RMS, bool GATED, bool FOLD, int P>
+template <int NV, bool RMS, bool GATED, int P>
 __global__ __launch_bounds__(256) void row_mixed_kernel(const RowArgs a) {
   __shared__ float4 lds_s1[NV * 128], lds_sh[RMS ? 1 : NV * 128];
   __shared__ uint4 lds_sh16[RMS ? NV * 64 : 1], lds_w[RMS ? NV * 64 : 1];
@@ -714,16 +704,15 @@ __global__ __launch_bounds__(256) void row_mixed_kernel(const RowArgs a) {
   const int w = wave_id();
   if ((int64_t)blockIdx.x < a.full_blocks) {
     const int64_t row0 = (int64_t)blockIdx.x * 4;
-    row_segment<NV, NV, RMS, GATED, FOLD>(a, lds_s1, lds_sh, lds_sh16, lds_w, red, row0, row0 + w,
-                                          0);
+    row_segment<NV, NV, RMS, GATED>(a, lds_s1, lds_sh, lds_sh16, lds_w, red, row0, row0 + w, 0);
   } else if constexpr (P == 2) {
     const int64_t row0 = a.full_blocks * 4 + ((int64_t)blockIdx.x - a.full_blocks) * 2;
-    row_segment<NV / 2, NV, RMS, GATED, FOLD>(a, lds_s1, lds_sh, lds_sh16, lds_w, red, row0,
-                                               row0 + (w >> 1), w & 1);
+    row_segment<NV / 2, NV, RMS, GATED>(a, lds_s1, lds_sh, lds_sh16, lds_w, red, row0,
+                                         row0 + (w >> 1), w & 1);
   } else {  // a row per workgroup, a quarter per wavefront
     const int64_t row0 = a.full_blocks * 4 + ((int64_t)blockIdx.x - a.full_blocks);
-    row_segment<NV / 4, NV, RMS, GATED, FOLD>(a, lds_s1, lds_sh, lds_sh16, lds_w, red, row0,
-                                               row0, w);
+    row_segment<NV / 4, NV, RMS, GATED>(a, lds_s1, lds_sh, lds_sh16, lds_w, red, row0, row0,
+                                         w);
   }
 }
 
@@ -732,8 +721,8 @@ __global__ __launch_bounds__(256) void row_mixed_kernel(const RowArgs a) {
 // (rows of 2048 or 4096 columns), in halves when it is at most half a round;
 // else every row whole.
 template <int NV>
-static hipError_t launch_mixed(const RowArgs &a0, bool rms, bool gated, bool fold,
-                               const DeviceInfo &dev, hipStream_t stream) {
+static hipError_t launch_mixed(const RowArgs &a0, bool rms, bool gated, const DeviceInfo &dev,
+                               hipStream_t stream) {
   RowArgs a = a0;
   const int64_t simds = (int64_t)dev.num_cu * 4;
   const int64_t whole = a.rows / simds * simds;
@@ -752,34 +741,43 @@ static hipError_t launch_mixed(const RowArgs &a0, bool rms, bool gated, bool fol
     blocks = a.full_blocks;
   }
   const dim3 grid((unsigned)blocks), block(256);
-#define DITNORM_MIXED(R, G, F)                                                        \
-  do {                                                                                \
-    if (P == 4)                                                                       \
-      hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, F, (NV % 4 == 0 ? 4 : 2)>), grid, \
-                         block, 0, stream, a);                                        \
-    else                                                                              \
-      hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, F, 2>), grid, block, 0, stream, a); \
+#define DITNORM_MIXED(R, G)                                                              \
+  do {                                                                                   \
+    if (P == 4)                                                                          \
+      hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, (NV % 4 == 0 ? 4 : 2)>), grid, block, 0, \
+                         stream, a);                                                     \
+    else                                                                                 \
+      hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, 2>), grid, block, 0, stream, a);    \
   } while (0)
-  if (fold) DITNORM_MIXED(false, false, true);
-  else if (!rms && !gated) DITNORM_MIXED(false, false, false);
-  else if (!rms && gated) DITNORM_MIXED(false, true, false);
-  else if (rms && !gated) DITNORM_MIXED(true, false, false);
-  else DITNORM_MIXED(true, true, false);
+  if (!rms && !gated) DITNORM_MIXED(false, false);
+  else if (!rms && gated) DITNORM_MIXED(false, true);
+  else if (rms && !gated) DITNORM_MIXED(true, false);
+  else DITNORM_MIXED(true, true);
 #undef DITNORM_MIXED
   return hipGetLastError();
 }
 
-template <int NV, bool FULL, int MODE = MOD_LDS>
+template <int NV, bool FULL>
 hipError_t launch_wave(const RowArgs &a, bool rms, bool gated, bool fold, hipStream_t stream) {
   const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
 #define DITNORM_WAVE(R, G, F) \
-  hipLaunchKernelGGL((row_wave_kernel<NV, FULL, R, G, MODE, F>), grid, block, 0, stream, a)
+  hipLaunchKernelGGL((row_wave_kernel<NV, FULL, R, G, MOD_LDS, F>), grid, block, 0, stream, a)
   if (fold) DITNORM_WAVE(false, false, true);  // LN only
   else if (!rms && !gated) DITNORM_WAVE(false, false, false);
   else if (!rms && gated) DITNORM_WAVE(false, true, false);
   else if (rms && !gated) DITNORM_WAVE(true, false, false);
   else DITNORM_WAVE(true, true, false);
 #undef DITNORM_WAVE
+  return hipGetLastError();
+}
+
+// The folded form at 1024-4096 columns (multiples of 1024): one wavefront per
+// row, modulation rows read per row.
+template <int NV>
+hipError_t launch_folded(const RowArgs &a, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
+  hipLaunchKernelGGL((row_wave_kernel<NV, true, false, false, MOD_SERIAL, true>), grid, block, 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -819,18 +817,18 @@ hipError_t launch_row(const RowArgs &a, bool rms, bool gated, bool fold, const D
   // them per row.  Other widths up to 4096: one wavefront per row.
   if (fold) {
     switch (nvec) {
-      case 128: return launch_wave<2, true, MOD_SERIAL>(a, rms, gated, fold, stream);
-      case 256: return launch_wave<4, true, MOD_SERIAL>(a, rms, gated, fold, stream);
-      case 384: return launch_wave<6, true, MOD_SERIAL>(a, rms, gated, fold, stream);
-      case 512: return launch_wave<8, true, MOD_SERIAL>(a, rms, gated, fold, stream);
+      case 128: return launch_folded<2>(a, stream);
+      case 256: return launch_folded<4>(a, stream);
+      case 384: return launch_folded<6>(a, stream);
+      case 512: return launch_folded<8>(a, stream);
       default: break;
     }
   }
   switch (nvec) {
-    case 128: return launch_mixed<2>(a, rms, gated, fold, dev, stream);
-    case 256: return launch_mixed<4>(a, rms, gated, fold, dev, stream);
-    case 384: return launch_mixed<6>(a, rms, gated, fold, dev, stream);
-    case 512: return launch_mixed<8>(a, rms, gated, fold, dev, stream);
+    case 128: return launch_mixed<2>(a, rms, gated, dev, stream);
+    case 256: return launch_mixed<4>(a, rms, gated, dev, stream);
+    case 384: return launch_mixed<6>(a, rms, gated, dev, stream);
+    case 512: return launch_mixed<8>(a, rms, gated, dev, stream);
     default: break;
   }
   if (nvec <= 64) return launch_wave<1, false>(a, rms, gated, fold, stream);
