@@ -86,10 +86,11 @@ extern "C" {
 #define DITNORM_MAX_CHANNELS 4096
 /* Largest row width of ln_modulate_backward. */
 #define DITNORM_MAX_BACKWARD_COLS 4096
-/* Most rows of one call (a row has up to one 64-lane wavefront, and a launch
- * at most 2^31 - 1 work-items), and most 16-byte vectors in one activation of
- * modulate_scale_shift, residual_gate_add and conv_bias_epilogue (one
- * work-item per vector). */
+/* Most rows of one call (a row has up to one 64-lane wavefront, so at this
+ * limit a launch of 4-row workgroups holds 2^31 work-items, within the 32-bit
+ * grid size; every kernel indexes in 64 bits), and most 16-byte vectors in
+ * one activation of modulate_scale_shift, residual_gate_add and
+ * conv_bias_epilogue (one work-item per vector). */
 #define DITNORM_MAX_ROWS 33554431LL
 #define DITNORM_MAX_VECTORS 2147483647LL
 

@@ -490,6 +490,32 @@ def test_split_rows_equal_whole_rows(gpu, kind, cols, rows, lo):
                 f"{kind}: rows {a}:{b} differ between the split and the whole-row launch"
 
 
+def test_max_rows(gpu, orc):
+    """The largest row count a call takes (2^25 - 1 rows; a launch of 4-row
+    workgroups then holds 2^31 work-items), with 8-column rows: sampled rows,
+    the first and the last among them, equal the oracle's."""
+    rows, cols = (1 << 25) - 1, 8
+    log(f"max rows: {rows} x {cols}")
+    g = torch.Generator(device="cuda").manual_seed(1400)
+    x = torch.randn((rows, cols), generator=g, device="cuda").to(torch.bfloat16)
+    sc = dev(rand((1, cols), 0, 0.1, 1401))
+    sh = dev(rand((1, cols), 0, 0.1, 1402))
+    w = dev(rand((cols,), 1, 0.05, 1403))
+    idx = torch.cat([torch.arange(0, 64, device="cuda"),
+                     torch.randint(0, rows, (4096,), generator=g, device="cuda"),
+                     torch.arange(rows - 64, rows, device="cuda")])
+    xs = host(x[idx])
+    out = gpu.ln_modulate(x, sc, sh, 1e-6)
+    torch.cuda.synchronize()
+    ref = orc.ln_modulate(xs, host(sc), host(sh), 1e-6)
+    assert same_bits(host(out[idx]), ref["out"])
+    del out
+    out = gpu.rms_modulate(x, w, sc, sh, 1e-6)
+    torch.cuda.synchronize()
+    ref = orc.rms_modulate(xs, host(w), host(sc), host(sh), 1e-6)
+    assert same_bits(host(out[idx]), ref["out"])
+
+
 def test_rejections_raise(gpu):
     x = torch.zeros((4, 1024), dtype=torch.bfloat16, device="cuda")
     s = torch.zeros((1, 1024), dtype=torch.bfloat16, device="cuda")
