@@ -60,7 +60,8 @@ def check(got, ref, x, sc, dout, rpb, what):
 SHAPES = [(1, 1, 8), (1, 5, 40), (1, 32, 1024), (1, 33, 1024), (2, 77, 1024), (1, 1025, 512),
           (3, 100, 3072), (2048, 3, 64), (1, 40000, 64), (4, 257, 4096), (1, 300, 1000),
           (3, 4, 3072), (2, 8, 3072), (2, 9, 3072), (5, 16, 4096), (3, 5, 4096),
-          (2, 1024, 3072), (1, 9000, 3080), (1, 8192, 256), (1, 8193, 64), (2, 2500, 4096)]
+          (2, 1024, 3072), (1, 9000, 3080), (1, 8192, 256), (1, 8193, 64), (2, 2500, 4096),
+          (1, 1100000, 8)]  # four tree launches after the fused pass
 
 
 @pytest.mark.parametrize("B,S,D", SHAPES)
@@ -72,6 +73,19 @@ def test_backward_shapes(gpu, orc, B, S, D):
     got = run(x, sc, dout, S)
     ref = orc.ln_modulate_backward(x, sc, dout, 1e-6, rows_per_batch=S)
     check(got, ref, x, sc, dout, S, f"bwd {B}x{S}x{D}")
+
+
+def test_backward_max_rows(gpu, orc):
+    """The most tokens a call takes: 2^25 - 8 tokens in one batch (4194303
+    eight-token workgroups of 512 work-items, 2^31 - 512 in all), 8 columns."""
+    S, D = (1 << 25) - 8, 8
+    log(f"ln_modulate_backward max rows: 1x{S}x{D}")
+    x = rand((S, D), 0.2, 1.5, 960)
+    sc = rand((1, D), 0, 0.1, 961)
+    dout = rand((S, D), 0, 1.0, 962)
+    got = run(x, sc, dout, S)
+    ref = orc.ln_modulate_backward(x, sc, dout, 1e-6, rows_per_batch=S)
+    check(got, ref, x, sc, dout, S, "bwd max rows")
 
 
 def test_backward_chunk_view_scale(gpu, orc):
