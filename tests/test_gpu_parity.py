@@ -516,6 +516,41 @@ def test_max_rows(gpu, orc):
     assert same_bits(host(out[idx]), ref["out"])
 
 
+def test_max_rows_qk_and_wan(gpu, orc):
+    """qk_layernorm at the largest total of head rows (2^25 - 1: 2^24 of q,
+    the rest of k) and rmsnorm_silu_bias at the largest pixel count with
+    C = 96 (its tuned two-group layout); sampled rows against the oracle."""
+    n = (1 << 25) - 1
+    g = torch.Generator(device="cuda").manual_seed(1500)
+
+    def sample(rows):
+        return torch.cat([torch.arange(0, 64, device="cuda"),
+                          torch.randint(0, rows, (2048,), generator=g, device="cuda"),
+                          torch.arange(rows - 64, rows, device="cuda")])
+
+    rq = 1 << 24
+    log(f"max rows qk: {rq} + {n - rq}")
+    q = torch.empty((rq, 128), dtype=torch.bfloat16, device="cuda").normal_(0, 2, generator=g)
+    k = torch.empty((n - rq, 128), dtype=torch.bfloat16, device="cuda").normal_(0, 2, generator=g)
+    qo, ko = gpu.qk_layernorm(q, k, 1e-5)
+    torch.cuda.synchronize()
+    iq, ik = sample(rq), sample(n - rq)
+    ref = orc.qk_layernorm(host(q[iq]), host(k[ik]), 1e-5)
+    assert same_bits(host(qo[iq]), ref["q_out"]) and same_bits(host(ko[ik]), ref["k_out"])
+    del q, k, qo, ko
+    torch.cuda.empty_cache()
+
+    log(f"max rows wan: {n} x 96")
+    x = torch.empty((n, 96), dtype=torch.bfloat16, device="cuda").normal_(0, 1, generator=g)
+    b = gen.normal((96,), 0, 0.05, 1501, "f32")
+    gm = gen.normal((96,), 1, 0.05, 1502, "f32_bf16vals")
+    out = gpu.rmsnorm_silu_bias(x, gm.cuda(), b.cuda(), 1e-6)
+    torch.cuda.synchronize()
+    ix = sample(n)
+    ref = orc.rmsnorm_silu_bias(host(x[ix]), b.numpy(), gm.numpy(), 1e-6)
+    assert ulp_diff(host(out[ix]), ref["out"]).max() <= 1
+
+
 def test_rejections_raise(gpu):
     x = torch.zeros((4, 1024), dtype=torch.bfloat16, device="cuda")
     s = torch.zeros((1, 1024), dtype=torch.bfloat16, device="cuda")
