@@ -140,3 +140,35 @@ def test_elementwise_rejections(gpu):
     g = torch.zeros((3, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
         dn.residual_gate_add(x, x, g)                    # 4 rows over 3 batches
+
+
+def test_max_vectors(gpu, orc):
+    """The largest activations the one-work-item-per-vector kernels take
+    (2^25 - 1 rows, the most a call takes, of 512 columns: 2^31 - 64
+    vectors, 34 GB): modulate_scale_shift and conv_bias_epilogue.  Sampled
+    rows, the first and last among them, against the oracle."""
+    g = torch.Generator(device="cuda").manual_seed(1600)
+
+    def sample(rows):
+        return torch.cat([torch.arange(0, 64, device="cuda"),
+                          torch.randint(0, rows, (2048,), generator=g, device="cuda"),
+                          torch.arange(rows - 64, rows, device="cuda")])
+
+    rows, c = (1 << 25) - 1, 512
+    x = torch.empty((rows, c), dtype=torch.bfloat16, device="cuda").normal_(0, 1.5, generator=g)
+    sc, sh = rand((1, c), 0, 0.1, 1601, "bf16"), rand((1, c), 0, 0.1, 1602, "bf16")
+    out = dn.modulate_scale_shift(x, dev(sc), dev(sh))
+    torch.cuda.synchronize()
+    i = sample(rows)
+    assert same_bits(host(out[i]), orc.modulate_dt(host(x[i]), sc, sh, "bf16"), "bf16")
+    del x, out
+    torch.cuda.empty_cache()
+
+    x = torch.empty((rows, c), dtype=torch.bfloat16, device="cuda").normal_(0, 1, generator=g)
+    bias = gen.normal((c,), 0, 0.05, 1603, "f32")
+    out = dn.conv_bias_epilogue(x, bias.cuda())
+    torch.cuda.synchronize()
+    i = sample(rows)
+    assert same_bits(host(out[i]), orc.conv_bias_epilogue(host(x[i]), bias.numpy()), "bf16")
+    del x, out
+    torch.cuda.empty_cache()
