@@ -329,10 +329,18 @@ BwdLayout bwd_layout(int64_t rows, int64_t cols, int64_t rows_per_batch) {
   BwdLayout L{};
   const int64_t nb = rows / rows_per_batch;
   auto up = [](int64_t v) { return (v + 255) / 256 * 256; };
-  // 8 tokens per workgroup; 4 for short batches, and for rows over 3072
-  // columns, whose register footprint leaves room for one 8-wavefront
-  // workgroup per compute unit but three of 4
-  L.rows_per_chunk = (rows_per_batch <= 4 || cols > 3072) ? 4 : 8;
+  // 8 tokens per workgroup; 4 for batches of at most 4 tokens, for rows over
+  // 3072 columns (whose register footprint leaves room for one 8-wavefront
+  // workgroup per compute unit but three of 4), and for batches of more than
+  // 8 tokens that 8-token workgroups would spread over at most 128 of them
+  // (half the 256 compute units): there each workgroup's serial chain of rows
+  // sets the time, and 4-row workgroups halve it (measured 2-15% faster up to
+  // 128 eight-token workgroups, slower from 138 on, where the doubled run
+  // sums cost more).  Batches of 5-8 tokens keep one 8-row workgroup and one
+  // launch.
+  const int64_t wg8 = nb * ((rows_per_batch + 7) / 8);
+  L.rows_per_chunk =
+      (rows_per_batch <= 4 || cols > 3072 || (rows_per_batch > 8 && wg8 <= 128)) ? 4 : 8;
   L.chunks = (rows_per_batch + L.rows_per_chunk - 1) / L.rows_per_chunk;
   int64_t n1 = 1;
   if (L.chunks > 1) {

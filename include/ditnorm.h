@@ -291,10 +291,11 @@ int residual_gate_add(const void *update, const void *residual, const void *gate
  * rows and its token count (bitwise batch-invariant).
  * x, d_out, d_x: bf16 [rows, cols]; scale: bf16 [B, cols], row stride
  * mod_batch_stride; d_scale, d_shift: fp32 [B, cols] dense.  cols: multiple
- * of 8, at most DITNORM_MAX_BACKWARD_COLS.  B times rows_per_batch rounded up
- * to a multiple of 4 (of 8 when rows_per_batch > 4 and cols <= 3072) at most
- * DITNORM_MAX_ROWS.  No output may overlap an input or
- * another output.
+ * of 8, at most DITNORM_MAX_BACKWARD_COLS.  B times rows_per_batch, rounded
+ * up to a multiple of the kernel's tokens per workgroup, at most
+ * DITNORM_MAX_ROWS; that count is 8 when cols <= 3072 and either
+ * rows_per_batch is 5-8 or the batches fill more than 128 eight-token
+ * workgroups, else 4.  No output may overlap an input or another output.
  * workspace: device memory of at least
  * ln_modulate_backward_workspace_bytes(rows, cols, rows_per_batch) bytes,
  * 256-byte aligned, owned by the caller, clobbered by the call (it holds the

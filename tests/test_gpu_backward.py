@@ -54,14 +54,17 @@ def check(got, ref, x, sc, dout, rpb, what):
 
 # Token counts around the kernels' structure: a batch of at most 8 tokens (4
 # over 3072 columns) in one workgroup and one launch (1, 3, 4, 5, 8), runs of
-# 8 / 4 tokens folded by 4 / 8 within one 32-token group (9, 16, 32), one
-# level of 128 / 256 runs (33, 1024, 1025, 2500, 8192), several levels (8193,
-# 9000, 40000), ragged column counts (40, 1000, 3080) and 4096 columns.
+# 8 / 4 tokens folded by 4 / 8 within one 32-token group (9, 16, 32; 4-token
+# runs for launches that 8-token workgroups would leave under half the chip,
+# 8-token runs with many batches), one level of 128 / 256 runs (33, 1024,
+# 1025, 2500, 8192), several levels (8193, 9000, 40000, 1.1M), ragged column
+# counts (40, 1000, 3080) and 4096 columns.
 SHAPES = [(1, 1, 8), (1, 5, 40), (1, 32, 1024), (1, 33, 1024), (2, 77, 1024), (1, 1025, 512),
           (3, 100, 3072), (2048, 3, 64), (1, 40000, 64), (4, 257, 4096), (1, 300, 1000),
           (3, 4, 3072), (2, 8, 3072), (2, 9, 3072), (5, 16, 4096), (3, 5, 4096),
           (2, 1024, 3072), (1, 9000, 3080), (1, 8192, 256), (1, 8193, 64), (2, 2500, 4096),
-          (1, 1100000, 8)]  # four tree launches after the fused pass
+          (1, 1100000, 8),  # four tree launches after the fused pass
+          (64, 32, 1024), (150, 9, 1024)]  # 8-token runs within one group, many batches
 
 
 @pytest.mark.parametrize("B,S,D", SHAPES)
