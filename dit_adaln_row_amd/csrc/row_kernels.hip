@@ -496,8 +496,9 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
 // rows plus one half row per SIMD; or, when the remainder is at most a
 // quarter round, quarters (P = 4, a workgroup per row), so 4216 rows of 4096
 // are 4 whole rows plus a quarter row on 480 SIMDs instead of a half row on
-// 240.  The segments' binary64 moments meet through LDS; the sums are exact,
-// so the statistics carry the same bits either way.  Everything else is the
+// 240.  A launch with no whole round (at most a quarter or half a round of
+// rows in all) splits every row.  The segments' binary64 moments meet through
+// LDS; the sums are exact, so the statistics carry the same bits either way.  Everything else is the
 // wavefront-per-row kernel's MOD_LDS path (rows of NV * 512 columns).
 template <int NVW, int NV, bool RMS, bool GATED>
 __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, float4 *lds_sh,
@@ -719,7 +720,9 @@ __global__ __launch_bounds__(256) void row_mixed_kernel(const RowArgs a) {
 // Whole rounds of rows (one row per wavefront, one wavefront per SIMD per
 // round) and the remainder in quarters when it is at most a quarter round
 // (rows of 2048 or 4096 columns), in halves when it is at most half a round;
-// else every row whole.
+// else every row whole.  A launch of fewer rows than that (no whole round)
+// splits every row the same way, so that it spreads over the SIMDs instead
+// of leaving most of them idle.
 template <int NV>
 static hipError_t launch_mixed(const RowArgs &a0, bool rms, bool gated, const DeviceInfo &dev,
                                hipStream_t stream) {
@@ -736,6 +739,13 @@ static hipError_t launch_mixed(const RowArgs &a0, bool rms, bool gated, const De
   } else if (whole > 0 && rem > 0 && 2 * rem <= simds) {
     a.full_blocks = whole / 4;
     blocks = a.full_blocks + (rem + 1) / 2;
+  } else if (whole == 0 && 4 * rem <= simds && NV % 4 == 0) {
+    a.full_blocks = 0;  // fewer rows than a quarter round: every row in quarters
+    blocks = rem;
+    P = 4;
+  } else if (whole == 0 && 2 * rem <= simds) {
+    a.full_blocks = 0;  // fewer rows than half a round: every row in halves
+    blocks = (rem + 1) / 2;
   } else {
     a.full_blocks = (a.rows + 3) / 4;
     blocks = a.full_blocks;

@@ -454,9 +454,11 @@ def test_row_position_batch_and_chunking_invariance(gpu, orc):
 @pytest.mark.parametrize("kind", ["ln", "gated_ln", "rms", "gated_rms"])
 def test_split_rows_equal_whole_rows(gpu, kind, cols, rows, lo):
     """The balanced launch computes the rows past the whole rounds as half or
-    quarter rows; launched on their own (fewer rows than SIMDs) the same rows
-    run whole, one wavefront each.  Every output and statistic is bitwise
-    the same either way (the segments' binary64 moment sums are exact)."""
+    quarter rows; in a launch of 700 rows (more than half a round of the 1024
+    SIMDs, less than a whole one) every row runs whole, one wavefront each;
+    in a launch of at most half a round every row is split again.  Every
+    output and statistic is bitwise the same in all three (the segments'
+    binary64 moment sums are exact)."""
     log(f"split vs whole {kind} rows={rows} cols={cols}")
     x = rand((rows, cols), 0.1, 1.5, 1300 + cols)
     res = rand((rows, cols), 0, 1, 1301 + cols)
@@ -484,10 +486,15 @@ def test_split_rows_equal_whole_rows(gpu, kind, cols, rows, lo):
 
     full = run(0, rows)
     for a, b in [(lo, rows), (rows - 1, rows), (lo - 3, lo + 5)]:
-        part = run(a, b)
-        for f, p_ in zip(full, part):
-            assert np.array_equal(np.asarray(f)[a:b].view(np.uint8), np.asarray(p_).view(np.uint8)), \
+        w0 = b - 700  # a whole-row launch holding rows a:b
+        whole = run(w0, b)
+        small = run(a, b)  # at most half a round: split rows
+        for f, wh, sm in zip(full, whole, small):
+            got = np.asarray(f)[a:b].view(np.uint8)
+            assert np.array_equal(got, np.asarray(wh)[a - w0:].view(np.uint8)), \
                 f"{kind}: rows {a}:{b} differ between the split and the whole-row launch"
+            assert np.array_equal(got, np.asarray(sm).view(np.uint8)), \
+                f"{kind}: rows {a}:{b} differ between the large and the small launch"
 
 
 def test_max_rows(gpu, orc):
