@@ -11,8 +11,9 @@
 // leaves of one value of the second level; the kernels follow those subtrees:
 //
 //  bwd_fused_kernel  a workgroup of R wavefronts owns R consecutive tokens of
-//                    one batch (R = 8; 4 for batches of at most 4 tokens and
-//                    rows over 3072 columns), one row per wavefront.  One
+//                    one batch (R = 8; 4 for batches of at most 4 tokens, for
+//                    rows over 3072 columns and for small launches -- see
+//                    bwd_layout), one row per wavefront.  One
 //                    pass of binary64 sums over the raw row (sum x, sum x^2,
 //                    sum g, sum g x with g = d_out * (1 + scale)) gives the
 //                    fp32 statistics and
