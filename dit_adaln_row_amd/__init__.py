@@ -119,13 +119,22 @@ def _stream(t):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _act(t, name, dtype=torch.bfloat16):
+def _act(t, name, dtype=torch.bfloat16, device=None):
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if not t.is_cuda:
-        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_cuda or (device is not None and t.device != device):
+        raise TypeError(f"{name} must be a device tensor on {device or 'the GPU'}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous (row-major)")
+    return t
+
+
+def _like(t, ref, name):
+    """A tensor the kernels read or write with the layout of `ref`: same dtype,
+    device and shape, contiguous (the library cannot check allocation sizes)."""
+    _act(t, name, ref.dtype, ref.device)
+    if t.shape != ref.shape:
+        raise ValueError(f"{name} must have the shape of the input, {tuple(ref.shape)}")
     return t
 
 
@@ -150,11 +159,13 @@ def _mod(t, name, cols, device, dtype=torch.bfloat16):
     return t, b, (stride if b > 1 else cols)
 
 
-def _f32_out(t, n, name):
+def _f32_out(t, n, name, device):
     if t is None:
         return None
     if t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous fp32 tensor of {n} elements")
+    if t.device != device:
+        raise TypeError(f"{name} must be on {device}")
     return t
 
 
@@ -182,11 +193,12 @@ def ln_modulate(x, scale, shift, eps=1e-6, out=None, *, mean_out=None, rstd_out=
     shift, b2, stride2 = _mod(shift, "shift", cols, x.device)
     if (b, stride) != (b2, stride2):
         raise ValueError("scale and shift must have the same batch count and stride")
-    out = torch.empty_like(x) if out is None else _act(out, "out")
+    out = torch.empty_like(x) if out is None else _like(out, x, "out")
+    dv = x.device
     _call("ln_modulate", _p(x), _p(scale), _p(shift), _p(out), rows, cols, _batch(rows, b),
-          stride, eps, _p(_f32_out(mean_out, rows, "mean_out")),
-          _p(_f32_out(rstd_out, rows, "rstd_out")),
-          _p(None if y_out is None else _act(y_out, "y_out")), _stream(x))
+          stride, eps, _p(_f32_out(mean_out, rows, "mean_out", dv)),
+          _p(_f32_out(rstd_out, rows, "rstd_out", dv)),
+          _p(None if y_out is None else _like(y_out, x, "y_out")), _stream(x))
     return out
 
 
@@ -199,10 +211,10 @@ def ln_modulate_folded(x, scale, shift, eps=1e-6, out=None, *, mean_out=None, rs
     shift, b2, stride2 = _mod(shift, "shift", cols, x.device)
     if (b, stride) != (b2, stride2):
         raise ValueError("scale and shift must have the same batch count and stride")
-    out = torch.empty_like(x) if out is None else _act(out, "out")
+    out = torch.empty_like(x) if out is None else _like(out, x, "out")
     _call("ln_modulate_folded", _p(x), _p(scale), _p(shift), _p(out), rows, cols,
-          _batch(rows, b), stride, eps, _p(_f32_out(mean_out, rows, "mean_out")),
-          _p(_f32_out(rstd_out, rows, "rstd_out")), _stream(x))
+          _batch(rows, b), stride, eps, _p(_f32_out(mean_out, rows, "mean_out", x.device)),
+          _p(_f32_out(rstd_out, rows, "rstd_out", x.device)), _stream(x))
     return out
 
 
@@ -210,19 +222,21 @@ def gated_ln_modulate(x, residual, gate, scale, shift, eps=1e-6, out=None, resid
                       *, mean_out=None, rstd_out=None, y_out=None):
     """h = bf16(residual + bf16(gate * x)); out = ln_modulate(h).  Returns (h, out)."""
     _act(x, "x")
-    _act(residual, "residual")
+    _like(residual, x, "residual")
     rows, cols = _rows_cols(x)
     gate, b, stride = _mod(gate, "gate", cols, x.device)
     scale, b2, s2 = _mod(scale, "scale", cols, x.device)
     shift, b3, s3 = _mod(shift, "shift", cols, x.device)
     if not (b == b2 == b3 and stride == s2 == s3):
         raise ValueError("gate, scale and shift must share batch count and stride")
-    h = torch.empty_like(x) if residual_out is None else _act(residual_out, "residual_out")
-    out = torch.empty_like(x) if out is None else _act(out, "out")
+    h = torch.empty_like(x) if residual_out is None else _like(residual_out, x, "residual_out")
+    out = torch.empty_like(x) if out is None else _like(out, x, "out")
+    dv = x.device
     _call("gated_ln_modulate", _p(x), _p(residual), _p(gate), _p(scale), _p(shift), _p(h),
           _p(out), rows, cols, _batch(rows, b), stride, eps,
-          _p(_f32_out(mean_out, rows, "mean_out")), _p(_f32_out(rstd_out, rows, "rstd_out")),
-          _p(None if y_out is None else _act(y_out, "y_out")), _stream(x))
+          _p(_f32_out(mean_out, rows, "mean_out", dv)),
+          _p(_f32_out(rstd_out, rows, "rstd_out", dv)),
+          _p(None if y_out is None else _like(y_out, x, "y_out")), _stream(x))
     return h, out
 
 
@@ -233,7 +247,7 @@ def rms_modulate(x, weight, scale, shift, eps=1e-6, out=None, *, residual=None, 
     otherwise out."""
     _act(x, "x")
     rows, cols = _rows_cols(x)
-    _act(weight, "weight")
+    _act(weight, "weight", device=x.device)
     if weight.numel() != cols:
         raise ValueError("weight must have cols elements")
     scale, b, stride = _mod(scale, "scale", cols, x.device)
@@ -242,19 +256,19 @@ def rms_modulate(x, weight, scale, shift, eps=1e-6, out=None, *, residual=None, 
     if gated != (gate is not None):
         raise ValueError("residual and gate go together")
     if gated:
-        _act(residual, "residual")
+        _like(residual, x, "residual")
         gate, b3, s3 = _mod(gate, "gate", cols, x.device)
         if (b3, s3) != (b, stride):
             raise ValueError("gate must share batch count and stride with scale")
-        residual_out = torch.empty_like(x) if residual_out is None else _act(residual_out,
-                                                                             "residual_out")
+        residual_out = (torch.empty_like(x) if residual_out is None
+                        else _like(residual_out, x, "residual_out"))
     if (b, stride) != (b2, s2):
         raise ValueError("scale and shift must share batch count and stride")
-    out = torch.empty_like(x) if out is None else _act(out, "out")
+    out = torch.empty_like(x) if out is None else _like(out, x, "out")
     _call("rms_modulate", _p(x), _p(weight), _p(scale), _p(shift), _p(out), _p(residual),
           _p(gate), _p(residual_out if gated else None), rows, cols, _batch(rows, b), stride,
-          eps, _p(_f32_out(rstd_out, rows, "rstd_out")),
-          _p(None if y_out is None else _act(y_out, "y_out")), _stream(x))
+          eps, _p(_f32_out(rstd_out, rows, "rstd_out", x.device)),
+          _p(None if y_out is None else _like(y_out, x, "y_out")), _stream(x))
     return (residual_out, out) if gated else out
 
 
@@ -263,17 +277,17 @@ def qk_layernorm(q, k, eps=1e-5, q_out=None, k_out=None, *, mean_out=None, rstd_
     _act(q, "q")
     rows_q = q.numel() // 128 if q.shape[-1] == 128 else -1
     if k is not None:
-        _act(k, "k")
+        _act(k, "k", device=q.device)
     rows_k = 0 if k is None else (k.numel() // 128 if k.shape[-1] == 128 else -1)
     if rows_q < 0 or rows_k < 0:
         raise ValueError("head_dim must be 128")
-    q_out = torch.empty_like(q) if q_out is None else _act(q_out, "q_out")
+    q_out = torch.empty_like(q) if q_out is None else _like(q_out, q, "q_out")
     if k is not None:
-        k_out = torch.empty_like(k) if k_out is None else _act(k_out, "k_out")
+        k_out = torch.empty_like(k) if k_out is None else _like(k_out, k, "k_out")
     n = rows_q + rows_k
     _call("qk_layernorm", _p(q), _p(k), _p(q_out), _p(k_out if k is not None else None),
-          rows_q, rows_k, 128, eps, _p(_f32_out(mean_out, n, "mean_out")),
-          _p(_f32_out(rstd_out, n, "rstd_out")), _stream(q))
+          rows_q, rows_k, 128, eps, _p(_f32_out(mean_out, n, "mean_out", q.device)),
+          _p(_f32_out(rstd_out, n, "rstd_out", q.device)), _stream(q))
     return q_out, k_out
 
 
@@ -295,8 +309,9 @@ def _channels_last_rows(x):
 def _out_like(x, out):
     if out is None:
         return torch.empty_like(x)  # keeps channels_last strides
-    if out.shape != x.shape or out.stride() != x.stride() or out.dtype != x.dtype:
-        raise ValueError("out must match x in shape, strides and dtype")
+    if (out.shape != x.shape or out.stride() != x.stride() or out.dtype != x.dtype
+            or out.device != x.device):
+        raise ValueError("out must match x in shape, strides, dtype and device")
     return out
 
 
@@ -314,7 +329,7 @@ def rmsnorm_silu_bias(x, gamma, bias=None, eps=1e-6, out=None, *, rstd_out=None,
     if xb_out is not None:
         xb_out = _out_like(x, xb_out)
     _call("rmsnorm_silu_bias", _p(x), _p(bias), _p(gamma), _p(out), rows, c, eps,
-          _p(_f32_out(rstd_out, rows, "rstd_out")), _p(xb_out), _stream(x))
+          _p(_f32_out(rstd_out, rows, "rstd_out", x.device)), _p(xb_out), _stream(x))
     return out
 
 
@@ -323,10 +338,12 @@ def conv_bias_epilogue(x, bias, h=None, out=None):
     if x.dtype != torch.bfloat16 or not x.is_cuda:
         raise TypeError("x must be a bf16 device tensor")
     rows2d, c = _channels_last_rows(x)
-    if bias.dtype != torch.float32 or bias.numel() != c or not bias.is_contiguous():
-        raise ValueError(f"bias must be a dense fp32 [{c}] tensor")
-    if h is not None and (h.shape != x.shape or h.stride() != x.stride() or h.dtype != x.dtype):
-        raise ValueError("h must match x in shape, strides and dtype")
+    if (bias.dtype != torch.float32 or bias.numel() != c or not bias.is_contiguous()
+            or bias.device != x.device):
+        raise ValueError(f"bias must be a dense fp32 [{c}] tensor on {x.device}")
+    if h is not None and (h.shape != x.shape or h.stride() != x.stride() or h.dtype != x.dtype
+                          or h.device != x.device):
+        raise ValueError("h must match x in shape, strides, dtype and device")
     out = _out_like(x, out)
     _call("conv_bias_epilogue", _p(x), _p(bias), _p(h), _p(out), rows2d.shape[0], c, _stream(x))
     return out
@@ -349,9 +366,7 @@ def modulate_scale_shift(x, scale, shift, out=None):
     shift, b2, stride2 = _mod(shift, "shift", cols, x.device, dt)
     if (b, stride) != (b2, stride2):
         raise ValueError("scale and shift must have the same batch count and stride")
-    out = torch.empty_like(x) if out is None else _act(out, "out", dt)
-    if out.shape != x.shape:
-        raise ValueError("out must have the shape of x")
+    out = torch.empty_like(x) if out is None else _like(out, x, "out")
     _call("modulate_scale_shift", _p(x), _p(scale), _p(shift), _p(out), rows, cols,
           _batch(rows, b), stride, _DTYPE_CODES[dt], _stream(x))
     return out
@@ -363,14 +378,10 @@ def residual_gate_add(update, residual, gate, out=None):
     out may be residual (in place)."""
     dt = _ew_dtype(update)
     _act(update, "update", dt)
-    _act(residual, "residual", dt)
-    if residual.shape != update.shape:
-        raise ValueError("residual must have the shape of update")
+    _like(residual, update, "residual")
     rows, cols = _rows_cols(update)
     gate, b, stride = _mod(gate, "gate", cols, update.device, dt)
-    out = torch.empty_like(update) if out is None else _act(out, "out", dt)
-    if out.shape != update.shape:
-        raise ValueError("out must have the shape of update")
+    out = torch.empty_like(update) if out is None else _like(out, update, "out")
     _call("residual_gate_add", _p(update), _p(residual), _p(gate), _p(out), rows, cols,
           _batch(rows, b), stride, _DTYPE_CODES[dt], _stream(update))
     return out
@@ -391,31 +402,36 @@ def ln_modulate_backward(x, scale, d_out, eps=1e-6, *, d_x=None, d_scale=None, d
     (D,), (B, D) or (B, 1, D) bf16.  The workspace (uint8 device tensor) is
     allocated here when the call needs one and none is given."""
     _act(x, "x")
-    _act(d_out, "d_out")
-    if d_out.shape != x.shape:
-        raise ValueError("d_out must have the shape of x")
+    _like(d_out, x, "d_out")
     rows, cols = _rows_cols(x)
     scale, b, stride = _mod(scale, "scale", cols, x.device)
     rpb = _batch(rows, b)
-    d_x = torch.empty_like(x) if d_x is None else _act(d_x, "d_x")
+    d_x = torch.empty_like(x) if d_x is None else _like(d_x, x, "d_x")
     f32 = dict(dtype=torch.float32, device=x.device)
     d_scale = torch.empty((b, cols), **f32) if d_scale is None else d_scale
     d_shift = torch.empty((b, cols), **f32) if d_shift is None else d_shift
     for t, nm in ((d_scale, "d_scale"), (d_shift, "d_shift")):
-        if t.dtype != torch.float32 or t.numel() != b * cols or not t.is_contiguous():
-            raise ValueError(f"{nm} must be a contiguous fp32 tensor of {b}x{cols}")
+        if (t.dtype != torch.float32 or t.numel() != b * cols or not t.is_contiguous()
+                or t.device != x.device):
+            raise ValueError(f"{nm} must be a contiguous fp32 tensor of {b}x{cols} on {x.device}")
     need = ln_modulate_backward_workspace_bytes(rows, cols, rpb) if rows else 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is not None and (workspace.device != x.device or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous device tensor on {x.device}")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _call("ln_modulate_backward", _p(x), _p(scale), _p(d_out), _p(d_x), _p(d_scale), _p(d_shift),
           rows, cols, rpb, stride, eps, _p(workspace), ws_bytes,
-          _p(_f32_out(mean_out, rows, "mean_out")), _p(_f32_out(rstd_out, rows, "rstd_out")),
-          _stream(x))
+          _p(_f32_out(mean_out, rows, "mean_out", x.device)),
+          _p(_f32_out(rstd_out, rows, "rstd_out", x.device)), _stream(x))
     return d_x, d_scale, d_shift
 
 
 def copy(src, dst):
     """Plain device copy through the library's 16-byte copy kernel (measurement utility)."""
-    _call("ditnorm_copy", _p(src), _p(dst), src.numel() * src.element_size(), _stream(src))
+    n = src.numel() * src.element_size()
+    if (not src.is_cuda or dst.device != src.device or not src.is_contiguous()
+            or not dst.is_contiguous() or dst.numel() * dst.element_size() < n):
+        raise ValueError("copy: contiguous device tensors on one device, dst at least src's size")
+    _call("ditnorm_copy", _p(src), _p(dst), n, _stream(src))
     return dst

@@ -558,6 +558,37 @@ def test_max_rows_qk_and_wan(gpu, orc):
     assert ulp_diff(host(out[ix]), ref["out"]).max() <= 1
 
 
+def test_binding_rejects_mismatched_tensors(gpu):
+    """The library cannot see allocation sizes: the binding refuses, before any
+    launch, outputs and companion inputs whose shape differs from the input's,
+    fp32 outputs in host memory, and tensors on another device type."""
+    x = torch.zeros((8, 1024), dtype=torch.bfloat16, device="cuda")
+    s = torch.zeros((1, 1024), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones((1024,), dtype=torch.bfloat16, device="cuda")
+    small = torch.empty((4, 1024), dtype=torch.bfloat16, device="cuda")
+    cases = [
+        lambda: gpu.ln_modulate(x, s, s, out=small),
+        lambda: gpu.ln_modulate(x, s, s, y_out=small),
+        lambda: gpu.ln_modulate(x, s, s, mean_out=torch.empty(8, dtype=torch.float32)),
+        lambda: gpu.ln_modulate_folded(x, s, s, out=small),
+        lambda: gpu.gated_ln_modulate(x, small, s, s, s),
+        lambda: gpu.gated_ln_modulate(x, x, s, s, s, residual_out=small),
+        lambda: gpu.rms_modulate(x, w, s, s, out=small),
+        lambda: gpu.rms_modulate(x, w.cpu(), s, s),
+        lambda: gpu.rms_modulate(x, w, s, s, residual=small, gate=s),
+        lambda: gpu.qk_layernorm(x.view(-1, 128), None, q_out=small.view(-1, 128)),
+        lambda: gpu.modulate_scale_shift(x, s, s, out=small),
+        lambda: gpu.residual_gate_add(x, small, s),
+        lambda: gpu.ln_modulate_backward(x, s, small),
+        lambda: gpu.ln_modulate_backward(x, s, x, d_scale=torch.empty((1, 1024))),
+        lambda: gpu.copy(x, small),
+    ]
+    for i, call in enumerate(cases):
+        with pytest.raises((ValueError, TypeError)):
+            call()
+    torch.cuda.synchronize()
+
+
 def test_rejections_raise(gpu):
     x = torch.zeros((4, 1024), dtype=torch.bfloat16, device="cuda")
     s = torch.zeros((1, 1024), dtype=torch.bfloat16, device="cuda")
