@@ -110,7 +110,8 @@ int check_rows(int64_t rows, int64_t cols, int64_t rows_per_batch, int64_t mod_b
   if (rows < 0 || cols <= 0 || rows_per_batch <= 0 || mod_batch_stride < cols || !eps_ok(eps))
     return DITNORM_INVALID_ARGUMENT;
   if (rows % rows_per_batch != 0) return DITNORM_INVALID_ARGUMENT;
-  if (cols % 8 != 0 || cols > DITNORM_MAX_COLS || rows > DITNORM_MAX_ROWS)
+  if (cols % 8 != 0 || cols > DITNORM_MAX_COLS || rows > DITNORM_MAX_ROWS ||
+      mod_batch_stride > DITNORM_MAX_MOD_STRIDE)
     return DITNORM_UNSUPPORTED;
   const int64_t nb = rows / rows_per_batch;
   if (nb > 1 && mod_batch_stride % 8 != 0) return DITNORM_UNSUPPORTED;

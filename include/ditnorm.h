@@ -34,8 +34,9 @@
  *       qk_layernorm), more than DITNORM_MAX_VECTORS 16-byte vectors in an
  *       activation of the elementwise entry points, head_dim other than 128,
  *       a pointer not 16-byte aligned, a modulation row stride that breaks
- *       16-byte alignment, or an output that overlaps an input other than in
- *       the exact in-place forms allowed.
+ *       16-byte alignment or exceeds DITNORM_MAX_MOD_STRIDE, or an output
+ *       that overlaps an input other than in the exact in-place forms
+ *       allowed.
  *   DITNORM_DEVICE_ERROR (3): the current device is not gfx950, or a HIP call
  *       or kernel launch failed (ditnorm_last_hip_error() keeps the code).
  *   All argument checks run on the host before any HIP call; a call that
@@ -93,6 +94,9 @@ extern "C" {
  * conv_bias_epilogue (one work-item per vector). */
 #define DITNORM_MAX_ROWS 33554431LL
 #define DITNORM_MAX_VECTORS 2147483647LL
+/* Largest modulation row stride, in elements (far beyond any real tensor; it
+ * keeps every byte-span computation of the argument checks inside int64). */
+#define DITNORM_MAX_MOD_STRIDE 68719476736LL
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *ditnorm_status_string(int status);

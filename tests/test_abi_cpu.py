@@ -167,6 +167,14 @@ def test_other_entry_validation(lib):
     assert bw(rows=0) == dn.OK
     assert lib.ln_modulate_backward_supported(A, B, C, D, E, E + 0x100000, 64, 3072, 64, 3072,
                                               1e-6, W, 1 << 24, None, None) == 1
+    # the modulation row stride is bounded (byte spans stay inside int64)
+    MS, T = 1 << 36, 1 << 40  # fake buffers a terabyte apart: the spans do not overlap
+    assert lib.ln_modulate_supported(T, 2 * T, 3 * T, 4 * T, 16, 8, 8, MS, 1e-6, None, None,
+                                     None) == 1
+    assert lib.ln_modulate_supported(T, 2 * T, 3 * T, 4 * T, 16, 8, 8, MS + 8, 1e-6, None, None,
+                                     None) == 0
+    assert lib.ln_modulate(T, 2 * T, 3 * T, 4 * T, 16, 8, 8, 1 << 62, 1e-6, None, None, None,
+                           None) == dn.UNSUPPORTED
     # size limits: rows (one wavefront per row) and 16-byte vectors per launch
     MR = 33554431
     assert lib.ln_modulate(A, B, C, D, MR + 1, 8, MR + 1, 8, 1e-6, None, None, None, None) \
