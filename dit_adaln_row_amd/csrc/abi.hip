@@ -185,7 +185,8 @@ int validate_qk(const void *q, const void *k, const void *q_out, const void *k_o
                 int64_t rows_q, int64_t rows_k, int64_t head_dim, float eps,
                 const float *mean_out, const float *rstd_out) {
   if (rows_q < 0 || rows_k < 0 || head_dim <= 0 || !eps_ok(eps)) return DITNORM_INVALID_ARGUMENT;
-  if (head_dim != 128 || rows_q + rows_k > DITNORM_MAX_ROWS) return DITNORM_UNSUPPORTED;
+  if (head_dim != 128 || rows_q > DITNORM_MAX_ROWS || rows_k > DITNORM_MAX_ROWS - rows_q)
+    return DITNORM_UNSUPPORTED;
   if (rows_q + rows_k == 0) return DITNORM_OK;
   if (rows_q > 0 && (!q || !q_out)) return DITNORM_INVALID_ARGUMENT;
   if (rows_k > 0 && (!k || !k_out)) return DITNORM_INVALID_ARGUMENT;

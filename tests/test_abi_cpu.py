@@ -181,6 +181,8 @@ def test_other_entry_validation(lib):
         == dn.UNSUPPORTED
     assert lib.ln_modulate_supported(A, B, C, D, MR, 8, MR, 8, 1e-6, None, None, None) == 1
     assert lib.qk_layernorm(A, B, C, D, MR, 1, 128, 1e-5, None, None, None) == dn.UNSUPPORTED
+    big = (1 << 63) - 1  # a sum of row counts that would overflow int64
+    assert lib.qk_layernorm(A, B, C, D, big, big, 128, 1e-5, None, None, None) == dn.UNSUPPORTED
     assert lib.rmsnorm_silu_bias(A, E, E + 4096, D, MR + 1, 96, 1e-6, None, None, None) \
         == dn.UNSUPPORTED
     # 2^31 - 1 vectors of 512 per row: 4194303 rows fit, 4194304 do not (buffers 64 GB apart)
