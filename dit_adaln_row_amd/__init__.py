@@ -414,7 +414,8 @@ def ln_modulate_backward(x, scale, d_out, eps=1e-6, *, d_x=None, d_scale=None, d
         if (t.dtype != torch.float32 or t.numel() != b * cols or not t.is_contiguous()
                 or t.device != x.device):
             raise ValueError(f"{nm} must be a contiguous fp32 tensor of {b}x{cols} on {x.device}")
-    need = ln_modulate_backward_workspace_bytes(rows, cols, rpb) if rows else 0
+    # -1 (sizes the call rejects): no workspace, and the call reports why
+    need = load().ln_modulate_backward_workspace_bytes(rows, cols, rpb) if rows else 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     if workspace is not None and (workspace.device != x.device or not workspace.is_contiguous()):

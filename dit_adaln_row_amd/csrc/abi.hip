@@ -557,6 +557,7 @@ int residual_gate_add_supported(const void *update, const void *residual, const 
 int64_t ln_modulate_backward_workspace_bytes(int64_t rows, int64_t cols,
                                              int64_t rows_per_batch) {
   if (rows < 0 || cols <= 0 || rows_per_batch <= 0 || rows % rows_per_batch != 0) return -1;
+  if (rows > DITNORM_MAX_ROWS || cols > DITNORM_MAX_BACKWARD_COLS) return -1;  // the call rejects them
   if (rows == 0) return 0;
   return bwd_layout(rows, cols, rows_per_batch).bytes;
 }

@@ -315,8 +315,10 @@ int ln_modulate_backward(const void *x, const void *scale, const void *d_out, vo
                          void *workspace, int64_t workspace_bytes, float *mean_out,
                          float *rstd_out, void *stream);
 
-/* Workspace bytes ln_modulate_backward needs (0 for rows == 0, -1 for invalid
- * sizes).  Host-only, never touches the GPU. */
+/* Workspace bytes ln_modulate_backward needs (0 for rows == 0; -1 for invalid
+ * sizes and for rows above DITNORM_MAX_ROWS or cols above
+ * DITNORM_MAX_BACKWARD_COLS, which the call rejects).  Host-only, never
+ * touches the GPU. */
 int64_t ln_modulate_backward_workspace_bytes(int64_t rows, int64_t cols,
                                              int64_t rows_per_batch);
 

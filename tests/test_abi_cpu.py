@@ -154,6 +154,8 @@ def test_other_entry_validation(lib):
     assert dn.ln_modulate_backward_workspace_bytes(4 * 8, 3072, 8) == 0
     assert dn.ln_modulate_backward_workspace_bytes(4 * 8, 4096, 8) > 0
     assert lib.ln_modulate_backward_workspace_bytes(10, 3072, 3) == -1
+    assert lib.ln_modulate_backward_workspace_bytes(1 << 62, 1 << 40, 1 << 62) == -1  # no overflow
+    assert lib.ln_modulate_backward_workspace_bytes(4, 4104, 4) == -1
     W = 0xA0000000
     bw = lambda **k: lib.ln_modulate_backward(
         k.get("x", A), k.get("sc", B), k.get("do", C), k.get("dx", D), k.get("ds", E),
