@@ -589,6 +589,27 @@ def test_binding_rejects_mismatched_tensors(gpu):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("cols", [1024, 2048, 3072, 4096])
+def test_every_launch_partition(gpu, orc, cols):
+    """The balanced launch picks whole, half or quarter rows from the row count
+    alone (rounds of the 1024 SIMDs, the remainder, small launches): row counts
+    across every boundary of that choice give the oracle's bits."""
+    n_max = 2100
+    x = rand((n_max, cols), 0.1, 1.5, 1700 + cols)
+    sc, sh = rand((1, cols), 0, 0.1, 1701), rand((1, cols), 0, 0.1, 1702)
+    ref = orc.ln_modulate(x, sc, sh, 1e-6)["out"]
+    rng = np.random.default_rng(cols)
+    counts = set(range(1, 65))
+    for b in (256, 512, 768, 1024, 1280, 1536, 1792, 2048):
+        counts |= {b - 1, b, b + 1}
+    counts |= set(int(v) for v in rng.integers(65, n_max + 1, 40))
+    xd, scd, shd = dev(x), dev(sc), dev(sh)
+    for n in sorted(counts):
+        out = gpu.ln_modulate(xd[:n], scd, shd, 1e-6)
+        torch.cuda.synchronize()
+        assert same_bits(host(out), ref[:n]), f"{n} rows of {cols}"
+
+
 def test_rejections_raise(gpu):
     x = torch.zeros((4, 1024), dtype=torch.bfloat16, device="cuda")
     s = torch.zeros((1, 1024), dtype=torch.bfloat16, device="cuda")
