@@ -78,6 +78,23 @@ def test_backward_shapes(gpu, orc, B, S, D):
     check(got, ref, x, sc, dout, S, f"bwd {B}x{S}x{D}")
 
 
+# On both sides of the switch between 4- and 8-token workgroups (at most 128
+# eight-token workgroups take 4-token ones), for long and short batches.
+BOUNDARY = [(1, 1024, 3072), (1, 1025, 3072), (16, 64, 1024), (16, 65, 1024),
+            (42, 24, 3072), (43, 24, 3072), (128, 9, 2048), (8, 129, 3072)]
+
+
+@pytest.mark.parametrize("B,S,D", BOUNDARY)
+def test_backward_workgroup_switch(gpu, orc, B, S, D):
+    log(f"ln_modulate_backward boundary B={B} S={S} D={D}")
+    x = rand((B * S, D), 0.2, 1.5, 970 + S)
+    sc = rand((B, D), 0, 0.1, 971 + B)
+    dout = rand((B * S, D), 0, 1.0, 972 + D)
+    got = run(x, sc, dout, S)
+    ref = orc.ln_modulate_backward(x, sc, dout, 1e-6, rows_per_batch=S)
+    check(got, ref, x, sc, dout, S, f"bwd boundary {B}x{S}x{D}")
+
+
 def test_backward_max_rows(gpu, orc):
     """The most tokens a call takes: 2^25 - 8 tokens in one batch (4194303
     eight-token workgroups of 512 work-items, 2^31 - 512 in all), 8 columns."""
