@@ -610,6 +610,33 @@ def test_every_launch_partition(gpu, orc, cols):
         assert same_bits(host(out), ref[:n]), f"{n} rows of {cols}"
 
 
+@pytest.mark.parametrize("c", [96, 384])
+def test_every_pixel_partition(gpu, orc, c):
+    """rmsnorm_silu_bias takes pixels in groups (16 at C = 96, 4 at C = 384), two
+    groups per wavefront and four wavefronts per workgroup: pixel counts across
+    those boundaries give the oracle's bias stage and rstd bits and its SiLU
+    output within 1 ulp."""
+    n_max = 700
+    x = rand((n_max, c), 0, 1, 1800 + c)
+    b = gen.normal((c,), 0, 0.05, 1801, "f32")
+    g = gen.normal((c,), 1, 0.05, 1802, "f32_bf16vals")
+    ref = orc.rmsnorm_silu_bias(x, b.numpy(), g.numpy(), 1e-6)
+    counts = set(range(1, 70))
+    for m in (128, 256, 512):
+        counts |= {m - 1, m, m + 1}
+    counts.add(n_max)
+    xd, bd, gd = dev(x), b.cuda(), g.cuda()
+    for n in sorted(counts):
+        rstd = empty_f32(n)
+        xb = torch.empty((n, c), dtype=torch.bfloat16, device="cuda")
+        out = gpu.rmsnorm_silu_bias(xd[:n], gd, bd, 1e-6, rstd_out=rstd, xb_out=xb)
+        torch.cuda.synchronize()
+        assert same_bits(host(xb), ref["xb"][:n]), f"{n} pixels: bias stage"
+        assert np.array_equal(host(rstd).view(np.uint32), ref["rstd"][:n].view(np.uint32)), \
+            f"{n} pixels: rstd"
+        assert ulp_diff(host(out), ref["out"][:n]).max() <= 1, f"{n} pixels: out"
+
+
 def test_rejections_raise(gpu):
     x = torch.zeros((4, 1024), dtype=torch.bfloat16, device="cuda")
     s = torch.zeros((1, 1024), dtype=torch.bfloat16, device="cuda")
