@@ -637,6 +637,23 @@ def test_every_pixel_partition(gpu, orc, c):
         assert ulp_diff(host(out), ref["out"][:n]).max() <= 1, f"{n} pixels: out"
 
 
+def test_every_qk_partition(gpu, orc):
+    """qk_layernorm numbers q's head rows, then k's, 8 to a wavefront
+    instruction and 32 to a workgroup, so groups straddle the q/k boundary at
+    most counts: q and k counts around those boundaries against the oracle."""
+    q = rand((80, 128), 0, 2, 1900)
+    k = rand((80, 128), 0.5, 2, 1901)
+    qd, kd = dev(q), dev(k)
+    for rq in list(range(1, 41)) + [63, 64, 65, 80]:
+        for rk in (0, 1, 7, 8, 9, 31, 32, 33, 80):
+            qo, ko = gpu.qk_layernorm(qd[:rq], kd[:rk] if rk else None, 1e-5)
+            torch.cuda.synchronize()
+            ref = orc.qk_layernorm(q[:rq], k[:rk], 1e-5)
+            assert same_bits(host(qo), ref["q_out"]), (rq, rk)
+            if rk:
+                assert same_bits(host(ko), ref["k_out"]), (rq, rk)
+
+
 def test_rejections_raise(gpu):
     x = torch.zeros((4, 1024), dtype=torch.bfloat16, device="cuda")
     s = torch.zeros((1, 1024), dtype=torch.bfloat16, device="cuda")
