@@ -304,7 +304,8 @@ def test_rmsnorm_silu_channels_last_5d(gpu, orc):
 
 
 @pytest.mark.parametrize("rows,c,res", [(1, 96, False), (1000, 96, True), (777, 384, True),
-                                        (3, 8, False), (12345, 40, True)])
+                                        (3, 8, False), (12345, 40, True), (5, 4096, True),
+                                        (333, 200, False), (64, 1000, True)])
 def test_conv_bias_epilogue(gpu, orc, rows, c, res):
     log(f"conv_bias_epilogue rows={rows} C={c} residual={res}")
     x = rand((rows, c), 0, 1, 101)
