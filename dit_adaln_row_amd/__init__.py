@@ -11,7 +11,8 @@ the call raises.
 Entry points (same names as the C ABI):
     ln_modulate, ln_modulate_folded, gated_ln_modulate, rms_modulate, qk_layernorm,
     rmsnorm_silu_bias, conv_bias_epilogue, modulate_scale_shift, residual_gate_add,
-    ln_modulate_backward (+ ln_modulate_backward_workspace_bytes), copy
+    ln_modulate_backward (+ ln_modulate_backward_workspace_bytes),
+    ln_modulate_backward_noalloc, copy
 """
 from __future__ import annotations
 
@@ -23,11 +24,14 @@ import torch
 __all__ = ["load", "ln_modulate", "ln_modulate_folded", "gated_ln_modulate", "rms_modulate", "qk_layernorm",
            "rmsnorm_silu_bias", "conv_bias_epilogue", "modulate_scale_shift",
            "residual_gate_add", "ln_modulate_backward", "ln_modulate_backward_workspace_bytes",
-           "copy", "DitnormError", "LIB_PATH"]
+           "ln_modulate_backward_noalloc", "copy", "DitnormError", "LIB_PATH",
+           "NOALLOC_SCRATCH_BYTES"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditnorm.so")
 
-OK, INVALID_ARGUMENT, UNSUPPORTED, DEVICE_ERROR = 0, 1, 2, 3
+OK, INVALID_ARGUMENT, UNSUPPORTED, DEVICE_ERROR, SCRATCH_EXCEEDED = 0, 1, 2, 3, 4
+# bytes of the library's per-device scratch array (DITNORM_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 33554432
 
 
 class DitnormError(RuntimeError):
@@ -61,6 +65,8 @@ _SIGNATURES = {
     "residual_gate_add": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp],
     "ln_modulate_backward": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp,
                              _i64, _vp, _vp, _vp],
+    "ln_modulate_backward_noalloc": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                     _f32, _vp, _vp, _vp],
     "ditnorm_copy": [_vp, _vp, _i64, _vp],
     "ln_modulate_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp],
     "ln_modulate_folded_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp,
@@ -423,6 +429,35 @@ def ln_modulate_backward(x, scale, d_out, eps=1e-6, *, d_x=None, d_scale=None, d
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _call("ln_modulate_backward", _p(x), _p(scale), _p(d_out), _p(d_x), _p(d_scale), _p(d_shift),
           rows, cols, rpb, stride, eps, _p(workspace), ws_bytes,
+          _p(_f32_out(mean_out, rows, "mean_out", x.device)),
+          _p(_f32_out(rstd_out, rows, "rstd_out", x.device)), _stream(x))
+    return d_x, d_scale, d_shift
+
+
+def ln_modulate_backward_noalloc(x, scale, d_out, eps=1e-6, *, d_x=None, d_scale=None,
+                                 d_shift=None, mean_out=None, rstd_out=None):
+    """ln_modulate_backward with its partial sums in the library's own
+    per-device scratch array instead of a workspace: the library call
+    allocates nothing (outputs not given are allocated here with torch, so a
+    caller that must not allocate passes d_x, d_scale and d_shift).  Raises
+    DitnormError with status SCRATCH_EXCEEDED when the partial sums do not
+    fit NOALLOC_SCRATCH_BYTES.  Calls overlapping in time on one device race
+    on that array."""
+    _act(x, "x")
+    _like(d_out, x, "d_out")
+    rows, cols = _rows_cols(x)
+    scale, b, stride = _mod(scale, "scale", cols, x.device)
+    rpb = _batch(rows, b)
+    d_x = torch.empty_like(x) if d_x is None else _like(d_x, x, "d_x")
+    f32 = dict(dtype=torch.float32, device=x.device)
+    d_scale = torch.empty((b, cols), **f32) if d_scale is None else d_scale
+    d_shift = torch.empty((b, cols), **f32) if d_shift is None else d_shift
+    for t, nm in ((d_scale, "d_scale"), (d_shift, "d_shift")):
+        if (t.dtype != torch.float32 or t.numel() != b * cols or not t.is_contiguous()
+                or t.device != x.device):
+            raise ValueError(f"{nm} must be a contiguous fp32 tensor of {b}x{cols} on {x.device}")
+    _call("ln_modulate_backward_noalloc", _p(x), _p(scale), _p(d_out), _p(d_x), _p(d_scale),
+          _p(d_shift), rows, cols, rpb, stride, eps,
           _p(_f32_out(mean_out, rows, "mean_out", x.device)),
           _p(_f32_out(rstd_out, rows, "rstd_out", x.device)), _stream(x))
     return d_x, d_scale, d_shift

@@ -17,6 +17,14 @@
 
 using namespace ditnorm;
 
+// Scratch memory of ln_modulate_backward_noalloc: the partial token sums that
+// ln_modulate_backward keeps in the caller's workspace.  Every device the
+// library runs on holds one copy, loaded with the library's code object and
+// kept until the process ends.  In host code this name is only a host-side
+// stand-in: its device address on each device comes from hipGetSymbolAddress
+// (scratch_address below), and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[DITNORM_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -54,6 +62,27 @@ int current_device(DeviceInfo *out) {
   }
   if (st != 1) return DITNORM_DEVICE_ERROR;
   *out = g_dev_info[dev];
+  return DITNORM_OK;
+}
+
+// Device address of `scratch` on the current device `dev`, looked up once per
+// device (with that device current) and kept.
+void *g_scratch_ptr[kMaxDevices];
+std::atomic<int> g_scratch_state[kMaxDevices];  // 0 not looked up, 1 g_scratch_ptr valid
+
+int scratch_address(int dev, char **out) {
+  if (g_scratch_state[dev].load(std::memory_order_acquire) == 0) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_scratch_state[dev].load(std::memory_order_relaxed) == 0) {
+      void *p = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return device_error(e);
+      if (p == nullptr || ((uintptr_t)p & 255u) != 0) return DITNORM_DEVICE_ERROR;
+      g_scratch_ptr[dev] = p;
+      g_scratch_state[dev].store(1, std::memory_order_release);
+    }
+  }
+  *out = (char *)g_scratch_ptr[dev];
   return DITNORM_OK;
 }
 
@@ -236,10 +265,12 @@ int validate_epilogue(const void *x, const float *bias, const void *h, const voi
   return aliasing_ok(in, o, alias) ? DITNORM_OK : DITNORM_UNSUPPORTED;
 }
 
+// lib_scratch: the call uses the library's scratch array (ws, ws_bytes are
+// ignored), which the partial sums must fit.
 int validate_backward(const void *x, const void *scale, const void *d_out, const void *d_x,
                       const float *d_scale, const float *d_shift, int64_t rows, int64_t cols,
                       int64_t rpb, int64_t mbs, float eps, const void *ws, int64_t ws_bytes,
-                      const float *mean_out, const float *rstd_out) {
+                      const float *mean_out, const float *rstd_out, bool lib_scratch = false) {
   int st = check_rows(rows, cols, rpb, mbs, eps);
   if (st != DITNORM_OK || rows == 0) return st;
   if (cols > DITNORM_MAX_BACKWARD_COLS) return DITNORM_UNSUPPORTED;
@@ -248,7 +279,12 @@ int validate_backward(const void *x, const void *scale, const void *d_out, const
   // one wavefront per row slot of the fused kernel's workgroups
   if ((rows / rpb) * L.chunks * L.rows_per_chunk > DITNORM_MAX_ROWS) return DITNORM_UNSUPPORTED;
   const int64_t need = L.bytes;
-  if (need > 0 && (!ws || ws_bytes < need)) return DITNORM_INVALID_ARGUMENT;
+  if (lib_scratch) {
+    ws = nullptr;  // a static array: it cannot overlap the caller's buffers
+    ws_bytes = 0;
+  } else if (need > 0 && (!ws || ws_bytes < need)) {
+    return DITNORM_INVALID_ARGUMENT;
+  }
   if (!aligned16(x) || !aligned16(scale) || !aligned16(d_out) || !aligned16(d_x) ||
       !aligned16(d_scale) || !aligned16(d_shift) || ((uintptr_t)ws & 255u) != 0 ||
       !aligned4(mean_out) || !aligned4(rstd_out))
@@ -258,7 +294,33 @@ int validate_backward(const void *x, const void *scale, const void *d_out, const
   const Buf o[] = {{d_x, act}, {d_scale, nb * cols * 4}, {d_shift, nb * cols * 4},
                    {ws, need}, {mean_out, rows * 4}, {rstd_out, rows * 4}};
   const int alias[] = {-1, -1, -1, -1, -1, -1};
-  return aliasing_ok(in, o, alias) ? DITNORM_OK : DITNORM_UNSUPPORTED;
+  if (!aliasing_ok(in, o, alias)) return DITNORM_UNSUPPORTED;
+  if (lib_scratch && need > DITNORM_NOALLOC_SCRATCH_BYTES) return DITNORM_SCRATCH_EXCEEDED;
+  return DITNORM_OK;
+}
+
+// The backward on validated arguments, its partial sums in `ws`.
+int backward_launch(const void *x, const void *scale, const void *d_out, void *d_x,
+                    float *d_scale, float *d_shift, int64_t rows, int64_t cols, int64_t rpb,
+                    int64_t mbs, float eps, char *ws, float *mean_out, float *rstd_out,
+                    void *stream) {
+  const BwdLayout L = bwd_layout(rows, cols, rpb);
+  BwdArgs a{};
+  a.x = (const uint16_t *)x;
+  a.scale = (const uint16_t *)scale;
+  a.d_out = (const uint16_t *)d_out;
+  a.d_x = (uint16_t *)d_x;
+  a.d_scale = d_scale;
+  a.d_shift = d_shift;
+  a.mean_out = mean_out;
+  a.rstd_out = rstd_out;
+  a.rows = rows;
+  a.rows_per_batch = rpb;
+  a.mod_stride = mbs;
+  a.cols = (int32_t)cols;
+  a.eps = eps;
+  return finish(launch_backward(a, L, (float *)(ws + L.part0_off), (float *)(ws + L.part1_off),
+                                (hipStream_t)stream));
 }
 
 int validate_elementwise(int op, const void *a, const void *b, const void *m0, const void *m1,
@@ -311,6 +373,7 @@ const char *ditnorm_status_string(int status) {
     case DITNORM_INVALID_ARGUMENT: return "DITNORM_INVALID_ARGUMENT";
     case DITNORM_UNSUPPORTED: return "DITNORM_UNSUPPORTED";
     case DITNORM_DEVICE_ERROR: return "DITNORM_DEVICE_ERROR";
+    case DITNORM_SCRATCH_EXCEEDED: return "DITNORM_SCRATCH_EXCEEDED";
     default: return "DITNORM_UNKNOWN_STATUS";
   }
 }
@@ -573,24 +636,23 @@ int ln_modulate_backward(const void *x, const void *scale, const void *d_out, vo
   if (st != DITNORM_OK || rows == 0) return st;
   DeviceInfo dev;
   if ((st = current_device(&dev)) != DITNORM_OK) return st;
-  const BwdLayout L = bwd_layout(rows, cols, rows_per_batch);
-  char *ws = (char *)workspace;
-  BwdArgs a{};
-  a.x = (const uint16_t *)x;
-  a.scale = (const uint16_t *)scale;
-  a.d_out = (const uint16_t *)d_out;
-  a.d_x = (uint16_t *)d_x;
-  a.d_scale = d_scale;
-  a.d_shift = d_shift;
-  a.mean_out = mean_out;
-  a.rstd_out = rstd_out;
-  a.rows = rows;
-  a.rows_per_batch = rows_per_batch;
-  a.mod_stride = mod_batch_stride;
-  a.cols = (int32_t)cols;
-  a.eps = eps;
-  return finish(launch_backward(a, L, (float *)(ws + L.part0_off), (float *)(ws + L.part1_off),
-                                (hipStream_t)stream));
+  return backward_launch(x, scale, d_out, d_x, d_scale, d_shift, rows, cols, rows_per_batch,
+                         mod_batch_stride, eps, (char *)workspace, mean_out, rstd_out, stream);
+}
+
+int ln_modulate_backward_noalloc(const void *x, const void *scale, const void *d_out, void *d_x,
+                                 float *d_scale, float *d_shift, int64_t rows, int64_t cols,
+                                 int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
+                                 float *mean_out, float *rstd_out, void *stream) {
+  int st = validate_backward(x, scale, d_out, d_x, d_scale, d_shift, rows, cols, rows_per_batch,
+                             mod_batch_stride, eps, nullptr, 0, mean_out, rstd_out, true);
+  if (st != DITNORM_OK || rows == 0) return st;
+  DeviceInfo dev;
+  if ((st = current_device(&dev)) != DITNORM_OK) return st;
+  char *ws = nullptr;
+  if ((st = scratch_address(dev.device, &ws)) != DITNORM_OK) return st;
+  return backward_launch(x, scale, d_out, d_x, d_scale, d_shift, rows, cols, rows_per_batch,
+                         mod_batch_stride, eps, ws, mean_out, rstd_out, stream);
 }
 
 int ln_modulate_backward_supported(const void *x, const void *scale, const void *d_out,

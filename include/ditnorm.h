@@ -39,6 +39,9 @@
  *       allowed.
  *   DITNORM_DEVICE_ERROR (3): the current device is not gfx950, or a HIP call
  *       or kernel launch failed (ditnorm_last_hip_error() keeps the code).
+ *   DITNORM_SCRATCH_EXCEEDED (4): ln_modulate_backward_noalloc only: the call
+ *       needs more partial-sum memory than the library's fixed scratch array
+ *       holds (DITNORM_NOALLOC_SCRATCH_BYTES).
  *   All argument checks run on the host before any HIP call; a call that
  *   fails them has no effect.  rows == 0 is a valid no-op.  No exception
  *   crosses the ABI and nothing falls back to another implementation.
@@ -61,7 +64,9 @@
  *
  * Thread safety.  Entry points may be called concurrently from several host
  *   threads; the library keeps only per-device read-only state and the last
- *   HIP error code (thread-local).
+ *   HIP error code (thread-local).  The one exception is
+ *   ln_modulate_backward_noalloc, whose calls on one device share that
+ *   device's scratch array (see there).
  */
 #ifndef DITNORM_H
 #define DITNORM_H
@@ -76,6 +81,7 @@ extern "C" {
 #define DITNORM_INVALID_ARGUMENT 1
 #define DITNORM_UNSUPPORTED 2
 #define DITNORM_DEVICE_ERROR 3
+#define DITNORM_SCRATCH_EXCEEDED 4
 
 /* Storage types of the standalone elementwise entry points. */
 #define DITNORM_DTYPE_BF16 0
@@ -87,6 +93,9 @@ extern "C" {
 #define DITNORM_MAX_CHANNELS 4096
 /* Largest row width of ln_modulate_backward. */
 #define DITNORM_MAX_BACKWARD_COLS 4096
+/* Bytes of the per-device scratch array of ln_modulate_backward_noalloc
+ * (32 MiB). */
+#define DITNORM_NOALLOC_SCRATCH_BYTES 33554432LL
 /* Most rows of one call (a row has up to one 64-lane wavefront, so at this
  * limit a launch of 4-row workgroups holds 2^31 work-items, within the 32-bit
  * grid size; every kernel indexes in 64 bits), and most 16-byte vectors in
@@ -314,6 +323,35 @@ int ln_modulate_backward(const void *x, const void *scale, const void *d_out, vo
                          int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
                          void *workspace, int64_t workspace_bytes, float *mean_out,
                          float *rstd_out, void *stream);
+
+/*
+ * ln_modulate_backward_noalloc -- ln_modulate_backward without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, results, kernels and launches as ln_modulate_backward,
+ * bitwise the same outputs; the partial tree sums go to a scratch array of
+ * DITNORM_NOALLOC_SCRATCH_BYTES that the library holds on every device it
+ * runs on (loaded with the library, kept until the process ends).  The call
+ * makes no allocation of any kind (no hipMalloc, no hipFree).  A call whose
+ * ln_modulate_backward_workspace_bytes(rows, cols, rows_per_batch) exceeds
+ * DITNORM_NOALLOC_SCRATCH_BYTES returns DITNORM_SCRATCH_EXCEEDED and enqueues
+ * nothing.  The partial sums take about one byte per element of x when the
+ * kernel runs 8 tokens per workgroup and two when it runs 4 (see
+ * ln_modulate_backward), nothing for batches of at most 8 tokens (4 over 3072
+ * columns): 6889 tokens of 3072 columns need 21.4 MB.  The scratch needs no
+ * clearing between calls: every
+ * value a call reads there was written earlier in the same call.  Calls on
+ * one device share its array: two calls whose work overlaps in time on one
+ * device (different streams, or host threads racing on one stream's order)
+ * race on it and give wrong results; order them on one stream or with
+ * events.  The first call on a device looks the array's address up there
+ * (hipGetSymbolAddress; DITNORM_DEVICE_ERROR if that fails).
+ */
+int ln_modulate_backward_noalloc(const void *x, const void *scale, const void *d_out, void *d_x,
+                                 float *d_scale, float *d_shift, int64_t rows, int64_t cols,
+                                 int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
+                                 float *mean_out, float *rstd_out, void *stream);
 
 /* Workspace bytes ln_modulate_backward needs (0 for rows == 0; -1 for invalid
  * sizes and for rows above DITNORM_MAX_ROWS or cols above

@@ -53,6 +53,7 @@ def test_status_strings(lib):
     assert lib.ditnorm_status_string(1) == b"DITNORM_INVALID_ARGUMENT"
     assert lib.ditnorm_status_string(2) == b"DITNORM_UNSUPPORTED"
     assert lib.ditnorm_status_string(3) == b"DITNORM_DEVICE_ERROR"
+    assert lib.ditnorm_status_string(4) == b"DITNORM_SCRATCH_EXCEEDED"
     assert lib.ditnorm_status_string(99) == b"DITNORM_UNKNOWN_STATUS"
     assert lib.ditnorm_version() >= 100
 
@@ -200,6 +201,21 @@ def test_other_entry_validation(lib):
     assert bw3(3 * (MR // 4) + 3) == dn.UNSUPPORTED    # 3-token batches take 4 row slots each
     assert lib.ln_modulate_backward_supported(A, B, C, D, E, E + 0x20000000, 3 * (MR // 4), 8,
                                               3, 8, 1e-6, None, 0, None, None) == 1
+    # the no-allocation backward: the same checks, then the partial sums must
+    # fit the library's scratch array (refused before any HIP call)
+    na = lambda **k: lib.ln_modulate_backward_noalloc(
+        k.get("x", A), k.get("sc", B), k.get("do", C), k.get("dx", D), k.get("ds", E),
+        k.get("dh", E + 0x100000), k.get("rows", 64), k.get("cols", 3072), k.get("rpb", 64),
+        k.get("mbs", 3072), 1e-6, None, None, None)
+    assert na(do=None) == dn.INVALID_ARGUMENT
+    assert na(dx=C) == dn.UNSUPPORTED
+    assert na(cols=4104, mbs=4104) == dn.UNSUPPORTED
+    assert na(rows=0) == dn.OK
+    big = 12000  # 12000 tokens of 3072 columns: 36.9 MB of partial sums
+    assert dn.ln_modulate_backward_workspace_bytes(big, 3072, big) > dn.NOALLOC_SCRATCH_BYTES
+    assert na(rows=big, rpb=big, dh=E + 0x1000000) == dn.SCRATCH_EXCEEDED
+    assert na(rows=big, rpb=big, dh=E + 0x1000000, mbs=3000) == dn.INVALID_ARGUMENT
+    assert dn.ln_modulate_backward_workspace_bytes(6889, 3072, 6889) <= dn.NOALLOC_SCRATCH_BYTES
     assert lib.ditnorm_copy(A, B, 15, None) == dn.UNSUPPORTED
     assert lib.ditnorm_copy(A, A + 16, 64, None) == dn.UNSUPPORTED
 
