@@ -40,10 +40,8 @@
  *  - Weighted RMSNorm ("ERNIE-Image bit-exact fused RMSNorm+scale/shift",
  *    section "What rounding-faithful means here"): mean of squares over the
  *    H columns (no mean subtraction), rstd = 1/sqrt(ms + eps) in fp32, and one
- *    rounding of the product x * rstd * w evaluated left to right.  That
- *    order is a reading no independent pin fixes: parity unpinned for the
- *    last bit of the RMS normalise order ((x * rstd) * w against
- *    x * (rstd * w), which differ on rare elements).
+ *    rounding of the product x * rstd * w evaluated left to right in binary32
+ *    ((x * rstd) * w; x * (rstd * w) differs on rare elements).
  *
  *  - fp16 storage of the standalone modulate and residual-gate add (FLUX.1
  *    page, Commit 2: bf16 and fp16): the same binary32 operations, each
