@@ -47,10 +47,10 @@ def _ln_gpu(dn, x, sc, sh, eps, mod_dev=None, debug=True):
 
 def _ln_check(orc, what, x, sc, sh, eps, rpb, out_g, mean_g, rstd_g, y_g, ref=None):
     ref = ref or orc.ln_modulate(x, sc, sh, eps, rows_per_batch=rpb)
-    differ = check_stats(mean_g, rstd_g, ref["mean"], ref["rstd"], what)
+    check_stats(mean_g, rstd_g, ref["mean"], ref["rstd"], what)
     assert same_bits(y_g, orc.ln_normalize(x, mean_g, rstd_g)), f"{what}: y stage"
     assert same_bits(out_g, orc.modulate(y_g, sc, sh, rows_per_batch=rpb)), f"{what}: modulate stage"
-    check_rows_end_to_end(out_g, ref["out"], np.repeat(differ[:, None], x.shape[1], 1), what)
+    check_rows_end_to_end(out_g, ref["out"], what)
     return ref
 
 
@@ -132,8 +132,8 @@ def test_ln_modulate_folded(gpu, orc, rows, cols, B):
     assert same_bits(out, fast), "statistics outputs changed the result"
     sc = np.concatenate([emb.ravel()[cols:], np.zeros(cols, np.uint16)]).reshape(B, 6 * cols)
     ref = orc.ln_modulate_folded(x, sc, emb, 1e-6, rows_per_batch=rows // B)
-    differ = check_stats(mean, rstd, ref["mean"], ref["rstd"], "folded")
-    check_rows_end_to_end(out, ref["out"], np.repeat(differ[:, None], cols, 1), "folded")
+    check_stats(mean, rstd, ref["mean"], ref["rstd"], "folded")
+    check_rows_end_to_end(out, ref["out"], "folded")
 
 
 def test_gated_ln_modulate_shapes(gpu, orc):
@@ -189,10 +189,10 @@ def _rms_run_check(gpu, orc, what, x, w, sc, sh, eps, rpb, res=None, gate=None, 
         h = host(h)
         assert same_bits(h, ref["h"]), f"{what}: gate stage"
         src = h
-    differ = check_stats(None, rstd, None, ref["rstd"], what)
+    check_stats(None, rstd, None, ref["rstd"], what)
     assert same_bits(y, orc.rms_normalize(src, rstd, w)), f"{what}: y stage"
     assert same_bits(out, orc.modulate(y, sc, sh, rows_per_batch=rpb)), f"{what}: modulate stage"
-    check_rows_end_to_end(out, ref["out"], np.repeat(differ[:, None], cols, 1), what)
+    check_rows_end_to_end(out, ref["out"], what)
     assert np.all(ulp_diff(out, ref["out"]) <= 1), f"{what}: beyond 1 ulp"
 
 
@@ -225,12 +225,11 @@ def _qk_run_check(gpu, orc, what, q, k, eps):
     kk = k if k is not None else np.zeros((0, 128), np.uint16)
     ref = orc.qk_layernorm(q, kk, eps)
     mean, rstd = host(mean), host(rstd)
-    differ = check_stats(mean, rstd, ref["mean"], ref["rstd"], what)
+    check_stats(mean, rstd, ref["mean"], ref["rstd"], what)
     both = np.concatenate([q, kk])
     got = np.concatenate([qo, ko])
     assert same_bits(got, orc.ln_normalize(both, mean, rstd)), f"{what}: normalise stage"
-    check_rows_end_to_end(got, np.concatenate([ref["q_out"], ref["k_out"]]),
-                          np.repeat(differ[:, None], 128, 1), what)
+    check_rows_end_to_end(got, np.concatenate([ref["q_out"], ref["k_out"]]), what)
 
 
 @pytest.mark.parametrize("rq,rk", [(1, 0), (4, 4), (3, 5), (17, 1), (4360 * 32, 4360 * 32),
@@ -277,6 +276,29 @@ def test_rmsnorm_silu_bias_shapes(gpu, orc, rows, c, bias):
     b = gen.normal((c,), 0, 0.05, 92, "f32").numpy() if bias else None
     g = gen.normal((c,), 1, 0.05, 93, "f32_bf16vals").numpy()
     _wan_run_check(gpu, orc, f"wan {rows}x{c}", x, b, g, 1e-6)
+
+
+@pytest.mark.parametrize("rows,c", [(16 * 1000 + 5, 96), (37, 96), (4 * 777 + 3, 384), (1, 384),
+                                    (2 * 4160 + 1, 96)])
+def test_rmsnorm_silu_bias_fold_equals_prebiased_input(gpu, rows, c):
+    """Wan VAE page ("[Diffusion] Fuse the Wan VAE conv bias epilogue and tile
+    the RMSNorm+SiLU kernel"), Tests / docs: the conv bias folded into the
+    kernel equals the kernel run on the pre-biased tensor, bit for bit.  The
+    pre-biased tensor is made the eager way, torch's add_ of the bias cast to
+    bf16; ragged pixel counts leave partial pixel groups."""
+    log(f"wan bias fold rows={rows} C={c}")
+    x = gen.normal((rows, c), 0, 1, 3100 + c).cuda()
+    b = gen.normal((c,), 0, 0.05, 3101, "f32").cuda()
+    g = gen.normal((c,), 1, 0.05, 3102, "f32_bf16vals").cuda()
+    r1, r2 = empty_f32(rows), empty_f32(rows)
+    xb = torch.empty_like(x)
+    folded = gpu.rmsnorm_silu_bias(x, g, b, 1e-6, rstd_out=r1, xb_out=xb)
+    pre = x.clone().add_(b.to(torch.bfloat16))
+    plain = gpu.rmsnorm_silu_bias(pre, g, None, 1e-6, rstd_out=r2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(xb), host(pre)), "bias stage differs from add_"
+    assert np.array_equal(host(r1).view(np.uint32), host(r2).view(np.uint32)), "rstd"
+    assert np.array_equal(host(folded), host(plain)), "folded bias differs from the pre-biased input"
 
 
 def test_rmsnorm_silu_extreme_t(gpu, orc):
@@ -346,8 +368,8 @@ def test_full_workload(gpu, orc, key):
             torch.cuda.synchronize()
             ref = by_row_chunks(lambda lo, hi: orc.ln_modulate_folded(x[lo:hi], sc, sh, l.eps),
                                 None, rows)
-            differ = check_stats(host(mean), host(rstd), ref["mean"], ref["rstd"], l.name)
-            check_rows_end_to_end(out, ref["out"], np.repeat(differ[:, None], x.shape[1], 1), l.name)
+            check_stats(host(mean), host(rstd), ref["mean"], ref["rstd"], l.name)
+            check_rows_end_to_end(out, ref["out"], l.name)
         elif l.entry == "gated_ln_modulate":
             upd, res, gate, sc, sh = (t[n] for n in ("update", "residual", "gate", "scale", "shift"))
             rows, cols = upd.shape
@@ -401,12 +423,11 @@ def test_full_workload(gpu, orc, key):
                                                              mean_out=mean, rstd_out=rstd)
             torch.cuda.synchronize()
             ref = orc.ln_modulate_backward(x, sc, dout, l.eps, rows_per_batch=rpb)
-            differ = check_stats(host(mean), host(rstd), ref["mean"], ref["rstd"], l.name)
+            check_stats(host(mean), host(rstd), ref["mean"], ref["rstd"], l.name)
             d = ulp_diff(host(d_x), ref["d_x"])
             assert d.max() <= 1 and (d == 0).mean() >= 0.9999, l.name
-            if not differ.any():
-                assert np.array_equal(host(d_scale), ref["d_scale"]), l.name
-                assert np.array_equal(host(d_shift), ref["d_shift"]), l.name
+            assert np.array_equal(host(d_shift), ref["d_shift"]), l.name
+            assert np.array_equal(host(d_scale), ref["d_scale"]), l.name
         else:
             raise KeyError(l.entry)
 

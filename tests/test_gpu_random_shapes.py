@@ -73,10 +73,10 @@ def test_random_pixels_and_heads(gpu, orc, i, c, pixels, bias, rq, rk):
     qo, ko = gpu.qk_layernorm(dev(q), dev(k) if rk else None, 1e-5, mean_out=mean, rstd_out=rs)
     torch.cuda.synchronize()
     qref = orc.qk_layernorm(q, k if rk else np.zeros((0, 128), np.uint16), 1e-5)
-    differ = check_stats(host(mean), host(rs), qref["mean"], qref["rstd"], "qk")
+    check_stats(host(mean), host(rs), qref["mean"], qref["rstd"], "qk")
     got = np.concatenate([host(qo)] + ([host(ko)] if rk else []))
     want = np.concatenate([qref["q_out"]] + ([qref["k_out"]] if rk else []))
-    check_rows_end_to_end(got, want, np.repeat(differ[:, None], 128, 1), "qk")
+    check_rows_end_to_end(got, want, "qk")
 
 
 def _mod(B, cols, extra, seed):
@@ -100,8 +100,8 @@ def test_random_shape(gpu, orc, i, B, S, cols, extra):
         torch.cuda.synchronize()
         ref = (orc.ln_modulate if kind == "ln" else orc.ln_modulate_folded)(
             x, sc, sh, 1e-6, rows_per_batch=S)
-        differ = check_stats(host(mean), host(rstd), ref["mean"], ref["rstd"], kind)
-        check_rows_end_to_end(out, ref["out"], np.repeat(differ[:, None], cols, 1), kind)
+        check_stats(host(mean), host(rstd), ref["mean"], ref["rstd"], kind)
+        check_rows_end_to_end(out, ref["out"], kind)
     elif kind == "gated":
         res = rand((rows, cols), 0, 1, 1000 + i)
         _, gd, g = _mod(B, cols, extra, 1100 + i)
@@ -110,8 +110,8 @@ def test_random_shape(gpu, orc, i, B, S, cols, extra):
         torch.cuda.synchronize()
         ref = orc.gated_ln_modulate(x, res, g, sc, sh, 1e-6, rows_per_batch=S)
         assert same_bits(host(h), ref["h"])
-        differ = check_stats(host(mean), host(rstd), ref["mean"], ref["rstd"], kind)
-        check_rows_end_to_end(host(out), ref["out"], np.repeat(differ[:, None], cols, 1), kind)
+        check_stats(host(mean), host(rstd), ref["mean"], ref["rstd"], kind)
+        check_rows_end_to_end(host(out), ref["out"], kind)
     elif kind in ("rms", "gated_rms"):
         w = rand((cols,), 1, 0.05, 1200 + i)
         kw, res, g = {}, None, None
@@ -126,8 +126,8 @@ def test_random_shape(gpu, orc, i, B, S, cols, extra):
         if kind == "gated_rms":
             h, out = r
             assert same_bits(host(h), ref["h"])
-        differ = check_stats(None, host(rstd), None, ref["rstd"], kind)
-        check_rows_end_to_end(host(out), ref["out"], np.repeat(differ[:, None], cols, 1), kind)
+        check_stats(None, host(rstd), None, ref["rstd"], kind)
+        check_rows_end_to_end(host(out), ref["out"], kind)
     else:
         if cols > 4096:
             pytest.skip("the backward serves rows up to 4096 columns")
@@ -136,9 +136,8 @@ def test_random_shape(gpu, orc, i, B, S, cols, extra):
                                                          mean_out=mean, rstd_out=rstd)
         torch.cuda.synchronize()
         ref = orc.ln_modulate_backward(x, sc, dout, 1e-6, rows_per_batch=S)
-        differ = check_stats(host(mean), host(rstd), ref["mean"], ref["rstd"], kind)
+        check_stats(host(mean), host(rstd), ref["mean"], ref["rstd"], kind)
         d = ulp_diff(host(d_x), ref["d_x"])
         assert d.max() <= 1 and (d == 0).mean() >= 0.9999
-        if not differ.any():
-            assert np.array_equal(host(d_scale), ref["d_scale"])
-            assert np.array_equal(host(d_shift), ref["d_shift"])
+        assert np.array_equal(host(d_shift), ref["d_shift"])
+        assert np.array_equal(host(d_scale), ref["d_scale"])
