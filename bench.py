@@ -4,16 +4,16 @@
 
 A step is one pass of the hot path over the FLUX.1-like adaLN workload
 (1, 4608, 3072): the plain LayerNorm + modulate site and the gated-residual
-site, two launches through the C ABI.  W untimed steps, then K timed steps
-bracketed by torch.cuda.synchronize().  The default W = 2000 (~65 ms of GPU
-work) is what the GPU needs to settle: in a fresh process the first ~60 ms of
-back-to-back launches run up to 7% slower (the gated launch measured
-21.5 us after 20 warmup steps, 20.4 after 200, 20.1 after 2000 and in every
-later loop).  Inputs are resident in HBM and rotate
-over enough independent buffer sets (>= 1 GiB for every launch) that no
-launch finds its data in the 256 MB Infinity Cache.  Each launch kind runs as
-a burst between HIP events on the stream it runs on, which gives each
-kernel's average duration.
+site, two launches through the C ABI.  At least W untimed steps run first,
+and at least WARMUP_FLOOR_MS of them in wall time whatever W is: in a fresh
+process the first ~60 ms of back-to-back launches run up to 7% slower (the
+gated launch measured 21.5 us after 20 warm-up steps, 20.4 after 200, 20.1
+after 2000 and in every later loop).  Then K timed steps, bracketed by
+torch.cuda.synchronize(), timed by HIP events recorded on the stream the
+launches go to.  Inputs are resident in HBM and rotate over enough
+independent buffer sets (>= 1 GiB for every launch) that no launch finds its
+data in the 256 MB Infinity Cache.  Each launch kind runs as a burst between
+HIP events, which gives each kernel's average duration.
 
 Prints ONE JSON line: the step's throughput (algorithmic GB/s = bytes every
 launch must move / time), the roofline of the dominant kernel, the CPU oracle
@@ -40,6 +40,7 @@ from dit_adaln_row_amd import inputs as gen  # noqa: E402
 from dit_adaln_row_amd.workloads import HEADLINE, WORKLOADS  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
+WARMUP_FLOOR_MS = 200.0         # least wall time of warm-up steps before the timed loop
 ROTATE_BYTES = 1 << 30          # >= 4x the 256 MB Infinity Cache
 METRIC = "achieved HBM GB/s (% of MI355X peak) and rows/s per fused norm+modulate kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -141,27 +142,38 @@ def check_status(st, what):
 # GPU timing
 # ---------------------------------------------------------------------------
 
-def time_step_loop(calls_per_set, steps, warmup):
+def time_step_loop(calls_per_set, steps, warmup, floor_ms=WARMUP_FLOOR_MS):
     """calls_per_set[s] = [(fn, args, name), ...]: the launches of one step on
-    rotation set s.  Runs `warmup` untimed steps, then `steps` timed steps.
-    Inside the timed region each launch kind runs as one back-to-back burst
-    (the K plain launches, then the K gated launches, every launch on its own
-    rotating buffer set), with a HIP event on the launch stream between
-    bursts: a kind's average launch duration is its burst interval / K, which
-    is what rocprofv3 reports as the kernel's average duration.  Returns
-    (wall seconds for the `steps` steps, {name: average ms per launch})."""
+    rotation set s.  Runs at least `warmup` untimed steps and at least
+    `floor_ms` of them in wall time, then `steps` timed steps.  Inside the
+    timed region each launch kind runs as one back-to-back burst (the K plain
+    launches, then the K gated launches, every launch on its own rotating
+    buffer set), with a HIP event on the launch stream before, between and
+    after the bursts: the step time is the first-to-last event interval / K,
+    and a kind's average launch duration is its burst interval / K, which is
+    what rocprofv3 reports as the kernel's average duration.  Returns a dict:
+    seconds (event time of the K steps), wall_seconds (host clock between the
+    two synchronisations), per ({name: average ms per launch}), warmup_steps
+    and warmup_ms (what the warm-up ran)."""
     nsets = len(calls_per_set)
     names = [c[2] for c in calls_per_set[0]]
-    for i in range(warmup):
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or (time.perf_counter() - t0) * 1e3 < floor_ms:
         for fn, args, name in calls_per_set[i % nsets]:
             check_status(fn(*args), name)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()  # the wall clock then follows the GPU's work
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t0) * 1e3
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record()
     for j, name in enumerate(names):
-        for i in range(steps):
-            fn, args, _ = calls_per_set[(warmup + i) % nsets][j]
+        for k in range(steps):
+            fn, args, _ = calls_per_set[(i + k) % nsets][j]
             st = fn(*args)
             if st != 0:
                 check_status(st, name)
@@ -169,7 +181,8 @@ def time_step_loop(calls_per_set, steps, warmup):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     per = {n: ev[j].elapsed_time(ev[j + 1]) / steps for j, n in enumerate(names)}
-    return t1 - t0, per
+    return {"seconds": ev[0].elapsed_time(ev[-1]) * 1e-3, "wall_seconds": t1 - t0, "per": per,
+            "warmup_steps": i, "warmup_ms": warm_ms}
 
 
 def time_kernel(calls, iters=100, reps=5, warmup=20, warm_ms=50.0):
@@ -227,14 +240,48 @@ def traffic_for(workload, launch):
 # CPU baseline: the oracle on this host's cores
 # ---------------------------------------------------------------------------
 
-def _cpu_model():
+def _cpu_info():
+    """The host CPU as /proc/cpuinfo names it (first processor's entries)."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            k, _, v = line.partition(":")
+            k, v = k.strip(), v.strip()
+            if k in ("model name", "vendor_id", "cpu family", "model", "stepping",
+                     "cache size") and k not in info:
+                info[k] = v
     except OSError:
         pass
-    return "unknown"
+    return info
+
+
+def _cpu_model():
+    i = _cpu_info()
+    name = i.get("model name", "unknown")
+    ids = ", ".join(f"{k} {i[k]}" for k in ("cpu family", "model", "stepping") if k in i)
+    return f"{name} ({i.get('vendor_id', '?')}; {ids}; cache {i.get('cache size', '?')})"
+
+
+def _cpu_quota():
+    """The cgroup's CPU quota in CPUs (cgroup v2 cpu.max), or None."""
+    try:
+        q, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        return None if q == "max" else round(int(q) / int(period), 2)
+    except (OSError, ValueError):
+        return None
+
+
+def host_threads():
+    """(threads for the CPU legs, CPUs this process may run on).  Every CPU in
+    the process's affinity mask, but no more than the CPU share a job here is
+    given when one is set (OMP_NUM_THREADS), so that the threads do not
+    oversubscribe the share."""
+    aff = len(os.sched_getaffinity(0))
+    n = aff
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n), aff
 
 
 def _oracle_call(oracle, l, t, lo, hi):
@@ -300,54 +347,68 @@ def _host_tensors(w, cap=None):
     return out
 
 
-def cpu_baseline(w, min_seconds=10.0, single_seconds=3.0):
+def cpu_baseline(w, runs=5, run_seconds=2.5, single_runs=3, single_seconds=1.0):
     """The oracle on the host's cores: the whole headline step, rows split
-    over threads, repeated for about min_seconds; and single-threaded on a
-    row sample for about single_seconds."""
+    over threads, repeated for about run_seconds per run, median of `runs`
+    runs; and single-threaded on a row sample (the first 1/8 of each launch's
+    rows), median of `single_runs` runs of about single_seconds."""
     import concurrent.futures as cf
+    import statistics
 
     import oracle
     oracle.build()
     _keep_freed_memory()
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads, affinity = host_threads()
     t = _host_tensors(w)
 
     def chunks(rows):
         step = -(-rows // (threads * 4))
         return [(lo, min(rows, lo + step)) for lo in range(0, rows, step)]
 
-    reps = 0
+    rates, row_rates, total_reps, total_s = [], [], 0, 0.0
     with cf.ThreadPoolExecutor(threads) as ex:
+        for _ in range(runs):
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                for l in w.launches:
+                    list(ex.map(lambda b, l=l: _oracle_call(oracle, l, t, b[0], b[1]),
+                                chunks(l.rows)))
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= run_seconds or reps >= 5000:
+                    break
+            rates.append(w.algorithmic_bytes() * reps / el / 1e9)
+            row_rates.append(w.rows() * reps / el)
+            total_reps += reps
+            total_s += el
+    single, single_rows = [], []
+    for _ in range(single_runs):
+        n1, el1, b1, r1 = 0, 0.0, 0, 0
         t0 = time.perf_counter()
-        while True:
+        while el1 < single_seconds and n1 < 5000:
             for l in w.launches:
-                list(ex.map(lambda b, l=l: _oracle_call(oracle, l, t, b[0], b[1]),
-                            chunks(l.rows)))
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= min_seconds or reps >= 5000:
-                break
-    gbps = w.algorithmic_bytes() * reps / el / 1e9
-    # single thread: every launch on its first 1/8 of the rows
-    n1, el1, b1, r1 = 0, 0.0, 0, 0
-    t0 = time.perf_counter()
-    while el1 < single_seconds and n1 < 5000:
-        for l in w.launches:
-            n = max(1, l.rows // 8)
-            _oracle_call(oracle, l, t, 0, n)
-            b1 += l.algorithmic_bytes() * n / l.rows
-            r1 += n
-        n1 += 1
-        el1 = time.perf_counter() - t0
-    return {"value": round(gbps, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+                n = max(1, l.rows // 8)
+                _oracle_call(oracle, l, t, 0, n)
+                b1 += l.algorithmic_bytes() * n / l.rows
+                r1 += n
+            n1 += 1
+            el1 = time.perf_counter() - t0
+        single.append(b1 / el1 / 1e9)
+        single_rows.append(r1 / el1)
+    return {"value": round(statistics.median(rates), 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
             "sample": f"the full {w.key} step ({' + '.join(l.name for l in w.launches)}, "
-                      f"{w.rows()} rows) x {reps} repetitions, {el:.1f} s wall, rows split over "
+                      f"{w.rows()} rows), median of {runs} runs of about {run_seconds} s "
+                      f"({total_reps} repetitions, {total_s:.1f} s in all), rows split over "
                       f"{threads} threads; the oracle is single-threaded C, unchanged",
-            "rows_per_s": round(w.rows() * reps / el, 1),
-            "single_thread": {"value": round(b1 / el1 / 1e9, 3), "unit": "GB/s",
-                              "rows_per_s": round(r1 / el1, 1),
-                              "sample": f"the first 1/8 of each launch's rows x {n1}, "
-                                        f"{el1:.1f} s"},
+            "runs_gbps": [round(r, 3) for r in rates],
+            "rows_per_s": round(statistics.median(row_rates), 1),
+            "threads": threads, "host_cores": affinity, "host_cpus_online": os.cpu_count(),
+            "cpu_quota": _cpu_quota(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "single_thread": {"value": round(statistics.median(single), 3), "unit": "GB/s",
+                              "rows_per_s": round(statistics.median(single_rows), 1),
+                              "sample": f"the first 1/8 of each launch's rows, median of "
+                                        f"{single_runs} runs of about {single_seconds} s"},
             "cpu_model": _cpu_model()}
 
 
@@ -360,7 +421,7 @@ def cpu_oracle_table(seconds=0.5, skip=()):
     import oracle
     oracle.build()
     _keep_freed_memory()
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads, _ = host_threads()
     table = {}
     with cf.ThreadPoolExecutor(threads) as ex:
         for key, w in WORKLOADS.items():
@@ -415,7 +476,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-kernels", action="store_true")
     ap.add_argument("--only", default=None, help="time only this workload's kernels (profiling)")
@@ -460,11 +521,13 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] {len(sets)} rotation sets of {w.algorithmic_bytes() / 1e6:.1f} MB; "
         f"warmup {args.warmup}, steps {args.steps}")
-    wall, per = time_step_loop(calls, args.steps, args.warmup)
-    log("[bench] timed loop done")
+    tl = time_step_loop(calls, args.steps, args.warmup)
+    per = tl["per"]
+    log(f"[bench] timed loop done (warm-up {tl['warmup_steps']} steps, {tl['warmup_ms']:.0f} ms)")
     step_bytes = w.algorithmic_bytes()
-    ms_per_step = wall / args.steps * 1e3
-    value = step_bytes / (wall / args.steps) / 1e9
+    sec = tl["seconds"]
+    ms_per_step = sec / args.steps * 1e3
+    value = step_bytes / (sec / args.steps) / 1e9
 
     kinfo = {}
     for l in w.launches:
@@ -482,6 +545,9 @@ def main():
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "warmup_steps_run": tl["warmup_steps"], "warmup_ms": round(tl["warmup_ms"], 1),
+        "timing": "HIP events on the launch stream around the K timed steps",
+        "wall_ms_per_step": round(tl["wall_seconds"] / args.steps * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "accumulate": "f64 statistics, f32 elementwise ops rounded to bf16 per op",
         "data": "synthetic (seeded, distributions of the workload description)",
@@ -489,7 +555,7 @@ def main():
                    "launches": [l.name for l in w.launches], "rows_per_step": w.rows(),
                    "bytes_per_step": step_bytes, "rotation_sets": len(sets)},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
-        "rows_per_s": round(w.rows() / (wall / args.steps), 1),
+        "rows_per_s": round(w.rows() / (sec / args.steps), 1),
         "per_launch": {n: {"avg_ms": round(v["avg_ms"], 5), "gbps": round(v["gbps"], 1),
                            "pct_peak": round(100 * v["gbps"] / PEAK_HBM_GBPS, 2),
                            "rows_per_s": round(v["rows"] / (v["avg_ms"] * 1e-3), 1)}

@@ -244,5 +244,29 @@ WORKLOADS = {
     ),
 }
 
+
+def _flux_micro(L: int, cfg: int) -> Workload:
+    """The FLUX.1 page's micro-benchmark shapes (1, L, 3072) ("[diffusion] FLUX.1
+    fused adaLN modulate (bit-exact) + RoPE cache hoist, LN-affine folding
+    behind quality=high", Speed Tests): the modulate chain alone, the LayerNorm
+    with the fused modulate (here one lossless launch), and the folded LN."""
+    key = f"flux_1x{L}x3072"
+    return Workload(
+        key, cfg,
+        f"FLUX.1 micro-benchmark shape (1,{L},3072): x ~N(0,1.5), scale/shift (1,3072) "
+        "~N(0,0.1); the modulate chain alone, LN + fused modulate, and the folded LN",
+        (Tensor("x", (L, 3072), 0.0, 1.5), Tensor("scale", (1, 3072), 0.0, 0.1),
+         Tensor("shift", (1, 3072), 0.0, 0.1)),
+        (Launch("modulate_bf16", "modulate_scale_shift", L, 3072, ("x", "scale", "shift"), 0.0,
+                extra={"dtype": "bf16"}),
+         Launch("ln_modulate", "ln_modulate", L, 3072, ("x", "scale", "shift"), 1e-6),
+         Launch("ln_modulate_folded", "ln_modulate_folded", L, 3072, ("x", "scale", "shift"),
+                1e-6)),
+    )
+
+
+WORKLOADS["flux_1x4096x3072"] = _flux_micro(4096, 13)
+WORKLOADS["flux_1x512x3072"] = _flux_micro(512, 14)
+
 # The workload the headline metric is quoted on (FLUX.1-like adaLN).
 HEADLINE = "flux_1x4608x3072"
