@@ -1,9 +1,9 @@
 // Standalone elementwise adaLN stages, for sites whose norm is not fused.
 //
-// modulate_scale_shift (FLUX.1 page, "Commit 2": a fused modulate kernel
-// whose intermediates are rounded back to the storage dtype exactly like the
-// eager chain's kernel boundaries; bf16 and fp16, batched rows, adaLN chunk
-// views):
+// modulate_scale_shift (FLUX.1 page, Commit 2: the modulate in one kernel,
+// each of the eager chain's three results rounded to the storage type where
+// the eager kernels round it; bf16 or fp16 storage, one modulation row per
+// batch, chunked embedding views):
 //     out = rnd(rnd(x * rnd(1 + scale)) + shift)
 // residual_gate_add (GLM-Image page, the ff gate reusing residual_gate_add;
 // ERNIE-Image page, the residual variant):

@@ -241,9 +241,10 @@ int rmsnorm_silu_bias(const void *x, const float *bias, const float *gamma, void
  * conv_bias_epilogue -- the channels_last conv-bias add, optionally fused
  * with the residual add that follows the conv.
  *
- * Wan VAE page (same title), Modifications, "New kernel, lossless": the
- * arithmetic of aten's add_ with an fp32 bias cast to the activation dtype
- * first, and with the residual the two roundings of the eager conv(x) + h:
+ * Wan VAE page (same title), Modifications, the lossless epilogue kernel:
+ * the bias is cast from fp32 to bf16 before it is added, as aten's add_
+ * does, and the residual form rounds twice, once after the bias and once
+ * after adding h, as the eager conv output plus h does:
  *     out = bf16( x + bf16(bias) )                      (h == NULL)
  *     out = bf16( bf16( x + bf16(bias) ) + h )          (h != NULL)
  * x, h, out: bf16 [rows, channels] (channels_last pixels); bias: fp32 [C].
@@ -257,9 +258,10 @@ int conv_bias_epilogue(const void *x, const float *bias, const void *h, void *ou
  * not fused into it.
  *
  * FLUX.1 page ("[diffusion] FLUX.1 fused adaLN modulate (bit-exact) + RoPE
- * cache hoist, LN-affine folding behind quality=high", Commit 2): each
- * intermediate rounded back to the storage dtype exactly like the eager
- * chain's kernel boundaries, bf16 and fp16, batched rows, adaLN chunk views:
+ * cache hoist, LN-affine folding behind quality=high", Commit 2): the three
+ * results of the eager chain each rounded to the storage type where the
+ * eager kernels round them; bf16 or fp16 storage, one modulation row per
+ * batch, chunked embedding views:
  *     out = rnd( rnd( x * rnd(1 + scale) ) + shift )
  * dtype: DITNORM_DTYPE_BF16 or DITNORM_DTYPE_F16 -- x, scale, shift and out
  * all of that type, rnd rounding to it nearest-even.  x, out: [rows, cols];
