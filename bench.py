@@ -477,6 +477,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup-ms", type=float, default=WARMUP_FLOOR_MS,
+                    help="least wall time of the warm-up steps (0 for counter runs, whose "
+                         "every dispatch is serialised)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-kernels", action="store_true")
     ap.add_argument("--only", default=None, help="time only this workload's kernels (profiling)")
@@ -521,7 +524,7 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] {len(sets)} rotation sets of {w.algorithmic_bytes() / 1e6:.1f} MB; "
         f"warmup {args.warmup}, steps {args.steps}")
-    tl = time_step_loop(calls, args.steps, args.warmup)
+    tl = time_step_loop(calls, args.steps, args.warmup, args.warmup_ms)
     per = tl["per"]
     log(f"[bench] timed loop done (warm-up {tl['warmup_steps']} steps, {tl['warmup_ms']:.0f} ms)")
     step_bytes = w.algorithmic_bytes()

@@ -500,11 +500,14 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
 // rows in all) splits every row.  The segments' binary64 moments meet through
 // LDS; the sums are exact, so the statistics carry the same bits either way.  Everything else is the
 // wavefront-per-row kernel's MOD_LDS path (rows of NV * 512 columns).
-template <int NVW, int NV, bool RMS, bool GATED>
+template <int NVW, int NV, bool RMS, bool GATED, int WPB>
 __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, float4 *lds_sh,
-                                            uint4 *lds_sh16, uint4 *lds_w, double (*red)[2],
-                                            int64_t row0, int64_t row, int seg) {
+                                            uint4 *lds_sh16, uint4 *lds_w, float4 *lds_w32,
+                                            double (*red)[2], int64_t row0, int64_t row, int seg) {
   constexpr bool SPLIT = NVW != NV;
+  constexpr int NT = 64 * WPB;
+  // RMS with 8-wavefront workgroups: the shift and the weight staged as fp32
+  constexpr bool F32W = RMS && WPB == 8;
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
   const int cols = a.cols;
@@ -515,12 +518,12 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
   auto col = [&](int k) { return vid(k) * 8; };
 
   // modulation rows of the workgroup's first batch, then this segment
-  constexpr int FILL = (NV * 64 + 255) / 256;
+  constexpr int FILL = (NV * 64 + NT - 1) / NT;
   const int64_t b0 = row0 / a.rows_per_batch;
   uint4 fsc[FILL], fsh[FILL], fw[RMS ? FILL : 1];
 #pragma unroll
   for (int i = 0; i < FILL; ++i) {
-    const int j = threadIdx.x + 256 * i;
+    const int j = threadIdx.x + NT * i;
     const bool in = j < NV * 64;
     fsc[i] = in ? ld16(a.scale + b0 * a.mod_stride + j * 8) : zero;
     fsh[i] = in ? ld16(a.shift + b0 * a.mod_stride + j * 8) : zero;
@@ -536,7 +539,7 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
   const int64_t mo = ((live ? row : row0) / a.rows_per_batch) * a.mod_stride;
 #pragma unroll
   for (int i = 0; i < FILL; ++i) {
-    const int j = threadIdx.x + 256 * i;
+    const int j = threadIdx.x + NT * i;
     if (j >= NV * 64) break;
     float sc[8];
     unpack8(fsc[i], sc);
@@ -548,7 +551,15 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
     }
     lds_s1[mod_slot(j, 0) / 4] = make_float4(sc[0], sc[1], sc[2], sc[3]);
     lds_s1[mod_slot(j, 1) / 4] = make_float4(sc[4], sc[5], sc[6], sc[7]);
-    if constexpr (RMS) {
+    if constexpr (F32W) {
+      float sh[8], wt[8];
+      unpack8(fsh[i], sh);
+      unpack8(fw[i], wt);
+      lds_sh[mod_slot(j, 0) / 4] = make_float4(sh[0], sh[1], sh[2], sh[3]);
+      lds_sh[mod_slot(j, 1) / 4] = make_float4(sh[4], sh[5], sh[6], sh[7]);
+      lds_w32[mod_slot(j, 0) / 4] = make_float4(wt[0], wt[1], wt[2], wt[3]);
+      lds_w32[mod_slot(j, 1) / 4] = make_float4(wt[4], wt[5], wt[6], wt[7]);
+    } else if constexpr (RMS) {
       // shift and weight as bf16, widened where they are used: with the
       // weight staged too, fp32 copies would cost a workgroup of occupancy
       lds_sh16[j] = fsh[i];
@@ -641,7 +652,7 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
         const float4 a0 = lds_s1[mod_slot(j, 0) / 4], a1 = lds_s1[mod_slot(j, 1) / 4];
         s1v[0] = a0.x; s1v[1] = a0.y; s1v[2] = a0.z; s1v[3] = a0.w;
         s1v[4] = a1.x; s1v[5] = a1.y; s1v[6] = a1.z; s1v[7] = a1.w;
-        if constexpr (RMS) {
+        if constexpr (RMS && !F32W) {
           unpack8(lds_sh16[j], shv);
         } else {
           const float4 c0 = lds_sh[mod_slot(j, 0) / 4], c1 = lds_sh[mod_slot(j, 1) / 4];
@@ -660,7 +671,13 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
       }
       if constexpr (RMS) {
         float wt[8];
-        unpack8(lds_w[j], wt);
+        if constexpr (F32W) {
+          const float4 w0 = lds_w32[mod_slot(j, 0) / 4], w1 = lds_w32[mod_slot(j, 1) / 4];
+          wt[0] = w0.x; wt[1] = w0.y; wt[2] = w0.z; wt[3] = w0.w;
+          wt[4] = w1.x; wt[5] = w1.y; wt[6] = w1.z; wt[7] = w1.w;
+        } else {
+          unpack8(lds_w[j], wt);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = (v[e] * rstd_f) * wt[e];
       } else {
@@ -697,23 +714,31 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
   }
 }
 
-template <int NV, bool RMS, bool GATED, int P>
-__global__ __launch_bounds__(256) void row_mixed_kernel(const RowArgs a) {
-  __shared__ float4 lds_s1[NV * 128], lds_sh[RMS ? 1 : NV * 128];
-  __shared__ uint4 lds_sh16[RMS ? NV * 64 : 1], lds_w[RMS ? NV * 64 : 1];
-  __shared__ double red[4][2];
+template <int NV, bool RMS, bool GATED, int P, int WPB = 4, bool REMFIRST = false>
+__global__ __launch_bounds__(64 * WPB) void row_mixed_kernel(const RowArgs a) {
+  constexpr bool F32W = RMS && WPB == 8;
+  __shared__ float4 lds_s1[NV * 128], lds_sh[(RMS && !F32W) ? 1 : NV * 128];
+  __shared__ uint4 lds_sh16[(RMS && !F32W) ? NV * 64 : 1], lds_w[(RMS && !F32W) ? NV * 64 : 1];
+  __shared__ float4 lds_w32[F32W ? NV * 128 : 1];
+  __shared__ double red[WPB][2];
   const int w = wave_id();
-  if ((int64_t)blockIdx.x < a.full_blocks) {
-    const int64_t row0 = (int64_t)blockIdx.x * 4;
-    row_segment<NV, NV, RMS, GATED>(a, lds_s1, lds_sh, lds_sh16, lds_w, red, row0, row0 + w, 0);
-  } else if constexpr (P == 2) {
-    const int64_t row0 = a.full_blocks * 4 + ((int64_t)blockIdx.x - a.full_blocks) * 2;
-    row_segment<NV / 2, NV, RMS, GATED>(a, lds_s1, lds_sh, lds_sh16, lds_w, red, row0,
-                                         row0 + (w >> 1), w & 1);
-  } else {  // a row per workgroup, a quarter per wavefront
-    const int64_t row0 = a.full_blocks * 4 + ((int64_t)blockIdx.x - a.full_blocks);
-    row_segment<NV / 4, NV, RMS, GATED>(a, lds_s1, lds_sh, lds_sh16, lds_w, red, row0, row0,
-                                         w);
+  int64_t g = blockIdx.x;
+  if constexpr (REMFIRST) {  // the remainder's workgroups first in the grid
+    const int64_t nrem = (int64_t)gridDim.x - a.full_blocks;
+    g = g < nrem ? a.full_blocks + g : g - nrem;
+  }
+  if (g < a.full_blocks) {
+    const int64_t row0 = g * WPB;
+    row_segment<NV, NV, RMS, GATED, WPB>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32, red, row0,
+                                         row0 + w, 0);
+  } else if constexpr (P == 2) {  // WPB / 2 rows per workgroup, a half per wavefront
+    const int64_t row0 = a.full_blocks * WPB + (g - a.full_blocks) * (WPB / 2);
+    row_segment<NV / 2, NV, RMS, GATED, WPB>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32, red,
+                                             row0, row0 + (w >> 1), w & 1);
+  } else {  // WPB / 4 rows per workgroup, a quarter per wavefront
+    const int64_t row0 = a.full_blocks * WPB + (g - a.full_blocks) * (WPB / 4);
+    row_segment<NV / 4, NV, RMS, GATED, WPB>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32, red,
+                                             row0, row0 + (w >> 2), w & 3);
   }
 }
 
@@ -723,9 +748,36 @@ __global__ __launch_bounds__(256) void row_mixed_kernel(const RowArgs a) {
 // else every row whole.  A launch of fewer rows than that (no whole round)
 // splits every row the same way, so that it spreads over the SIMDs instead
 // of leaving most of them idle.
-template <int NV>
-static hipError_t launch_mixed(const RowArgs &a0, bool rms, bool gated, const DeviceInfo &dev,
-                               hipStream_t stream) {
+// The remainder's workgroups go first in the grid for the gated forms at
+// 4096 columns with a quarter-round remainder of at least 64 rows.  There four
+// whole-row workgroups fill a compute unit, so a remainder dispatched last
+// waits for free slots and adds its whole latency as a tail; dispatched first,
+// it overlaps the whole rows and only displaces as many of them: gated RMS at
+// 4216 rows 26.10 -> 24.55 us, gated LN 26.16 -> 23.99 us, 4160 rows 25.25 ->
+// 24.79 / 25.60 -> 24.20 us.  With fewer remainder rows (4112, 4128: 1-5%
+// slower), for the plain forms (the displaced whole rows cost more than the
+// tail: up to 5% slower) and at other widths (room for the remainder beside
+// the whole rows) the remainder stays last.
+template <int NV, int WPB, bool R, bool G>
+static void launch_mixed_kind(const RowArgs &a, int P, bool remfirst, dim3 grid,
+                              hipStream_t stream) {
+  constexpr int P4 = NV % 4 == 0 ? 4 : 2;
+  const dim3 block(64 * WPB);
+  if constexpr (NV == 8 && WPB == 4 && G) {
+    if (P == 4 && remfirst) {
+      hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, 4, 4, true>), grid, block, 0, stream, a);
+      return;
+    }
+  }
+  if (P == 4)
+    hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, P4, WPB>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, 2, WPB>), grid, block, 0, stream, a);
+}
+
+template <int NV, int WPB>
+static hipError_t launch_mixed_w(const RowArgs &a0, bool rms, bool gated, const DeviceInfo &dev,
+                                 hipStream_t stream) {
   RowArgs a = a0;
   const int64_t simds = (int64_t)dev.num_cu * 4;
   const int64_t whole = a.rows / simds * simds;
@@ -733,38 +785,52 @@ static hipError_t launch_mixed(const RowArgs &a0, bool rms, bool gated, const De
   int64_t blocks;
   int P = 2;
   if (whole > 0 && rem > 0 && 4 * rem <= simds && NV % 4 == 0) {
-    a.full_blocks = whole / 4;
-    blocks = a.full_blocks + rem;
+    a.full_blocks = whole / WPB;
+    blocks = a.full_blocks + (rem + WPB / 4 - 1) / (WPB / 4);
     P = 4;
   } else if (whole > 0 && rem > 0 && 2 * rem <= simds) {
-    a.full_blocks = whole / 4;
-    blocks = a.full_blocks + (rem + 1) / 2;
+    a.full_blocks = whole / WPB;
+    blocks = a.full_blocks + (rem + WPB / 2 - 1) / (WPB / 2);
   } else if (whole == 0 && 4 * rem <= simds && NV % 4 == 0) {
     a.full_blocks = 0;  // fewer rows than a quarter round: every row in quarters
-    blocks = rem;
+    blocks = (rem + WPB / 4 - 1) / (WPB / 4);
     P = 4;
   } else if (whole == 0 && 2 * rem <= simds) {
     a.full_blocks = 0;  // fewer rows than half a round: every row in halves
-    blocks = (rem + 1) / 2;
+    blocks = (rem + WPB / 2 - 1) / (WPB / 2);
   } else {
-    a.full_blocks = (a.rows + 3) / 4;
+    a.full_blocks = (a.rows + WPB - 1) / WPB;
     blocks = a.full_blocks;
   }
-  const dim3 grid((unsigned)blocks), block(256);
-#define DITNORM_MIXED(R, G)                                                              \
-  do {                                                                                   \
-    if (P == 4)                                                                          \
-      hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, (NV % 4 == 0 ? 4 : 2)>), grid, block, 0, \
-                         stream, a);                                                     \
-    else                                                                                 \
-      hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, 2>), grid, block, 0, stream, a);    \
-  } while (0)
-  if (!rms && !gated) DITNORM_MIXED(false, false);
-  else if (!rms && gated) DITNORM_MIXED(false, true);
-  else if (rms && !gated) DITNORM_MIXED(true, false);
-  else DITNORM_MIXED(true, true);
-#undef DITNORM_MIXED
+  const dim3 grid((unsigned)blocks), block(64 * WPB);
+  const bool remfirst = gated && P == 4 && whole > 0 && rem >= 64;
+  if constexpr (WPB == 8) {  // the plain RMS form only
+    launch_mixed_kind<NV, 8, true, false>(a, P, false, grid, stream);
+  } else {
+    if (!rms && !gated) launch_mixed_kind<NV, 4, false, false>(a, P, remfirst, grid, stream);
+    else if (!rms && gated) launch_mixed_kind<NV, 4, false, true>(a, P, remfirst, grid, stream);
+    else if (rms && !gated) launch_mixed_kind<NV, 4, true, false>(a, P, remfirst, grid, stream);
+    else launch_mixed_kind<NV, 4, true, true>(a, P, remfirst, grid, stream);
+  }
   return hipGetLastError();
+}
+
+// The plain RMS form at 4096 columns with at least four whole rounds (the
+// chip's resident capacity of 4096-column rows) runs in 8-wavefront
+// workgroups, whose 48 KB of fp32 modulation rows and weight spare the two
+// bf16 widenings per element: 4096 rows 13.65 -> 12.61 us, 4216 rows 14.56 ->
+// 14.30 us, 4608 rows 16.14 -> 15.49 us (bitwise the same).  Smaller launches
+// keep 4-wavefront workgroups (1024 rows: 6.60 against 5.84 us, half of the
+// compute units would idle); so do the gated forms, which measured 2-3%
+// slower in 8-wavefront workgroups.
+template <int NV>
+static hipError_t launch_mixed(const RowArgs &a, bool rms, bool gated, const DeviceInfo &dev,
+                               hipStream_t stream) {
+  if constexpr (NV == 8) {
+    if (rms && !gated && a.rows >= 4 * (int64_t)dev.num_cu * 4)
+      return launch_mixed_w<NV, 8>(a, rms, gated, dev, stream);
+  }
+  return launch_mixed_w<NV, 4>(a, rms, gated, dev, stream);
 }
 
 template <int NV, bool FULL>

@@ -472,7 +472,10 @@ def test_row_position_batch_and_chunking_invariance(gpu, orc):
 
 @pytest.mark.parametrize("cols,rows,lo", [(3072, 1024 + 300, 1024),   # halves
                                            (4096, 1024 + 16, 1024),    # quarters
-                                           (2048, 2048 + 200, 2048)])  # quarters
+                                           (2048, 2048 + 200, 2048),   # quarters
+                                           # quarters first in the grid (gated forms),
+                                           # 8-wavefront workgroups (plain RMS)
+                                           (4096, 4096 + 120, 4096)])
 @pytest.mark.parametrize("kind", ["ln", "gated_ln", "rms", "gated_rms"])
 def test_split_rows_equal_whole_rows(gpu, kind, cols, rows, lo):
     """The balanced launch computes the rows past the whole rounds as half or
@@ -709,7 +712,16 @@ SPLIT_CASES = [(3072, 4096 + 512, 4096 + 512), (3072, 1024 + 1, 1025), (4096, 20
                (1024, 4096 + 3, 4099), (2048, 3072 + 511, 3583), (3072, 4096 + 256, 17),
                # quarters
                (4096, 1024 + 120, 1144), (2048, 2048 + 256, 2304), (4096, 1024 + 16, 13),
-               (4096, 4096 + 1, 4097)]
+               (4096, 4096 + 1, 4097),
+               # quarters at 4096 columns: the gated forms' remainder dispatched first
+               # (at least 64 rows), batch boundaries inside its workgroups
+               (4096, 4096 + 120, 17), (4096, 2048 + 256, 9), (4096, 1024 + 255, 1279),
+               (4096, 1024 + 63, 1087),
+               # the plain RMS form in 8-wavefront workgroups (at least four whole
+               # rounds): quarters, halves, every row whole with a partly live last
+               # workgroup, and only whole rounds
+               (4096, 8192 + 100, 12), (4096, 4096 + 300, 7), (4096, 4096 + 700, 11),
+               (4096, 4096, 64)]
 
 
 @pytest.mark.parametrize("cols,rows,rpb", SPLIT_CASES)
