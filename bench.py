@@ -52,7 +52,7 @@ KERNEL_SOURCES = {
     "modulate_scale_shift": "elementwise.hip", "residual_gate_add": "elementwise.hip",
     "ln_modulate_backward": "backward.hip",
 }
-DTYPE_CODES = {"bf16": 0, "f16": 1}
+DTYPE_CODES = {"bf16": 0, "f16": 1, "f32": 2}
 
 
 def log(msg):
@@ -114,7 +114,10 @@ def make_call(lib, launch, t, stream):
                                           None, None, stream), (d_x, d_scale, d_shift, ws)
     if e == "conv_bias_epilogue":          # inputs: x, bias, h
         out = torch.empty_like(a)
-        return lib.conv_bias_epilogue, (_p(a), _p(b), _p(c), _p(out), rows, cols, stream), out
+        dt = DTYPE_CODES[launch.extra.get("dtype", "bf16")]
+        bdt = DTYPE_CODES[launch.extra.get("bias_dtype", "f32")]
+        return lib.conv_bias_epilogue, (_p(a), _p(b), _p(c), _p(out), rows, cols, dt, bdt,
+                                        stream), out
     if e in ("modulate_scale_shift", "residual_gate_add"):
         # modulate: x, scale, shift; gate add: update, residual, gate
         out = torch.empty_like(a)
@@ -305,7 +308,9 @@ def _oracle_call(oracle, l, t, lo, hi):
     if e == "rmsnorm_silu_bias":
         return oracle.rmsnorm_silu_bias(x[lo:hi], t["bias"], t["gamma"], l.eps)
     if e == "conv_bias_epilogue":
-        return oracle.conv_bias_epilogue(x[lo:hi], t["bias"], t["h"][lo:hi])
+        return oracle.conv_bias_epilogue_dt(x[lo:hi], t[l.inputs[1]], t[l.inputs[2]][lo:hi],
+                                            l.extra.get("dtype", "bf16"),
+                                            l.extra.get("bias_dtype", "f32"))
     if e == "modulate_scale_shift":
         return oracle.modulate_dt(x[lo:hi], t[l.inputs[1]], t[l.inputs[2]], l.extra["dtype"])
     if e == "residual_gate_add":
@@ -681,8 +686,12 @@ def _kernel_label(name):
         op, dt = (a.strip() for a in name.split("_kernel<", 1)[1].split(">", 1)[0].split(",")[:2])
         return ("modulate_scale_shift" if op == "0" else "residual_gate_add") + \
             ("_bf16" if dt == "0" else "_f16")
+    if "ditnorm::epilogue_kernel<" in name:
+        # epilogue_kernel<DT, F32BIAS, RES, U>
+        dt = name.split("_kernel<", 1)[1].split(",")[0].strip()
+        return "conv_bias_epilogue" + {"0": "", "1": "_f16", "2": "_f32"}[dt]
     for key, label in (("qk_kernel", "qk_layernorm"), ("wan_kernel", "rmsnorm_silu_bias"),
-                       ("epilogue_kernel", "conv_bias_epilogue"), ("copy_kernel", "copy")):
+                       ("copy_kernel", "copy")):
         if f"ditnorm::{key}" in name:
             return label
     return None

@@ -50,6 +50,8 @@ _i32 = ctypes.c_int
 
 # storage types of the standalone elementwise entry points (DITNORM_DTYPE_*)
 _DTYPE_CODES = {torch.bfloat16: 0, torch.float16: 1}
+# ... and of the conv-bias epilogue
+_EPI_DTYPES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
 
 _SIGNATURES = {
     "ln_modulate": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp],
@@ -60,7 +62,7 @@ _SIGNATURES = {
                      _vp, _vp, _vp],
     "qk_layernorm": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp, _vp, _vp],
     "rmsnorm_silu_bias": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp, _vp],
-    "conv_bias_epilogue": [_vp, _vp, _vp, _vp, _i64, _i64, _vp],
+    "conv_bias_epilogue": [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp],
     "modulate_scale_shift": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp],
     "residual_gate_add": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp],
     "ln_modulate_backward": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp,
@@ -77,7 +79,7 @@ _SIGNATURES = {
                                _f32, _vp, _vp],
     "qk_layernorm_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp, _vp],
     "rmsnorm_silu_bias_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp],
-    "conv_bias_epilogue_supported": [_vp, _vp, _vp, _vp, _i64, _i64],
+    "conv_bias_epilogue_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32],
     "modulate_scale_shift_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32],
     "residual_gate_add_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32],
     "ln_modulate_backward_supported": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
@@ -340,18 +342,21 @@ def rmsnorm_silu_bias(x, gamma, bias=None, eps=1e-6, out=None, *, rstd_out=None,
 
 
 def conv_bias_epilogue(x, bias, h=None, out=None):
-    """channels_last x: out = bf16(x + bf16(bias)) [then bf16(out + h)]."""
-    if x.dtype != torch.bfloat16 or not x.is_cuda:
-        raise TypeError("x must be a bf16 device tensor")
+    """channels_last x of bf16, fp16 or fp32: out = rnd(x + rnd(bias)) [then
+    rnd(out + h)], rnd the rounding to x's type (the identity for fp32); the
+    bias is fp32 or of x's type."""
+    if x.dtype not in _EPI_DTYPES or not x.is_cuda:
+        raise TypeError("x must be a bf16, fp16 or fp32 device tensor")
     rows2d, c = _channels_last_rows(x)
-    if (bias.dtype != torch.float32 or bias.numel() != c or not bias.is_contiguous()
-            or bias.device != x.device):
-        raise ValueError(f"bias must be a dense fp32 [{c}] tensor on {x.device}")
+    if (bias.dtype not in (torch.float32, x.dtype) or bias.numel() != c
+            or not bias.is_contiguous() or bias.device != x.device):
+        raise ValueError(f"bias must be a dense fp32 or {x.dtype} [{c}] tensor on {x.device}")
     if h is not None and (h.shape != x.shape or h.stride() != x.stride() or h.dtype != x.dtype
                           or h.device != x.device):
         raise ValueError("h must match x in shape, strides, dtype and device")
     out = _out_like(x, out)
-    _call("conv_bias_epilogue", _p(x), _p(bias), _p(h), _p(out), rows2d.shape[0], c, _stream(x))
+    _call("conv_bias_epilogue", _p(x), _p(bias), _p(h), _p(out), rows2d.shape[0], c,
+          _EPI_DTYPES[x.dtype], _EPI_DTYPES[bias.dtype], _stream(x))
     return out
 
 

@@ -248,25 +248,34 @@ int validate_wan(const void *x, const float *bias, const float *gamma, const voi
   return aliasing_ok(in, o, alias) ? DITNORM_OK : DITNORM_UNSUPPORTED;
 }
 
-int validate_epilogue(const void *x, const float *bias, const void *h, const void *out,
-                      int64_t rows, int64_t channels) {
-  if (rows < 0 || channels <= 0) return DITNORM_INVALID_ARGUMENT;
+// Element size of a storage type, 0 if the code names none.
+int64_t dtype_size(int dtype) {
+  return dtype == DITNORM_DTYPE_BF16 || dtype == DITNORM_DTYPE_F16 ? 2
+         : dtype == DITNORM_DTYPE_F32                              ? 4
+                                                                   : 0;
+}
+
+int validate_epilogue(const void *x, const void *bias, const void *h, const void *out,
+                      int64_t rows, int64_t channels, int dtype, int bias_dtype) {
+  if (rows < 0 || channels <= 0 || dtype_size(dtype) == 0 || dtype_size(bias_dtype) == 0)
+    return DITNORM_INVALID_ARGUMENT;
+  // the bias is fp32 or of the activation's own type
+  if (bias_dtype != DITNORM_DTYPE_F32 && bias_dtype != dtype) return DITNORM_UNSUPPORTED;
+  const int64_t es = dtype_size(dtype);
   if (channels % 8 != 0 || channels > DITNORM_MAX_CHANNELS || rows > DITNORM_MAX_ROWS ||
-      rows * (channels / 8) > DITNORM_MAX_VECTORS)
+      rows * (channels * es / 16) > DITNORM_MAX_VECTORS)
     return DITNORM_UNSUPPORTED;
   if (rows == 0) return DITNORM_OK;
   if (!x || !bias || !out) return DITNORM_INVALID_ARGUMENT;
   if (!aligned16(x) || !aligned16(bias) || !aligned16(h) || !aligned16(out))
     return DITNORM_UNSUPPORTED;
-  const int64_t act = rows * channels * 2;
-  const Buf in[] = {{x, act}, {bias, channels * 4}, {h, h ? act : 0}};
+  const int64_t act = rows * channels * es;
+  const Buf in[] = {{x, act}, {bias, channels * dtype_size(bias_dtype)}, {h, h ? act : 0}};
   const Buf o[] = {{out, act}};
   const int alias[] = {0};
   return aliasing_ok(in, o, alias) ? DITNORM_OK : DITNORM_UNSUPPORTED;
 }
 
-// lib_scratch: the call uses the library's scratch array (ws, ws_bytes are
-// ignored), which the partial sums must fit.
 int validate_backward(const void *x, const void *scale, const void *d_out, const void *d_x,
                       const float *d_scale, const float *d_shift, int64_t rows, int64_t cols,
                       int64_t rpb, int64_t mbs, float eps, const void *ws, int64_t ws_bytes,
@@ -519,19 +528,21 @@ int rmsnorm_silu_bias(const void *x, const float *bias, const float *gamma, void
   return finish(launch_wan(a, dev, (hipStream_t)stream));
 }
 
-int conv_bias_epilogue(const void *x, const float *bias, const void *h, void *out, int64_t rows,
-                       int64_t channels, void *stream) {
-  int st = validate_epilogue(x, bias, h, out, rows, channels);
+int conv_bias_epilogue(const void *x, const void *bias, const void *h, void *out, int64_t rows,
+                       int64_t channels, int dtype, int bias_dtype, void *stream) {
+  int st = validate_epilogue(x, bias, h, out, rows, channels, dtype, bias_dtype);
   if (st != DITNORM_OK || rows == 0) return st;
   DeviceInfo dev;
   if ((st = current_device(&dev)) != DITNORM_OK) return st;
   EpilogueArgs a{};
-  a.x = (const uint16_t *)x;
+  a.x = x;
   a.bias = bias;
-  a.h = (const uint16_t *)h;
-  a.out = (uint16_t *)out;
+  a.h = h;
+  a.out = out;
   a.rows = rows;
   a.channels = (int32_t)channels;
+  a.dtype = dtype;
+  a.bias_dtype = bias_dtype;
   return finish(launch_epilogue(a, dev, (hipStream_t)stream));
 }
 
@@ -584,9 +595,10 @@ int rmsnorm_silu_bias_supported(const void *x, const float *bias, const float *g
   return validate_wan(x, bias, gamma, out, rows, channels, eps, rstd_out, xb_out) == DITNORM_OK;
 }
 
-int conv_bias_epilogue_supported(const void *x, const float *bias, const void *h,
-                                 const void *out, int64_t rows, int64_t channels) {
-  return validate_epilogue(x, bias, h, out, rows, channels) == DITNORM_OK;
+int conv_bias_epilogue_supported(const void *x, const void *bias, const void *h,
+                                 const void *out, int64_t rows, int64_t channels, int dtype,
+                                 int bias_dtype) {
+  return validate_epilogue(x, bias, h, out, rows, channels, dtype, bias_dtype) == DITNORM_OK;
 }
 
 int modulate_scale_shift(const void *x, const void *scale, const void *shift, void *out,

@@ -142,16 +142,17 @@ __device__ __forceinline__ void bwd_row(const BwdArgs &a, int64_t row, int64_t m
     // unless the binary32 value is inexact and lands exactly on a bf16
     // halfway point (low 16 bits 0x8000): only then, and only for the
     // wavefront that meets one, the rounding goes through round-to-odd.
+    // (one ballot per element, the wave masks OR-ed in scalar registers)
     double t[8];
-    bool tie = false;
+    uint64_t tie = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const double g = (double)d[e] * (double)(1.0f + sc[e]);
       t[e] = __builtin_fma(B, (double)v[e], __builtin_fma(A, g, C));
       o[e] = (float)t[e];
-      tie |= (__float_as_uint(o[e]) & 0xFFFFu) == 0x8000u;
+      tie |= __builtin_amdgcn_ballot_w64((__float_as_uint(o[e]) & 0xFFFFu) == 0x8000u);
     }
-    if (__builtin_amdgcn_ballot_w64(tie) != 0) {
+    if (tie != 0) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = f64_round_odd_f32(t[e]);
     }

@@ -182,6 +182,53 @@ __device__ __forceinline__ double group_sum(double v) {
 }
 
 // --------------------------------------------------------------------------
+// 16-bit storage types: DT 0 bf16, 1 fp16.  widen8 is exact; narrow8 rounds
+// to nearest even (fp16: overflow to infinity, subnormals kept); round8 is
+// the value a storage-type kernel boundary keeps.
+// --------------------------------------------------------------------------
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+__device__ __forceinline__ void widen8(const uint4 v, float f[8]) {
+  if constexpr (DT == 0) {
+    unpack8(v, f);
+  } else {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 p = __builtin_convertvector(__builtin_bit_cast(f16x2, w[i]), f32x2);
+      f[2 * i] = p.x;
+      f[2 * i + 1] = p.y;
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint4 narrow8(const float f[8]) {
+  if constexpr (DT == 0) {
+    return pack8(f);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 p = {f[2 * i], f[2 * i + 1]};
+      w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, f16x2));
+    }
+    uint4 r;
+    r.x = w[0]; r.y = w[1]; r.z = w[2]; r.w = w[3];
+    return r;
+  }
+}
+
+// the value a storage-type kernel boundary keeps
+template <int DT>
+__device__ __forceinline__ void round8(float f[8]) {
+  const uint4 p = narrow8<DT>(f);
+  widen8<DT>(p, f);
+}
+
+// --------------------------------------------------------------------------
 // workgroup barrier for LDS traffic only (global loads stay in flight)
 // --------------------------------------------------------------------------
 

@@ -67,13 +67,17 @@ struct WanArgs {
 hipError_t launch_wan(const WanArgs &a, const DeviceInfo &dev, hipStream_t stream);
 
 // channels_last conv-bias epilogue (+ residual).
+// x, h, out of storage type dtype (0 bf16, 1 fp16, 2 fp32); bias of
+// bias_dtype (2 fp32, else equal to dtype).
 struct EpilogueArgs {
-  const uint16_t *x;
-  const float *bias;
-  const uint16_t *h;   // nullable
-  uint16_t *out;
+  const void *x;
+  const void *bias;
+  const void *h;       // nullable
+  void *out;
   int64_t rows;
   int32_t channels;
+  int32_t dtype;
+  int32_t bias_dtype;
 };
 hipError_t launch_epilogue(const EpilogueArgs &a, const DeviceInfo &dev, hipStream_t stream);
 

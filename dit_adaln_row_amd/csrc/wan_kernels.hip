@@ -291,42 +291,76 @@ hipError_t launch_wan(const WanArgs &a, const DeviceInfo &dev, hipStream_t strea
 }
 
 // ---------------------------------------------------------------------------
-// conv-bias epilogue: out = bf16(x + bf16(bias)) [then bf16(out + h)]
+// conv-bias epilogue: out = rnd(x + rnd(bias)) [then rnd(out + h)]
 // ---------------------------------------------------------------------------
 //
-// The tensor is walked as one flat run of 16-byte vectors: each wave
-// instruction moves 64 consecutive vectors (1 KB, whole cache lines), a lane
-// handling U of them (U = 1 measured best on MI355X: 82% of 8 TB/s at both
-// Wan VAE shapes, against 80% for U = 2 or 4 and 76% for U = 8).  The vector at flat index v belongs to
-// channel slot v % (C/8); the bias, already rounded to bf16 as the eager chain
-// rounds it, sits in LDS so any slot costs one 16-byte LDS read.  A lane's
-// slot advances by 64 mod (C/8) from one instruction to the next (one add and
-// one conditional subtract).  One-shot grid.
+// x, h and out share one storage type (DT 0 bf16, 1 fp16, 2 fp32); rnd is the
+// rounding to it (the identity for fp32) and each addition is one fp32
+// addition.  The bias is fp32 (cast to the storage type first, as autocast
+// casts it before the conv) or already of the storage type.  The tensor is
+// walked as one flat run of 16-byte vectors (8 half-precision or 4 fp32
+// values): each wave instruction moves 64 consecutive vectors (1 KB, whole
+// cache lines), a lane handling U of them (U = 1 measured best on MI355X: 82%
+// of 8 TB/s at both Wan VAE shapes, against 80% for U = 2 or 4 and 76% for
+// U = 8).  The vector at flat index v belongs to channel slot v % (C/VE); the
+// bias, already rounded to the storage type, sits in LDS in that type's bits
+// so any slot costs one 16-byte LDS read.  A lane's slot advances by 64 mod
+// (C/VE) from one instruction to the next (one add and one conditional
+// subtract).  One-shot grid.
 
 constexpr int EPI_U = 1;
 
-template <bool RES, int U>
+// 16-byte vector of storage type DT widened to fp32 (VE = 8 or 4 values)
+template <int DT>
+__device__ __forceinline__ void epi_widen(const uint4 v, float f[8]) {
+  if constexpr (DT == 2) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  } else {
+    widen8<DT>(v, f);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint4 epi_narrow(const float f[8]) {
+  if constexpr (DT == 2) {
+    uint4 r;
+    r.x = __float_as_uint(f[0]); r.y = __float_as_uint(f[1]);
+    r.z = __float_as_uint(f[2]); r.w = __float_as_uint(f[3]);
+    return r;
+  } else {
+    return narrow8<DT>(f);
+  }
+}
+
+template <int DT, bool F32BIAS, bool RES, int U>
 __global__ __launch_bounds__(WAN_BLOCK) void epilogue_kernel(const EpilogueArgs a) {
-  __shared__ uint4 bias_lds[DITNORM_MAX_CHANNELS / 8];
-  const int nvec = a.channels >> 3;
+  constexpr int VE = DT == 2 ? 4 : 8;  // values per 16-byte vector
+  __shared__ uint4 bias_lds[DITNORM_MAX_CHANNELS / VE];
+  const int nvec = a.channels / VE;
   for (int i = threadIdx.x; i < nvec; i += WAN_BLOCK) {
-    const float4 lo = ld16f(a.bias + i * 8), hi = ld16f(a.bias + i * 8 + 4);
-    uint4 q;
-    q.x = pack_rn(lo.x, lo.y); q.y = pack_rn(lo.z, lo.w);
-    q.z = pack_rn(hi.x, hi.y); q.w = pack_rn(hi.z, hi.w);
-    bias_lds[i] = q;
+    if constexpr (F32BIAS && DT != 2) {  // cast to the storage type
+      const float *b = (const float *)a.bias + i * 8;
+      const float4 lo = ld16f(b), hi = ld16f(b + 4);
+      const float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      bias_lds[i] = narrow8<DT>(f);
+    } else {  // already of the storage type
+      bias_lds[i] = *((const uint4 *)a.bias + i);
+    }
   }
   const int lane = threadIdx.x & 63;
   const int64_t total = a.rows * (int64_t)nvec;
   const int64_t base = ((int64_t)blockIdx.x * (WAN_BLOCK / 64) + wave_id()) * (64 * U);
+  const uint4 *xp = (const uint4 *)a.x, *hp = (const uint4 *)a.h;
+  uint4 *op = (uint4 *)a.out;
 
   uint4 xv[U], hv[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t v = base + u * 64 + lane;
     if (v < total) {
-      xv[u] = ld16s(a.x + v * 8);
-      if constexpr (RES) hv[u] = ld16s(a.h + v * 8);
+      xv[u] = ld16s((const uint16_t *)(xp + v));
+      if constexpr (RES) hv[u] = ld16s((const uint16_t *)(hp + v));
     }
   }
   __syncthreads();  // bias_lds filled
@@ -338,42 +372,48 @@ __global__ __launch_bounds__(WAN_BLOCK) void epilogue_kernel(const EpilogueArgs 
     const int64_t v = base + u * 64 + lane;
     if (v < total) {
       float f[8], b[8];
-      unpack8(xv[u], f);
-      unpack8(bias_lds[slot], b);
+      epi_widen<DT>(xv[u], f);
+      epi_widen<DT>(bias_lds[slot], b);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = f[e] + b[e];
+      for (int e = 0; e < VE; ++e) f[e] = f[e] + b[e];
       if constexpr (RES) {
         float h[8];
-        unpack8(pack8(f), f);
-        unpack8(hv[u], h);
+        if constexpr (DT != 2) round8<DT>(f);
+        epi_widen<DT>(hv[u], h);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = f[e] + h[e];
+        for (int e = 0; e < VE; ++e) f[e] = f[e] + h[e];
       }
-      st16s(a.out + v * 8, pack8(f));
+      st16s((uint16_t *)(op + v), epi_narrow<DT>(f));
     }
     slot += step;
     if (slot >= nvec) slot -= nvec;
   }
 }
 
-template <int U>
-hipError_t launch_epilogue_u(const EpilogueArgs &a, hipStream_t stream) {
-  const int64_t total = a.rows * (int64_t)(a.channels >> 3);
-  const int64_t per_block = (int64_t)WAN_BLOCK * U;
+template <int DT, bool F32BIAS>
+static hipError_t launch_epilogue_t(const EpilogueArgs &a, hipStream_t stream) {
+  constexpr int VE = DT == 2 ? 4 : 8;
+  const int64_t total = a.rows * (int64_t)(a.channels / VE);
+  const int64_t per_block = (int64_t)WAN_BLOCK * EPI_U;
   const int64_t grid = (total + per_block - 1) / per_block;
   if (grid > (int64_t)INT32_MAX) return hipErrorInvalidConfiguration;
   if (a.h)
-    hipLaunchKernelGGL((epilogue_kernel<true, U>), dim3((unsigned)grid), dim3(WAN_BLOCK), 0,
-                       stream, a);
+    hipLaunchKernelGGL((epilogue_kernel<DT, F32BIAS, true, EPI_U>), dim3((unsigned)grid),
+                       dim3(WAN_BLOCK), 0, stream, a);
   else
-    hipLaunchKernelGGL((epilogue_kernel<false, U>), dim3((unsigned)grid), dim3(WAN_BLOCK), 0,
-                       stream, a);
+    hipLaunchKernelGGL((epilogue_kernel<DT, F32BIAS, false, EPI_U>), dim3((unsigned)grid),
+                       dim3(WAN_BLOCK), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_epilogue(const EpilogueArgs &a, const DeviceInfo &dev, hipStream_t stream) {
   (void)dev;
-  return launch_epilogue_u<EPI_U>(a, stream);
+  const bool f32b = a.bias_dtype == 2;
+  switch (a.dtype) {
+    case 0: return f32b ? launch_epilogue_t<0, true>(a, stream) : launch_epilogue_t<0, false>(a, stream);
+    case 1: return f32b ? launch_epilogue_t<1, true>(a, stream) : launch_epilogue_t<1, false>(a, stream);
+    default: return launch_epilogue_t<2, true>(a, stream);  // fp32 x: fp32 bias
+  }
 }
 
 // ---------------------------------------------------------------------------

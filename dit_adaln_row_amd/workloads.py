@@ -61,8 +61,10 @@ class Launch:
             vec = (2 if self.extra.get("bias", True) else 1) * c * F32
             return 2 * r * c * BF16 + vec
         if self.entry == "conv_bias_epilogue":
-            act = (3 if self.extra.get("residual", False) else 2) * r * c * BF16
-            return act + c * F32
+            es = F32 if self.extra.get("dtype") == "f32" else BF16  # bf16 and fp16: 2 bytes
+            bs = BF16 if self.extra.get("bias_dtype", "f32") != "f32" else F32
+            act = (3 if self.extra.get("residual", False) else 2) * r * c * es
+            return act + c * bs
         # standalone elementwise stages: bf16 and fp16 are both 2-byte types
         if self.entry == "modulate_scale_shift":
             return 2 * r * c * BF16 + 2 * self.n_mod_rows * c * BF16
@@ -79,6 +81,8 @@ class Launch:
             return "gated_rms_modulate"
         if self.entry in ("modulate_scale_shift", "residual_gate_add"):
             return f"{self.entry}_{self.extra.get('dtype', 'bf16')}"
+        if self.entry == "conv_bias_epilogue" and self.extra.get("dtype", "bf16") != "bf16":
+            return f"{self.entry}_{self.extra['dtype']}"
         return self.entry
 
 
@@ -227,20 +231,28 @@ WORKLOADS = {
     "wan_epilogue_1x96x4x480x832": Workload(
         "wan_epilogue_1x96x4x480x832", 8,
         "Wan-VAE-like conv-bias epilogue with residual, channels_last [1,96,4,480,832]: "
-        "x, h ~N(0,1), bias (96) fp32 ~N(0,0.05)",
+        "x, h ~N(0,1) in bf16 and (separately drawn) fp16, bias (96) fp32 ~N(0,0.05)",
         (Tensor("x", (4 * 480 * 832, 96), 0.0, 1.0), Tensor("bias", (96,), 0.0, 0.05, "f32"),
-         Tensor("h", (4 * 480 * 832, 96), 0.0, 1.0)),
+         Tensor("h", (4 * 480 * 832, 96), 0.0, 1.0),
+         Tensor("x16", (4 * 480 * 832, 96), 0.0, 1.0, "f16"),
+         Tensor("h16", (4 * 480 * 832, 96), 0.0, 1.0, "f16")),
         (Launch("conv_bias_epilogue", "conv_bias_epilogue", 4 * 480 * 832, 96,
-                ("x", "bias", "h"), 0.0, extra={"residual": True}),),
+                ("x", "bias", "h"), 0.0, extra={"residual": True}),
+         Launch("conv_bias_epilogue_f16", "conv_bias_epilogue", 4 * 480 * 832, 96,
+                ("x16", "bias", "h16"), 0.0, extra={"residual": True, "dtype": "f16"})),
     ),
     "wan_epilogue_1x384x4x240x416": Workload(
         "wan_epilogue_1x384x4x240x416", 9,
         "Wan-VAE-like conv-bias epilogue with residual, channels_last [1,384,4,240,416]: "
-        "x, h ~N(0,1), bias (384) fp32 ~N(0,0.05)",
+        "x, h ~N(0,1) in bf16 and (separately drawn) fp16, bias (384) fp32 ~N(0,0.05)",
         (Tensor("x", (4 * 240 * 416, 384), 0.0, 1.0), Tensor("bias", (384,), 0.0, 0.05, "f32"),
-         Tensor("h", (4 * 240 * 416, 384), 0.0, 1.0)),
+         Tensor("h", (4 * 240 * 416, 384), 0.0, 1.0),
+         Tensor("x16", (4 * 240 * 416, 384), 0.0, 1.0, "f16"),
+         Tensor("h16", (4 * 240 * 416, 384), 0.0, 1.0, "f16")),
         (Launch("conv_bias_epilogue", "conv_bias_epilogue", 4 * 240 * 416, 384,
-                ("x", "bias", "h"), 0.0, extra={"residual": True}),),
+                ("x", "bias", "h"), 0.0, extra={"residual": True}),
+         Launch("conv_bias_epilogue_f16", "conv_bias_epilogue", 4 * 240 * 416, 384,
+                ("x16", "bias", "h16"), 0.0, extra={"residual": True, "dtype": "f16"})),
     ),
 }
 

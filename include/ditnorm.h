@@ -83,9 +83,11 @@ extern "C" {
 #define DITNORM_DEVICE_ERROR 3
 #define DITNORM_SCRATCH_EXCEEDED 4
 
-/* Storage types of the standalone elementwise entry points. */
+/* Storage types of the standalone elementwise entry points and of the
+ * conv-bias epilogue (fp32 only there). */
 #define DITNORM_DTYPE_BF16 0
 #define DITNORM_DTYPE_F16 1
+#define DITNORM_DTYPE_F32 2
 
 /* Largest row width of the row kernels (ln_modulate, gated_ln_modulate,
  * rms_modulate) and the largest channel count of the channels_last kernels. */
@@ -242,16 +244,23 @@ int rmsnorm_silu_bias(const void *x, const float *bias, const float *gamma, void
  * with the residual add that follows the conv.
  *
  * Wan VAE page (same title), Modifications, the lossless epilogue kernel:
- * the bias is cast from fp32 to bf16 before it is added, as aten's add_
- * does, and the residual form rounds twice, once after the bias and once
- * after adding h, as the eager conv output plus h does:
- *     out = bf16( x + bf16(bias) )                      (h == NULL)
- *     out = bf16( bf16( x + bf16(bias) ) + h )          (h != NULL)
- * x, h, out: bf16 [rows, channels] (channels_last pixels); bias: fp32 [C].
- * channels: multiple of 8, at most DITNORM_MAX_CHANNELS.  out == x allowed.
+ * the arithmetic of aten's add_ (the sum formed in fp32, rounded once to the
+ * activation's type); an fp32 bias on a half-precision activation is cast to
+ * the activation's type first, as autocast does before the conv; the
+ * residual form rounds twice, once after the bias and once after adding h,
+ * as the eager conv output plus h does.  With rnd the rounding to dtype
+ * (nearest even; the identity for fp32):
+ *     out = rnd( x + rnd(bias) )                       (h == NULL)
+ *     out = rnd( rnd( x + rnd(bias) ) + h )            (h != NULL)
+ * dtype: DITNORM_DTYPE_BF16, _F16 or _F32, the type of x, h and out
+ * ([rows, channels], channels_last pixels).  bias: [C] of bias_dtype,
+ * DITNORM_DTYPE_F32 or dtype itself (UNSUPPORTED otherwise).  channels:
+ * multiple of 8, at most DITNORM_MAX_CHANNELS; at most DITNORM_MAX_VECTORS
+ * 16-byte vectors in x.  out == x allowed.
  */
-int conv_bias_epilogue(const void *x, const float *bias, const void *h, void *out,
-                       int64_t rows, int64_t channels, void *stream);
+int conv_bias_epilogue(const void *x, const void *bias, const void *h, void *out,
+                       int64_t rows, int64_t channels, int dtype, int bias_dtype,
+                       void *stream);
 
 /*
  * modulate_scale_shift -- the adaLN modulate alone, for sites whose norm is
@@ -393,8 +402,9 @@ int qk_layernorm_supported(const void *q, const void *k, const void *q_out,
 int rmsnorm_silu_bias_supported(const void *x, const float *bias, const float *gamma,
                                 const void *out, int64_t rows, int64_t channels, float eps,
                                 const float *rstd_out, const void *xb_out);
-int conv_bias_epilogue_supported(const void *x, const float *bias, const void *h,
-                                 const void *out, int64_t rows, int64_t channels);
+int conv_bias_epilogue_supported(const void *x, const void *bias, const void *h,
+                                 const void *out, int64_t rows, int64_t channels, int dtype,
+                                 int bias_dtype);
 int ln_modulate_backward_supported(const void *x, const void *scale, const void *d_out,
                                    const void *d_x, const float *d_scale, const float *d_shift,
                                    int64_t rows, int64_t cols, int64_t rows_per_batch,

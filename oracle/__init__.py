@@ -81,6 +81,9 @@ def _load():
             "oracle_rmsnorm_silu_bias": [_u16p, _f32p, _f32p, _u16p, _i64, _i64,
                                          ctypes.c_float, _f32p, _u16p],
             "oracle_conv_bias_epilogue": [_u16p, _f32p, _u16p, _u16p, _i64, _i64],
+            "oracle_conv_bias_epilogue_dt": [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, _i64, _i64, ctypes.c_int,
+                                             ctypes.c_int],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -149,7 +152,7 @@ def widen_f16(h):
     return out
 
 
-DTYPES = {"bf16": 0, "f16": 1}
+DTYPES = {"bf16": 0, "f16": 1, "f32": 2}
 
 
 def modulate_dt(x, scale, shift, dtype="bf16", rows_per_batch=None):
@@ -414,4 +417,21 @@ def conv_bias_epilogue(x, bias, h=None):
     out = np.empty_like(x)
     _check(_load().oracle_conv_bias_epilogue(_p(x, _u16p), _p(bias, _f32p), _p(h, _u16p),
                                              _p(out, _u16p), rows, ch))
+    return out
+
+
+def conv_bias_epilogue_dt(x, bias, h=None, dtype="bf16", bias_dtype="f32"):
+    """Conv-bias epilogue over a storage type: x, h as uint16 bit patterns
+    (bf16, f16) or float32 (f32); bias float32 (bias_dtype "f32") or of x's
+    type."""
+    def arr(a, dt):
+        return np.ascontiguousarray(a, np.float32 if dt == "f32" else np.uint16)
+    x = arr(x, dtype)
+    rows, ch = x.shape
+    bias = arr(bias, bias_dtype)
+    h = None if h is None else arr(h, dtype)
+    out = np.empty_like(x)
+    ptr = lambda a: None if a is None else a.ctypes.data
+    _check(_load().oracle_conv_bias_epilogue_dt(ptr(x), ptr(bias), ptr(h), ptr(out), rows, ch,
+                                                DTYPES[dtype], DTYPES[bias_dtype]))
     return out

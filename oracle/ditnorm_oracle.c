@@ -777,6 +777,44 @@ int oracle_rmsnorm_silu_bias(const uint16_t *x, const float *bias, const float *
     return OR_OK;
 }
 
+/* Conv-bias epilogue over a storage type ("[Diffusion] Fuse the Wan VAE conv
+ * bias epilogue and tile the RMSNorm+SiLU kernel", Modifications and Tests /
+ * docs): aten's add_ forms x + bias in fp32 and rounds once to x's type; an
+ * fp32 bias on a half-precision x is cast to x's type first; the residual form
+ * then adds h the same way.  dtype: 0 bf16, 1 fp16 (x, h, out as uint16 bit
+ * patterns), 2 fp32 (as float); bias_dtype: 2 (fp32) or dtype.  With rnd the
+ * rounding to dtype (the identity for fp32):
+ *     out = rnd(x + rnd(bias)),   then   out = rnd(out + h). */
+int oracle_conv_bias_epilogue_dt(const void *x, const void *bias, const void *h, void *out,
+                                 int64_t rows, int64_t channels, int dtype, int bias_dtype)
+{
+    if (rows < 0 || channels <= 0 || dtype < 0 || dtype > 2)
+        return OR_INVALID;
+    if (bias_dtype != 2 && bias_dtype != dtype)
+        return OR_INVALID;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < channels; ++c) {
+            const int64_t i = r * channels + c;
+            if (dtype == 2) {
+                float v = ((const float *)x)[i] + ((const float *)bias)[c];
+                if (h)
+                    v = v + ((const float *)h)[i];
+                ((float *)out)[i] = v;
+                continue;
+            }
+            /* the bias in x's type: cast from fp32, or as given */
+            uint16_t b = bias_dtype == 2 ? f32_to_st(((const float *)bias)[c], dtype)
+                                         : ((const uint16_t *)bias)[c];
+            float sum = st_to_f32(((const uint16_t *)x)[i], dtype) + st_to_f32(b, dtype);
+            uint16_t v = f32_to_st(sum, dtype);
+            if (h)
+                v = f32_to_st(st_to_f32(v, dtype) + st_to_f32(((const uint16_t *)h)[i], dtype),
+                              dtype);
+            ((uint16_t *)out)[i] = v;
+        }
+    return OR_OK;
+}
+
 /* Standalone conv-bias epilogue: out = bf16(x + bf16(bias[c])), then, when h
  * is given, out = bf16(out + h). */
 int oracle_conv_bias_epilogue(const uint16_t *x, const float *bias, const uint16_t *h,

@@ -104,9 +104,16 @@ def test_supported_predicates_never_touch_the_gpu(lib):
     assert lib.rmsnorm_silu_bias_supported(A, None, C, D, 100, 96, 1e-6, None, None) == 1
     assert lib.rmsnorm_silu_bias_supported(A, B, C, D, 100, 100, 1e-6, None, None) == 0
     assert lib.rmsnorm_silu_bias_supported(A, B + 4, C, D, 100, 96, 1e-6, None, None) == 0
-    assert lib.conv_bias_epilogue_supported(A, B, C, D, 100, 96) == 1
-    assert lib.conv_bias_epilogue_supported(A, B, C, A, 100, 96) == 1      # in place
-    assert lib.conv_bias_epilogue_supported(A, B, C, C, 100, 96) == 0      # out over h
+    assert lib.conv_bias_epilogue_supported(A, B, C, D, 100, 96, 0, 2) == 1
+    assert lib.conv_bias_epilogue_supported(A, B, C, A, 100, 96, 0, 2) == 1   # in place
+    assert lib.conv_bias_epilogue_supported(A, B, C, C, 100, 96, 0, 2) == 0   # out over h
+    # storage types: fp32 or the activation's own type for the bias
+    for dt, bdt, ok in ((1, 2, 1), (1, 1, 1), (2, 2, 1), (0, 0, 1), (0, 1, 0), (1, 0, 0),
+                        (2, 0, 0), (2, 1, 0)):
+        assert lib.conv_bias_epilogue_supported(A, B, C, D, 100, 96, dt, bdt) == ok, (dt, bdt)
+    assert lib.conv_bias_epilogue(A, B, None, D, 10, 96, 3, 2, None) == dn.INVALID_ARGUMENT
+    assert lib.conv_bias_epilogue(A, B, None, D, 10, 96, 0, 7, None) == dn.INVALID_ARGUMENT
+    assert lib.conv_bias_epilogue(A, B, None, D, 10, 96, 2, 0, None) == dn.UNSUPPORTED
     assert lib.ln_modulate_folded_supported(A, B, C, D, 4, 3072, 4, 3072, 1e-6, None, None) == 1
     assert lib.ln_modulate_folded_supported(A, B, C, A, 4, 3072, 4, 3072, 1e-6, None, None) == 1
     assert lib.ln_modulate_folded_supported(A, B, C, D, 4, 3076, 4, 3076, 1e-6, None, None) == 0
@@ -133,7 +140,7 @@ def test_other_entry_validation(lib):
     assert lib.qk_layernorm(A, B, A + 128, D, 4, 4, 128, 1e-5, None, None, None) == dn.UNSUPPORTED
     assert lib.rmsnorm_silu_bias(A, B, None, D, 10, 96, 1e-6, None, None, None) == dn.INVALID_ARGUMENT
     assert lib.rmsnorm_silu_bias(A, B, C, D, 10, 4104, 1e-6, None, None, None) == dn.UNSUPPORTED
-    assert lib.conv_bias_epilogue(A, None, None, D, 10, 96, None) == dn.INVALID_ARGUMENT
+    assert lib.conv_bias_epilogue(A, None, None, D, 10, 96, 0, 2, None) == dn.INVALID_ARGUMENT
     assert lib.ln_modulate_folded(A, B, None, D, 4, 3072, 4, 3072, 1e-6, None, None,
                                   None) == dn.INVALID_ARGUMENT
     assert lib.ln_modulate_folded(A, B, C, D, 4, 3072, 3, 3072, 1e-6, None, None,
@@ -191,7 +198,9 @@ def test_other_entry_validation(lib):
     # 2^31 - 1 vectors of 512 per row: 4194303 rows fit, 4194304 do not (buffers 64 GB apart)
     G = 1 << 36
     for rows, ok in ((4194303, 1), (4194304, 0)):
-        assert lib.conv_bias_epilogue_supported(G, E, None, 2 * G, rows, 4096) == ok
+        assert lib.conv_bias_epilogue_supported(G, E, None, 2 * G, rows, 4096, 0, 2) == ok
+        # fp32 activations: 16-byte vectors of 4 values, half the rows fit
+        assert lib.conv_bias_epilogue_supported(G, E, None, 2 * G, rows // 2, 4096, 2, 2) == ok
         assert lib.modulate_scale_shift_supported(G, B, C, 2 * G, rows, 4096, rows, 4096,
                                                   0) == ok
     # (fake buffers spaced so that only the size decides: d_scale / d_shift

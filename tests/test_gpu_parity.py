@@ -338,6 +338,79 @@ def test_conv_bias_epilogue(gpu, orc, rows, c, res):
     assert same_bits(host(out), orc.conv_bias_epilogue(x, b, h))
 
 
+_TD = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+def _epi_case(dtype, bias_dtype, rows, c, seed):
+    """x, h ~N(0,1) of the storage type with special values planted (signed
+    zeros, subnormals, infinities, a NaN, the largest finite magnitude, so
+    that adding the bias overflows); bias ~N(0, 0.05), fp32 or of x's type."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((rows, c), generator=g).to(_TD[dtype])
+    h = torch.randn((rows, c), generator=g).to(_TD[dtype])
+    fi = torch.finfo(_TD[dtype])
+    sp = torch.tensor([0.0, -0.0, fi.smallest_normal / 4, -fi.smallest_normal / 4, fi.max,
+                       -fi.max, float("inf"), float("-inf"), float("nan")]).to(_TD[dtype])
+    n = min(sp.numel(), rows * c)
+    x.view(-1)[:n] = sp[:n]
+    h.view(-1)[-n:] = sp[:n]
+    b = (torch.randn(c, generator=g) * 0.05).to(_TD[bias_dtype])
+    return x, h, b
+
+
+def _np(t, dt):
+    return t.numpy() if dt == "f32" else gen.to_u16(t)
+
+
+@pytest.mark.parametrize("dtype,bias_dtype", [("bf16", "f32"), ("bf16", "bf16"), ("f16", "f32"),
+                                              ("f16", "f16"), ("f32", "f32")])
+@pytest.mark.parametrize("rows,c,res", [(1, 8, False), (777, 96, True), (1001, 384, True),
+                                        (333, 200, False), (5, 4096, True), (12345, 40, True)])
+def test_conv_bias_epilogue_dtypes(gpu, orc, dtype, bias_dtype, rows, c, res):
+    """Wan VAE page (Tests / docs: bf16 / fp16 / fp32 x with an fp32 or
+    half-precision bias, with and without the residual): every storage type
+    bitwise equal to the oracle, special values and ragged vector counts
+    included."""
+    log(f"conv_bias_epilogue {dtype}/{bias_dtype} rows={rows} C={c} residual={res}")
+    x, h, b = _epi_case(dtype, bias_dtype, rows, c, 2100 + c + rows)
+    out = gpu.conv_bias_epilogue(x.cuda(), b.cuda(), h.cuda() if res else None)
+    torch.cuda.synchronize()
+    ref = orc.conv_bias_epilogue_dt(_np(x, dtype), _np(b, bias_dtype),
+                                    _np(h, dtype) if res else None, dtype, bias_dtype)
+    got = out.cpu()
+    if dtype == "f32":
+        a, r = got.numpy(), ref
+        assert np.array_equal(np.isnan(a), np.isnan(r))
+        assert np.array_equal(a[~np.isnan(a)].view(np.uint32), r[~np.isnan(r)].view(np.uint32))
+    else:
+        assert same_bits(gen.to_u16(got), ref, dtype)
+
+
+def test_conv_bias_epilogue_in_place_and_channels_last(gpu, orc):
+    """out == x for fp16 and fp32, and a channels_last 5-D fp16 tensor."""
+    for dt in ("f16", "f32"):
+        x, h, b = _epi_case(dt, "f32", 300, 96, 2200)
+        xd = x.cuda()
+        ref = orc.conv_bias_epilogue_dt(_np(x, dt), b.numpy(), _np(h, dt), dt, "f32")
+        out = gpu.conv_bias_epilogue(xd, b.cuda(), h.cuda(), out=xd)
+        torch.cuda.synchronize()
+        assert out.data_ptr() == xd.data_ptr()
+        got = out.cpu()
+        if dt == "f32":
+            assert np.array_equal(np.nan_to_num(got.numpy(), nan=7.0), np.nan_to_num(ref, nan=7.0))
+        else:
+            assert same_bits(gen.to_u16(got), ref, dt)
+    n, c, d, hh, w = 1, 96, 2, 6, 10
+    xt = gen.normal((n, c, d, hh, w), 0, 1, 2201, "f16").to(memory_format=torch.channels_last_3d)
+    b = gen.normal((c,), 0, 0.05, 2202, "f32")
+    out = gpu.conv_bias_epilogue(xt.cuda(), b.cuda())
+    torch.cuda.synchronize()
+    assert out.is_contiguous(memory_format=torch.channels_last_3d)
+    rows = gen.to_u16(xt.permute(0, 2, 3, 4, 1).reshape(-1, c).contiguous())
+    got = gen.to_u16(out.permute(0, 2, 3, 4, 1).reshape(-1, c).contiguous())
+    assert same_bits(got, orc.conv_bias_epilogue_dt(rows, b.numpy(), None, "f16", "f32"), "f16")
+
+
 # ---------------------------------------------------------------------------
 # every workload at full size
 # ---------------------------------------------------------------------------
@@ -398,10 +471,12 @@ def test_full_workload(gpu, orc, key):
         elif l.entry == "rmsnorm_silu_bias":
             _wan_run_check(gpu, orc, f"{key}/{l.name}", t["x"], t["bias"], t["gamma"], l.eps)
         elif l.entry == "conv_bias_epilogue":
+            dt = l.extra.get("dtype", "bf16")
+            td = torch.float16 if dt == "f16" else torch.bfloat16
             x, b, h = (t[n] for n in l.inputs)
-            out = gpu.conv_bias_epilogue(dev(x), dev(b), dev(h))
+            out = gpu.conv_bias_epilogue(dev(x, dtype=td), dev(b), dev(h, dtype=td))
             torch.cuda.synchronize()
-            assert same_bits(host(out), orc.conv_bias_epilogue(x, b, h)), l.name
+            assert same_bits(host(out), orc.conv_bias_epilogue_dt(x, b, h, dt, "f32"), dt), l.name
         elif l.entry in ("modulate_scale_shift", "residual_gate_add"):
             dt = l.extra["dtype"]
             td = torch.float16 if dt == "f16" else torch.bfloat16

@@ -242,6 +242,77 @@ def test_conv_bias_epilogue_matches_eager(orc):
     assert same_bits(orc.conv_bias_epilogue(x, bias, h), to_u16(xb + t_bf16(h)))
 
 
+def _epilogue_inputs(dtype, bias_dtype, rows, C, seed):
+    """x, h ~N(0,1) with special values planted (signed zeros, subnormals,
+    infinities, a NaN, values at the type's largest finite magnitude so that
+    adding the bias overflows); bias ~N(0, 0.05) in fp32 or x's type."""
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((rows, C), generator=g).to(tdt[dtype])
+    h = torch.randn((rows, C), generator=g).to(tdt[dtype])
+    big = torch.finfo(tdt[dtype]).max
+    tiny = torch.finfo(tdt[dtype]).smallest_normal / 4  # subnormal
+    special = torch.tensor([0.0, -0.0, tiny, -tiny, big, -big, float("inf"), float("-inf"),
+                            float("nan")], dtype=torch.float32).to(tdt[dtype])
+    x.view(-1)[:special.numel()] = special
+    h.view(-1)[C:C + special.numel()] = special
+    bias = (torch.randn(C, generator=g) * 0.05).to(tdt[bias_dtype])
+    bias[0] = big if bias_dtype != "f32" else 3.0e38  # overflows x's type where it is narrower
+    return x, h, bias
+
+
+def _as_oracle(t, dtype):
+    return t.numpy() if dtype == "f32" else to_u16(t)
+
+
+def _same(a, b, dtype):
+    if dtype == "f32":
+        a, b = np.asarray(a, np.float32), np.asarray(b, np.float32)
+        return np.array_equal(np.isnan(a), np.isnan(b)) and \
+            np.array_equal(a[~np.isnan(a)].view(np.uint32), b[~np.isnan(b)].view(np.uint32))
+    if dtype == "f16":
+        an = ((a & 0x7C00) == 0x7C00) & ((a & 0x3FF) != 0)
+        bn = ((b & 0x7C00) == 0x7C00) & ((b & 0x3FF) != 0)
+        return np.array_equal(an, bn) and np.array_equal(a[~an], b[~bn])
+    return same_bits(a, b)
+
+
+@pytest.mark.parametrize("dtype,bias_dtype", [("bf16", "f32"), ("bf16", "bf16"), ("f16", "f32"),
+                                              ("f16", "f16"), ("f32", "f32")])
+def test_conv_bias_epilogue_dtypes_match_eager(orc, dtype, bias_dtype):
+    """The Wan VAE page's epilogue for bf16 / fp16 / fp32 activations with an
+    fp32 or same-type bias ("[Diffusion] Fuse the Wan VAE conv bias epilogue
+    and tile the RMSNorm+SiLU kernel", Tests / docs: the aten oracle
+    x.clone().add_(bias), then + h): torch's CPU eager chain, the bias cast to
+    x's type first as autocast does, bit for bit -- special values included."""
+    rows, C = 333, 96
+    x, h, bias = _epilogue_inputs(dtype, bias_dtype, rows, C, 20)
+    xb = x.clone().add_(bias.to(x.dtype))
+    got = orc.conv_bias_epilogue_dt(_as_oracle(x, dtype), _as_oracle(bias, bias_dtype), None,
+                                    dtype, bias_dtype)
+    assert _same(got, _as_oracle(xb, dtype), dtype)
+    got = orc.conv_bias_epilogue_dt(_as_oracle(x, dtype), _as_oracle(bias, bias_dtype),
+                                    _as_oracle(h, dtype), dtype, bias_dtype)
+    assert _same(got, _as_oracle(xb + h, dtype), dtype)
+    if dtype == "bf16" and bias_dtype == "f32":  # the bf16-only form agrees
+        assert same_bits(got, orc.conv_bias_epilogue(to_u16(x), bias.numpy(), to_u16(h)))
+
+
+def test_conv_bias_epilogue_f32_bias_is_cast_first(orc):
+    """An fp32 bias on a half-precision x is rounded to x's type before the
+    add.  x = 1 and bias = 2^-11 + 2^-22 in fp16: the bias rounds to 2^-11
+    (a tie, to even), and 1 + 2^-11 is again a tie that rounds to 1; the
+    uncast fp32 sum 1 + 2^-11 + 2^-22 lies above that tie and would round to
+    1 + 2^-10."""
+    x = torch.full((1, 8), 1.0, dtype=torch.float16)
+    b = torch.full((8,), 2.0 ** -11 + 2.0 ** -22, dtype=torch.float32)
+    got = orc.conv_bias_epilogue_dt(to_u16(x), b.numpy(), None, "f16", "f32")
+    assert np.all(got == to_u16(torch.ones((1, 8), dtype=torch.float16)))
+    uncast = (x.float() + b).to(torch.float16)
+    assert np.all(to_u16(uncast) == to_u16(torch.full((1, 8), 1.0 + 2.0 ** -10,
+                                                      dtype=torch.float16)))
+
+
 # ---------------------------------------------------------------------------
 # statistics vs exact rational arithmetic
 # ---------------------------------------------------------------------------
