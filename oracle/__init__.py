@@ -81,6 +81,9 @@ def _load():
             "oracle_rmsnorm_silu_bias": [_u16p, _f32p, _f32p, _u16p, _i64, _i64,
                                          ctypes.c_float, _f32p, _u16p],
             "oracle_conv_bias_epilogue": [_u16p, _f32p, _u16p, _u16p, _i64, _i64],
+            "oracle_ln_modulate_backward_f32": [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64,
+                                                ctypes.c_float, _f32p, _f32p, _f32p, _f32p,
+                                                _f32p],
             "oracle_conv_bias_epilogue_dt": [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_void_p, _i64, _i64, ctypes.c_int,
                                              ctypes.c_int],
@@ -337,6 +340,29 @@ def ln_modulate_backward(x, scale, d_out, eps, rows_per_batch=None):
     _check(_load().oracle_ln_modulate_backward(
         _p(x, _u16p), _p(scale, _u16p), _p(d_out, _u16p), rows, cols, rpb, stride, eps,
         _p(d_x, _u16p), _p(d_scale, _f32p), _p(d_shift, _f32p), _p(mean, _f32p),
+        _p(rstd, _f32p)))
+    return dict(d_x=d_x, d_scale=d_scale, d_shift=d_shift, mean=mean, rstd=rstd)
+
+
+def ln_modulate_backward_f32(x, scale, d_out, eps, rows_per_batch=None):
+    """The fp32 stream of the backward: x, scale, d_out float32; returns
+    dict(d_x (float32), d_scale, d_shift, mean, rstd)."""
+    x, d_out = _f32(x), _f32(d_out)
+    rows, cols = x.shape
+    scale = _f32(scale)
+    if scale.ndim == 1:
+        scale = scale.reshape(1, -1)
+    stride = scale.shape[1]
+    rpb = rows_per_batch or max(rows, 1)
+    nb = rows // rpb if rows else 0
+    d_x = np.empty_like(x)
+    d_scale = np.empty((nb, cols), np.float32)
+    d_shift = np.empty((nb, cols), np.float32)
+    mean = np.empty(rows, np.float32)
+    rstd = np.empty(rows, np.float32)
+    _check(_load().oracle_ln_modulate_backward_f32(
+        _p(x, _f32p), _p(scale, _f32p), _p(d_out, _f32p), rows, cols, rpb, stride, eps,
+        _p(d_x, _f32p), _p(d_scale, _f32p), _p(d_shift, _f32p), _p(mean, _f32p),
         _p(rstd, _f32p)))
     return dict(d_x=d_x, d_scale=d_scale, d_shift=d_shift, mean=mean, rstd=rstd)
 

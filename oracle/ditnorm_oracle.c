@@ -601,11 +601,19 @@ float oracle_tree32_sum(float *v, int64_t n)
  * scale: [B, cols] bf16 at row stride mod_batch_stride; d_x: bf16 [rows,
  * cols]; d_scale, d_shift: fp32 [B, cols] (dense).  mean_out / rstd_out may be
  * NULL. */
-int oracle_ln_modulate_backward(const uint16_t *x, const uint16_t *scale, const uint16_t *d_out,
-                                int64_t rows, int64_t cols, int64_t rows_per_batch,
-                                int64_t mod_batch_stride, float eps, uint16_t *d_x,
-                                float *d_scale, float *d_shift, float *mean_out,
-                                float *rstd_out)
+/* One value of a backward operand: dtype 0 bf16 (uint16 bit patterns), 2 fp32. */
+static float bwd_ld(const void *p, int64_t i, int dtype)
+{
+    return dtype == 2 ? ((const float *)p)[i] : bf16_to_f32(((const uint16_t *)p)[i]);
+}
+
+/* The backward over a storage type (0 bf16, 2 fp32); d_x is the binary64
+ * value rounded once to that type. */
+static int ln_modulate_backward_dt(const void *x, const void *scale, const void *d_out,
+                                   int64_t rows, int64_t cols, int64_t rows_per_batch,
+                                   int64_t mod_batch_stride, float eps, void *d_x,
+                                   float *d_scale, float *d_shift, float *mean_out,
+                                   float *rstd_out, int dtype)
 {
     if (!mod_args_ok(rows, cols, rows_per_batch, mod_batch_stride))
         return OR_INVALID;
@@ -614,17 +622,18 @@ int oracle_ln_modulate_backward(const uint16_t *x, const uint16_t *scale, const 
     int64_t nb = rows / rows_per_batch;
     float *mean = (float *)malloc(sizeof(float) * (size_t)(rows > 0 ? rows : 1));
     float *rstd = (float *)malloc(sizeof(float) * (size_t)(rows > 0 ? rows : 1));
+    float *xr = (float *)malloc(sizeof(float) * (size_t)cols);
     float *ts = (float *)malloc(sizeof(float) * (size_t)(rows_per_batch > 0 ? rows_per_batch : 1));
     float *tc = (float *)malloc(sizeof(float) * (size_t)(rows_per_batch > 0 ? rows_per_batch : 1));
-    if (!mean || !rstd || !ts || !tc) {
-        free(mean); free(rstd); free(ts); free(tc);
+    if (!mean || !rstd || !xr || !ts || !tc) {
+        free(mean); free(rstd); free(xr); free(ts); free(tc);
         return OR_INVALID;
     }
     /* per row: statistics and d_x */
     for (int64_t r = 0; r < rows; ++r) {
-        const float *xr = widen_row(x + r * cols, cols);
-        const uint16_t *sr = scale + (r / rows_per_batch) * mod_batch_stride;
-        const uint16_t *gr = d_out + r * cols;
+        for (int64_t c = 0; c < cols; ++c)
+            xr[c] = bwd_ld(x, r * cols + c, dtype);
+        int64_t so = (r / rows_per_batch) * mod_batch_stride;
         ln_stats(xr, cols, eps, &mean[r], &rstd[r]);
         if (mean_out)
             mean_out[r] = mean[r];
@@ -634,7 +643,8 @@ int oracle_ln_modulate_backward(const uint16_t *x, const uint16_t *scale, const 
         double c1 = 0.0, c2 = 0.0;
         for (int64_t c = 0; c < cols; ++c) {
             double xh = ((double)xr[c] - m) * rs;
-            double g = (double)bf16_to_f32(gr[c]) * (double)(1.0f + bf16_to_f32(sr[c]));
+            double g = (double)bwd_ld(d_out, r * cols + c, dtype) *
+                       (double)(1.0f + bwd_ld(scale, so + c, dtype));
             c1 += g;
             c2 += g * xh;
         }
@@ -642,8 +652,13 @@ int oracle_ln_modulate_backward(const uint16_t *x, const uint16_t *scale, const 
         c2 /= (double)cols;
         for (int64_t c = 0; c < cols; ++c) {
             double xh = ((double)xr[c] - m) * rs;
-            double g = (double)bf16_to_f32(gr[c]) * (double)(1.0f + bf16_to_f32(sr[c]));
-            d_x[r * cols + c] = f64_to_bf16(rs * (g - c1 - xh * c2));
+            double g = (double)bwd_ld(d_out, r * cols + c, dtype) *
+                       (double)(1.0f + bwd_ld(scale, so + c, dtype));
+            double v = rs * (g - c1 - xh * c2);
+            if (dtype == 2)
+                ((float *)d_x)[r * cols + c] = (float)v;
+            else
+                ((uint16_t *)d_x)[r * cols + c] = f64_to_bf16(v);
         }
     }
     /* per batch and column: the two token sums */
@@ -651,8 +666,8 @@ int oracle_ln_modulate_backward(const uint16_t *x, const uint16_t *scale, const 
         for (int64_t c = 0; c < cols; ++c) {
             for (int64_t s = 0; s < rows_per_batch; ++s) {
                 int64_t r = b * rows_per_batch + s;
-                float dout = bf16_to_f32(d_out[r * cols + c]);
-                float xh = rstd[r] * (bf16_to_f32(x[r * cols + c]) - mean[r]);
+                float dout = bwd_ld(d_out, r * cols + c, dtype);
+                float xh = rstd[r] * (bwd_ld(x, r * cols + c, dtype) - mean[r]);
                 ts[s] = dout;
                 tc[s] = dout * xh;
             }
@@ -660,8 +675,32 @@ int oracle_ln_modulate_backward(const uint16_t *x, const uint16_t *scale, const 
             d_scale[b * cols + c] = tree32_sum(tc, rows_per_batch);
         }
     }
-    free(mean); free(rstd); free(ts); free(tc);
+    free(mean); free(rstd); free(xr); free(ts); free(tc);
     return OR_OK;
+}
+
+int oracle_ln_modulate_backward(const uint16_t *x, const uint16_t *scale, const uint16_t *d_out,
+                                int64_t rows, int64_t cols, int64_t rows_per_batch,
+                                int64_t mod_batch_stride, float eps, uint16_t *d_x,
+                                float *d_scale, float *d_shift, float *mean_out,
+                                float *rstd_out)
+{
+    return ln_modulate_backward_dt(x, scale, d_out, rows, cols, rows_per_batch, mod_batch_stride,
+                                   eps, d_x, d_scale, d_shift, mean_out, rstd_out, 0);
+}
+
+/* The fp32 stream ("[WS1][Qwen-Image][CUDA] Final AdaLN output
+ * (final_adaln_out)", the FP32 column of its forward + backward table and
+ * its BF16/FP32 accuracy gates): the same computation on fp32 x, scale and
+ * d_out, d_x rounded once from binary64 to fp32. */
+int oracle_ln_modulate_backward_f32(const float *x, const float *scale, const float *d_out,
+                                    int64_t rows, int64_t cols, int64_t rows_per_batch,
+                                    int64_t mod_batch_stride, float eps, float *d_x,
+                                    float *d_scale, float *d_shift, float *mean_out,
+                                    float *rstd_out)
+{
+    return ln_modulate_backward_dt(x, scale, d_out, rows, cols, rows_per_batch, mod_batch_stride,
+                                   eps, d_x, d_scale, d_shift, mean_out, rstd_out, 2);
 }
 
 /* Gated residual, then LN (no affine) + modulate on h.  Writes h and out. */

@@ -801,3 +801,89 @@ def test_backward_batch_invariance_and_closed_forms(orc):
     half = 0.5 * ulp_bf16(dx)
     assert np.all(np.abs(dx.sum(1)) <= half.sum(1) * 1.01)
     assert np.all(np.abs((dx * xh).sum(1)) <= (half * np.abs(xh)).sum(1) * 1.01 + 1e-3 * np.abs(dx * xh).sum(1) * 2 ** -10)
+
+
+# ---------------------------------------------------------------------------
+# the backward's fp32 stream
+# ---------------------------------------------------------------------------
+
+def _f32_normal(shape, mu, sigma, seed):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g, dtype=torch.float64) * sigma + mu).float().numpy()
+
+
+def test_backward_f32_vs_torch_autograd(orc):
+    """The fp32 stream (Qwen-Image page, the FP32 column of the final stream's
+    table and its BF16/FP32 accuracy gates) against torch float64 autograd of
+    LN(x) * (1 + scale) + shift: d_x within its fp32 rounding plus what the
+    fp32 rounding of mean and rstd moves it by; the token sums within the
+    fixed tree's error bound over the exact sums."""
+    B, S, D = 2, 77, 1024
+    x = _f32_normal((B * S, D), 0.3, 1.5, 840)
+    sc = _f32_normal((B, D), 0, 0.1, 841)
+    dout = _f32_normal((B * S, D), 0, 1.0, 842)
+    r = orc.ln_modulate_backward_f32(x, sc, dout, 1e-6, rows_per_batch=S)
+    xt = torch.from_numpy(x.astype(np.float64)).requires_grad_()
+    st = torch.from_numpy(sc.astype(np.float64)).requires_grad_()
+    ht = torch.zeros_like(st, requires_grad=True)
+    b = torch.arange(B * S) // S
+    out = torch.nn.functional.layer_norm(xt, (D,), eps=1e-6) * (1 + st[b]) + ht[b]
+    out.backward(torch.from_numpy(dout.astype(np.float64)))
+    gx, gs, gh = xt.grad.numpy(), st.grad.numpy(), ht.grad.numpy()
+    xh = torch.nn.functional.layer_norm(xt.detach(), (D,), eps=1e-6).numpy()
+    g = dout.astype(np.float64) * (1 + np.repeat(sc.astype(np.float64), S, 0))
+    rstd = r["rstd"].astype(np.float64)[:, None]
+    c1 = g.mean(1, keepdims=True)
+    c2 = (g * xh).mean(1, keepdims=True)
+    # mean and rstd rounded to fp32 (2^-24 relative each) move x_hat and the
+    # three terms by a few parts in 2^24
+    slack = 8 * U24 * rstd * (np.abs(g) + np.abs(c1) + np.abs(xh * c2)) * (1 + np.abs(xh))
+    assert np.all(np.abs(r["d_x"].astype(np.float64) - gx) <= U24 * np.abs(gx) + slack + 1e-30)
+    depth = 5 * 2
+    tsh = np.abs(dout.astype(np.float64)).reshape(B, S, D).sum(1)
+    assert np.all(np.abs(r["d_shift"] - gh) <= depth * U24 * tsh + 1e-30)
+    tsc = np.abs(dout.astype(np.float64) * xh).reshape(B, S, D).sum(1)
+    assert np.all(np.abs(r["d_scale"] - gs) <= (depth + 4) * U24 * tsc + 1e-30)
+
+
+def test_backward_f32_agrees_with_bf16_stream_on_bf16_values(orc):
+    """On fp32 inputs that hold bf16 values the two streams see the same
+    numbers: the statistics and both token sums are bitwise the bf16
+    stream's, and d_x, rounded to fp32 there and to bf16 here from the same
+    binary64 value, differs by at most one bf16 ulp after rounding the fp32
+    value to bf16 (only where the fp32 value lands on a bf16 halfway point)."""
+    B, S, D = 3, 40, 768
+    x = rand_bf16((B * S, D), 0.2, 1.5, 850)
+    sc = rand_bf16((B, D), 0, 0.1, 851)
+    dout = rand_bf16((B * S, D), 0, 1.0, 852)
+    rb = orc.ln_modulate_backward(x, sc, dout, 1e-6, rows_per_batch=S)
+    rf = orc.ln_modulate_backward_f32(f32_from_u16(x), f32_from_u16(sc), f32_from_u16(dout), 1e-6,
+                                      rows_per_batch=S)
+    for k in ("mean", "rstd", "d_shift", "d_scale"):
+        assert np.array_equal(rb[k].view(np.uint32), rf[k].view(np.uint32)), k
+    d32 = bf16_bits_from_f32(rf["d_x"])
+    d = np.abs(d32.astype(np.int32) - rb["d_x"].astype(np.int32))
+    assert d.max() <= 1 and (d == 0).mean() >= 0.9999
+
+
+def test_backward_f32_batch_invariance_and_closed_forms(orc):
+    S, D = 45, 256
+    xs = [_f32_normal((S, D), 0, 1, 860 + i) for i in range(3)]
+    scs = [_f32_normal((1, D), 0, 0.1, 870 + i) for i in range(3)]
+    ds = [_f32_normal((S, D), 0, 1, 880 + i) for i in range(3)]
+    whole = orc.ln_modulate_backward_f32(np.concatenate(xs), np.concatenate(scs),
+                                         np.concatenate(ds), 1e-6, rows_per_batch=S)
+    for i in range(3):
+        alone = orc.ln_modulate_backward_f32(xs[i], scs[i], ds[i], 1e-6)
+        assert np.array_equal(alone["d_x"].view(np.uint32),
+                              whole["d_x"][i * S:(i + 1) * S].view(np.uint32))
+        for k in ("d_scale", "d_shift"):
+            assert np.array_equal(alone[k][0].view(np.uint32), whole[k][i].view(np.uint32))
+    # d_out constant c with few significant bits: every partial sum is exact,
+    # so d_shift = S * c whatever the tree
+    c = np.full((S, D), 0.375, np.float32)
+    r = orc.ln_modulate_backward_f32(xs[0], scs[0], c, 1e-6)
+    assert np.all(r["d_shift"] == np.float32(S * 0.375))
+    r1 = orc.ln_modulate_backward_f32(xs[0], np.full((1, D), -1.0, np.float32), ds[0], 1e-6)
+    assert np.all(r1["d_x"] == 0)
+
