@@ -107,11 +107,12 @@ def make_call(lib, launch, t, stream):
         d_x = torch.empty_like(a)
         d_scale = torch.empty((nb, cols), dtype=torch.float32, device=a.device)
         d_shift = torch.empty((nb, cols), dtype=torch.float32, device=a.device)
-        ws_bytes = lib.ln_modulate_backward_workspace_bytes(rows, cols, rpb)
+        dt = DTYPE_CODES[launch.extra.get("dtype", "bf16")]
+        ws_bytes = lib.ln_modulate_backward_workspace_bytes(rows, cols, rpb, dt)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a.device)
         return lib.ln_modulate_backward, (_p(a), _p(b), _p(c), _p(d_x), _p(d_scale), _p(d_shift),
                                           rows, cols, rpb, cols, launch.eps, _p(ws), ws_bytes,
-                                          None, None, stream), (d_x, d_scale, d_shift, ws)
+                                          None, None, dt, stream), (d_x, d_scale, d_shift, ws)
     if e == "conv_bias_epilogue":          # inputs: x, bias, h
         out = torch.empty_like(a)
         dt = DTYPE_CODES[launch.extra.get("dtype", "bf16")]
@@ -318,11 +319,12 @@ def _oracle_call(oracle, l, t, lo, hi):
                                        l.extra["dtype"])
     if e == "ln_modulate_backward":
         rpb = l.extra["rows_per_batch"]
+        fn = oracle.ln_modulate_backward_f32 if l.extra.get("dtype") == "f32" else \
+            oracle.ln_modulate_backward
+        sc, dout = t[l.inputs[1]], t[l.inputs[2]]
         if hi - lo <= rpb:  # part of one batch: a batch of that many tokens
-            return oracle.ln_modulate_backward(x[lo:hi], t["scale"][:1], t["d_out"][lo:hi], l.eps,
-                                               rows_per_batch=hi - lo)
-        return oracle.ln_modulate_backward(x[lo:hi], t["scale"][lo // rpb:hi // rpb],
-                                           t["d_out"][lo:hi], l.eps, rows_per_batch=rpb)
+            return fn(x[lo:hi], sc[:1], dout[lo:hi], l.eps, rows_per_batch=hi - lo)
+        return fn(x[lo:hi], sc[lo // rpb:hi // rpb], dout[lo:hi], l.eps, rows_per_batch=rpb)
     raise KeyError(e)
 
 

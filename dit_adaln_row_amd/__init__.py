@@ -50,8 +50,9 @@ _i32 = ctypes.c_int
 
 # storage types of the standalone elementwise entry points (DITNORM_DTYPE_*)
 _DTYPE_CODES = {torch.bfloat16: 0, torch.float16: 1}
-# ... and of the conv-bias epilogue
+# ... of the conv-bias epilogue, and of the backward
 _EPI_DTYPES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
+_BWD_DTYPES = {torch.bfloat16: 0, torch.float32: 2}
 
 _SIGNATURES = {
     "ln_modulate": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp],
@@ -66,9 +67,9 @@ _SIGNATURES = {
     "modulate_scale_shift": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp],
     "residual_gate_add": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp],
     "ln_modulate_backward": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp,
-                             _i64, _vp, _vp, _vp],
+                             _i64, _vp, _vp, _i32, _vp],
     "ln_modulate_backward_noalloc": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
-                                     _f32, _vp, _vp, _vp],
+                                     _f32, _vp, _vp, _i32, _vp],
     "ditnorm_copy": [_vp, _vp, _i64, _vp],
     "ln_modulate_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp],
     "ln_modulate_folded_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _vp,
@@ -83,7 +84,7 @@ _SIGNATURES = {
     "modulate_scale_shift_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32],
     "residual_gate_add_supported": [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32],
     "ln_modulate_backward_supported": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
-                                       _f32, _vp, _i64, _vp, _vp],
+                                       _f32, _vp, _i64, _vp, _vp, _i32],
     "ditnorm_last_hip_error": [],
     "ditnorm_version": [],
 }
@@ -100,7 +101,7 @@ def load(path: str = LIB_PATH):
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
-        lib.ln_modulate_backward_workspace_bytes.argtypes = [_i64, _i64, _i64]
+        lib.ln_modulate_backward_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32]
         lib.ln_modulate_backward_workspace_bytes.restype = _i64
         lib.ditnorm_status_string.argtypes = [ctypes.c_int]
         lib.ditnorm_status_string.restype = ctypes.c_char_p
@@ -398,24 +399,24 @@ def residual_gate_add(update, residual, gate, out=None):
     return out
 
 
-def ln_modulate_backward_workspace_bytes(rows, cols, rows_per_batch):
+def ln_modulate_backward_workspace_bytes(rows, cols, rows_per_batch, dtype=torch.bfloat16):
     """Bytes of device workspace ln_modulate_backward needs (host-only)."""
-    n = load().ln_modulate_backward_workspace_bytes(rows, cols, rows_per_batch)
+    n = load().ln_modulate_backward_workspace_bytes(rows, cols, rows_per_batch,
+                                                    _BWD_DTYPES[dtype])
     if n < 0:
         raise ValueError("invalid sizes")
     return n
 
 
-def ln_modulate_backward(x, scale, d_out, eps=1e-6, *, d_x=None, d_scale=None, d_shift=None,
-                         workspace=None, mean_out=None, rstd_out=None):
-    """Gradients of LN(x) * (1 + scale) + shift: returns (d_x bf16 like x,
-    d_scale fp32 [B, D], d_shift fp32 [B, D]).  x, d_out (..., D) bf16; scale
-    (D,), (B, D) or (B, 1, D) bf16.  The workspace (uint8 device tensor) is
-    allocated here when the call needs one and none is given."""
-    _act(x, "x")
+def _bwd_args(x, scale, d_out, d_x, d_scale, d_shift):
+    """Checked backward operands: x, d_out (..., D) and scale (D,), (B, D) or
+    (B, 1, D) of one storage type (bf16, or fp32 for the fp32 stream)."""
+    if x.dtype not in _BWD_DTYPES:
+        raise TypeError(f"x must be bf16 or fp32, got {x.dtype}")
+    _act(x, "x", dtype=x.dtype)
     _like(d_out, x, "d_out")
     rows, cols = _rows_cols(x)
-    scale, b, stride = _mod(scale, "scale", cols, x.device)
+    scale, b, stride = _mod(scale, "scale", cols, x.device, dtype=x.dtype)
     rpb = _batch(rows, b)
     d_x = torch.empty_like(x) if d_x is None else _like(d_x, x, "d_x")
     f32 = dict(dtype=torch.float32, device=x.device)
@@ -425,8 +426,21 @@ def ln_modulate_backward(x, scale, d_out, eps=1e-6, *, d_x=None, d_scale=None, d
         if (t.dtype != torch.float32 or t.numel() != b * cols or not t.is_contiguous()
                 or t.device != x.device):
             raise ValueError(f"{nm} must be a contiguous fp32 tensor of {b}x{cols} on {x.device}")
+    return rows, cols, scale, stride, rpb, d_x, d_scale, d_shift
+
+
+def ln_modulate_backward(x, scale, d_out, eps=1e-6, *, d_x=None, d_scale=None, d_shift=None,
+                         workspace=None, mean_out=None, rstd_out=None):
+    """Gradients of LN(x) * (1 + scale) + shift: returns (d_x like x,
+    d_scale fp32 [B, D], d_shift fp32 [B, D]).  x, d_out (..., D) and scale
+    (D,), (B, D) or (B, 1, D), all bf16 or all fp32.  The workspace (uint8
+    device tensor) is allocated here when the call needs one and none is
+    given."""
+    rows, cols, scale, stride, rpb, d_x, d_scale, d_shift = _bwd_args(
+        x, scale, d_out, d_x, d_scale, d_shift)
+    dt = _BWD_DTYPES[x.dtype]
     # -1 (sizes the call rejects): no workspace, and the call reports why
-    need = load().ln_modulate_backward_workspace_bytes(rows, cols, rpb) if rows else 0
+    need = load().ln_modulate_backward_workspace_bytes(rows, cols, rpb, dt) if rows else 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     if workspace is not None and (workspace.device != x.device or not workspace.is_contiguous()):
@@ -435,7 +449,7 @@ def ln_modulate_backward(x, scale, d_out, eps=1e-6, *, d_x=None, d_scale=None, d
     _call("ln_modulate_backward", _p(x), _p(scale), _p(d_out), _p(d_x), _p(d_scale), _p(d_shift),
           rows, cols, rpb, stride, eps, _p(workspace), ws_bytes,
           _p(_f32_out(mean_out, rows, "mean_out", x.device)),
-          _p(_f32_out(rstd_out, rows, "rstd_out", x.device)), _stream(x))
+          _p(_f32_out(rstd_out, rows, "rstd_out", x.device)), dt, _stream(x))
     return d_x, d_scale, d_shift
 
 
@@ -448,23 +462,12 @@ def ln_modulate_backward_noalloc(x, scale, d_out, eps=1e-6, *, d_x=None, d_scale
     DitnormError with status SCRATCH_EXCEEDED when the partial sums do not
     fit NOALLOC_SCRATCH_BYTES.  Calls overlapping in time on one device race
     on that array."""
-    _act(x, "x")
-    _like(d_out, x, "d_out")
-    rows, cols = _rows_cols(x)
-    scale, b, stride = _mod(scale, "scale", cols, x.device)
-    rpb = _batch(rows, b)
-    d_x = torch.empty_like(x) if d_x is None else _like(d_x, x, "d_x")
-    f32 = dict(dtype=torch.float32, device=x.device)
-    d_scale = torch.empty((b, cols), **f32) if d_scale is None else d_scale
-    d_shift = torch.empty((b, cols), **f32) if d_shift is None else d_shift
-    for t, nm in ((d_scale, "d_scale"), (d_shift, "d_shift")):
-        if (t.dtype != torch.float32 or t.numel() != b * cols or not t.is_contiguous()
-                or t.device != x.device):
-            raise ValueError(f"{nm} must be a contiguous fp32 tensor of {b}x{cols} on {x.device}")
+    rows, cols, scale, stride, rpb, d_x, d_scale, d_shift = _bwd_args(
+        x, scale, d_out, d_x, d_scale, d_shift)
     _call("ln_modulate_backward_noalloc", _p(x), _p(scale), _p(d_out), _p(d_x), _p(d_scale),
           _p(d_shift), rows, cols, rpb, stride, eps,
           _p(_f32_out(mean_out, rows, "mean_out", x.device)),
-          _p(_f32_out(rstd_out, rows, "rstd_out", x.device)), _stream(x))
+          _p(_f32_out(rstd_out, rows, "rstd_out", x.device)), _BWD_DTYPES[x.dtype], _stream(x))
     return d_x, d_scale, d_shift
 
 

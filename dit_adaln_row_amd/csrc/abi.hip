@@ -279,12 +279,16 @@ int validate_epilogue(const void *x, const void *bias, const void *h, const void
 int validate_backward(const void *x, const void *scale, const void *d_out, const void *d_x,
                       const float *d_scale, const float *d_shift, int64_t rows, int64_t cols,
                       int64_t rpb, int64_t mbs, float eps, const void *ws, int64_t ws_bytes,
-                      const float *mean_out, const float *rstd_out, bool lib_scratch = false) {
+                      const float *mean_out, const float *rstd_out, int dtype,
+                      bool lib_scratch = false) {
+  if (dtype != DITNORM_DTYPE_BF16 && dtype != DITNORM_DTYPE_F32) return DITNORM_INVALID_ARGUMENT;
   int st = check_rows(rows, cols, rpb, mbs, eps);
   if (st != DITNORM_OK || rows == 0) return st;
-  if (cols > DITNORM_MAX_BACKWARD_COLS) return DITNORM_UNSUPPORTED;
+  if (cols > (dtype == DITNORM_DTYPE_F32 ? DITNORM_MAX_BACKWARD_F32_COLS
+                                         : DITNORM_MAX_BACKWARD_COLS))
+    return DITNORM_UNSUPPORTED;
   if (!x || !scale || !d_out || !d_x || !d_scale || !d_shift) return DITNORM_INVALID_ARGUMENT;
-  const BwdLayout L = bwd_layout(rows, cols, rpb);
+  const BwdLayout L = bwd_layout(rows, cols, rpb, dtype);
   // one wavefront per row slot of the fused kernel's workgroups
   if ((rows / rpb) * L.chunks * L.rows_per_chunk > DITNORM_MAX_ROWS) return DITNORM_UNSUPPORTED;
   const int64_t need = L.bytes;
@@ -298,8 +302,8 @@ int validate_backward(const void *x, const void *scale, const void *d_out, const
       !aligned16(d_scale) || !aligned16(d_shift) || ((uintptr_t)ws & 255u) != 0 ||
       !aligned4(mean_out) || !aligned4(rstd_out))
     return DITNORM_UNSUPPORTED;
-  const int64_t act = rows * cols * 2, nb = rows / rpb;
-  const Buf in[] = {{x, act}, {scale, mod_bytes(nb, mbs, cols)}, {d_out, act}};
+  const int64_t es = dtype_size(dtype), act = rows * cols * es, nb = rows / rpb;
+  const Buf in[] = {{x, act}, {scale, mod_bytes(nb, mbs, cols) / 2 * es}, {d_out, act}};
   const Buf o[] = {{d_x, act}, {d_scale, nb * cols * 4}, {d_shift, nb * cols * 4},
                    {ws, need}, {mean_out, rows * 4}, {rstd_out, rows * 4}};
   const int alias[] = {-1, -1, -1, -1, -1, -1};
@@ -312,13 +316,14 @@ int validate_backward(const void *x, const void *scale, const void *d_out, const
 int backward_launch(const void *x, const void *scale, const void *d_out, void *d_x,
                     float *d_scale, float *d_shift, int64_t rows, int64_t cols, int64_t rpb,
                     int64_t mbs, float eps, char *ws, float *mean_out, float *rstd_out,
-                    void *stream) {
-  const BwdLayout L = bwd_layout(rows, cols, rpb);
+                    int dtype, void *stream) {
+  const BwdLayout L = bwd_layout(rows, cols, rpb, dtype);
   BwdArgs a{};
-  a.x = (const uint16_t *)x;
-  a.scale = (const uint16_t *)scale;
-  a.d_out = (const uint16_t *)d_out;
-  a.d_x = (uint16_t *)d_x;
+  a.x = x;
+  a.scale = scale;
+  a.d_out = d_out;
+  a.d_x = d_x;
+  a.dtype = dtype;
   a.d_scale = d_scale;
   a.d_shift = d_shift;
   a.mean_out = mean_out;
@@ -630,41 +635,46 @@ int residual_gate_add_supported(const void *update, const void *residual, const 
 }
 
 int64_t ln_modulate_backward_workspace_bytes(int64_t rows, int64_t cols,
-                                             int64_t rows_per_batch) {
+                                             int64_t rows_per_batch, int dtype) {
   if (rows < 0 || cols <= 0 || rows_per_batch <= 0 || rows % rows_per_batch != 0) return -1;
-  if (rows > DITNORM_MAX_ROWS || cols > DITNORM_MAX_BACKWARD_COLS) return -1;  // the call rejects them
+  if (dtype != DITNORM_DTYPE_BF16 && dtype != DITNORM_DTYPE_F32) return -1;
+  if (rows > DITNORM_MAX_ROWS ||
+      cols > (dtype == DITNORM_DTYPE_F32 ? DITNORM_MAX_BACKWARD_F32_COLS
+                                         : DITNORM_MAX_BACKWARD_COLS))
+    return -1;  // the call rejects them
   if (rows == 0) return 0;
-  return bwd_layout(rows, cols, rows_per_batch).bytes;
+  return bwd_layout(rows, cols, rows_per_batch, dtype).bytes;
 }
 
 int ln_modulate_backward(const void *x, const void *scale, const void *d_out, void *d_x,
                          float *d_scale, float *d_shift, int64_t rows, int64_t cols,
                          int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
                          void *workspace, int64_t workspace_bytes, float *mean_out,
-                         float *rstd_out, void *stream) {
+                         float *rstd_out, int dtype, void *stream) {
   int st = validate_backward(x, scale, d_out, d_x, d_scale, d_shift, rows, cols, rows_per_batch,
                              mod_batch_stride, eps, workspace, workspace_bytes, mean_out,
-                             rstd_out);
+                             rstd_out, dtype);
   if (st != DITNORM_OK || rows == 0) return st;
   DeviceInfo dev;
   if ((st = current_device(&dev)) != DITNORM_OK) return st;
   return backward_launch(x, scale, d_out, d_x, d_scale, d_shift, rows, cols, rows_per_batch,
-                         mod_batch_stride, eps, (char *)workspace, mean_out, rstd_out, stream);
+                         mod_batch_stride, eps, (char *)workspace, mean_out, rstd_out, dtype,
+                         stream);
 }
 
 int ln_modulate_backward_noalloc(const void *x, const void *scale, const void *d_out, void *d_x,
                                  float *d_scale, float *d_shift, int64_t rows, int64_t cols,
                                  int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
-                                 float *mean_out, float *rstd_out, void *stream) {
+                                 float *mean_out, float *rstd_out, int dtype, void *stream) {
   int st = validate_backward(x, scale, d_out, d_x, d_scale, d_shift, rows, cols, rows_per_batch,
-                             mod_batch_stride, eps, nullptr, 0, mean_out, rstd_out, true);
+                             mod_batch_stride, eps, nullptr, 0, mean_out, rstd_out, dtype, true);
   if (st != DITNORM_OK || rows == 0) return st;
   DeviceInfo dev;
   if ((st = current_device(&dev)) != DITNORM_OK) return st;
   char *ws = nullptr;
   if ((st = scratch_address(dev.device, &ws)) != DITNORM_OK) return st;
   return backward_launch(x, scale, d_out, d_x, d_scale, d_shift, rows, cols, rows_per_batch,
-                         mod_batch_stride, eps, ws, mean_out, rstd_out, stream);
+                         mod_batch_stride, eps, ws, mean_out, rstd_out, dtype, stream);
 }
 
 int ln_modulate_backward_supported(const void *x, const void *scale, const void *d_out,
@@ -672,10 +682,10 @@ int ln_modulate_backward_supported(const void *x, const void *scale, const void 
                                    int64_t rows, int64_t cols, int64_t rows_per_batch,
                                    int64_t mod_batch_stride, float eps, const void *workspace,
                                    int64_t workspace_bytes, const float *mean_out,
-                                   const float *rstd_out) {
+                                   const float *rstd_out, int dtype) {
   return validate_backward(x, scale, d_out, d_x, d_scale, d_shift, rows, cols, rows_per_batch,
                            mod_batch_stride, eps, workspace, workspace_bytes, mean_out,
-                           rstd_out) == DITNORM_OK;
+                           rstd_out, dtype) == DITNORM_OK;
 }
 
 int ditnorm_copy(const void *src, void *dst, int64_t bytes, void *stream) {

@@ -33,6 +33,14 @@
 //
 // The result depends only on the batch's token count: no atomics, no order
 // chosen at run time, bitwise equal for any batch size or batch position.
+//
+// Storage types (DT): bf16 (0) and the page's fp32 stream (2).  A 16-byte
+// vector holds 8 bf16 or 4 fp32 values, so a lane keeps the same 48 values of
+// a 3072-column row either way; in fp32 those take twice the registers, so
+// 1 + scale is not kept per lane but staged once per workgroup in LDS (the
+// workgroup's tokens share one batch), the workgroups hold 4 tokens, and d_x
+// is the binary64 value rounded once to fp32.
+#include "../../include/ditnorm.h"
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -55,6 +63,25 @@ __device__ __forceinline__ float f64_round_odd_f32(double d) {
   return f;
 }
 
+// Address of element `elem` of a DT array, as the 16-bit pointer the vector
+// load and store helpers take.
+template <int DT>
+__device__ __forceinline__ const uint16_t *at(const void *base, int64_t elem) {
+  if constexpr (DT == 2) return (const uint16_t *)((const float *)base + elem);
+  else return (const uint16_t *)base + elem;
+}
+
+// A 16-byte vector of DT values widened to fp32 (8 bf16 or 4 fp32 values).
+template <int DT>
+__device__ __forceinline__ void widen_vec(const uint4 v, float f[8]) {
+  if constexpr (DT == 2) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  } else {
+    unpack8(v, f);
+  }
+}
+
 // The balanced fold of N values by adjacent pairs (N a power of two).
 template <int N>
 __device__ __forceinline__ float tree_fold(const float *v) {
@@ -68,24 +95,32 @@ __device__ __forceinline__ float tree_fold(const float *v) {
 // ---------------------------------------------------------------------------
 // one row: statistics and d_x.  xv / dv keep the raw row for the token sums.
 // ---------------------------------------------------------------------------
-template <int NV, bool FULL>
+template <int NV, bool FULL, int DT>
 __device__ __forceinline__ void bwd_row(const BwdArgs &a, int64_t row, int64_t mo, int lane,
                                         uint4 (&xv)[NV], uint4 (&dv)[NV], float &mean_f,
-                                        float &rstd_f) {
+                                        float &rstd_f, const float *s1_lds) {
+  constexpr int VE = DT == 2 ? 4 : 8;  // values per 16-byte vector
   const int cols = a.cols;
-  const int nvec = cols >> 3;
+  const int nvec = cols / VE;
   const int64_t base = row * (int64_t)cols;
   const uint4 zero = {0, 0, 0, 0};
   auto ok = [&](int k) { return FULL || lane + 64 * k < nvec; };
-  auto col = [&](int k) { return (lane + 64 * k) * 8; };
+  auto col = [&](int k) { return (lane + 64 * k) * VE; };
+  // fp32: 1 + scale of the vector's 4 columns from the workgroup's LDS copy
+  auto scale1 = [&](const uint4 &, int k, float s1[8]) {
+    const float4 q = *reinterpret_cast<const float4 *>(s1_lds + col(k));
+    s1[0] = q.x; s1[1] = q.y; s1[2] = q.z; s1[3] = q.w;
+  };
 
-  uint4 sv[NV];
+  uint4 sv[DT == 2 ? 1 : NV];
 #pragma unroll
-  for (int k = 0; k < NV; ++k) xv[k] = ok(k) ? ld16s(a.x + base + col(k)) : zero;
+  for (int k = 0; k < NV; ++k) xv[k] = ok(k) ? ld16s(at<DT>(a.x, base + col(k))) : zero;
 #pragma unroll
-  for (int k = 0; k < NV; ++k) dv[k] = ok(k) ? ld16s(a.d_out + base + col(k)) : zero;
+  for (int k = 0; k < NV; ++k) dv[k] = ok(k) ? ld16s(at<DT>(a.d_out, base + col(k))) : zero;
+  if constexpr (DT != 2) {
 #pragma unroll
-  for (int k = 0; k < NV; ++k) sv[k] = ok(k) ? ld16(a.scale + mo + col(k)) : zero;
+    for (int k = 0; k < NV; ++k) sv[k] = ok(k) ? ld16(at<DT>(a.scale, mo + col(k))) : zero;
+  }
 
   // one pass of binary64 sums over the raw inputs (padding contributes
   // zeros): S1 = sum x, S2 = sum x^2 (the statistics), G = sum g and
@@ -95,15 +130,21 @@ __device__ __forceinline__ void bwd_row(const BwdArgs &a, int64_t row, int64_t m
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     float v[8], d[8], sc[8];
-    unpack8(xv[k], v);
-    unpack8(dv[k], d);
-    unpack8(sv[k], sc);
+    widen_vec<DT>(xv[k], v);
+    widen_vec<DT>(dv[k], d);
+    if constexpr (DT == 2) {
+      if (!ok(k)) continue;  // (the LDS copy ends at cols)
+      scale1(sv[0], k, sc);  // 1 + scale
+    } else {
+      unpack8(sv[k], sc);  // scale
+    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < VE; ++e) {
       const double xd = (double)v[e];
       m.s1 += xd;
       m.s2 = __builtin_fma(xd, xd, m.s2);
-      const double g = (double)d[e] * (double)(1.0f + sc[e]);
+      const double g = DT == 2 ? (double)d[e] * (double)sc[e]
+                               : (double)d[e] * (double)(1.0f + sc[e]);
       sg += g;
       sgx = __builtin_fma(g, xd, sgx);
     }
@@ -127,36 +168,50 @@ __device__ __forceinline__ void bwd_row(const BwdArgs &a, int64_t row, int64_t m
   for (int k = 0; k < NV; ++k) {
     launder(xv[k]);
     launder(dv[k]);
-    launder(sv[k]);
+    if constexpr (DT != 2) launder(sv[k]);
   }
 
-  // d_x, one rounding to bf16
+  // d_x, one rounding to the storage type
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     if (!ok(k)) continue;
     float v[8], d[8], sc[8], o[8];
-    unpack8(xv[k], v);
-    unpack8(dv[k], d);
-    unpack8(sv[k], sc);
-    // Nearest-even into binary32 and then into bf16 rounds once, correctly,
-    // unless the binary32 value is inexact and lands exactly on a bf16
-    // halfway point (low 16 bits 0x8000): only then, and only for the
-    // wavefront that meets one, the rounding goes through round-to-odd.
-    // (one ballot per element, the wave masks OR-ed in scalar registers)
-    double t[8];
-    uint64_t tie = 0;
+    widen_vec<DT>(xv[k], v);
+    widen_vec<DT>(dv[k], d);
+    if constexpr (DT == 2) {  // binary64 -> fp32: one correctly rounded conversion
+      scale1(sv[0], k, sc);  // 1 + scale
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const double g = (double)d[e] * (double)(1.0f + sc[e]);
-      t[e] = __builtin_fma(B, (double)v[e], __builtin_fma(A, g, C));
-      o[e] = (float)t[e];
-      tie |= __builtin_amdgcn_ballot_w64((__float_as_uint(o[e]) & 0xFFFFu) == 0x8000u);
-    }
-    if (tie != 0) {
+      for (int e = 0; e < 4; ++e) {
+        const double g = (double)d[e] * (double)sc[e];
+        o[e] = (float)__builtin_fma(B, (double)v[e], __builtin_fma(A, g, C));
+      }
+      uint4 q;
+      q.x = __float_as_uint(o[0]); q.y = __float_as_uint(o[1]);
+      q.z = __float_as_uint(o[2]); q.w = __float_as_uint(o[3]);
+      st16s((uint16_t *)at<DT>(a.d_x, base + col(k)), q);
+      continue;
+    } else {
+      // Nearest-even into binary32 and then into bf16 rounds once, correctly,
+      // unless the binary32 value is inexact and lands exactly on a bf16
+      // halfway point (low 16 bits 0x8000): only then, and only for the
+      // wavefront that meets one, the rounding goes through round-to-odd.
+      // (one ballot per element, the wave masks OR-ed in scalar registers)
+      unpack8(sv[k], sc);  // scale
+      double t[8];
+      uint64_t tie = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = f64_round_odd_f32(t[e]);
+      for (int e = 0; e < 8; ++e) {
+        const double g = (double)d[e] * (double)(1.0f + sc[e]);
+        t[e] = __builtin_fma(B, (double)v[e], __builtin_fma(A, g, C));
+        o[e] = (float)t[e];
+        tie |= __builtin_amdgcn_ballot_w64((__float_as_uint(o[e]) & 0xFFFFu) == 0x8000u);
+      }
+      if (tie != 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = f64_round_odd_f32(t[e]);
+      }
+      st16s((uint16_t *)at<DT>(a.d_x, base + col(k)), pack8(o));
     }
-    st16s(a.d_x + base + col(k), pack8(o));
   }
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
@@ -171,16 +226,19 @@ __device__ __forceinline__ void bwd_row(const BwdArgs &a, int64_t row, int64_t m
 // subtree sums; with a single chunk per batch they are the final sums, and
 // the +0 padding of the rest of the 32-token group is added here.
 // ---------------------------------------------------------------------------
-template <int NV, bool FULL, int R>
+template <int NV, bool FULL, int R, int DT>
 __global__ __launch_bounds__(64 * R) void bwd_fused_kernel(const BwdArgs a, int64_t chunks,
                                                            float *out_shift, float *out_scale,
                                                            int final_level) {
-  // a step moves VS 16-byte vectors per lane (VS * 512 columns) through LDS,
-  // and every thread folds one column pair of them
+  // a step moves VS 16-byte vectors per lane through LDS (VS * 256 dwords:
+  // 512 bf16 or 256 fp32 columns), and every thread folds one dword column
+  // of them (2 bf16 columns or 1 fp32 column)
   constexpr int VS = R / 4;
   constexpr int STEPS = (NV + VS - 1) / VS;
+  constexpr int CPD = DT == 2 ? 1 : 2;  // columns per dword
   __shared__ float stat[R][2];
   __shared__ __attribute__((aligned(16))) uint32_t tile[2][R][2][VS * 256];  // [buffer][row][x | d_out][dword]
+  __shared__ __attribute__((aligned(16))) float s1_lds[DT == 2 ? DITNORM_MAX_BACKWARD_F32_COLS : 1];
 
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
@@ -188,12 +246,18 @@ __global__ __launch_bounds__(64 * R) void bwd_fused_kernel(const BwdArgs a, int6
   const int64_t left = a.rows_per_batch - j * R;
   const int nrow = (int)(left < R ? left : R);  // tokens of this chunk
   const int64_t row = b * a.rows_per_batch + j * R + w;
-  const int nvec = a.cols >> 3;
+  const int nvec = a.cols / (DT == 2 ? 4 : 8);
+
+  if constexpr (DT == 2) {  // 1 + scale of the chunk's batch, once per workgroup
+    const float *sc = (const float *)a.scale + b * a.mod_stride;
+    for (int i = threadIdx.x; i < a.cols; i += 64 * R) s1_lds[i] = 1.0f + sc[i];
+    lds_barrier();
+  }
 
   uint4 xv[NV], dv[NV];
   if (w < nrow) {
     float mean_f, rstd_f;
-    bwd_row<NV, FULL>(a, row, b * a.mod_stride, lane, xv, dv, mean_f, rstd_f);
+    bwd_row<NV, FULL, DT>(a, row, b * a.mod_stride, lane, xv, dv, mean_f, rstd_f, s1_lds);
     if (lane == 0) {
       stat[w][0] = mean_f;
       stat[w][1] = rstd_f;
@@ -204,7 +268,7 @@ __global__ __launch_bounds__(64 * R) void bwd_fused_kernel(const BwdArgs a, int6
 
   // token sums of the chunk
   const int vk = (int)(threadIdx.x >> 8);  // vector of the step this thread folds
-  const int pr = (int)(threadIdx.x & 255);  // its column pair within that vector
+  const int pr = (int)(threadIdx.x & 255);  // its dword within that vector
   float mu[R], rs[R];
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
@@ -228,7 +292,7 @@ __global__ __launch_bounds__(64 * R) void bwd_fused_kernel(const BwdArgs a, int6
       }
     }
     const int k = s * VS + vk;
-    const int c = k * 512 + 2 * pr;
+    const int c = (k * 256 + pr) * CPD;
     if (k < NV && (FULL || c < a.cols)) {
       float s0[R], s1[R], c0[R], c1[R];
 #pragma unroll
@@ -236,26 +300,42 @@ __global__ __launch_bounds__(64 * R) void bwd_fused_kernel(const BwdArgs a, int6
         if (i < nrow) {
           const uint32_t xw = tile[buf][i][0][vk * 256 + pr];
           const uint32_t dw = tile[buf][i][1][vk * 256 + pr];
-          const float x0 = bf_lo(xw), x1 = bf_hi(xw), d0 = bf_lo(dw), d1 = bf_hi(dw);
-          s0[i] = d0;
-          s1[i] = d1;
-          c0[i] = d0 * (rs[i] * (x0 - mu[i]));
-          c1[i] = d1 * (rs[i] * (x1 - mu[i]));
+          if constexpr (DT == 2) {
+            const float x0 = __uint_as_float(xw), d0 = __uint_as_float(dw);
+            s0[i] = d0;
+            c0[i] = d0 * (rs[i] * (x0 - mu[i]));
+          } else {
+            const float x0 = bf_lo(xw), x1 = bf_hi(xw), d0 = bf_lo(dw), d1 = bf_hi(dw);
+            s0[i] = d0;
+            s1[i] = d1;
+            c0[i] = d0 * (rs[i] * (x0 - mu[i]));
+            c1[i] = d1 * (rs[i] * (x1 - mu[i]));
+          }
         } else {  // the tree's padding
           s0[i] = s1[i] = c0[i] = c1[i] = 0.0f;
         }
       }
-      float2 hs = make_float2(tree_fold<R>(s0), tree_fold<R>(s1));
-      float2 hc = make_float2(tree_fold<R>(c0), tree_fold<R>(c1));
-      if (final_level) {  // the rest of the 32-token group is +0
-        hs.x += 0.0f;
-        hs.y += 0.0f;
-        hc.x += 0.0f;
-        hc.y += 0.0f;
-      }
       const int64_t o = (int64_t)blockIdx.x * a.cols + c;
-      *reinterpret_cast<float2 *>(out_shift + o) = hs;
-      *reinterpret_cast<float2 *>(out_scale + o) = hc;
+      if constexpr (DT == 2) {
+        float hs = tree_fold<R>(s0), hc = tree_fold<R>(c0);
+        if (final_level) {  // the rest of the 32-token group is +0
+          hs += 0.0f;
+          hc += 0.0f;
+        }
+        out_shift[o] = hs;
+        out_scale[o] = hc;
+      } else {
+        float2 hs = make_float2(tree_fold<R>(s0), tree_fold<R>(s1));
+        float2 hc = make_float2(tree_fold<R>(c0), tree_fold<R>(c1));
+        if (final_level) {  // the rest of the 32-token group is +0
+          hs.x += 0.0f;
+          hs.y += 0.0f;
+          hc.x += 0.0f;
+          hc.y += 0.0f;
+        }
+        *reinterpret_cast<float2 *>(out_shift + o) = hs;
+        *reinterpret_cast<float2 *>(out_scale + o) = hc;
+      }
     }
   }
 }
@@ -327,7 +407,7 @@ static int64_t first_fanin(int64_t rows_per_batch, int rows_per_chunk) {
   return rows_per_batch <= 32 ? per_group : 32 * per_group;
 }
 
-BwdLayout bwd_layout(int64_t rows, int64_t cols, int64_t rows_per_batch) {
+BwdLayout bwd_layout(int64_t rows, int64_t cols, int64_t rows_per_batch, int dtype) {
   BwdLayout L{};
   const int64_t nb = rows / rows_per_batch;
   auto up = [](int64_t v) { return (v + 255) / 256 * 256; };
@@ -341,8 +421,11 @@ BwdLayout bwd_layout(int64_t rows, int64_t cols, int64_t rows_per_batch) {
   // sums cost more).  Batches of 5-8 tokens keep one 8-row workgroup and one
   // launch.
   const int64_t wg8 = nb * ((rows_per_batch + 7) / 8);
-  L.rows_per_chunk =
-      (rows_per_batch <= 4 || cols > 3072 || (rows_per_batch > 8 && wg8 <= 128)) ? 4 : 8;
+  // (fp32: 4 tokens, whose rows already take the registers 8 bf16 rows do)
+  L.rows_per_chunk = (dtype == 2 || rows_per_batch <= 4 || cols > 3072 ||
+                      (rows_per_batch > 8 && wg8 <= 128))
+                         ? 4
+                         : 8;
   L.chunks = (rows_per_batch + L.rows_per_chunk - 1) / L.rows_per_chunk;
   int64_t n1 = 1;
   if (L.chunks > 1) {
@@ -357,29 +440,46 @@ BwdLayout bwd_layout(int64_t rows, int64_t cols, int64_t rows_per_batch) {
   return L;
 }
 
-template <int NV, bool FULL, int R>
+template <int NV, bool FULL, int R, int DT>
 static void launch_fused(const BwdArgs &a, int64_t nb, int64_t chunks, float *os, float *oc,
                          hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_fused_kernel<NV, FULL, R>), dim3((unsigned)(nb * chunks)), dim3(64 * R),
-                     0, stream, a, chunks, os, oc, chunks == 1 ? 1 : 0);
+  hipLaunchKernelGGL((bwd_fused_kernel<NV, FULL, R, DT>), dim3((unsigned)(nb * chunks)),
+                     dim3(64 * R), 0, stream, a, chunks, os, oc, chunks == 1 ? 1 : 0);
 }
 
 template <int R>
 static void launch_fused_r(const BwdArgs &a, int64_t nb, int64_t chunks, float *os, float *oc,
                            hipStream_t stream) {
   switch (a.cols >> 3) {
-    case 128: launch_fused<2, true, R>(a, nb, chunks, os, oc, stream); return;
-    case 256: launch_fused<4, true, R>(a, nb, chunks, os, oc, stream); return;
-    case 384: launch_fused<6, true, R>(a, nb, chunks, os, oc, stream); return;
-    case 512: launch_fused<8, true, R>(a, nb, chunks, os, oc, stream); return;
+    case 128: launch_fused<2, true, R, 0>(a, nb, chunks, os, oc, stream); return;
+    case 256: launch_fused<4, true, R, 0>(a, nb, chunks, os, oc, stream); return;
+    case 384: launch_fused<6, true, R, 0>(a, nb, chunks, os, oc, stream); return;
+    case 512: launch_fused<8, true, R, 0>(a, nb, chunks, os, oc, stream); return;
     default: break;
   }
   const int nvec = a.cols >> 3;
-  if (nvec <= 64) launch_fused<1, false, R>(a, nb, chunks, os, oc, stream);
-  else if (nvec <= 128) launch_fused<2, false, R>(a, nb, chunks, os, oc, stream);
-  else if (nvec <= 256) launch_fused<4, false, R>(a, nb, chunks, os, oc, stream);
-  else if (nvec <= 384) launch_fused<6, false, R>(a, nb, chunks, os, oc, stream);
-  else launch_fused<8, false, R>(a, nb, chunks, os, oc, stream);
+  if (nvec <= 64) launch_fused<1, false, R, 0>(a, nb, chunks, os, oc, stream);
+  else if (nvec <= 128) launch_fused<2, false, R, 0>(a, nb, chunks, os, oc, stream);
+  else if (nvec <= 256) launch_fused<4, false, R, 0>(a, nb, chunks, os, oc, stream);
+  else if (nvec <= 384) launch_fused<6, false, R, 0>(a, nb, chunks, os, oc, stream);
+  else launch_fused<8, false, R, 0>(a, nb, chunks, os, oc, stream);
+}
+
+// fp32 rows (4 values per vector, up to DITNORM_MAX_BACKWARD_F32_COLS columns)
+static void launch_fused_f32(const BwdArgs &a, int64_t nb, int64_t chunks, float *os, float *oc,
+                             hipStream_t stream) {
+  switch (a.cols >> 2) {
+    case 256: launch_fused<4, true, 4, 2>(a, nb, chunks, os, oc, stream); return;
+    case 512: launch_fused<8, true, 4, 2>(a, nb, chunks, os, oc, stream); return;
+    case 768: launch_fused<12, true, 4, 2>(a, nb, chunks, os, oc, stream); return;
+    default: break;
+  }
+  const int nvec = a.cols >> 2;
+  if (nvec <= 64) launch_fused<1, false, 4, 2>(a, nb, chunks, os, oc, stream);
+  else if (nvec <= 128) launch_fused<2, false, 4, 2>(a, nb, chunks, os, oc, stream);
+  else if (nvec <= 256) launch_fused<4, false, 4, 2>(a, nb, chunks, os, oc, stream);
+  else if (nvec <= 512) launch_fused<8, false, 4, 2>(a, nb, chunks, os, oc, stream);
+  else launch_fused<12, false, 4, 2>(a, nb, chunks, os, oc, stream);
 }
 
 hipError_t launch_backward(const BwdArgs &a, const BwdLayout &L, float *part0, float *part1,
@@ -389,7 +489,8 @@ hipError_t launch_backward(const BwdArgs &a, const BwdLayout &L, float *part0, f
   float *s_out = L.chunks == 1 ? a.d_shift : part0;
   float *c_out = L.chunks == 1 ? a.d_scale : part0 + pf;
   if (nb * L.chunks * 64 * L.rows_per_chunk > (int64_t)INT32_MAX) return hipErrorInvalidConfiguration;
-  if (L.rows_per_chunk == 4) launch_fused_r<4>(a, nb, L.chunks, s_out, c_out, stream);
+  if (a.dtype == 2) launch_fused_f32(a, nb, L.chunks, s_out, c_out, stream);
+  else if (L.rows_per_chunk == 4) launch_fused_r<4>(a, nb, L.chunks, s_out, c_out, stream);
   else launch_fused_r<8>(a, nb, L.chunks, s_out, c_out, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -99,11 +99,12 @@ hipError_t launch_elementwise(const ElementwiseArgs &a, int op, int dtype, hipSt
 
 // Backward of LN (no affine) + modulate: d_x, and the token sums d_scale,
 // d_shift by fixed balanced trees.
+// x, scale, d_out, d_x of storage type dtype (0 bf16, 2 fp32).
 struct BwdArgs {
-  const uint16_t *x;      // [rows, cols]
-  const uint16_t *scale;  // [B, mod_stride]
-  const uint16_t *d_out;  // [rows, cols]
-  uint16_t *d_x;          // [rows, cols]
+  const void *x;          // [rows, cols]
+  const void *scale;      // [B, mod_stride]
+  const void *d_out;      // [rows, cols]
+  void *d_x;              // [rows, cols]
   float *d_scale;         // [B, cols]
   float *d_shift;         // [B, cols]
   float *mean_out;        // optional [rows]
@@ -113,6 +114,7 @@ struct BwdArgs {
   int64_t mod_stride;
   int32_t cols;
   float eps;
+  int32_t dtype;
 };
 // Workspace layout (byte offsets; every region 256-byte aligned): the
 // partial tree sums.  None when a batch has at most rows_per_chunk tokens.
@@ -124,7 +126,7 @@ struct BwdLayout {
                                     // 0 if that level is the last
   int64_t bytes;
 };
-BwdLayout bwd_layout(int64_t rows, int64_t cols, int64_t rows_per_batch);
+BwdLayout bwd_layout(int64_t rows, int64_t cols, int64_t rows_per_batch, int dtype);
 hipError_t launch_backward(const BwdArgs &a, const BwdLayout &L, float *part0, float *part1,
                            hipStream_t stream);
 

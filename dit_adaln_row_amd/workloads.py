@@ -72,7 +72,8 @@ class Launch:
             return 3 * r * c * BF16 + self.n_mod_rows * c * BF16
         if self.entry == "ln_modulate_backward":
             # x and d_out read, d_x written, scale read, d_scale and d_shift written
-            return 3 * r * c * BF16 + self.n_mod_rows * c * (BF16 + 2 * F32)
+            es = F32 if self.extra.get("dtype") == "f32" else BF16
+            return 3 * r * c * es + self.n_mod_rows * c * (es + 2 * F32)
         raise KeyError(self.entry)
 
     def label(self) -> str:
@@ -255,6 +256,18 @@ WORKLOADS = {
                 ("x16", "bias", "h16"), 0.0, extra={"residual": True, "dtype": "f16"})),
     ),
 }
+
+
+WORKLOADS["qwen_bwd_f32_2048x3x3072"] = Workload(
+    "qwen_bwd_f32_2048x3x3072", 15,
+    "Qwen-Image-like final adaLN output backward, the fp32 stream at a large conditioning "
+    "batch, (2048,3,3072) fp32: x ~N(0,1.5), d_out ~N(0,1), scale (2048,3072) ~N(0,0.1)",
+    (Tensor("x", (2048 * 3, 3072), 0.0, 1.5, "f32"), Tensor("d_out", (2048 * 3, 3072), 0.0, 1.0, "f32"),
+     Tensor("scale", (2048, 3072), 0.0, 0.1, "f32")),
+    (Launch("ln_modulate_backward_f32", "ln_modulate_backward", 2048 * 3, 3072,
+            ("x", "scale", "d_out"), 1e-6, n_mod_rows=2048,
+            extra={"rows_per_batch": 3, "dtype": "f32"}),),
+)
 
 
 def _flux_micro(L: int, cfg: int) -> Workload:

@@ -93,8 +93,10 @@ extern "C" {
  * rms_modulate) and the largest channel count of the channels_last kernels. */
 #define DITNORM_MAX_COLS 16384
 #define DITNORM_MAX_CHANNELS 4096
-/* Largest row width of ln_modulate_backward. */
+/* Largest row width of ln_modulate_backward (bf16; fp32 rows up to
+ * DITNORM_MAX_BACKWARD_F32_COLS). */
 #define DITNORM_MAX_BACKWARD_COLS 4096
+#define DITNORM_MAX_BACKWARD_F32_COLS 3072
 /* Bytes of the per-device scratch array of ln_modulate_backward_noalloc
  * (32 MiB). */
 #define DITNORM_NOALLOC_SCRATCH_BYTES 33554432LL
@@ -313,15 +315,18 @@ int residual_gate_add(const void *update, const void *residual, const void *gate
  * the group sums again in groups of 32, until one value remains; a short
  * group is padded with +0.  The result for a batch depends only on its own
  * rows and its token count (bitwise batch-invariant).
- * x, d_out, d_x: bf16 [rows, cols]; scale: bf16 [B, cols], row stride
- * mod_batch_stride; d_scale, d_shift: fp32 [B, cols] dense.  cols: multiple
- * of 8, at most DITNORM_MAX_BACKWARD_COLS.  B times rows_per_batch, rounded
- * up to a multiple of the kernel's tokens per workgroup, at most
- * DITNORM_MAX_ROWS; that count is 8 when cols <= 3072 and either
- * rows_per_batch is 5-8 or the batches fill more than 128 eight-token
- * workgroups, else 4.  No output may overlap an input or another output.
+ * dtype: DITNORM_DTYPE_BF16, or DITNORM_DTYPE_F32 for the page's fp32
+ * stream (d_x then the binary64 value rounded once to fp32).  x, d_out, d_x:
+ * dtype [rows, cols]; scale: dtype [B, cols], row stride mod_batch_stride;
+ * d_scale, d_shift: fp32 [B, cols] dense.  cols: multiple of 8, at most
+ * DITNORM_MAX_BACKWARD_COLS (bf16) or DITNORM_MAX_BACKWARD_F32_COLS (fp32).
+ * B times rows_per_batch, rounded up to a multiple of the kernel's tokens
+ * per workgroup, at most DITNORM_MAX_ROWS; that count is 8 for bf16 when
+ * cols <= 3072 and either rows_per_batch is 5-8 or the batches fill more
+ * than 128 eight-token workgroups, else 4 (always 4 for fp32).  No output
+ * may overlap an input or another output.
  * workspace: device memory of at least
- * ln_modulate_backward_workspace_bytes(rows, cols, rows_per_batch) bytes,
+ * ln_modulate_backward_workspace_bytes(rows, cols, rows_per_batch, dtype) bytes,
  * 256-byte aligned, owned by the caller, clobbered by the call (it holds the
  * partial tree sums); when that size is 0 (batches of at most 8 tokens, 4
  * for rows over 3072 columns) workspace may be NULL.  mean_out, rstd_out
@@ -333,7 +338,7 @@ int ln_modulate_backward(const void *x, const void *scale, const void *d_out, vo
                          float *d_scale, float *d_shift, int64_t rows, int64_t cols,
                          int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
                          void *workspace, int64_t workspace_bytes, float *mean_out,
-                         float *rstd_out, void *stream);
+                         float *rstd_out, int dtype, void *stream);
 
 /*
  * ln_modulate_backward_noalloc -- ln_modulate_backward without a workspace
@@ -345,7 +350,7 @@ int ln_modulate_backward(const void *x, const void *scale, const void *d_out, vo
  * DITNORM_NOALLOC_SCRATCH_BYTES that the library holds on every device it
  * runs on (loaded with the library, kept until the process ends).  The call
  * makes no allocation of any kind (no hipMalloc, no hipFree).  A call whose
- * ln_modulate_backward_workspace_bytes(rows, cols, rows_per_batch) exceeds
+ * ln_modulate_backward_workspace_bytes(rows, cols, rows_per_batch, dtype) exceeds
  * DITNORM_NOALLOC_SCRATCH_BYTES returns DITNORM_SCRATCH_EXCEEDED and enqueues
  * nothing.  The partial sums take about one byte per element of x when the
  * kernel runs 8 tokens per workgroup and two when it runs 4 (see
@@ -362,14 +367,14 @@ int ln_modulate_backward(const void *x, const void *scale, const void *d_out, vo
 int ln_modulate_backward_noalloc(const void *x, const void *scale, const void *d_out, void *d_x,
                                  float *d_scale, float *d_shift, int64_t rows, int64_t cols,
                                  int64_t rows_per_batch, int64_t mod_batch_stride, float eps,
-                                 float *mean_out, float *rstd_out, void *stream);
+                                 float *mean_out, float *rstd_out, int dtype, void *stream);
 
 /* Workspace bytes ln_modulate_backward needs (0 for rows == 0; -1 for invalid
- * sizes and for rows above DITNORM_MAX_ROWS or cols above
- * DITNORM_MAX_BACKWARD_COLS, which the call rejects).  Host-only, never
- * touches the GPU. */
+ * sizes or storage type and for rows above DITNORM_MAX_ROWS or cols above
+ * the type's maximum, which the call rejects).  Host-only, never touches the
+ * GPU. */
 int64_t ln_modulate_backward_workspace_bytes(int64_t rows, int64_t cols,
-                                             int64_t rows_per_batch);
+                                             int64_t rows_per_batch, int dtype);
 
 /*
  * *_supported -- 1 if the same call would pass every argument check (it may
@@ -410,7 +415,7 @@ int ln_modulate_backward_supported(const void *x, const void *scale, const void 
                                    int64_t rows, int64_t cols, int64_t rows_per_batch,
                                    int64_t mod_batch_stride, float eps, const void *workspace,
                                    int64_t workspace_bytes, const float *mean_out,
-                                   const float *rstd_out);
+                                   const float *rstd_out, int dtype);
 int modulate_scale_shift_supported(const void *x, const void *scale, const void *shift,
                                    const void *out, int64_t rows, int64_t cols,
                                    int64_t rows_per_batch, int64_t mod_batch_stride, int dtype);

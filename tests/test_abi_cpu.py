@@ -9,6 +9,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import dit_adaln_row_amd as dn
 
@@ -161,22 +162,33 @@ def test_other_entry_validation(lib):
     assert dn.ln_modulate_backward_workspace_bytes(2048 * 3, 3072, 3) == 0
     assert dn.ln_modulate_backward_workspace_bytes(4 * 8, 3072, 8) == 0
     assert dn.ln_modulate_backward_workspace_bytes(4 * 8, 4096, 8) > 0
-    assert lib.ln_modulate_backward_workspace_bytes(10, 3072, 3) == -1
-    assert lib.ln_modulate_backward_workspace_bytes(1 << 62, 1 << 40, 1 << 62) == -1  # no overflow
-    assert lib.ln_modulate_backward_workspace_bytes(4, 4104, 4) == -1
+    assert lib.ln_modulate_backward_workspace_bytes(10, 3072, 3, 0) == -1
+    assert lib.ln_modulate_backward_workspace_bytes(1 << 62, 1 << 40, 1 << 62, 0) == -1  # no overflow
+    assert lib.ln_modulate_backward_workspace_bytes(4, 4104, 4, 0) == -1
+    # fp32 rows: 4-token workgroups, at most 3072 columns; no other storage type
+    assert lib.ln_modulate_backward_workspace_bytes(4, 4096, 4, 2) == -1
+    assert lib.ln_modulate_backward_workspace_bytes(4, 3072, 4, 1) == -1
+    assert dn.ln_modulate_backward_workspace_bytes(8, 3072, 8, torch.float32) > 0
+    assert dn.ln_modulate_backward_workspace_bytes(2048 * 3, 3072, 3, torch.float32) == 0
     W = 0xA0000000
     bw = lambda **k: lib.ln_modulate_backward(
         k.get("x", A), k.get("sc", B), k.get("do", C), k.get("dx", D), k.get("ds", E),
         k.get("dh", E + 0x100000), k.get("rows", 64), k.get("cols", 3072), k.get("rpb", 64),
-        k.get("mbs", 3072), 1e-6, k.get("ws", W), k.get("wsb", 1 << 24), None, None, None)
+        k.get("mbs", 3072), 1e-6, k.get("ws", W), k.get("wsb", 1 << 24), None, None,
+        k.get("dt", 0), None)
     assert bw(wsb=100) == dn.INVALID_ARGUMENT                  # workspace too small
     assert bw(ws=W + 16) == dn.UNSUPPORTED                     # workspace not 256-aligned
     assert bw(cols=4104, mbs=4104) == dn.UNSUPPORTED           # wider than the backward serves
     assert bw(dx=C) == dn.UNSUPPORTED                          # d_x over d_out
     assert bw(do=None) == dn.INVALID_ARGUMENT
     assert bw(rows=0) == dn.OK
+    assert bw(dt=1) == dn.INVALID_ARGUMENT                     # fp16: not a backward type
+    assert bw(dt=2, cols=4096, mbs=4096) == dn.UNSUPPORTED     # fp32 rows: at most 3072
+    assert bw(dt=2, dx=C) == dn.UNSUPPORTED
     assert lib.ln_modulate_backward_supported(A, B, C, D, E, E + 0x100000, 64, 3072, 64, 3072,
-                                              1e-6, W, 1 << 24, None, None) == 1
+                                              1e-6, W, 1 << 24, None, None, 0) == 1
+    assert lib.ln_modulate_backward_supported(A, B, C, D, E, E + 0x100000, 64, 3072, 64, 3072,
+                                              1e-6, W, 1 << 24, None, None, 2) == 1
     # the modulation row stride is bounded (byte spans stay inside int64)
     MS, T = 1 << 36, 1 << 40  # fake buffers a terabyte apart: the spans do not overlap
     assert lib.ln_modulate_supported(T, 2 * T, 3 * T, 4 * T, 16, 8, 8, MS, 1e-6, None, None,
@@ -206,17 +218,18 @@ def test_other_entry_validation(lib):
     # (fake buffers spaced so that only the size decides: d_scale / d_shift
     # of 8.4M batches span 268 MB each)
     bw3 = lambda rows: lib.ln_modulate_backward(A, B, C, D, E, E + 0x20000000, rows, 8, 3, 8,
-                                                1e-6, None, 0, None, None, None)
+                                                1e-6, None, 0, None, None, 0, None)
     assert bw3(3 * (MR // 4) + 3) == dn.UNSUPPORTED    # 3-token batches take 4 row slots each
     assert lib.ln_modulate_backward_supported(A, B, C, D, E, E + 0x20000000, 3 * (MR // 4), 8,
-                                              3, 8, 1e-6, None, 0, None, None) == 1
+                                              3, 8, 1e-6, None, 0, None, None, 0) == 1
     # the no-allocation backward: the same checks, then the partial sums must
     # fit the library's scratch array (refused before any HIP call)
     na = lambda **k: lib.ln_modulate_backward_noalloc(
         k.get("x", A), k.get("sc", B), k.get("do", C), k.get("dx", D), k.get("ds", E),
         k.get("dh", E + 0x100000), k.get("rows", 64), k.get("cols", 3072), k.get("rpb", 64),
-        k.get("mbs", 3072), 1e-6, None, None, None)
+        k.get("mbs", 3072), 1e-6, None, None, k.get("dt", 0), None)
     assert na(do=None) == dn.INVALID_ARGUMENT
+    assert na(dt=1) == dn.INVALID_ARGUMENT
     assert na(dx=C) == dn.UNSUPPORTED
     assert na(cols=4104, mbs=4104) == dn.UNSUPPORTED
     assert na(rows=0) == dn.OK

@@ -211,6 +211,93 @@ def test_backward_workload_in_five_chunkings(gpu):
             _bytes_equal(ref, o, f"chunking {parts[:4]}")
 
 
+# ---------------------------------------------------------------------------
+# the fp32 stream (Qwen-Image page: the FP32 column of the final stream's
+# table, its BF16/FP32 accuracy gates)
+# ---------------------------------------------------------------------------
+
+def _f32_rand(shape, mu, sigma, seed):
+    return gen.normal(shape, mu, sigma, seed, "f32").numpy()
+
+
+def _ulp32(a, b):
+    """Distance in fp32 ulps (ordered-integer difference)."""
+    ia = a.view(np.int32).astype(np.int64)
+    ib = b.view(np.int32).astype(np.int64)
+    ia = np.where(ia < 0, -(ia & 0x7FFFFFFF), ia)
+    ib = np.where(ib < 0, -(ib & 0x7FFFFFFF), ib)
+    return np.abs(ia - ib)
+
+
+def check_f32(got, ref, what):
+    check_stats(got["mean"], got["rstd"], ref["mean"], ref["rstd"], what)
+    d = _ulp32(got["d_x"], ref["d_x"])
+    log(f"  {what}: d_x exact on {(d == 0).mean():.6f} of elements, max {int(d.max())} ulp")
+    assert d.max() <= 1 and (d == 0).mean() >= 0.9999, f"{what}: d_x"
+    assert np.array_equal(got["d_shift"].view(np.uint32), ref["d_shift"].view(np.uint32)), what
+    assert np.array_equal(got["d_scale"].view(np.uint32), ref["d_scale"].view(np.uint32)), what
+
+
+def run_f32(x, sc, dout, eps=1e-6):
+    rows = x.shape[0]
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    d_x, d_scale, d_shift = dn.ln_modulate_backward(dev(x), dev(sc), dev(dout), eps,
+                                                    mean_out=mean, rstd_out=rstd)
+    torch.cuda.synchronize()
+    return dict(d_x=host(d_x), d_scale=host(d_scale), d_shift=host(d_shift), mean=host(mean),
+                rstd=host(rstd))
+
+
+# one token, batches of at most 4 tokens (one launch), runs of 4 within a
+# 32-token group, one and two tree levels, ragged columns, the vector-count
+# forms (64, 128, 256, 512, 768 vectors of 4) and many small batches
+F32_SHAPES = [(1, 1, 8), (3, 4, 3072), (2, 5, 40), (1, 32, 1024), (1, 33, 3072), (2, 77, 1000),
+              (1, 1025, 512), (2048, 3, 3072), (1, 6889, 3072), (1, 9000, 2048), (5, 16, 256),
+              (64, 9, 1536), (1, 300, 3064)]
+
+
+@pytest.mark.parametrize("B,S,D", F32_SHAPES)
+def test_backward_f32_shapes(gpu, orc, B, S, D):
+    log(f"ln_modulate_backward fp32 B={B} S={S} D={D}")
+    x = _f32_rand((B * S, D), 0.2, 1.5, 960 + D + S)
+    sc = _f32_rand((B, D), 0, 0.1, 961 + B)
+    dout = _f32_rand((B * S, D), 0, 1.0, 962 + S)
+    got = run_f32(x, sc, dout)
+    ref = orc.ln_modulate_backward_f32(x, sc, dout, 1e-6, rows_per_batch=S)
+    check_f32(got, ref, f"bwd f32 {B}x{S}x{D}")
+
+
+@pytest.mark.parametrize("S", [31, 32, 33, 6889])
+def test_backward_f32_two_batches_vs_one(gpu, S):
+    D = 3072
+    x = _f32_rand((2 * S, D), 0.2, 1.5, 970 + S)
+    sc = _f32_rand((2, D), 0, 0.1, 971)
+    dout = _f32_rand((2 * S, D), 0, 1.0, 972 + S)
+    whole = run_f32(x, sc, dout)
+    for b in range(2):
+        alone = run_f32(x[b * S:(b + 1) * S], sc[b:b + 1], dout[b * S:(b + 1) * S])
+        assert np.array_equal(alone["d_x"].view(np.uint32),
+                              whole["d_x"][b * S:(b + 1) * S].view(np.uint32))
+        for k in ("d_scale", "d_shift"):
+            assert np.array_equal(alone[k][0].view(np.uint32), whole[k][b].view(np.uint32))
+
+
+def test_backward_f32_matches_bf16_stream_on_bf16_values(gpu):
+    """fp32 inputs holding bf16 values: statistics and token sums bitwise the
+    bf16 stream's, d_x rounded to bf16 within one ulp of it."""
+    B, S, D = 3, 100, 3072
+    x = rand((B * S, D), 0, 1.5, 980)
+    sc = rand((B, D), 0, 0.1, 981)
+    dout = rand((B * S, D), 0, 1.0, 982)
+    rb = run(x, sc, dout, S)
+    rf = run_f32(gen.f32_from_u16(x), gen.f32_from_u16(sc), gen.f32_from_u16(dout))
+    for k in ("mean", "rstd", "d_shift", "d_scale"):
+        assert np.array_equal(rb[k].view(np.uint32), rf[k].view(np.uint32)), k
+    d = ulp_diff(gen.bf16_bits_from_f32(rf["d_x"]), rb["d_x"])
+    assert d.max() <= 1 and (d == 0).mean() >= 0.9999
+
+
 def test_backward_workspace_and_rejections(gpu):
     x = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
     sc = torch.zeros((256,), dtype=torch.bfloat16, device="cuda")
