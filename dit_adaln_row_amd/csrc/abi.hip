@@ -370,7 +370,7 @@ int launch_ew(int op, const void *a, const void *b, const void *m0, const void *
   e.cols = (int32_t)cols;
   e.rows_per_batch = rpb;
   e.mod_stride = mbs;
-  return finish(launch_elementwise(e, op, dtype, (hipStream_t)stream));
+  return finish(launch_elementwise(e, op, dtype, dev, (hipStream_t)stream));
 }
 
 }  // namespace

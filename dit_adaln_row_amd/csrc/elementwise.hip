@@ -19,13 +19,29 @@
 // shift; or the gate) is loaded once and reused; consecutive threads touch
 // consecutive 16-byte vectors of a row, and each of the U row accesses is a
 // separate fully coalesced instruction.  One-shot grid.
+//
+// U is chosen per launch so that every wavefront is resident at once and the
+// busiest SIMD carries as few row vectors as the launch allows: a launch
+// lasts as long as its busiest SIMD.  4608 x 3072 at U = 2 puts 14
+// wavefronts (28 vectors per lane) on some SIMDs and streams in rounds; at
+// U = 9 it is 3 wavefronts of 9 rows on every SIMD (27, the minimum).
+// Measured on 4096 x 3072: U = 8 (3 wavefronts per SIMD) 9.65 us, U = 4 (6)
+// 11.13 us, U = 2 10.91 us, against 9.98 us for a plain copy of the bytes;
+// 4608 x 3072 at U = 9 11.10 us against 11.92 at U = 2.  Launches too large
+// for that (more than 12 rows per thread) keep U = 2.  The gate add, with
+// two input rows per vector, keeps U = 2 throughout: the same choice made it
+// 6-10% slower (4608 x 3072: 17.12 us against 15.57).
+#include <atomic>
+#include <utility>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace ditnorm {
 
 constexpr int EW_BLOCK = 256;
-constexpr int EW_ROWS = 2;  // rows per thread (2 measured best on MI355X; 1, 4, 8 within 7%)
+constexpr int EW_MAX_ROWS = 12;  // rows per thread, at most
+constexpr int EW_MAX_WAVES = 4;  // resident wavefronts per SIMD the choice may use
 
 // OP 0: modulate (x, scale, shift); OP 1: gate add (update, residual, gate)
 template <int OP, int DT, int U>
@@ -42,7 +58,7 @@ __global__ __launch_bounds__(EW_BLOCK) void elementwise_kernel(const Elementwise
   uint4 in0[U], in1[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (u >= nr) break;
+    if (u >= nr) continue;  // (continue, not break: the loops stay fully unrolled)
     const int64_t off = (r0 + u) * (int64_t)a.cols + c8;
     in0[u] = ld16s(a.a + off);
     if constexpr (OP == 1) in1[u] = ld16s(a.b + off);
@@ -52,7 +68,7 @@ __global__ __launch_bounds__(EW_BLOCK) void elementwise_kernel(const Elementwise
   float m0[8], m1[8];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (u >= nr) break;
+    if (u >= nr) continue;
     const int64_t r = r0 + u;
     const int64_t b = r / a.rows_per_batch;
     if (b != cur_b) {  // the first row, and batch boundaries
@@ -87,21 +103,76 @@ __global__ __launch_bounds__(EW_BLOCK) void elementwise_kernel(const Elementwise
   }
 }
 
-template <int U>
-hipError_t launch_elementwise_u(const ElementwiseArgs &a, int op, int dtype, hipStream_t stream) {
+template <int OP, int U>
+static hipError_t launch_u(const ElementwiseArgs &a, int dtype, hipStream_t stream) {
   const int64_t nvec = a.cols >> 3;
   const int64_t threads = nvec * ((a.rows + U - 1) / U);
   if (threads > (int64_t)INT32_MAX) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((threads + EW_BLOCK - 1) / EW_BLOCK)), block(EW_BLOCK);
-  if (op == 0 && dtype == 0) hipLaunchKernelGGL((elementwise_kernel<0, 0, U>), grid, block, 0, stream, a);
-  if (op == 0 && dtype == 1) hipLaunchKernelGGL((elementwise_kernel<0, 1, U>), grid, block, 0, stream, a);
-  if (op == 1 && dtype == 0) hipLaunchKernelGGL((elementwise_kernel<1, 0, U>), grid, block, 0, stream, a);
-  if (op == 1 && dtype == 1) hipLaunchKernelGGL((elementwise_kernel<1, 1, U>), grid, block, 0, stream, a);
+  if (dtype == 0) hipLaunchKernelGGL((elementwise_kernel<OP, 0, U>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((elementwise_kernel<OP, 1, U>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_elementwise(const ElementwiseArgs &a, int op, int dtype, hipStream_t stream) {
-  return launch_elementwise_u<EW_ROWS>(a, op, dtype, stream);
+// Workgroups of the modulate's <dtype, U> instantiation resident per compute
+// unit (= its wavefronts per SIMD: a workgroup is 4 wavefronts on 4 SIMDs),
+// cached per process.
+template <int U>
+static int resident_u(int dtype) {
+  static std::atomic<int> cache[2];
+  int r = cache[dtype].load(std::memory_order_relaxed);
+  if (r > 0) return r;
+  const void *k = dtype == 0 ? (const void *)elementwise_kernel<0, 0, U>
+                             : (const void *)elementwise_kernel<0, 1, U>;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, k, EW_BLOCK, 0) != hipSuccess || r < 1) r = 1;
+  cache[dtype].store(r, std::memory_order_relaxed);
+  return r;
+}
+
+template <int... Us>
+static int resident(int u, int dtype, std::integer_sequence<int, Us...>) {
+  int r = 1;
+  ((u == Us + 1 ? (r = resident_u<Us + 1>(dtype), 0) : 0), ...);
+  return r;
+}
+
+// The modulate's rows per thread: every wavefront resident at once (at most
+// EW_MAX_WAVES per SIMD, and no more than the instantiation's registers
+// allow) and the fewest row vectors on the busiest SIMD; of equal choices the
+// larger U (fewer wavefronts).  0 if no U fits.
+static int rows_per_thread(int64_t rows, int64_t nvec, int dtype, int num_cu) {
+  const int64_t simds = 4LL * num_cu;
+  int best = 0;
+  int64_t best_cost = 0;
+  for (int u = 1; u <= EW_MAX_ROWS; ++u) {
+    const int64_t waves = ((rows + u - 1) / u * nvec + 63) / 64;
+    const int64_t per_simd = (waves + simds - 1) / simds;
+    if (per_simd > EW_MAX_WAVES ||
+        per_simd > resident(u, dtype, std::make_integer_sequence<int, EW_MAX_ROWS>{}))
+      continue;
+    const int64_t cost = per_simd * u;
+    if (best == 0 || cost <= best_cost) {
+      best = u;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+template <int... Us>
+static hipError_t launch_modulate(int u, const ElementwiseArgs &a, int dtype, hipStream_t stream,
+                                  std::integer_sequence<int, Us...>) {
+  hipError_t e = hipErrorInvalidValue;
+  ((u == Us + 1 ? (e = launch_u<0, Us + 1>(a, dtype, stream), 0) : 0), ...);
+  return e;
+}
+
+hipError_t launch_elementwise(const ElementwiseArgs &a, int op, int dtype, const DeviceInfo &dev,
+                              hipStream_t stream) {
+  if (op == 1) return launch_u<1, 2>(a, dtype, stream);
+  const int u = rows_per_thread(a.rows, a.cols >> 3, dtype, dev.num_cu);
+  if (u == 0) return launch_u<0, 2>(a, dtype, stream);  // streams in rounds
+  return launch_modulate(u, a, dtype, stream, std::make_integer_sequence<int, EW_MAX_ROWS>{});
 }
 
 }  // namespace ditnorm

@@ -95,7 +95,8 @@ struct ElementwiseArgs {
   int64_t mod_stride;
   int32_t cols;
 };
-hipError_t launch_elementwise(const ElementwiseArgs &a, int op, int dtype, hipStream_t stream);
+hipError_t launch_elementwise(const ElementwiseArgs &a, int op, int dtype, const DeviceInfo &dev,
+                              hipStream_t stream);
 
 // Backward of LN (no affine) + modulate: d_x, and the token sums d_scale,
 // d_shift by fixed balanced trees.

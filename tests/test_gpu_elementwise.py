@@ -70,6 +70,27 @@ def test_elementwise_shapes(gpu, orc, dt, op, rows, cols, B):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("u", range(1, 13))
+def test_modulate_every_rows_per_thread(gpu, orc, dt, u):
+    """The modulate gives each thread the U rows that keep every wavefront
+    resident and the busiest SIMD least loaded.  At 512 columns (one
+    wavefront per row group) a little under U * (4 * CUs) rows selects U:
+    U = 1..12, each with a ragged last group and the batch boundaries of
+    three batches inside a thread's rows."""
+    td = TORCH[dt]
+    simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    cols, B = 512, 3
+    rows = (simds * u - 4) // 3 * 3
+    log(f"mod {dt} U={u} rows={rows}")
+    x = rand((rows, cols), 0.2, 1.5, 70 + u, dt)
+    emb = rand((B, 6 * cols), 0.0, 0.1, 90 + u, dt)
+    sc, sh, _ = chunk_views(dev(emb, dtype=td), cols)
+    got = _run("mod", dt, dev(x, dtype=td), sc, sh, B)
+    ref = orc.modulate_dt(x, shifted(emb, cols), emb, dt, rows // B)
+    assert same_bits(got, ref, dt), f"{int((got != ref).sum())} elements differ"
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
 @pytest.mark.parametrize("op", ["mod", "gate"])
 def test_elementwise_every_bit_pattern(gpu, orc, dt, op):
     """x (update) runs through all 65536 patterns; the modulation and the
