@@ -16,7 +16,8 @@
 // uses L = 4 (16 pixels per instruction) and moves each 16-pixel group
 // through the wavefront's own LDS slice, so that global loads and stores are
 // three whole contiguous kilobytes instead of a quarter of every line; other
-// widths use a whole wavefront per pixel.  The sum of squares is a DPP
+// widths use the fewest lanes (4, 8, 16 or 64) and vectors per lane (1, 2, 4
+// or 8) that hold a pixel.  The sum of squares is a DPP
 // butterfly over the L lanes in binary64, the biased input stays in fp32
 // registers between the two passes, and the grid is one-shot: each wavefront
 // issues the loads of its G pixel groups first.  With two groups (C = 96 and
@@ -286,7 +287,30 @@ hipError_t launch_wan(const WanArgs &a, const DeviceInfo &dev, hipStream_t strea
     case 256: return launch_wan_cfg<8, 4, true, 1>(a, stream);
     case 384: return launch_wan_cfg<16, 3, true, 2>(a, stream);
     case 512: return launch_wan_cfg<16, 4, true, 1>(a, stream);
-    default: return launch_wan_cfg<64, 8, false, 1>(a, stream);  // any C <= 4096
+    default: break;
+  }
+  // any other C <= 4096: the fewest lane slots (L lanes x VPL vectors, L in
+  // 4, 8, 16, 64 and VPL in 1, 2, 4, 8) that hold a pixel, of those the
+  // fewest vectors per lane (a wavefront per pixel sized for 4096 channels
+  // ran C = 1024 at 28% of a copy's rate, C = 40 at 1%)
+  const int nvec = a.channels >> 3;
+  int best_l = 64, best_v = 8;
+  for (int v : {1, 2, 4, 8})
+    for (int l : {4, 8, 16, 64})
+      if (l * v >= nvec && l * v < best_l * best_v) {
+        best_l = l;
+        best_v = v;
+      }
+  // (slot counts 4, 8, 16, 32, 64, 128, 256, 512 give these eight shapes)
+  switch (best_l * 16 + best_v) {
+    case 4 * 16 + 1: return launch_wan_cfg<4, 1, false, 1>(a, stream);
+    case 8 * 16 + 1: return launch_wan_cfg<8, 1, false, 1>(a, stream);
+    case 16 * 16 + 1: return launch_wan_cfg<16, 1, false, 1>(a, stream);
+    case 16 * 16 + 2: return launch_wan_cfg<16, 2, false, 1>(a, stream);
+    case 64 * 16 + 1: return launch_wan_cfg<64, 1, false, 1>(a, stream);
+    case 64 * 16 + 2: return launch_wan_cfg<64, 2, false, 1>(a, stream);
+    case 64 * 16 + 4: return launch_wan_cfg<64, 4, false, 1>(a, stream);
+    default: return launch_wan_cfg<64, 8, false, 1>(a, stream);
   }
 }
 

@@ -269,7 +269,11 @@ def _wan_run_check(gpu, orc, what, x, bias, gamma, eps):
 @pytest.mark.parametrize("rows,c,bias", [(1, 96, True), (17, 96, True), (1000, 384, True),
                                          (333, 96, False), (64, 128, True), (77, 256, True),
                                          (50, 512, True), (13, 40, True), (9, 1000, False),
-                                         (5, 4096, True), (31, 192, True)])
+                                         (5, 4096, True), (31, 192, True), (100, 8, True),
+                                         (100, 64, False), (41, 136, True), (300, 1024, True),
+                                         (7, 2048, True), (3, 2056, False), (65, 520, True),
+                                         (200, 24, True), (90, 72, False), (33, 200, True),
+                                         (20, 264, True)])
 def test_rmsnorm_silu_bias_shapes(gpu, orc, rows, c, bias):
     log(f"rmsnorm_silu_bias rows={rows} C={c} bias={bias}")
     x = rand((rows, c), 0, 1, 91 + c)
