@@ -28,9 +28,12 @@
 // Measured on 4096 x 3072: U = 8 (3 wavefronts per SIMD) 9.65 us, U = 4 (6)
 // 11.13 us, U = 2 10.91 us, against 9.98 us for a plain copy of the bytes;
 // 4608 x 3072 at U = 9 11.10 us against 11.92 at U = 2.  Launches too large
-// for that (more than 12 rows per thread) keep U = 2.  The gate add, with
-// two input rows per vector, keeps U = 2 throughout: the same choice made it
-// 6-10% slower (4608 x 3072: 17.12 us against 15.57).
+// for that (more than 12 rows per thread) keep U = 2.  This holds for the
+// bf16 modulate only: the fp16 modulate measured 3-8% slower with the same
+// choice (4608 x 3072: 12.28 us against 11.73 at U = 2; its widening and
+// rounding keep 101 registers live at U = 9 against 69), and the gate add,
+// with two input rows per vector, 6-10% slower (17.12 us against 15.57):
+// both keep U = 2.
 #include <atomic>
 #include <utility>
 
@@ -103,44 +106,44 @@ __global__ __launch_bounds__(EW_BLOCK) void elementwise_kernel(const Elementwise
   }
 }
 
-template <int OP, int U>
-static hipError_t launch_u(const ElementwiseArgs &a, int dtype, hipStream_t stream) {
+template <int OP, int DT, int U>
+static hipError_t launch_u(const ElementwiseArgs &a, hipStream_t stream) {
   const int64_t nvec = a.cols >> 3;
   const int64_t threads = nvec * ((a.rows + U - 1) / U);
   if (threads > (int64_t)INT32_MAX) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((threads + EW_BLOCK - 1) / EW_BLOCK)), block(EW_BLOCK);
-  if (dtype == 0) hipLaunchKernelGGL((elementwise_kernel<OP, 0, U>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((elementwise_kernel<OP, 1, U>), grid, block, 0, stream, a);
+  hipLaunchKernelGGL((elementwise_kernel<OP, DT, U>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
-// Workgroups of the modulate's <dtype, U> instantiation resident per compute
+// Workgroups of the bf16 modulate's U instantiation resident per compute
 // unit (= its wavefronts per SIMD: a workgroup is 4 wavefronts on 4 SIMDs),
 // cached per process.
 template <int U>
-static int resident_u(int dtype) {
-  static std::atomic<int> cache[2];
-  int r = cache[dtype].load(std::memory_order_relaxed);
+static int resident_u() {
+  static std::atomic<int> cache;
+  int r = cache.load(std::memory_order_relaxed);
   if (r > 0) return r;
-  const void *k = dtype == 0 ? (const void *)elementwise_kernel<0, 0, U>
-                             : (const void *)elementwise_kernel<0, 1, U>;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, k, EW_BLOCK, 0) != hipSuccess || r < 1) r = 1;
-  cache[dtype].store(r, std::memory_order_relaxed);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, (const void *)elementwise_kernel<0, 0, U>,
+                                                   EW_BLOCK, 0) != hipSuccess ||
+      r < 1)
+    r = 1;
+  cache.store(r, std::memory_order_relaxed);
   return r;
 }
 
 template <int... Us>
-static int resident(int u, int dtype, std::integer_sequence<int, Us...>) {
+static int resident(int u, std::integer_sequence<int, Us...>) {
   int r = 1;
-  ((u == Us + 1 ? (r = resident_u<Us + 1>(dtype), 0) : 0), ...);
+  ((u == Us + 1 ? (r = resident_u<Us + 1>(), 0) : 0), ...);
   return r;
 }
 
-// The modulate's rows per thread: every wavefront resident at once (at most
-// EW_MAX_WAVES per SIMD, and no more than the instantiation's registers
+// The bf16 modulate's rows per thread: every wavefront resident at once (at
+// most EW_MAX_WAVES per SIMD, and no more than the instantiation's registers
 // allow) and the fewest row vectors on the busiest SIMD; of equal choices the
 // larger U (fewer wavefronts).  0 if no U fits.
-static int rows_per_thread(int64_t rows, int64_t nvec, int dtype, int num_cu) {
+static int rows_per_thread(int64_t rows, int64_t nvec, int num_cu) {
   const int64_t simds = 4LL * num_cu;
   int best = 0;
   int64_t best_cost = 0;
@@ -148,7 +151,7 @@ static int rows_per_thread(int64_t rows, int64_t nvec, int dtype, int num_cu) {
     const int64_t waves = ((rows + u - 1) / u * nvec + 63) / 64;
     const int64_t per_simd = (waves + simds - 1) / simds;
     if (per_simd > EW_MAX_WAVES ||
-        per_simd > resident(u, dtype, std::make_integer_sequence<int, EW_MAX_ROWS>{}))
+        per_simd > resident(u, std::make_integer_sequence<int, EW_MAX_ROWS>{}))
       continue;
     const int64_t cost = per_simd * u;
     if (best == 0 || cost <= best_cost) {
@@ -160,19 +163,20 @@ static int rows_per_thread(int64_t rows, int64_t nvec, int dtype, int num_cu) {
 }
 
 template <int... Us>
-static hipError_t launch_modulate(int u, const ElementwiseArgs &a, int dtype, hipStream_t stream,
+static hipError_t launch_modulate(int u, const ElementwiseArgs &a, hipStream_t stream,
                                   std::integer_sequence<int, Us...>) {
   hipError_t e = hipErrorInvalidValue;
-  ((u == Us + 1 ? (e = launch_u<0, Us + 1>(a, dtype, stream), 0) : 0), ...);
+  ((u == Us + 1 ? (e = launch_u<0, 0, Us + 1>(a, stream), 0) : 0), ...);
   return e;
 }
 
 hipError_t launch_elementwise(const ElementwiseArgs &a, int op, int dtype, const DeviceInfo &dev,
                               hipStream_t stream) {
-  if (op == 1) return launch_u<1, 2>(a, dtype, stream);
-  const int u = rows_per_thread(a.rows, a.cols >> 3, dtype, dev.num_cu);
-  if (u == 0) return launch_u<0, 2>(a, dtype, stream);  // streams in rounds
-  return launch_modulate(u, a, dtype, stream, std::make_integer_sequence<int, EW_MAX_ROWS>{});
+  if (op == 1) return dtype == 0 ? launch_u<1, 0, 2>(a, stream) : launch_u<1, 1, 2>(a, stream);
+  if (dtype == 1) return launch_u<0, 1, 2>(a, stream);
+  const int u = rows_per_thread(a.rows, a.cols >> 3, dev.num_cu);
+  if (u == 0) return launch_u<0, 0, 2>(a, stream);  // streams in rounds
+  return launch_modulate(u, a, stream, std::make_integer_sequence<int, EW_MAX_ROWS>{});
 }
 
 }  // namespace ditnorm

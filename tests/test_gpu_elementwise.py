@@ -72,11 +72,12 @@ def test_elementwise_shapes(gpu, orc, dt, op, rows, cols, B):
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 @pytest.mark.parametrize("u", range(1, 13))
 def test_modulate_every_rows_per_thread(gpu, orc, dt, u):
-    """The modulate gives each thread the U rows that keep every wavefront
-    resident and the busiest SIMD least loaded.  At 512 columns (one
+    """The bf16 modulate gives each thread the U rows that keep every
+    wavefront resident and the busiest SIMD least loaded.  At 512 columns (one
     wavefront per row group) a little under U * (4 * CUs) rows selects U:
     U = 1..12, each with a ragged last group and the batch boundaries of
-    three batches inside a thread's rows."""
+    three batches inside a thread's rows.  (fp16 runs the same shapes at
+    U = 2.)"""
     td = TORCH[dt]
     simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count
     cols, B = 512, 3
