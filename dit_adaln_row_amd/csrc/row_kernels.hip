@@ -498,16 +498,22 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
 // are 4 whole rows plus a quarter row on 480 SIMDs instead of a half row on
 // 240.  A launch with no whole round (at most a quarter or half a round of
 // rows in all) splits every row.  The segments' binary64 moments meet through
-// LDS; the sums are exact, so the statistics carry the same bits either way.  Everything else is the
-// wavefront-per-row kernel's MOD_LDS path (rows of NV * 512 columns).
+// LDS; the sums are exact, so the statistics carry the same bits either way.
+// Everything else is the wavefront-per-row kernel's MOD_LDS path (rows of
+// NV * 512 columns).
 template <int NVW, int NV, bool RMS, bool GATED, int WPB>
 __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, float4 *lds_sh,
                                             uint4 *lds_sh16, uint4 *lds_w, float4 *lds_w32,
+                                            uint4 *lds_s116,
                                             double (*red)[2], int64_t row0, int64_t row, int seg) {
   constexpr bool SPLIT = NVW != NV;
   constexpr int NT = 64 * WPB;
   // RMS with 8-wavefront workgroups: the shift and the weight staged as fp32
   constexpr bool F32W = RMS && WPB == 8;
+  // rows over 4096 columns: s1, the shift and the weight staged as bf16
+  // vectors (s1 is already a bf16 value), half the LDS of fp32 copies, so
+  // that four or five workgroups fit a compute unit instead of three
+  constexpr bool B16 = NV > 8;
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
   const int cols = a.cols;
@@ -548,6 +554,12 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
       sc[e] = 1.0f + sc[e];
       sc[e + 1] = 1.0f + sc[e + 1];
       round2(sc[e], sc[e + 1]);
+    }
+    if constexpr (B16) {
+      lds_s116[j] = pack8(sc);  // exact: sc holds bf16 values
+      lds_sh16[j] = fsh[i];
+      if constexpr (RMS) lds_w[j] = fw[i];
+      continue;
     }
     lds_s1[mod_slot(j, 0) / 4] = make_float4(sc[0], sc[1], sc[2], sc[3]);
     lds_s1[mod_slot(j, 1) / 4] = make_float4(sc[4], sc[5], sc[6], sc[7]);
@@ -648,7 +660,10 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
       float s1v[8], shv[8], y[8], o[8];
       const float *v = xf[k];
       const int j = vid(k);
-      if constexpr (FROM_LDS) {
+      if constexpr (FROM_LDS && B16) {
+        unpack8(lds_s116[j], s1v);
+        unpack8(lds_sh16[j], shv);
+      } else if constexpr (FROM_LDS) {
         const float4 a0 = lds_s1[mod_slot(j, 0) / 4], a1 = lds_s1[mod_slot(j, 1) / 4];
         s1v[0] = a0.x; s1v[1] = a0.y; s1v[2] = a0.z; s1v[3] = a0.w;
         s1v[4] = a1.x; s1v[5] = a1.y; s1v[6] = a1.z; s1v[7] = a1.w;
@@ -717,8 +732,11 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
 template <int NV, bool RMS, bool GATED, int P, int WPB = 4, bool REMFIRST = false>
 __global__ __launch_bounds__(64 * WPB) void row_mixed_kernel(const RowArgs a) {
   constexpr bool F32W = RMS && WPB == 8;
-  __shared__ float4 lds_s1[NV * 128], lds_sh[(RMS && !F32W) ? 1 : NV * 128];
-  __shared__ uint4 lds_sh16[(RMS && !F32W) ? NV * 64 : 1], lds_w[(RMS && !F32W) ? NV * 64 : 1];
+  constexpr bool B16 = NV > 8;  // modulation rows staged as bf16 (see row_segment)
+  __shared__ float4 lds_s1[B16 ? 1 : NV * 128], lds_sh[(RMS && !F32W) || B16 ? 1 : NV * 128];
+  __shared__ uint4 lds_sh16[(RMS && !F32W) || B16 ? NV * 64 : 1];
+  __shared__ uint4 lds_w[(RMS && !F32W) || (B16 && RMS) ? NV * 64 : 1];
+  __shared__ uint4 lds_s116[B16 ? NV * 64 : 1];
   __shared__ float4 lds_w32[F32W ? NV * 128 : 1];
   __shared__ double red[WPB][2];
   const int w = wave_id();
@@ -727,18 +745,21 @@ __global__ __launch_bounds__(64 * WPB) void row_mixed_kernel(const RowArgs a) {
     const int64_t nrem = (int64_t)gridDim.x - a.full_blocks;
     g = g < nrem ? a.full_blocks + g : g - nrem;
   }
-  if (g < a.full_blocks) {
+  // (rows over 4096 columns come only in halves: no whole-row path to hold
+  // their registers)
+  if (NV <= 8 && g < a.full_blocks) {
     const int64_t row0 = g * WPB;
-    row_segment<NV, NV, RMS, GATED, WPB>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32, red, row0,
-                                         row0 + w, 0);
+    if constexpr (NV <= 8)
+      row_segment<NV, NV, RMS, GATED, WPB>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32, lds_s116,
+                                           red, row0, row0 + w, 0);
   } else if constexpr (P == 2) {  // WPB / 2 rows per workgroup, a half per wavefront
     const int64_t row0 = a.full_blocks * WPB + (g - a.full_blocks) * (WPB / 2);
-    row_segment<NV / 2, NV, RMS, GATED, WPB>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32, red,
-                                             row0, row0 + (w >> 1), w & 1);
+    row_segment<NV / 2, NV, RMS, GATED, WPB>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
+                                             lds_s116, red, row0, row0 + (w >> 1), w & 1);
   } else {  // WPB / 4 rows per workgroup, a quarter per wavefront
     const int64_t row0 = a.full_blocks * WPB + (g - a.full_blocks) * (WPB / 4);
-    row_segment<NV / 4, NV, RMS, GATED, WPB>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32, red,
-                                             row0, row0 + (w >> 2), w & 3);
+    row_segment<NV / 4, NV, RMS, GATED, WPB>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
+                                             lds_s116, red, row0, row0 + (w >> 2), w & 3);
   }
 }
 
@@ -777,14 +798,18 @@ static void launch_mixed_kind(const RowArgs &a, int P, bool remfirst, dim3 grid,
 
 template <int NV, int WPB>
 static hipError_t launch_mixed_w(const RowArgs &a0, bool rms, bool gated, const DeviceInfo &dev,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, int split = 0) {
   RowArgs a = a0;
   const int64_t simds = (int64_t)dev.num_cu * 4;
-  const int64_t whole = a.rows / simds * simds;
+  const int64_t whole = split ? 0 : a.rows / simds * simds;
   const int64_t rem = a.rows - whole;
   int64_t blocks;
   int P = 2;
-  if (whole > 0 && rem > 0 && 4 * rem <= simds && NV % 4 == 0) {
+  if (split) {  // every row in `split` segments, whatever the row count
+    a.full_blocks = 0;
+    P = split;
+    blocks = (a.rows + WPB / P - 1) / (WPB / P);
+  } else if (whole > 0 && rem > 0 && 4 * rem <= simds && NV % 4 == 0) {
     a.full_blocks = whole / WPB;
     blocks = a.full_blocks + (rem + WPB / 4 - 1) / (WPB / 4);
     P = 4;
@@ -912,6 +937,30 @@ hipError_t launch_row(const RowArgs &a, bool rms, bool gated, bool fold, const D
   if (nvec <= 256) return launch_wave<4, false>(a, rms, gated, fold, stream);
   if (nvec <= 384) return launch_wave<6, false>(a, rms, gated, fold, stream);
   if (nvec <= 512) return launch_wave<8, false>(a, rms, gated, fold, stream);
+  // 5120-8192 columns (multiples of 1024): every row in two halves, one
+  // wavefront each, the halves' binary64 moments meeting through LDS -- the
+  // balanced kernel's half-row path, its modulation rows staged as bf16.
+  // Against a workgroup per row (below): LN 5120 x 4096 24.2 -> 17.6 us,
+  // 8192 x 2048 18.8 -> 14.4 us, 7168 x 1000 12.8 -> 7.9 us, gated LN 6144 x
+  // 2048 24.1 -> 19.4 us, 8192 x 2048 30.2 -> 24.3 us; RMS 5120 x 4096 20.2
+  // -> 18.7 us, 6144 x 2048 13.8 -> 12.5 us (gated 23.1 -> 20.3), but at 8192
+  // x 2048 15.9 -> 18.0 us (its weight too in LDS: three workgroups per
+  // compute unit), so RMS rows over 6144 columns keep the workgroup per row.
+  // Quarter rows measured slower than halves (6144 x 2048 LN 13.2 against
+  // 11.0 us).
+  if (!fold) {
+    switch (nvec) {
+      case 640: return launch_mixed_w<10, 4>(a, rms, gated, dev, stream, 2);
+      case 768: return launch_mixed_w<12, 4>(a, rms, gated, dev, stream, 2);
+      case 896:
+        if (!rms) return launch_mixed_w<14, 4>(a, rms, gated, dev, stream, 2);
+        break;
+      case 1024:
+        if (!rms) return launch_mixed_w<16, 4>(a, rms, gated, dev, stream, 2);
+        break;
+      default: break;
+    }
+  }
   // wider rows (4104-16384 columns): one workgroup per row, (threads,
   // vectors per thread) such that NT*NV vectors hold the row with 3-4
   // vectors (24-32 values) per thread

@@ -210,6 +210,50 @@ def test_rms_modulate_shapes(gpu, orc, rows, cols, B, gated):
     _rms_run_check(gpu, orc, f"rms {rows}x{cols}", x, w, sc, sh, 1e-6, rows // B, res, gate)
 
 
+@pytest.mark.parametrize("cols", [5120, 6144, 7168, 8192])
+@pytest.mark.parametrize("kind", ["ln", "gated_ln", "rms", "gated_rms"])
+@pytest.mark.parametrize("rows,B", [(74, 2), (1029, 1)])
+def test_wide_rows_in_halves(gpu, orc, cols, kind, rows, B):
+    """Rows of 5120-8192 columns go in halves, a wavefront each (RMS rows over
+    6144 columns a workgroup per row), their modulation rows staged in LDS as
+    bf16.  Two batches of 37 rows put a batch boundary inside a workgroup's
+    pair of rows; the call is made with the debug outputs (stage checks) and
+    without them (the timed form), and both outputs must be the same bits."""
+    log(f"{kind} rows={rows} cols={cols} B={B}")
+    rpb = rows // B
+    x = rand((rows, cols), 0.1, 1.3, 201 + cols + rows)
+    res = rand((rows, cols), 0, 1, 202) if kind.startswith("gated") else None
+    gate = rand((B, cols), 0, 0.1, 203) if res is not None else None
+    sc, sh = rand((B, cols), 0, 0.1, 204), rand((B, cols), 0, 0.1, 205)
+    what = f"{kind} {rows}x{cols}"
+    if kind.endswith("rms"):
+        w = rand((cols,), 1, 0.05, 206)
+        _rms_run_check(gpu, orc, what, x, w, sc, sh, 1e-6, rpb, res, gate)
+        plain = gpu.rms_modulate(dev(x), dev(w), dev(sc), dev(sh), 1e-6,
+                                 **({} if res is None else dict(residual=dev(res), gate=dev(gate))))
+        ref = orc.rms_modulate(x, w, sc, sh, 1e-6, residual=res, gate=gate, rows_per_batch=rpb)
+    elif res is None:
+        out, mean, rstd, y = _ln_gpu(gpu, x, sc, sh, 1e-6)
+        ref = _ln_check(orc, what, x, sc, sh, 1e-6, rpb, out, mean, rstd, y)
+        plain = gpu.ln_modulate(dev(x), dev(sc), dev(sh), 1e-6)
+    else:
+        kw = dict(mean_out=empty_f32(rows), rstd_out=empty_f32(rows), y_out=torch.empty(
+            (rows, cols), dtype=torch.bfloat16, device="cuda"))
+        h, out = gpu.gated_ln_modulate(dev(x), dev(res), dev(gate), dev(sc), dev(sh), 1e-6, **kw)
+        torch.cuda.synchronize()
+        h, out = host(h), host(out)
+        ref = orc.gated_ln_modulate(x, res, gate, sc, sh, 1e-6, rows_per_batch=rpb)
+        assert same_bits(h, ref["h"]), f"{what}: gate stage"
+        _ln_check(orc, what, h, sc, sh, 1e-6, rpb, out, host(kw["mean_out"]),
+                  host(kw["rstd_out"]), host(kw["y_out"]), ref=ref)
+        plain = gpu.gated_ln_modulate(dev(x), dev(res), dev(gate), dev(sc), dev(sh), 1e-6)
+    torch.cuda.synchronize()
+    if isinstance(plain, tuple):
+        assert same_bits(host(plain[0]), ref["h"]), f"{what}: gate stage (timed form)"
+        plain = plain[1]
+    check_rows_end_to_end(host(plain), ref["out"], f"{what} (timed form)")
+
+
 # ---------------------------------------------------------------------------
 # qk LayerNorm
 # ---------------------------------------------------------------------------
