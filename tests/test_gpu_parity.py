@@ -55,7 +55,9 @@ def _ln_check(orc, what, x, sc, sh, eps, rpb, out_g, mean_g, rstd_g, y_g, ref=No
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 8), (3, 40), (257, 1024), (100, 3072), (37, 4096),
-                                       (5, 2048), (9, 1536), (3, 16384), (1000, 512), (2, 9000)])
+                                       (5, 2048), (9, 1536), (3, 16384), (1000, 512), (2, 9000),
+                                       (100, 1152), (7, 2560), (33, 3584), (5, 1920), (65, 2304),
+                                       (3, 2432), (17, 1088), (2, 3000)])
 def test_ln_modulate_shapes(gpu, orc, rows, cols):
     log(f"ln_modulate rows={rows} cols={cols}")
     x = rand((rows, cols), 0.3, 1.5, 11 + cols)
@@ -199,7 +201,9 @@ def _rms_run_check(gpu, orc, what, x, w, sc, sh, eps, rpb, res=None, gate=None, 
 @pytest.mark.parametrize("rows,cols,B,gated", [(1, 4096, 1, False), (128, 2048, 1, False),
                                                (2 * 1140, 4096, 2, False), (257, 4096, 1, True),
                                                (2 * 65, 4096, 2, True), (11, 1024, 1, True),
-                                               (5, 24, 1, False), (3, 16384, 1, True)])
+                                               (5, 24, 1, False), (3, 16384, 1, True),
+                                               (2 * 50, 2560, 2, True), (64, 1536, 1, False),
+                                               (9, 3584, 1, True), (30, 1152, 1, False)])
 def test_rms_modulate_shapes(gpu, orc, rows, cols, B, gated):
     log(f"rms_modulate rows={rows} cols={cols} B={B} gated={gated}")
     x = rand((rows, cols), 0, 1, 71 + cols)
