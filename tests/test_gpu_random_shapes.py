@@ -1,6 +1,7 @@
 """Seeded random shapes across the entry points (a fixed list, so failures
 reproduce): widths that are any multiple of 8 up to 4096 (a wavefront per
-row, the balanced launch, ragged last vectors), several modulation batches
+row, the balanced launch, ragged last vectors) and up to 16384 (rows in
+halves, a workgroup per row), several modulation batches
 with chunk-view strides, row counts that leave remainders of every size
 against the 1024 SIMDs, token counts across the backward's tree levels, and
 Wan pixel counts and qk head-row counts that leave ragged last groups.
@@ -33,6 +34,24 @@ def _configs(n, seed):
 
 CONFIGS = _configs(32, 20261202)
 KINDS = ["ln", "gated", "rms", "gated_rms", "folded", "backward"]
+
+
+def _wide_configs(n, seed):
+    """Rows over 4096 columns: the half-row widths (5120-8192 in steps of
+    1024) and any multiple of 8 to 16384 (a workgroup per row)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        cols = int(rng.choice([5120, 6144, 7168, 8192, 8 * int(rng.integers(513, 2049))]))
+        B = int(rng.choice([1, 1, 2, 3]))
+        S = int(rng.integers(1, 700 // B + 2))
+        extra = int(rng.choice([0, 8, 8 * int(rng.integers(1, 64))]))
+        out.append((100 + i, B, S, cols, extra))
+    return out
+
+
+WIDE = _wide_configs(12, 20261204)
+WIDE_KINDS = ["ln", "gated", "rms", "gated_rms", "folded"]
 
 
 def _pixel_configs(n, seed):
@@ -87,7 +106,15 @@ def _mod(B, cols, extra, seed):
 
 @pytest.mark.parametrize("i,B,S,cols,extra", CONFIGS)
 def test_random_shape(gpu, orc, i, B, S, cols, extra):
-    kind = KINDS[i % len(KINDS)]
+    _check_shape(gpu, orc, i, KINDS[i % len(KINDS)], B, S, cols, extra)
+
+
+@pytest.mark.parametrize("i,B,S,cols,extra", WIDE)
+def test_random_wide_shape(gpu, orc, i, B, S, cols, extra):
+    _check_shape(gpu, orc, i, WIDE_KINDS[i % len(WIDE_KINDS)], B, S, cols, extra)
+
+
+def _check_shape(gpu, orc, i, kind, B, S, cols, extra):
     rows = B * S
     log(f"random shape {i}: {kind} B={B} S={S} cols={cols} stride pad={extra}")
     x = rand((rows, cols), 0.1 * (i % 3), 1.0 + 0.3 * (i % 4), 700 + i)
