@@ -282,20 +282,24 @@ def rms_modulate(x, weight, scale, shift, eps=1e-6, out=None, *, residual=None, 
 
 
 def qk_layernorm(q, k, eps=1e-5, q_out=None, k_out=None, *, mean_out=None, rstd_out=None):
-    """Per-head LayerNorm(128) of q (..., 128) and k (..., 128) in one launch."""
+    """Per-head LayerNorm of q (..., head_dim) and k (..., head_dim) in one
+    launch; head_dim a multiple of 8, at most 128 (the library rejects others)."""
     _act(q, "q")
-    rows_q = q.numel() // 128 if q.shape[-1] == 128 else -1
+    if q.dim() == 0:
+        raise ValueError("q needs a head dimension")
+    head_dim = q.shape[-1]
+    rows_q = q.numel() // head_dim if head_dim else 0
     if k is not None:
         _act(k, "k", device=q.device)
-    rows_k = 0 if k is None else (k.numel() // 128 if k.shape[-1] == 128 else -1)
-    if rows_q < 0 or rows_k < 0:
-        raise ValueError("head_dim must be 128")
+        if k.dim() == 0 or k.shape[-1] != head_dim:
+            raise ValueError("q and k must have the same head_dim")
+    rows_k = 0 if k is None else k.numel() // head_dim
     q_out = torch.empty_like(q) if q_out is None else _like(q_out, q, "q_out")
     if k is not None:
         k_out = torch.empty_like(k) if k_out is None else _like(k_out, k, "k_out")
     n = rows_q + rows_k
     _call("qk_layernorm", _p(q), _p(k), _p(q_out), _p(k_out if k is not None else None),
-          rows_q, rows_k, 128, eps, _p(_f32_out(mean_out, n, "mean_out", q.device)),
+          rows_q, rows_k, head_dim, eps, _p(_f32_out(mean_out, n, "mean_out", q.device)),
           _p(_f32_out(rstd_out, n, "rstd_out", q.device)), _stream(q))
     return q_out, k_out
 

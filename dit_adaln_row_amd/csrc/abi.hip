@@ -214,7 +214,8 @@ int validate_qk(const void *q, const void *k, const void *q_out, const void *k_o
                 int64_t rows_q, int64_t rows_k, int64_t head_dim, float eps,
                 const float *mean_out, const float *rstd_out) {
   if (rows_q < 0 || rows_k < 0 || head_dim <= 0 || !eps_ok(eps)) return DITNORM_INVALID_ARGUMENT;
-  if (head_dim != 128 || rows_q > DITNORM_MAX_ROWS || rows_k > DITNORM_MAX_ROWS - rows_q)
+  if (head_dim % 8 != 0 || head_dim > 128 || rows_q > DITNORM_MAX_ROWS ||
+      rows_k > DITNORM_MAX_ROWS - rows_q)
     return DITNORM_UNSUPPORTED;
   if (rows_q + rows_k == 0) return DITNORM_OK;
   if (rows_q > 0 && (!q || !q_out)) return DITNORM_INVALID_ARGUMENT;
@@ -223,8 +224,9 @@ int validate_qk(const void *q, const void *k, const void *q_out, const void *k_o
       !aligned4(mean_out) || !aligned4(rstd_out))
     return DITNORM_UNSUPPORTED;
   const int64_t total = rows_q + rows_k;
-  const Buf in[] = {{q, rows_q * 256}, {k, rows_k * 256}};
-  const Buf o[] = {{q_out, rows_q * 256}, {k_out, rows_k * 256}, {mean_out, total * 4},
+  const int64_t rb = head_dim * 2;  // bytes per head row
+  const Buf in[] = {{q, rows_q * rb}, {k, rows_k * rb}};
+  const Buf o[] = {{q_out, rows_q * rb}, {k_out, rows_k * rb}, {mean_out, total * 4},
                    {rstd_out, total * 4}};
   const int alias[] = {0, 1, -1, -1};
   return aliasing_ok(in, o, alias) ? DITNORM_OK : DITNORM_UNSUPPORTED;
@@ -509,6 +511,7 @@ int qk_layernorm(const void *q, const void *k, void *q_out, void *k_out, int64_t
   a.rstd_out = rstd_out;
   a.rows_q = rows_q;
   a.rows_k = rows_k;
+  a.head_dim = (int32_t)head_dim;
   a.eps = eps;
   return finish(launch_qk(a, dev, (hipStream_t)stream));
 }

@@ -48,6 +48,7 @@ struct QkArgs {
   float *rstd_out;  // optional
   int64_t rows_q;
   int64_t rows_k;
+  int32_t head_dim;  // a multiple of 8, at most 128
   float eps;
 };
 hipError_t launch_qk(const QkArgs &a, const DeviceInfo &dev, hipStream_t stream);

@@ -1,7 +1,8 @@
-// Per-head LayerNorm (no affine) over the 128-wide head rows of q and of k in
-// one launch (GLM-Image page, Motivation: nn.LayerNorm(128) per head on
+// Per-head LayerNorm (no affine) over the head rows of q and of k in one
+// launch (GLM-Image page, Motivation: nn.LayerNorm(128) per head on
 // (1, S, 32, 128); "What rounding-faithful means here": q and k handled by one
-// launch).  Per row: mean = fp32(S1/128), rstd = fp32(1/sqrt(M2/128 + eps)),
+// launch; its kernel takes head dims up to 128).  Per row of d = head_dim
+// values: mean = fp32(S1/d), rstd = fp32(1/sqrt(M2/d + eps)),
 // out = bf16(rstd * (x - mean)).
 //
 // The eager kernel spends a 128-thread block on each 128-element row (one
@@ -16,6 +17,11 @@
 // each wavefront owns G groups of 64/L consecutive rows and issues all their
 // loads before it reduces them.  Rows are numbered q first, then k; a group
 // may straddle the q/k boundary.
+//
+// Other head dims (multiples of 8 up to 128) take the same layout with the
+// head dim read at run time: 4 lanes per row up to 32 values, else 8, and as
+// many vectors per lane as the row needs, the vectors past the row's end
+// masked.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -24,10 +30,12 @@ namespace ditnorm {
 constexpr int QK_HEAD = 128;
 constexpr int QK_BLOCK = 256;
 
-template <int L, int G, bool NTL>
+// HEAD: the head dim, or 0 for a.head_dim (then VPL vectors per lane, masked)
+template <int L, int G, bool NTL, int HEAD = QK_HEAD, int VPL = HEAD / 8 / L>
 __global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
-  constexpr int VPL = 16 / L;   // 16-byte vectors per lane (a row is 16 vectors)
   constexpr int RPW = 64 / L;   // rows per wavefront instruction
+  const int head = HEAD > 0 ? HEAD : a.head_dim;
+  const int nvec = head >> 3;   // 16-byte vectors per row
   const int lane = threadIdx.x & 63;
   const int sub = lane / L;     // row within a group of RPW
   const int part = lane % L;    // lane within the row
@@ -37,11 +45,12 @@ __global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
   if (base >= total) return;
 
   auto src = [&](int64_t r) -> const uint16_t * {
-    return r < a.rows_q ? a.q + r * QK_HEAD : a.k + (r - a.rows_q) * QK_HEAD;
+    return r < a.rows_q ? a.q + r * head : a.k + (r - a.rows_q) * head;
   };
   auto dst = [&](int64_t r) -> uint16_t * {
-    return r < a.rows_q ? a.q_out + r * QK_HEAD : a.k_out + (r - a.rows_q) * QK_HEAD;
+    return r < a.rows_q ? a.q_out + r * head : a.k_out + (r - a.rows_q) * head;
   };
+  auto ok = [&](int k) { return HEAD > 0 || part + L * k < nvec; };
 
   uint4 xv[G][VPL];
 #pragma unroll
@@ -50,7 +59,7 @@ __global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       const uint4 zero = {0, 0, 0, 0};
-      xv[g][k] = r < total ? ld16x<NTL>(src(r) + (part + L * k) * 8) : zero;
+      xv[g][k] = (r < total && ok(k)) ? ld16x<NTL>(src(r) + (part + L * k) * 8) : zero;
     }
   }
 
@@ -67,8 +76,15 @@ __global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
       for (int e = 0; e < 8; ++e) accumulate(m, v[e]);
     }
     const double s1 = group_sum<L>(m.s1), s2 = group_sum<L>(m.s2);
-    const double mean_d = s1 * (1.0 / QK_HEAD);  // exact: 128 is a power of two
-    const double var_d = clamp_var(__builtin_fma(-s1, mean_d, s2) * (1.0 / QK_HEAD));
+    double mean_d, var_d;
+    if constexpr (HEAD == QK_HEAD) {  // exact: 128 is a power of two
+      mean_d = s1 * (1.0 / QK_HEAD);
+      var_d = clamp_var(__builtin_fma(-s1, mean_d, s2) * (1.0 / QK_HEAD));
+    } else {
+      const double n_d = (double)head;
+      mean_d = s1 / n_d;
+      var_d = clamp_var(__builtin_fma(-s1, mean_d, s2) / n_d);
+    }
     mean_f[g] = (float)mean_d;
     rstd_f[g] = rstd_from(var_d + eps);
   }
@@ -83,6 +99,7 @@ __global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
     uint16_t *d = dst(r);
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
+      if (!ok(k)) continue;
       float v[8], y[8];
       unpack8(xv[g][k], v);
 #pragma unroll
@@ -96,19 +113,24 @@ __global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
   }
 }
 
-template <int L, int G, bool NTL>
+template <int L, int G, bool NTL, int HEAD = QK_HEAD, int VPL = HEAD / 8 / L>
 hipError_t launch_qk_cfg(const QkArgs &a, hipStream_t stream) {
   const int64_t total = a.rows_q + a.rows_k;
   const int64_t rows_per_block = (QK_BLOCK / 64) * (64 / L) * G;
   const int64_t grid = (total + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((qk_kernel<L, G, NTL>), dim3((unsigned)grid), dim3(QK_BLOCK), 0, stream, a);
+  hipLaunchKernelGGL((qk_kernel<L, G, NTL, HEAD, VPL>), dim3((unsigned)grid), dim3(QK_BLOCK), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_qk(const QkArgs &a, const DeviceInfo &dev, hipStream_t stream) {
   (void)dev;
   // 8 lanes per row: each load instruction reads whole 128-byte lines
-  return launch_qk_cfg<8, 1, true>(a, stream);
+  if (a.head_dim == QK_HEAD) return launch_qk_cfg<8, 1, true>(a, stream);
+  const int nvec = a.head_dim >> 3;
+  if (nvec <= 4) return launch_qk_cfg<4, 1, true, 0, 1>(a, stream);
+  if (nvec <= 8) return launch_qk_cfg<8, 1, true, 0, 1>(a, stream);
+  return launch_qk_cfg<8, 1, true, 0, 2>(a, stream);
 }
 
 }  // namespace ditnorm

@@ -32,8 +32,8 @@
  *       kernels implement: cols not a multiple of 8 or above the stated
  *       maximum, more than DITNORM_MAX_ROWS rows (rows_q + rows_k for
  *       qk_layernorm), more than DITNORM_MAX_VECTORS 16-byte vectors in an
- *       activation of the elementwise entry points, head_dim other than 128,
- *       a pointer not 16-byte aligned, a modulation row stride that breaks
+ *       activation of the elementwise entry points, head_dim over 128 or
+ *       not a multiple of 8, a pointer not 16-byte aligned, a modulation row stride that breaks
  *       16-byte alignment or exceeds DITNORM_MAX_MOD_STRIDE, or an output
  *       that overlaps an input other than in the exact in-place forms
  *       allowed.
@@ -209,12 +209,14 @@ int rms_modulate(const void *x, const void *weight, const void *scale, const voi
  * qk_layernorm -- per-head affine-free LayerNorm of q and k in one launch.
  *
  * GLM-Image page, Motivation (nn.LayerNorm(128) per head on (1, S, 32, 128))
- * and "What rounding-faithful means here" (q and k in one launch):
+ * and "What rounding-faithful means here" (q and k in one launch; the page's
+ * kernel serves head dims up to 128):
  *     for every head_dim-wide row of q, then of k:
  *     out = bf16( rstd * (x - mean) ),  fp32 stats, eps (1e-5 on the page's model)
- * q, q_out: bf16 [rows_q, 128]; k, k_out: bf16 [rows_k, 128] (a (B, S, H, 128)
- * tensor is rows = B*S*H).  head_dim must be 128.  k and k_out may be NULL only
- * when rows_k == 0.  q_out == q and k_out == k allowed.
+ * q, q_out: bf16 [rows_q, head_dim]; k, k_out: bf16 [rows_k, head_dim] (a
+ * (B, S, H, head_dim) tensor is rows = B*S*H).  head_dim: a multiple of 8, at
+ * most 128 (else UNSUPPORTED); 128 is the tuned case.  k and k_out may be NULL
+ * only when rows_k == 0.  q_out == q and k_out == k allowed.
  * mean_out, rstd_out: optional fp32 [rows_q + rows_k], q rows first.
  */
 int qk_layernorm(const void *q, const void *k, void *q_out, void *k_out, int64_t rows_q,

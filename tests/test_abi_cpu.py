@@ -98,7 +98,11 @@ def test_supported_predicates_never_touch_the_gpu(lib):
     assert lib.rms_modulate_supported(A, B, C, C + 0x4000, D, E, None, None, 4, 4096, 4, 4096,
                                       1e-6, None, None) == 0   # half a gated group
     assert lib.qk_layernorm_supported(A, B, C, D, 10, 10, 128, 1e-5, None, None) == 1
-    assert lib.qk_layernorm_supported(A, B, C, D, 10, 10, 64, 1e-5, None, None) == 0
+    assert lib.qk_layernorm_supported(A, B, C, D, 10, 10, 64, 1e-5, None, None) == 1
+    assert lib.qk_layernorm_supported(A, B, C, D, 10, 10, 72, 1e-5, None, None) == 1
+    assert lib.qk_layernorm_supported(A, B, C, D, 10, 10, 8, 1e-5, None, None) == 1
+    assert lib.qk_layernorm_supported(A, B, C, D, 10, 10, 60, 1e-5, None, None) == 0  # % 8
+    assert lib.qk_layernorm_supported(A, B, C, D, 10, 10, 136, 1e-5, None, None) == 0  # > 128
     assert lib.qk_layernorm_supported(A, None, C, None, 10, 0, 128, 1e-5, None, None) == 1
     assert lib.qk_layernorm_supported(A, None, C, None, 10, 3, 128, 1e-5, None, None) == 0
     assert lib.rmsnorm_silu_bias_supported(A, B, C, D, 100, 96, 1e-6, None, None) == 1
@@ -136,7 +140,11 @@ def test_other_entry_validation(lib):
                                  None, None) == dn.INVALID_ARGUMENT
     assert lib.rms_modulate(A, B, C, C, D, E, None, None, 4, 1024, 4, 1024, 1e-6, None, None,
                             None) == dn.INVALID_ARGUMENT
-    assert lib.qk_layernorm(A, B, C, D, 4, 4, 64, 1e-5, None, None, None) == dn.UNSUPPORTED
+    assert lib.qk_layernorm(A, B, C, D, 4, 4, 60, 1e-5, None, None, None) == dn.UNSUPPORTED
+    assert lib.qk_layernorm(A, B, C, D, 4, 4, 256, 1e-5, None, None, None) == dn.UNSUPPORTED
+    assert lib.qk_layernorm(A, B, C, D, 4, 4, 0, 1e-5, None, None, None) == dn.INVALID_ARGUMENT
+    # an output overlapping the other tensor's input at 64-wide rows
+    assert lib.qk_layernorm(A, B, A + 64, D, 4, 4, 64, 1e-5, None, None, None) == dn.UNSUPPORTED
     assert lib.qk_layernorm(A, B, C, D, -1, 4, 128, 1e-5, None, None, None) == dn.INVALID_ARGUMENT
     assert lib.qk_layernorm(A, B, A + 128, D, 4, 4, 128, 1e-5, None, None, None) == dn.UNSUPPORTED
     assert lib.rmsnorm_silu_bias(A, B, None, D, 10, 96, 1e-6, None, None, None) == dn.INVALID_ARGUMENT

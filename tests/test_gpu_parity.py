@@ -289,6 +289,31 @@ def test_qk_layernorm_shapes(gpu, orc, rq, rk):
     _qk_run_check(gpu, orc, f"qk {rq}+{rk}", q, k, 1e-5)
 
 
+@pytest.mark.parametrize("d", [8, 16, 32, 40, 64, 72, 96, 112, 120])
+@pytest.mark.parametrize("rq,rk", [(1, 0), (37, 11), (4096, 4093)])
+def test_qk_layernorm_head_dims(gpu, orc, d, rq, rk):
+    """Head dims other than 128 (multiples of 8 up to 128): 4 lanes per row up
+    to 32, else 8, the vectors past the row's end masked; the statistics
+    divide by d.  Statistics to the bit, the normalise stage and every output
+    against the oracle."""
+    log(f"qk_layernorm head_dim={d} rows_q={rq} rows_k={rk}")
+    q = rand((rq, d), 0, 2, 83 + d)
+    k = rand((rk, d), 0.1, 2, 84 + d) if rk else None
+    mean, rstd = empty_f32(rq + rk), empty_f32(rq + rk)
+    qo, ko = gpu.qk_layernorm(dev(q), None if k is None else dev(k), 1e-5, mean_out=mean,
+                              rstd_out=rstd)
+    torch.cuda.synchronize()
+    kk = k if k is not None else np.zeros((0, d), np.uint16)
+    ref = orc.qk_layernorm(q, kk, 1e-5, head_dim=d)
+    mean, rstd = host(mean), host(rstd)
+    what = f"qk d={d} {rq}+{rk}"
+    check_stats(mean, rstd, ref["mean"], ref["rstd"], what)
+    got = np.concatenate([host(qo)] + ([host(ko)] if k is not None else []))
+    both = np.concatenate([q, kk])
+    assert same_bits(got, orc.ln_normalize(both, mean, rstd)), f"{what}: normalise stage"
+    check_rows_end_to_end(got, np.concatenate([ref["q_out"], ref["k_out"]]), what)
+
+
 # ---------------------------------------------------------------------------
 # channels_last RMSNorm + SiLU (+ bias) and the conv-bias epilogue
 # ---------------------------------------------------------------------------
