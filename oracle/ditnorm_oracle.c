@@ -64,8 +64,10 @@
  *    with fp32 statistics kept from the forward.  With x_hat the normalised
  *    value and g = d_out * (1 + scale):
  *      d_x     = rstd * (g - mean_row(g) - x_hat * mean_row(g * x_hat)),
- *                evaluated here in binary64 and rounded once to bf16 (the
- *                execution-dtype store);
+ *                evaluated here in binary64 and rounded once to the storage
+ *                type (the execution-dtype store): bf16, or binary32 for the
+ *                page's fp32 stream, where x, scale and d_out are binary32
+ *                too and 1 + scale is their binary32 sum;
  *      d_shift = sum over a batch's tokens of d_out,
  *      d_scale = sum over a batch's tokens of d_out * x_hat,
  *    the two token sums in fp32 by the page's fixed balanced trees: adjacent
@@ -91,9 +93,12 @@
  *    pass t = (xb * rstd) * gamma and a single rounding of SiLU(t).  SiLU is
  *    evaluated in binary64 and rounded once, directly, to bf16.
  *
- *  - Conv-bias epilogue (same Wan page, "New kernel"): x.dtype(x + bias) with
- *    the bias cast to the activation dtype first, optionally followed by the
- *    residual add as a second rounding: bf16(bf16(x + bf16(bias)) + h).
+ *  - Conv-bias epilogue (same Wan page, "New kernel"; its tests cover bf16,
+ *    fp16 and fp32 activations with an fp32 or same-type bias): x.dtype(x +
+ *    bias) with the bias cast to the activation dtype first, optionally
+ *    followed by the residual add as a second rounding, e.g. for bf16
+ *    bf16(bf16(x + bf16(bias)) + h); each addition one binary32 operation,
+ *    rounded to the storage type (the identity for fp32).
  *
  * Every function takes host pointers; bf16 tensors are passed as uint16_t bit
  * patterns.  Functions return 0 on success and 1 on an invalid argument.
