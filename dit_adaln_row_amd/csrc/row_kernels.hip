@@ -974,9 +974,9 @@ hipError_t launch_row(const RowArgs &a, bool rms, bool gated, bool fold, const D
       default: break;
     }
   }
-  // wider rows (4104-16384 columns): one workgroup per row, (threads,
-  // vectors per thread) such that NT*NV vectors hold the row with 3-4
-  // vectors (24-32 values) per thread
+  // the other rows over 4096 columns (to 16384) and the folded form there:
+  // one workgroup per row, (threads, vectors per thread) such that NT*NV
+  // vectors hold the row with 3-4 vectors (24-32 values) per thread
   if (nvec <= 768) return launch_cfg<256, 3>(a, rms, gated, fold, dev, stream);
   if (nvec <= 1024) return launch_cfg<256, 4>(a, rms, gated, fold, dev, stream);
   return launch_cfg<512, 4>(a, rms, gated, fold, dev, stream);  // up to 16384 columns
