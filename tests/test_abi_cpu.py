@@ -269,3 +269,22 @@ def test_product_never_uses_the_oracle():
                 assert "ditnorm_oracle" not in text and "libditnorm_oracle" not in text, f
     osrc = open(os.path.join(ROOT, "oracle", "ditnorm_oracle.c")).read()
     assert "#include \"" not in osrc   # the oracle includes no project header
+
+
+def test_header_is_c_and_cpp_and_a_c_program_links(tmp_path):
+    """include/ditnorm.h compiles as C99 and as C++11 with warnings as errors,
+    and the C-ABI test's plain C program builds against the library."""
+    import subprocess
+    src = tmp_path / "h.c"
+    src.write_text('#include "ditnorm.h"\nint main(void) { return ditnorm_last_hip_error(); }\n')
+    inc = os.path.join(ROOT, "include")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", inc, "-fsyntax-only",
+                    str(src)], check=True)
+    subprocess.run(["g++", "-std=c++11", "-Wall", "-Wextra", "-Werror", "-I", inc,
+                    "-fsyntax-only", "-x", "c++", str(src)], check=True)
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "c_abi_consumer_build", os.path.join(ROOT, "tests", "c_abi_consumer_build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert os.path.exists(mod.build(str(tmp_path / "consumer")))
