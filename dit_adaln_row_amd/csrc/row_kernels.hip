@@ -280,6 +280,11 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
   constexpr int NT = 64 * WPB;
   constexpr bool MODLDS = MODE == MOD_LDS;
   constexpr bool WLDS = MODLDS && RMS;  // RMS: the shift and the weight staged as bf16
+  // gated rows: every gate load ahead of the residual stores in the LN forms
+  // whose register footprint it leaves alone (measured: the RMS forms and
+  // the masked LN forms of 5-8 vectors per lane lost a wavefront per SIMD or
+  // ran slower with it)
+  constexpr bool GFIRST = !RMS && (FULL || NV <= 4);
   __shared__ float4 lds_s1[MODLDS ? NV * 128 : 1], lds_sh[(MODLDS && !RMS) ? NV * 128 : 1];
   __shared__ uint4 lds_sh16[WLDS ? NV * 64 : 1], lds_w[WLDS ? NV * 64 : 1];
   const int lane = threadIdx.x & 63;
@@ -366,7 +371,14 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
         u[e + 1] = r[e + 1] + g1;
       }
       xv[k] = pack8(u);
-      if (ok(k)) st16s(a.residual_out + base + col(k), xv[k]);
+      if (!GFIRST && ok(k)) st16s(a.residual_out + base + col(k), xv[k]);
+    }
+    // GFIRST: stored after every gate load has been issued (a store between
+    // them orders each load behind it, a cache round trip per vector)
+    if constexpr (GFIRST) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+        if (ok(k)) st16s(a.residual_out + base + col(k), xv[k]);
     }
   }
 
@@ -501,7 +513,7 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
 // LDS; the sums are exact, so the statistics carry the same bits either way.
 // Everything else is the wavefront-per-row kernel's MOD_LDS path (rows of
 // NV * 512 columns).
-template <int NVW, int NV, bool RMS, bool GATED, int WPB>
+template <int NVW, int NV, bool RMS, bool GATED, int WPB, bool GFIRST>
 __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, float4 *lds_sh,
                                             uint4 *lds_sh16, uint4 *lds_w, float4 *lds_w32,
                                             uint4 *lds_s116,
@@ -604,7 +616,13 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
         u[e + 1] = r[e + 1] + g1;
       }
       xv[k] = pack8(u);
-      if (live) st16s(a.residual_out + base + col(k), xv[k]);
+      if (!GFIRST && live) st16s(a.residual_out + base + col(k), xv[k]);
+    }
+    // GFIRST: stored after every gate load has been issued (a store between
+    // them orders each load behind it, a cache round trip per vector)
+    if (GFIRST && live) {
+#pragma unroll
+      for (int k = 0; k < NVW; ++k) st16s(a.residual_out + base + col(k), xv[k]);
     }
   }
 
@@ -732,6 +750,10 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
 template <int NV, bool RMS, bool GATED, int P, int WPB = 4, bool REMFIRST = false>
 __global__ __launch_bounds__(64 * WPB) void row_mixed_kernel(const RowArgs a) {
   constexpr bool F32W = RMS && WPB == 8;
+  // gated rows: every gate load ahead of the residual stores, except in the
+  // remainder-first launches and the 2048-column LN form (measured faster in
+  // the vector-by-vector order there)
+  constexpr bool GFIRST = !REMFIRST && !(NV == 4 && !RMS);
   constexpr bool B16 = NV > 8;  // modulation rows staged as bf16 (see row_segment)
   __shared__ float4 lds_s1[B16 ? 1 : NV * 128], lds_sh[(RMS && !F32W) || B16 ? 1 : NV * 128];
   __shared__ uint4 lds_sh16[(RMS && !F32W) || B16 ? NV * 64 : 1];
@@ -750,16 +772,16 @@ __global__ __launch_bounds__(64 * WPB) void row_mixed_kernel(const RowArgs a) {
   if (NV <= 8 && g < a.full_blocks) {
     const int64_t row0 = g * WPB;
     if constexpr (NV <= 8)
-      row_segment<NV, NV, RMS, GATED, WPB>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32, lds_s116,
-                                           red, row0, row0 + w, 0);
+      row_segment<NV, NV, RMS, GATED, WPB, GFIRST>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
+                                                   lds_s116, red, row0, row0 + w, 0);
   } else if constexpr (P == 2) {  // WPB / 2 rows per workgroup, a half per wavefront
     const int64_t row0 = a.full_blocks * WPB + (g - a.full_blocks) * (WPB / 2);
-    row_segment<NV / 2, NV, RMS, GATED, WPB>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
-                                             lds_s116, red, row0, row0 + (w >> 1), w & 1);
+    row_segment<NV / 2, NV, RMS, GATED, WPB, GFIRST>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
+                                                     lds_s116, red, row0, row0 + (w >> 1), w & 1);
   } else {  // WPB / 4 rows per workgroup, a quarter per wavefront
     const int64_t row0 = a.full_blocks * WPB + (g - a.full_blocks) * (WPB / 4);
-    row_segment<NV / 4, NV, RMS, GATED, WPB>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
-                                             lds_s116, red, row0, row0 + (w >> 2), w & 3);
+    row_segment<NV / 4, NV, RMS, GATED, WPB, GFIRST>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
+                                                     lds_s116, red, row0, row0 + (w >> 2), w & 3);
   }
 }
 
