@@ -1,4 +1,5 @@
-// C-ABI entry points of libditnorm.so (declared in include/ditnorm.h).
+// C-ABI entry points of libditnorm.so (declared in include/ditnorm.h; the
+// measurement copy in include/ditnorm_measure.h).
 //
 // Every entry point validates its arguments on the host first -- sizes,
 // alignment, aliasing -- and only then touches HIP: it looks up the current
@@ -13,6 +14,7 @@
 #include <mutex>
 
 #include "../../include/ditnorm.h"
+#include "../../include/ditnorm_measure.h"
 #include "launch.hpp"
 
 using namespace ditnorm;

@@ -425,16 +425,6 @@ int residual_gate_add_supported(const void *update, const void *residual, const 
                                 const void *out, int64_t rows, int64_t cols,
                                 int64_t rows_per_batch, int64_t mod_batch_stride, int dtype);
 
-/*
- * ditnorm_copy -- measurement utility, not part of the method: a plain
- * 16-byte-vector device-to-device copy of `bytes` bytes (a multiple of 16,
- * at most (DITNORM_MAX_VECTORS - 255) * 16, both pointers 16-byte aligned, no
- * overlap), one vector per work-item with streaming hints.  Used as the
- * practical HBM ceiling and to calibrate the FETCH_SIZE / WRITE_SIZE
- * counters.
- */
-int ditnorm_copy(const void *src, void *dst, int64_t bytes, void *stream);
-
 #ifdef __cplusplus
 }
 #endif

@@ -15,6 +15,8 @@ import dit_adaln_row_amd as dn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ditnorm.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 A = 0x10000        # a 16-byte-aligned fake device address (never dereferenced)
 B = 0x20000000
@@ -23,8 +25,8 @@ D = 0x60000000
 E = 0x80000000
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(headers=HEADERS):
+    text = "\n".join(open(h).read() for h in headers)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int64_t|int|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
                                  text, flags=re.M)))
@@ -47,6 +49,9 @@ def test_exports_every_declared_symbol(lib):
         assert must in names
     for n in names:
         assert hasattr(lib, n), n
+    # the measurement copy is declared apart from the method's entry points
+    assert "ditnorm_copy" not in declared_functions([HEADER])
+    assert "ditnorm_copy" in names
 
 
 def test_status_strings(lib):
@@ -276,7 +281,8 @@ def test_header_is_c_and_cpp_and_a_c_program_links(tmp_path):
     and the C-ABI test's plain C program builds against the library."""
     import subprocess
     src = tmp_path / "h.c"
-    src.write_text('#include "ditnorm.h"\nint main(void) { return ditnorm_last_hip_error(); }\n')
+    src.write_text('#include "ditnorm.h"\n#include "ditnorm_measure.h"\n'
+                   'int main(void) { return ditnorm_last_hip_error(); }\n')
     inc = os.path.join(ROOT, "include")
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", inc, "-fsyntax-only",
                     str(src)], check=True)
