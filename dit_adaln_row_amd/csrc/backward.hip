@@ -294,25 +294,34 @@ __global__ __launch_bounds__(64 * R) void bwd_fused_kernel(const BwdArgs a, int6
     const int k = s * VS + vk;
     const int c = (k * 256 + pr) * CPD;
     if (k < NV && (FULL || c < a.cols)) {
+      // Every row's words are read (rows past nrow hold stale words, in
+      // bounds) and the padding is selected afterwards: a branch per row
+      // would wait out each row's LDS latency in turn.
+      uint32_t xwv[R], dwv[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        xwv[i] = tile[buf][i][0][vk * 256 + pr];
+        dwv[i] = tile[buf][i][1][vk * 256 + pr];
+      }
+      asm volatile("" ::: "memory");  // (all the reads issued before any use)
       float s0[R], s1[R], c0[R], c1[R];
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        if (i < nrow) {
-          const uint32_t xw = tile[buf][i][0][vk * 256 + pr];
-          const uint32_t dw = tile[buf][i][1][vk * 256 + pr];
-          if constexpr (DT == 2) {
-            const float x0 = __uint_as_float(xw), d0 = __uint_as_float(dw);
-            s0[i] = d0;
-            c0[i] = d0 * (rs[i] * (x0 - mu[i]));
-          } else {
-            const float x0 = bf_lo(xw), x1 = bf_hi(xw), d0 = bf_lo(dw), d1 = bf_hi(dw);
-            s0[i] = d0;
-            s1[i] = d1;
-            c0[i] = d0 * (rs[i] * (x0 - mu[i]));
-            c1[i] = d1 * (rs[i] * (x1 - mu[i]));
-          }
-        } else {  // the tree's padding
-          s0[i] = s1[i] = c0[i] = c1[i] = 0.0f;
+        const bool live = i < nrow;  // else the tree's +0 padding
+        const uint32_t xw = xwv[i], dw = dwv[i];
+        if constexpr (DT == 2) {
+          const float x0 = __uint_as_float(xw), d0 = __uint_as_float(dw);
+          const float t0 = d0 * (rs[i] * (x0 - mu[i]));
+          s0[i] = live ? d0 : 0.0f;
+          c0[i] = live ? t0 : 0.0f;
+        } else {
+          const float x0 = bf_lo(xw), x1 = bf_hi(xw), d0 = bf_lo(dw), d1 = bf_hi(dw);
+          const float t0 = d0 * (rs[i] * (x0 - mu[i]));
+          const float t1 = d1 * (rs[i] * (x1 - mu[i]));
+          s0[i] = live ? d0 : 0.0f;
+          s1[i] = live ? d1 : 0.0f;
+          c0[i] = live ? t0 : 0.0f;
+          c1[i] = live ? t1 : 0.0f;
         }
       }
       const int64_t o = (int64_t)blockIdx.x * a.cols + c;
