@@ -83,7 +83,22 @@ __global__ __launch_bounds__(WAN_BLOCK) void wan_kernel(const WanArgs a) {
     ok[k] = EXACT || (part + k * L) < nvec;
   }
 
-  // the pixels' loads first
+  // The bias vectors (cache-resident) first, then the pixels': the bias is
+  // needed as soon as the pixels arrive, and loaded after them its cache
+  // latency followed theirs on every wavefront.  (The gamma loads stay where
+  // they are used: their latency hides behind the statistics, and holding
+  // them from here on would cost a wavefront per SIMD.)
+  float4 bia[BIAS ? VPL : 1][2];
+  if constexpr (BIAS) {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int c = ok[k] ? vch[k] : 0;
+      bia[k][0] = ld16f(a.bias + c);
+      bia[k][1] = ld16f(a.bias + c + 4);
+    }
+    asm volatile("" ::: "memory");  // (issued ahead of the pixels' loads)
+  }
+
   uint4 xv[G][VPL];
   if constexpr (TRANS) {
     static_assert(EXACT, "contiguous staging needs C == 8 * L * VPL");
@@ -137,8 +152,8 @@ __global__ __launch_bounds__(WAN_BLOCK) void wan_kernel(const WanArgs a) {
       unpack8(xv[g][k], xb[g][k]);
       if constexpr (BIAS) {
         const float4 zero = {0.f, 0.f, 0.f, 0.f};
-        const float4 b0 = ok[k] ? ld16f(a.bias + vch[k]) : zero;
-        const float4 b1 = ok[k] ? ld16f(a.bias + vch[k] + 4) : zero;
+        const float4 b0 = ok[k] ? bia[k][0] : zero;
+        const float4 b1 = ok[k] ? bia[k][1] : zero;
         float bq[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
