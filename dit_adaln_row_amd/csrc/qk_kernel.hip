@@ -52,14 +52,21 @@ __global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
   };
   auto ok = [&](int k) { return HEAD > 0 || part + L * k < nvec; };
 
+  // Every load unconditional, at a valid address: a load under a branch was
+  // waited for inside it, so a lane's loads went out one latency apart.  A
+  // row past the end reads the last row (its statistics are its own, and it
+  // is not stored); a vector past a head row's end (run-time head dims) reads
+  // the row's first vector and is zeroed.
   uint4 xv[G][VPL];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int64_t r = base + RPW * g + sub;
+    const int64_t rc = r < total ? r : total - 1;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       const uint4 zero = {0, 0, 0, 0};
-      xv[g][k] = (r < total && ok(k)) ? ld16x<NTL>(src(r) + (part + L * k) * 8) : zero;
+      const uint4 v = ld16x<NTL>(src(rc) + (ok(k) ? part + L * k : 0) * 8);
+      xv[g][k] = ok(k) ? v : zero;
     }
   }
 
