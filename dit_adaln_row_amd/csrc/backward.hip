@@ -112,14 +112,27 @@ __device__ __forceinline__ void bwd_row(const BwdArgs &a, int64_t row, int64_t m
     s1[0] = q.x; s1[1] = q.y; s1[2] = q.z; s1[3] = q.w;
   };
 
+  // Every load unconditional (a vector past the row's end reads the row's
+  // first vector and is zeroed): a load under a branch was waited for inside
+  // it, so a lane's loads went out one latency apart.
+  auto lc = [&](int k) { return ok(k) ? col(k) : 0; };
   uint4 sv[DT == 2 ? 1 : NV];
 #pragma unroll
-  for (int k = 0; k < NV; ++k) xv[k] = ok(k) ? ld16s(at<DT>(a.x, base + col(k))) : zero;
+  for (int k = 0; k < NV; ++k) {
+    const uint4 v = ld16s(at<DT>(a.x, base + lc(k)));
+    xv[k] = ok(k) ? v : zero;
+  }
 #pragma unroll
-  for (int k = 0; k < NV; ++k) dv[k] = ok(k) ? ld16s(at<DT>(a.d_out, base + col(k))) : zero;
+  for (int k = 0; k < NV; ++k) {
+    const uint4 v = ld16s(at<DT>(a.d_out, base + lc(k)));
+    dv[k] = ok(k) ? v : zero;
+  }
   if constexpr (DT != 2) {
 #pragma unroll
-    for (int k = 0; k < NV; ++k) sv[k] = ok(k) ? ld16(at<DT>(a.scale, mo + col(k))) : zero;
+    for (int k = 0; k < NV; ++k) {
+      const uint4 v = ld16(at<DT>(a.scale, mo + lc(k)));
+      sv[k] = ok(k) ? v : zero;
+    }
   }
 
   // one pass of binary64 sums over the raw inputs (padding contributes
