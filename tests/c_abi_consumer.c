@@ -6,14 +6,20 @@
  *
  *   c_abi_consumer DIR
  *
- * DIR/meta.txt holds "rows cols" for a single-batch LayerNorm + modulate
- * site; DIR/x.bin, scale.bin, shift.bin and d_out.bin hold the bf16 bit
- * patterns (rows x cols, cols, cols, rows x cols).  The program runs
- * ln_modulate, then ln_modulate_backward on the same rows (workspace sized by
- * ln_modulate_backward_workspace_bytes), and checks that a call with a null
- * input fails with DITNORM_INVALID_ARGUMENT and the matching status string.
- * It writes out.bin, d_x.bin, d_scale.bin and d_shift.bin to DIR and exits 0,
- * or prints the failing step and exits 1.
+ * DIR/meta.txt holds "rows cols" for a single batch (cols a multiple of 384);
+ * DIR/x.bin, scale.bin, shift.bin, d_out.bin, gate.bin and weight.bin hold
+ * bf16 bit patterns (rows x cols, cols, cols, rows x cols, cols, cols), and
+ * bias.bin and gamma.bin 96 fp32 values.  The program runs
+ *   ln_modulate(x, scale, shift)                       -> out.bin
+ *   ln_modulate_backward(x, scale, d_out)  (workspace sized by
+ *       ln_modulate_backward_workspace_bytes)           -> d_x, d_scale, d_shift.bin
+ *   gated_ln_modulate(x, residual = d_out, gate, scale, shift) -> h.bin, gated.bin
+ *   rms_modulate(x, weight, scale, shift)              -> rms.bin
+ *   qk_layernorm(q = x, k = d_out as rows of 128)      -> q_out.bin, k_out.bin
+ *   rmsnorm_silu_bias(x as pixels of 96 channels, bias, gamma) -> wan.bin
+ * and checks that a call with a null input fails with
+ * DITNORM_INVALID_ARGUMENT and the matching status string.  It exits 0, or
+ * prints the failing step and exits 1.
  */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -88,8 +94,10 @@ int main(int argc, char **argv) {
   const size_t act = (size_t)rows * (size_t)cols * 2, vec = (size_t)cols * 2;
   uint16_t *x = read_file("x.bin", act), *sc = read_file("scale.bin", vec);
   uint16_t *sh = read_file("shift.bin", vec), *dout = read_file("d_out.bin", act);
-  if (!x || !sc || !sh || !dout) {
-    fprintf(stderr, "missing input files in %s\n", g_dir);
+  uint16_t *gt = read_file("gate.bin", vec), *wt = read_file("weight.bin", vec);
+  float *bias = read_file("bias.bin", 96 * 4), *gamma = read_file("gamma.bin", 96 * 4);
+  if (!x || !sc || !sh || !dout || !gt || !wt || !bias || !gamma || cols % 384 != 0) {
+    fprintf(stderr, "missing input files in %s, or cols not a multiple of 384\n", g_dir);
     return 1;
   }
 
@@ -123,6 +131,31 @@ int main(int argc, char **argv) {
   CHECK_DN(ln_modulate_backward(dx_in, dsc, dd, ddx, dds, ddh, rows, cols, rows, cols, 1e-6f,
                                 dws, ws, NULL, NULL, DITNORM_DTYPE_BF16, NULL));
 
+  /* the other entry points on the same buffers */
+  void *dgt, *dwt, *dh, *dgo, *drms, *dqo, *dko, *dwan;
+  float *dbias, *dgamma;
+  CHECK_HIP(hipMalloc(&dgt, vec));
+  CHECK_HIP(hipMalloc(&dwt, vec));
+  CHECK_HIP(hipMalloc((void **)&dbias, 96 * 4));
+  CHECK_HIP(hipMalloc((void **)&dgamma, 96 * 4));
+  CHECK_HIP(hipMalloc(&dh, act));
+  CHECK_HIP(hipMalloc(&dgo, act));
+  CHECK_HIP(hipMalloc(&drms, act));
+  CHECK_HIP(hipMalloc(&dqo, act));
+  CHECK_HIP(hipMalloc(&dko, act));
+  CHECK_HIP(hipMalloc(&dwan, act));
+  CHECK_HIP(hipMemcpy(dgt, gt, vec, hipMemcpyHostToDevice));
+  CHECK_HIP(hipMemcpy(dwt, wt, vec, hipMemcpyHostToDevice));
+  CHECK_HIP(hipMemcpy(dbias, bias, 96 * 4, hipMemcpyHostToDevice));
+  CHECK_HIP(hipMemcpy(dgamma, gamma, 96 * 4, hipMemcpyHostToDevice));
+  CHECK_DN(gated_ln_modulate(dx_in, dd, dgt, dsc, dsh, dh, dgo, rows, cols, rows, cols, 1e-6f,
+                             NULL, NULL, NULL, NULL));
+  CHECK_DN(rms_modulate(dx_in, dwt, dsc, dsh, drms, NULL, NULL, NULL, rows, cols, rows, cols,
+                        1e-6f, NULL, NULL, NULL));
+  const int64_t heads = rows * cols / 128, pixels = rows * cols / 96;
+  CHECK_DN(qk_layernorm(dx_in, dd, dqo, dko, heads, heads, 128, 1e-5f, NULL, NULL, NULL));
+  CHECK_DN(rmsnorm_silu_bias(dx_in, dbias, dgamma, dwan, pixels, 96, 1e-6f, NULL, NULL, NULL));
+
   /* a rejected call: a null input, no launch */
   const int bad = ln_modulate(NULL, dsc, dsh, dout_ln, rows, cols, rows, cols, 1e-6f, NULL,
                               NULL, NULL, NULL);
@@ -144,6 +177,18 @@ int main(int argc, char **argv) {
       write_file("d_shift.bin", dshift, (size_t)cols * 4)) {
     fprintf(stderr, "cannot write outputs to %s\n", g_dir);
     return 1;
+  }
+  const struct {
+    const char *name;
+    void *dev;
+  } more[] = {{"h.bin", dh},         {"gated.bin", dgo}, {"rms.bin", drms},
+              {"q_out.bin", dqo},    {"k_out.bin", dko}, {"wan.bin", dwan}};
+  for (size_t i = 0; i < sizeof more / sizeof more[0]; ++i) {
+    CHECK_HIP(hipMemcpy(out, more[i].dev, act, hipMemcpyDeviceToHost));
+    if (write_file(more[i].name, out, act)) {
+      fprintf(stderr, "cannot write %s to %s\n", more[i].name, g_dir);
+      return 1;
+    }
   }
   printf("c_abi_consumer: %lld x %lld, workspace %lld bytes: ok\n", rows, cols, (long long)ws);
   return 0;

@@ -1,8 +1,10 @@
 """The C ABI from a plain C program (tests/c_abi_consumer.c, built by
 __graft_entry__.build()): device memory from the HIP runtime's C API, the
 entry points of include/ditnorm.h with raw pointers, no Python in between.
-Its ln_modulate output and its backward (d_x, d_scale, d_shift, over 300
-tokens: chunk sums and tree levels) against the oracle at the parity bar."""
+Its outputs against the oracle at the parity bar: ln_modulate, the backward
+(d_x, d_scale, d_shift over 300 tokens: chunk sums and tree levels),
+gated_ln_modulate, rms_modulate, qk_layernorm (the same buffers as rows of
+128) and rmsnorm_silu_bias (as pixels of 96 channels)."""
 import os
 import subprocess
 
@@ -25,8 +27,15 @@ def test_c_program_matches_oracle(gpu, orc, tmp_path):
     sc = gen.to_u16(gen.normal((cols,), 0, 0.1, 2102))
     sh = gen.to_u16(gen.normal((cols,), 0, 0.1, 2103))
     dout = gen.to_u16(gen.normal((rows, cols), 0, 1, 2104))
-    for name, arr in (("x", x), ("scale", sc), ("shift", sh), ("d_out", dout)):
+    gate = gen.to_u16(gen.normal((cols,), 0, 0.1, 2105))
+    weight = gen.to_u16(gen.normal((cols,), 1.0, 0.05, 2106))
+    bias = gen.normal((96,), 0, 0.05, 2107, "f32").numpy()
+    gamma = gen.normal((96,), 1.0, 0.05, 2108, "f32").numpy()
+    for name, arr in (("x", x), ("scale", sc), ("shift", sh), ("d_out", dout), ("gate", gate),
+                      ("weight", weight)):
         np.ascontiguousarray(arr, dtype=np.uint16).tofile(tmp_path / f"{name}.bin")
+    bias.astype(np.float32).tofile(tmp_path / "bias.bin")
+    gamma.astype(np.float32).tofile(tmp_path / "gamma.bin")
     (tmp_path / "meta.txt").write_text(f"{rows} {cols}\n")
     r = subprocess.run([BIN, str(tmp_path)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
@@ -42,3 +51,20 @@ def test_c_program_matches_oracle(gpu, orc, tmp_path):
     d_shift = np.fromfile(tmp_path / "d_shift.bin", np.float32).reshape(1, cols)
     assert np.array_equal(d_shift, bref["d_shift"]), "d_shift from C"
     assert np.array_equal(d_scale, bref["d_scale"]), "d_scale from C"
+
+    def got(name, shape):
+        return np.fromfile(tmp_path / name, np.uint16).reshape(shape)
+
+    g = orc.gated_ln_modulate(x, dout, gate.reshape(1, cols), sc.reshape(1, cols),
+                              sh.reshape(1, cols), 1e-6, rows_per_batch=rows)
+    assert same_bits(got("h.bin", (rows, cols)), g["h"]), "gated_ln_modulate h from C"
+    assert same_bits(got("gated.bin", (rows, cols)), g["out"]), "gated_ln_modulate from C"
+    r = orc.rms_modulate(x, weight, sc.reshape(1, cols), sh.reshape(1, cols), 1e-6,
+                         rows_per_batch=rows)
+    assert same_bits(got("rms.bin", (rows, cols)), r["out"]), "rms_modulate from C"
+    q = orc.qk_layernorm(x.reshape(-1, 128), dout.reshape(-1, 128), 1e-5)
+    assert same_bits(got("q_out.bin", (rows * cols // 128, 128)), q["q_out"]), "qk q from C"
+    assert same_bits(got("k_out.bin", (rows * cols // 128, 128)), q["k_out"]), "qk k from C"
+    w = orc.rmsnorm_silu_bias(x.reshape(-1, 96), bias, gamma, 1e-6)
+    dw = ulp_diff(got("wan.bin", (rows * cols // 96, 96)), w["out"])
+    assert dw.max() <= 1, "rmsnorm_silu_bias from C: beyond 1 ulp"
