@@ -649,14 +649,19 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
     }
     lds_barrier();  // the staged modulation rows and every segment's moments
     if (!live) return;  // whole wavefront; no barrier follows
-    constexpr int P = NV / NVW;  // segments per row: 2 or 4
+    constexpr int P = NV / NVW;  // segments per row: 2, 4 or 8
     const int pw = w & ~(P - 1);
     if constexpr (P == 2) {
       s1 = red[pw][0] + red[pw + 1][0];
       s2 = red[pw][1] + red[pw + 1][1];
-    } else {
+    } else if constexpr (P == 4) {
       s1 = (red[pw][0] + red[pw + 1][0]) + (red[pw + 2][0] + red[pw + 3][0]);
       s2 = (red[pw][1] + red[pw + 1][1]) + (red[pw + 2][1] + red[pw + 3][1]);
+    } else {
+      s1 = ((red[pw][0] + red[pw + 1][0]) + (red[pw + 2][0] + red[pw + 3][0])) +
+           ((red[pw + 4][0] + red[pw + 5][0]) + (red[pw + 6][0] + red[pw + 7][0]));
+      s2 = ((red[pw][1] + red[pw + 1][1]) + (red[pw + 2][1] + red[pw + 3][1])) +
+           ((red[pw + 4][1] + red[pw + 5][1]) + (red[pw + 6][1] + red[pw + 7][1]));
     }
   }
   const double n_d = (double)cols;
@@ -783,16 +788,24 @@ __global__ __launch_bounds__(64 * WPB) void row_mixed_kernel(const RowArgs a) {
     const int64_t row0 = a.full_blocks * WPB + (g - a.full_blocks) * (WPB / 2);
     row_segment<NV / 2, NV, RMS, GATED, WPB, GFIRST>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
                                                      lds_s116, red, row0, row0 + (w >> 1), w & 1);
-  } else {  // WPB / 4 rows per workgroup, a quarter per wavefront
+  } else if constexpr (P == 4) {  // WPB / 4 rows per workgroup, a quarter per wavefront
     const int64_t row0 = a.full_blocks * WPB + (g - a.full_blocks) * (WPB / 4);
     row_segment<NV / 4, NV, RMS, GATED, WPB, GFIRST>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
                                                      lds_s116, red, row0, row0 + (w >> 2), w & 3);
+  } else {  // (8-wavefront workgroups) a row per workgroup, an eighth per wavefront
+    static_assert(P == 8 && WPB == 8, "eighths: one row per 8-wavefront workgroup");
+    const int64_t row0 = a.full_blocks * WPB + (g - a.full_blocks);
+    row_segment<NV / 8, NV, RMS, GATED, WPB, GFIRST>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
+                                                     lds_s116, red, row0, row0, w);
   }
 }
 
 // Whole rounds of rows (one row per wavefront, one wavefront per SIMD per
-// round) and the remainder in quarters when it is at most a quarter round
-// (rows of 2048 or 4096 columns), in halves when it is at most half a round;
+// round) and the remainder in eighths when it is at most an eighth of a round
+// (the 8-wavefront plain RMS form: a row per workgroup; ERNIE's 120 extra rows
+// of 4096 14.27 -> 14.04 us, 1-3% at other such remainders, bitwise
+// unchanged), in quarters when it is at most a quarter round (rows of 2048 or
+// 4096 columns), in halves when it is at most half a round;
 // else every row whole.  A launch of fewer rows than that (no whole round)
 // splits every row the same way, so that it spreads over the SIMDs instead
 // of leaving most of them idle.
@@ -817,6 +830,12 @@ static void launch_mixed_kind(const RowArgs &a, int P, bool remfirst, dim3 grid,
       return;
     }
   }
+  if constexpr (WPB == 8 && NV % 8 == 0) {
+    if (P == 8) {
+      hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, 8, 8>), grid, block, 0, stream, a);
+      return;
+    }
+  }
   if (P == 4)
     hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, P4, WPB>), grid, block, 0, stream, a);
   else
@@ -836,6 +855,10 @@ static hipError_t launch_mixed_w(const RowArgs &a0, bool rms, bool gated, const 
     a.full_blocks = 0;
     P = split;
     blocks = (a.rows + WPB / P - 1) / (WPB / P);
+  } else if (WPB == 8 && whole > 0 && rem > 0 && 8 * rem <= simds && NV % 8 == 0) {
+    a.full_blocks = whole / WPB;
+    blocks = a.full_blocks + rem;  // a row per workgroup, an eighth per wavefront
+    P = 8;
   } else if (whole > 0 && rem > 0 && 4 * rem <= simds && NV % 4 == 0) {
     a.full_blocks = whole / WPB;
     blocks = a.full_blocks + (rem + WPB / 4 - 1) / (WPB / 4);

@@ -878,10 +878,11 @@ SPLIT_CASES = [(3072, 4096 + 512, 4096 + 512), (3072, 1024 + 1, 1025), (4096, 20
                (4096, 4096 + 120, 17), (4096, 2048 + 256, 9), (4096, 1024 + 255, 1279),
                (4096, 1024 + 63, 1087),
                # the plain RMS form in 8-wavefront workgroups (at least four whole
-               # rounds): quarters, halves, every row whole with a partly live last
+               # rounds): eighths (a row per workgroup) up to an eighth of a round,
+               # quarters past it, halves, every row whole with a partly live last
                # workgroup, and only whole rounds
-               (4096, 8192 + 100, 12), (4096, 4096 + 300, 7), (4096, 4096 + 700, 11),
-               (4096, 4096, 64)]
+               (4096, 8192 + 100, 12), (4096, 4096 + 128, 8), (4096, 4096 + 129, 13),
+               (4096, 4096 + 300, 7), (4096, 4096 + 700, 11), (4096, 4096, 64)]
 
 
 @pytest.mark.parametrize("cols,rows,rpb", SPLIT_CASES)
@@ -889,7 +890,9 @@ SPLIT_CASES = [(3072, 4096 + 512, 4096 + 512), (3072, 1024 + 1, 1025), (4096, 20
 def test_balanced_split_rows(gpu, orc, cols, rows, rpb, kind):
     """Row counts with a remainder of at most half a round take the half-row
     path (batch boundaries fall inside half-row workgroups at rpb = 17), at
-    most a quarter round of 2048 or 4096 columns the quarter-row path."""
+    most a quarter round of 2048 or 4096 columns the quarter-row path, and in
+    the plain RMS form's 8-wavefront workgroups at most an eighth of a round
+    the eighth-row path."""
     log(f"balanced {kind} rows={rows} cols={cols} rpb={rpb}")
     B = rows // rpb
     x = rand((rows, cols), 0.2, 1.5, 1100 + cols + rows)
