@@ -267,6 +267,10 @@ __global__ __launch_bounds__(64 * R) void bwd_fused_kernel(const BwdArgs a, int6
     lds_barrier();
   }
 
+  // A wavefront past the chunk's last token stands for the tree's +0
+  // padding: it puts a zero row and zero statistics (mean 0, rstd 0) into
+  // LDS, whose terms d_out = +0 and d_out * (rstd * (x - mean)) = +0 are
+  // exactly the padding, so the token step needs no per-row selects.
   uint4 xv[NV], dv[NV];
   if (w < nrow) {
     float mean_f, rstd_f;
@@ -277,6 +281,10 @@ __global__ __launch_bounds__(64 * R) void bwd_fused_kernel(const BwdArgs a, int6
       if (a.mean_out) a.mean_out[row] = mean_f;
       if (a.rstd_out) a.rstd_out[row] = rstd_f;
     }
+  } else {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) xv[k] = dv[k] = uint4{0, 0, 0, 0};
+    if (lane == 0) stat[w][0] = stat[w][1] = 0.0f;
   }
 
   // token sums of the chunk
@@ -286,14 +294,12 @@ __global__ __launch_bounds__(64 * R) void bwd_fused_kernel(const BwdArgs a, int6
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     const int buf = s & 1;
-    if (w < nrow) {
 #pragma unroll
-      for (int v = 0; v < VS; ++v) {
-        const int k = s * VS + v;
-        if (k < NV && (FULL || lane + 64 * k < nvec)) {
-          *reinterpret_cast<uint4 *>(&tile[buf][w][0][v * 256 + lane * 4]) = xv[k];
-          *reinterpret_cast<uint4 *>(&tile[buf][w][1][v * 256 + lane * 4]) = dv[k];
-        }
+    for (int v = 0; v < VS; ++v) {
+      const int k = s * VS + v;
+      if (k < NV && (FULL || lane + 64 * k < nvec)) {
+        *reinterpret_cast<uint4 *>(&tile[buf][w][0][v * 256 + lane * 4]) = xv[k];
+        *reinterpret_cast<uint4 *>(&tile[buf][w][1][v * 256 + lane * 4]) = dv[k];
       }
     }
     lds_barrier();
@@ -307,9 +313,8 @@ __global__ __launch_bounds__(64 * R) void bwd_fused_kernel(const BwdArgs a, int6
     const int k = s * VS + vk;
     const int c = (k * 256 + pr) * CPD;
     if (k < NV && (FULL || c < a.cols)) {
-      // Every row's words are read (rows past nrow hold stale words, in
-      // bounds) and the padding is selected afterwards: a branch per row
-      // would wait out each row's LDS latency in turn.
+      // Every row's words are read before any is used: a use between the
+      // reads would wait out each row's LDS latency in turn.
       uint32_t xwv[R], dwv[R];
 #pragma unroll
       for (int i = 0; i < R; ++i) {
@@ -320,21 +325,17 @@ __global__ __launch_bounds__(64 * R) void bwd_fused_kernel(const BwdArgs a, int6
       float s0[R], s1[R], c0[R], c1[R];
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const bool live = i < nrow;  // else the tree's +0 padding
         const uint32_t xw = xwv[i], dw = dwv[i];
         if constexpr (DT == 2) {
           const float x0 = __uint_as_float(xw), d0 = __uint_as_float(dw);
-          const float t0 = d0 * (rs[i] * (x0 - mu[i]));
-          s0[i] = live ? d0 : 0.0f;
-          c0[i] = live ? t0 : 0.0f;
+          s0[i] = d0;
+          c0[i] = d0 * (rs[i] * (x0 - mu[i]));
         } else {
           const float x0 = bf_lo(xw), x1 = bf_hi(xw), d0 = bf_lo(dw), d1 = bf_hi(dw);
-          const float t0 = d0 * (rs[i] * (x0 - mu[i]));
-          const float t1 = d1 * (rs[i] * (x1 - mu[i]));
-          s0[i] = live ? d0 : 0.0f;
-          s1[i] = live ? d1 : 0.0f;
-          c0[i] = live ? t0 : 0.0f;
-          c1[i] = live ? t1 : 0.0f;
+          s0[i] = d0;
+          s1[i] = d1;
+          c0[i] = d0 * (rs[i] * (x0 - mu[i]));
+          c1[i] = d1 * (rs[i] * (x1 - mu[i]));
         }
       }
       const int64_t o = (int64_t)blockIdx.x * a.cols + c;
