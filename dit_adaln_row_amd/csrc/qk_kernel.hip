@@ -1,7 +1,8 @@
 // Per-head LayerNorm (no affine) over the head rows of q and of k in one
-// launch (GLM-Image page, Motivation: nn.LayerNorm(128) per head on
-// (1, S, 32, 128); "What rounding-faithful means here": q and k handled by one
-// launch; its kernel takes head dims up to 128).  Per row of d = head_dim
+// launch (GLM-Image page, Motivation: the q and k tensors of shape
+// (1, S, 32, 128) normalised head by head over their 128 values; "What
+// rounding-faithful means here": q and k handled by one launch; its kernel
+// takes head dims up to 128).  Per row of d = head_dim
 // values: mean = fp32(S1/d), rstd = fp32(1/sqrt(M2/d + eps)),
 // out = bf16(rstd * (x - mean)).
 //
@@ -99,11 +100,19 @@ __global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int k = 0; k < VPL; ++k) launder(xv[g][k]);
+  // A wavefront whose rows all lie in q or all in k (every one but the
+  // wavefront across the boundary, when rows_q is not a multiple of its rows)
+  // writes them through one buffer resource at its first row, written
+  // through the L2 (about 1% faster); the one across the boundary stores
+  // row by row.
+  const bool one_side = base + RPW * G <= a.rows_q || base >= a.rows_q;
+  const auto out_r = wt_rsrc(dst(base));
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int64_t r = base + RPW * g + sub;
     if (r >= total) continue;
     uint16_t *d = dst(r);
+    const uint32_t rb = (uint32_t)((r - base) * head * 2);  // the row's byte offset
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       if (!ok(k)) continue;
@@ -111,7 +120,9 @@ __global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
       unpack8(xv[g][k], v);
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] = rstd_f[g] * (v[e] - mean_f[g]);
-      st16s(d + (part + L * k) * 8, pack8(y));
+      const int vo = (part + L * k) * 8;
+      if (one_side) st16w(out_r, rb + vo * 2, pack8(y));
+      else st16s(d + vo, pack8(y));
     }
     if (part == 0) {
       if (a.mean_out) a.mean_out[r] = mean_f[g];
