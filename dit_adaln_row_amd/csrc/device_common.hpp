@@ -244,6 +244,22 @@ __device__ __forceinline__ uint4 narrow8(const float f[8]) {
 }
 
 // the value a storage-type kernel boundary keeps
+// a 16-byte vector as four fp16 pairs, and back
+__device__ __forceinline__ void as_f16x2(const uint4 v, f16x2 h[4]) {
+  h[0] = __builtin_bit_cast(f16x2, v.x);
+  h[1] = __builtin_bit_cast(f16x2, v.y);
+  h[2] = __builtin_bit_cast(f16x2, v.z);
+  h[3] = __builtin_bit_cast(f16x2, v.w);
+}
+__device__ __forceinline__ uint4 from_f16x2(const f16x2 h[4]) {
+  uint4 v;
+  v.x = __builtin_bit_cast(uint32_t, h[0]);
+  v.y = __builtin_bit_cast(uint32_t, h[1]);
+  v.z = __builtin_bit_cast(uint32_t, h[2]);
+  v.w = __builtin_bit_cast(uint32_t, h[3]);
+  return v;
+}
+
 template <int DT>
 __device__ __forceinline__ void round8(float f[8]) {
   const uint4 p = narrow8<DT>(f);

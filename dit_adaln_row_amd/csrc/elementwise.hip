@@ -8,11 +8,14 @@
 // residual_gate_add (GLM-Image page, the ff gate reusing residual_gate_add;
 // ERNIE-Image page, the residual variant):
 //     out = rnd(residual + rnd(gate * update))
-// rnd rounds to the storage type (bf16 or fp16) nearest-even; each operation
-// is one binary32 operation on exactly widened operands.  For fp16 the
-// compiler may fuse a widen / operate / round triple into one fp16
-// instruction: a binary32 intermediate has at least 2p+2 significand bits for
-// p = 11, so the correctly rounded fp16 result is the same either way.
+// rnd rounds to the storage type (bf16 or fp16) nearest-even.  bf16: each
+// operation is one binary32 operation on exactly widened operands, rounded.
+// fp16: each operation is one packed fp16 instruction on a pair of values
+// (v_pk_mul_f16 / v_pk_add_f16, IEEE nearest-even with subnormals kept):
+// a binary32 intermediate has at least 2p+2 significand bits for p = 11, so
+// the binary32 operation rounded to fp16 and the direct fp16 operation give
+// the same bits, and the packed form takes one instruction per two values
+// where the widened chain took about ten.
 //
 // Work layout: thread t owns the 16-byte column slot t % (cols/8) of U
 // consecutive rows, so its modulation vector (already rounded 1 + scale, and
@@ -28,12 +31,11 @@
 // Measured on 4096 x 3072: U = 8 (3 wavefronts per SIMD) 9.65 us, U = 4 (6)
 // 11.13 us, U = 2 10.91 us, against 9.98 us for a plain copy of the bytes;
 // 4608 x 3072 at U = 9 11.10 us against 11.92 at U = 2.  Launches too large
-// for that (more than 12 rows per thread) keep U = 2.  This holds for the
-// bf16 modulate only: the fp16 modulate measured 3-8% slower with the same
-// choice (4608 x 3072: 12.28 us against 11.73 at U = 2; its widening and
-// rounding keep 101 registers live at U = 9 against 69), and the gate add,
-// with two input rows per vector, 6-10% slower (17.12 us against 15.57):
-// both keep U = 2.
+// for that (more than 12 rows per thread) keep U = 2.  The fp16 forms, in
+// packed fp16 arithmetic, take the same choice: 4608 x 3072 modulate 11.77
+// (U = 2, widened chain) -> 10.14 us, gate add 16.11 -> 15.41 us.  The bf16
+// gate add, with two input rows per vector, measured 6-10% slower with it
+// (17.12 us against 15.57) and keeps U = 2.
 #include <atomic>
 #include <utility>
 
@@ -65,6 +67,50 @@ __global__ __launch_bounds__(EW_BLOCK) void elementwise_kernel(const Elementwise
     const int64_t off = (r0 + u) * (int64_t)a.cols + c8;
     in0[u] = ld16s(a.a + off);
     if constexpr (OP == 1) in1[u] = ld16s(a.b + off);
+  }
+
+  if constexpr (DT == 1) {
+    // fp16: each eager op is one packed fp16 operation on a pair (IEEE
+    // nearest-even, subnormals kept): the binary32 operation rounded to fp16
+    // gives the same bits, since binary32 holds 2 * 11 + 2 significand bits
+    int64_t cb = -1;
+    f16x2 h0[4], h1[4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u >= nr) continue;
+      const int64_t r = r0 + u;
+      const int64_t b = r / a.rows_per_batch;
+      if (b != cb) {  // the first row, and batch boundaries
+        cb = b;
+        const int64_t mo = b * a.mod_stride + c8;
+        as_f16x2(ld16(a.m0 + mo), h0);
+        if constexpr (OP == 0) {
+          as_f16x2(ld16(a.m1 + mo), h1);
+          const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h0[i] = one + h0[i];  // s1 = rnd(1 + scale)
+        }
+      }
+      f16x2 v[4], o[4];
+      as_f16x2(in0[u], v);
+      if constexpr (OP == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f16x2 w = v[i] * h0[i];  // rnd(x * s1)
+          o[i] = w + h1[i];              // rnd(. + shift)
+        }
+      } else {
+        f16x2 res[4];
+        as_f16x2(in1[u], res);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f16x2 w = h0[i] * v[i];  // rnd(gate * update)
+          o[i] = res[i] + w;             // rnd(residual + .)
+        }
+      }
+      st16s(a.out + r * (int64_t)a.cols + c8, from_f16x2(o));
+    }
+    return;
   }
 
   int64_t cur_b = -1;
@@ -116,33 +162,34 @@ static hipError_t launch_u(const ElementwiseArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Workgroups of the bf16 modulate's U instantiation resident per compute
-// unit (= its wavefronts per SIMD: a workgroup is 4 wavefronts on 4 SIMDs),
-// cached per process.
-template <int U>
+// Workgroups of an instantiation resident per compute unit (= its
+// wavefronts per SIMD: a workgroup is 4 wavefronts on 4 SIMDs), cached per
+// process.
+template <int OP, int DT, int U>
 static int resident_u() {
   static std::atomic<int> cache;
   int r = cache.load(std::memory_order_relaxed);
   if (r > 0) return r;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, (const void *)elementwise_kernel<0, 0, U>,
-                                                   EW_BLOCK, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &r, (const void *)elementwise_kernel<OP, DT, U>, EW_BLOCK, 0) != hipSuccess ||
       r < 1)
     r = 1;
   cache.store(r, std::memory_order_relaxed);
   return r;
 }
 
-template <int... Us>
+template <int OP, int DT, int... Us>
 static int resident(int u, std::integer_sequence<int, Us...>) {
   int r = 1;
-  ((u == Us + 1 ? (r = resident_u<Us + 1>(), 0) : 0), ...);
+  ((u == Us + 1 ? (r = resident_u<OP, DT, Us + 1>(), 0) : 0), ...);
   return r;
 }
 
-// The bf16 modulate's rows per thread: every wavefront resident at once (at
-// most EW_MAX_WAVES per SIMD, and no more than the instantiation's registers
-// allow) and the fewest row vectors on the busiest SIMD; of equal choices the
-// larger U (fewer wavefronts).  0 if no U fits.
+// Rows per thread: every wavefront resident at once (at most EW_MAX_WAVES
+// per SIMD, and no more than the instantiation's registers allow) and the
+// fewest row vectors on the busiest SIMD; of equal choices the larger U
+// (fewer wavefronts).  0 if no U fits.
+template <int OP, int DT>
 static int rows_per_thread(int64_t rows, int64_t nvec, int num_cu) {
   const int64_t simds = 4LL * num_cu;
   int best = 0;
@@ -151,7 +198,7 @@ static int rows_per_thread(int64_t rows, int64_t nvec, int num_cu) {
     const int64_t waves = ((rows + u - 1) / u * nvec + 63) / 64;
     const int64_t per_simd = (waves + simds - 1) / simds;
     if (per_simd > EW_MAX_WAVES ||
-        per_simd > resident(u, std::make_integer_sequence<int, EW_MAX_ROWS>{}))
+        per_simd > resident<OP, DT>(u, std::make_integer_sequence<int, EW_MAX_ROWS>{}))
       continue;
     const int64_t cost = per_simd * u;
     if (best == 0 || cost <= best_cost) {
@@ -162,21 +209,33 @@ static int rows_per_thread(int64_t rows, int64_t nvec, int num_cu) {
   return best;
 }
 
-template <int... Us>
-static hipError_t launch_modulate(int u, const ElementwiseArgs &a, hipStream_t stream,
-                                  std::integer_sequence<int, Us...>) {
+template <int OP, int DT, int... Us>
+static hipError_t launch_rows(int u, const ElementwiseArgs &a, hipStream_t stream,
+                              std::integer_sequence<int, Us...>) {
   hipError_t e = hipErrorInvalidValue;
-  ((u == Us + 1 ? (e = launch_u<0, 0, Us + 1>(a, stream), 0) : 0), ...);
+  ((u == Us + 1 ? (e = launch_u<OP, DT, Us + 1>(a, stream), 0) : 0), ...);
   return e;
 }
 
+template <int OP, int DT>
+static hipError_t launch_balanced(const ElementwiseArgs &a, const DeviceInfo &dev,
+                                  hipStream_t stream) {
+  const int u = rows_per_thread<OP, DT>(a.rows, a.cols >> 3, dev.num_cu);
+  if (u == 0) return launch_u<OP, DT, 2>(a, stream);  // streams in rounds
+  return launch_rows<OP, DT>(u, a, stream, std::make_integer_sequence<int, EW_MAX_ROWS>{});
+}
+
+// The bf16 gate add keeps two rows per thread (the balanced choice measured
+// 6-10% slower for it); the modulate in both types and the fp16 gate add
+// take the balanced choice.
 hipError_t launch_elementwise(const ElementwiseArgs &a, int op, int dtype, const DeviceInfo &dev,
                               hipStream_t stream) {
-  if (op == 1) return dtype == 0 ? launch_u<1, 0, 2>(a, stream) : launch_u<1, 1, 2>(a, stream);
-  if (dtype == 1) return launch_u<0, 1, 2>(a, stream);
-  const int u = rows_per_thread(a.rows, a.cols >> 3, dev.num_cu);
-  if (u == 0) return launch_u<0, 0, 2>(a, stream);  // streams in rounds
-  return launch_modulate(u, a, stream, std::make_integer_sequence<int, EW_MAX_ROWS>{});
+  if (op == 1) {
+    if (dtype == 0) return launch_u<1, 0, 2>(a, stream);
+    return launch_balanced<1, 1>(a, dev, stream);
+  }
+  if (dtype == 1) return launch_balanced<0, 1>(a, dev, stream);
+  return launch_balanced<0, 0>(a, dev, stream);
 }
 
 }  // namespace ditnorm

@@ -69,25 +69,30 @@ def test_elementwise_shapes(gpu, orc, dt, op, rows, cols, B):
     assert same_bits(got, ref, dt), f"{int((got != ref).sum())} elements differ"
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("dt,op", [("bf16", "mod"), ("f16", "mod"), ("f16", "gate")])
 @pytest.mark.parametrize("u", range(1, 13))
-def test_modulate_every_rows_per_thread(gpu, orc, dt, u):
-    """The bf16 modulate gives each thread the U rows that keep every
-    wavefront resident and the busiest SIMD least loaded.  At 512 columns (one
-    wavefront per row group) a little under U * (4 * CUs) rows selects U:
-    U = 1..12, each with a ragged last group and the batch boundaries of
-    three batches inside a thread's rows.  (fp16 runs the same shapes at
-    U = 2.)"""
+def test_modulate_every_rows_per_thread(gpu, orc, dt, op, u):
+    """The modulate (bf16 and fp16) and the fp16 gate add give each thread
+    the U rows that keep every wavefront resident and the busiest SIMD least
+    loaded.  At 512 columns (one wavefront per row group) a little under
+    U * (4 * CUs) rows selects U: U = 1..12, each with a ragged last group
+    and the batch boundaries of three batches inside a thread's rows.  (The
+    bf16 gate add runs every shape at U = 2.)"""
     td = TORCH[dt]
     simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count
     cols, B = 512, 3
     rows = (simds * u - 4) // 3 * 3
-    log(f"mod {dt} U={u} rows={rows}")
+    log(f"{op} {dt} U={u} rows={rows}")
     x = rand((rows, cols), 0.2, 1.5, 70 + u, dt)
     emb = rand((B, 6 * cols), 0.0, 0.1, 90 + u, dt)
-    sc, sh, _ = chunk_views(dev(emb, dtype=td), cols)
-    got = _run("mod", dt, dev(x, dtype=td), sc, sh, B)
-    ref = orc.modulate_dt(x, shifted(emb, cols), emb, dt, rows // B)
+    sc, sh, gt = chunk_views(dev(emb, dtype=td), cols)
+    if op == "mod":
+        got = _run("mod", dt, dev(x, dtype=td), sc, sh, B)
+        ref = orc.modulate_dt(x, shifted(emb, cols), emb, dt, rows // B)
+    else:
+        res = rand((rows, cols), 0.0, 1.0, 110 + u, dt)
+        got = _run("gate", dt, dev(x, dtype=td), gt, dev(res, dtype=td), B)
+        ref = orc.gate_residual_dt(x, res, shifted(emb, 2 * cols), dt, rows // B)
     assert same_bits(got, ref, dt), f"{int((got != ref).sum())} elements differ"
 
 
