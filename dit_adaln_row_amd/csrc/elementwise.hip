@@ -51,45 +51,58 @@ constexpr int EW_MAX_WAVES = 4;  // resident wavefronts per SIMD the choice may 
 // OP 0: modulate (x, scale, shift); OP 1: gate add (update, residual, gate)
 template <int OP, int DT, int U>
 __global__ __launch_bounds__(EW_BLOCK) void elementwise_kernel(const ElementwiseArgs a) {
-  const int nvec = a.cols >> 3;
-  const int64_t t = (int64_t)blockIdx.x * EW_BLOCK + threadIdx.x;
-  const int64_t rg = t / nvec;
+  // Index arithmetic in 32 bits (the call's limits: rows < 2^25, cols <=
+  // 16384, under 2^31 threads) and the batch of each row found by stepping
+  // from the first row's: one division per thread instead of a 64-bit
+  // division per row, which had been a third of the instructions.
+  const uint32_t nvec = (uint32_t)a.cols >> 3;
+  const uint32_t t = blockIdx.x * EW_BLOCK + threadIdx.x;
+  const uint32_t rg = t / nvec;
   const int c8 = (int)(t - rg * nvec) * 8;
-  const int64_t r0 = rg * U;
-  if (r0 >= a.rows) return;
-  const int nr = (int)(a.rows - r0 < U ? a.rows - r0 : U);
+  const uint64_t r0w = (uint64_t)rg * U;
+  if (r0w >= (uint64_t)a.rows) return;
+  const uint32_t r0 = (uint32_t)r0w;
+  const int nr = (int)((uint32_t)a.rows - r0 < (uint32_t)U ? (uint32_t)a.rows - r0 : U);
+  const uint32_t rpb = (uint32_t)a.rows_per_batch;
+  const int64_t base = (int64_t)r0 * a.cols + c8;  // element offset of row r0
 
   // the rows first
   uint4 in0[U], in1[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (u >= nr) continue;  // (continue, not break: the loops stay fully unrolled)
-    const int64_t off = (r0 + u) * (int64_t)a.cols + c8;
+    const int64_t off = base + (int64_t)u * a.cols;
     in0[u] = ld16s(a.a + off);
     if constexpr (OP == 1) in1[u] = ld16s(a.b + off);
   }
+
+  // batch b of the current row; rows from `next` on belong to batch b + 1
+  uint32_t b = r0 / rpb;
+  uint32_t next = (b + 1) * rpb;
 
   if constexpr (DT == 1) {
     // fp16: each eager op is one packed fp16 operation on a pair (IEEE
     // nearest-even, subnormals kept): the binary32 operation rounded to fp16
     // gives the same bits, since binary32 holds 2 * 11 + 2 significand bits
-    int64_t cb = -1;
     f16x2 h0[4], h1[4];
+    auto load_mod = [&]() {
+      const int64_t mo = (int64_t)b * a.mod_stride + c8;
+      as_f16x2(ld16(a.m0 + mo), h0);
+      if constexpr (OP == 0) {
+        as_f16x2(ld16(a.m1 + mo), h1);
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h0[i] = one + h0[i];  // s1 = rnd(1 + scale)
+      }
+    };
+    load_mod();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (u >= nr) continue;
-      const int64_t r = r0 + u;
-      const int64_t b = r / a.rows_per_batch;
-      if (b != cb) {  // the first row, and batch boundaries
-        cb = b;
-        const int64_t mo = b * a.mod_stride + c8;
-        as_f16x2(ld16(a.m0 + mo), h0);
-        if constexpr (OP == 0) {
-          as_f16x2(ld16(a.m1 + mo), h1);
-          const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) h0[i] = one + h0[i];  // s1 = rnd(1 + scale)
-        }
+      if (u > 0 && r0 + u >= next) {  // a batch boundary
+        ++b;
+        next += rpb;
+        load_mod();
       }
       f16x2 v[4], o[4];
       as_f16x2(in0[u], v);
@@ -108,28 +121,30 @@ __global__ __launch_bounds__(EW_BLOCK) void elementwise_kernel(const Elementwise
           o[i] = res[i] + w;             // rnd(residual + .)
         }
       }
-      st16s(a.out + r * (int64_t)a.cols + c8, from_f16x2(o));
+      st16s(a.out + base + (int64_t)u * a.cols, from_f16x2(o));
     }
     return;
   }
 
-  int64_t cur_b = -1;
   float m0[8], m1[8];
+  auto load_mod = [&]() {
+    const int64_t mo = (int64_t)b * a.mod_stride + c8;
+    widen8<DT>(ld16(a.m0 + mo), m0);
+    if constexpr (OP == 0) {
+      widen8<DT>(ld16(a.m1 + mo), m1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m0[e] = 1.0f + m0[e];
+      round8<DT>(m0);  // s1 = rnd(1 + scale)
+    }
+  };
+  load_mod();
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (u >= nr) continue;
-    const int64_t r = r0 + u;
-    const int64_t b = r / a.rows_per_batch;
-    if (b != cur_b) {  // the first row, and batch boundaries
-      cur_b = b;
-      const int64_t mo = b * a.mod_stride + c8;
-      widen8<DT>(ld16(a.m0 + mo), m0);
-      if constexpr (OP == 0) {
-        widen8<DT>(ld16(a.m1 + mo), m1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) m0[e] = 1.0f + m0[e];
-        round8<DT>(m0);  // s1 = rnd(1 + scale)
-      }
+    if (u > 0 && r0 + u >= next) {  // a batch boundary
+      ++b;
+      next += rpb;
+      load_mod();
     }
     float v[8], w[8], o[8];
     widen8<DT>(in0[u], v);
@@ -148,7 +163,7 @@ __global__ __launch_bounds__(EW_BLOCK) void elementwise_kernel(const Elementwise
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = res[e] + w[e];
     }
-    st16s(a.out + r * (int64_t)a.cols + c8, narrow8<DT>(o));
+    st16s(a.out + base + (int64_t)u * a.cols, narrow8<DT>(o));
   }
 }
 
