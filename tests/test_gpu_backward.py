@@ -24,11 +24,19 @@ def rand(shape, mu, sigma, seed):
 
 
 def run(x, sc, dout, rpb, eps=1e-6, mod_dev=None):
-    rows = x.shape[0]
-    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
-    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    """The outputs start as NaN, so that a sum the kernels leave unwritten
+    (or a value an earlier call left in a reused buffer) cannot pass."""
+    rows, cols = x.shape
+    nb = rows // rpb
+    nan = float("nan")
+    mean = torch.full((rows,), nan, dtype=torch.float32, device="cuda")
+    rstd = torch.full((rows,), nan, dtype=torch.float32, device="cuda")
+    d_x = torch.full((rows, cols), nan, dtype=torch.bfloat16, device="cuda")
+    d_scale = torch.full((nb, cols), nan, dtype=torch.float32, device="cuda")
+    d_shift = torch.full((nb, cols), nan, dtype=torch.float32, device="cuda")
     scd = dev(sc) if mod_dev is None else mod_dev
-    d_x, d_scale, d_shift = dn.ln_modulate_backward(dev(x), scd, dev(dout), eps,
+    d_x, d_scale, d_shift = dn.ln_modulate_backward(dev(x), scd, dev(dout), eps, d_x=d_x,
+                                                    d_scale=d_scale, d_shift=d_shift,
                                                     mean_out=mean, rstd_out=rstd)
     torch.cuda.synchronize()
     return dict(d_x=host(d_x), d_scale=host(d_scale), d_shift=host(d_shift), mean=host(mean),

@@ -572,8 +572,16 @@ def test_full_workload(gpu, orc, key):
             f32 = l.extra.get("dtype") == "f32"
             rows, cols = x.shape
             mean, rstd = empty_f32(rows), empty_f32(rows)
+            # outputs start as NaN: no value may survive from a reused buffer
+            nan, nb = float("nan"), rows // rpb
+            d_x = torch.full((rows, cols), nan, dtype=torch.float32 if f32 else torch.bfloat16,
+                             device="cuda")
+            d_scale = torch.full((nb, cols), nan, dtype=torch.float32, device="cuda")
+            d_shift = torch.full((nb, cols), nan, dtype=torch.float32, device="cuda")
             d_x, d_scale, d_shift = gpu.ln_modulate_backward(dev(x), dev(sc), dev(dout), l.eps,
-                                                             mean_out=mean, rstd_out=rstd)
+                                                             d_x=d_x, d_scale=d_scale,
+                                                             d_shift=d_shift, mean_out=mean,
+                                                             rstd_out=rstd)
             torch.cuda.synchronize()
             ref = (orc.ln_modulate_backward_f32 if f32 else orc.ln_modulate_backward)(
                 x, sc, dout, l.eps, rows_per_batch=rpb)

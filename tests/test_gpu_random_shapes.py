@@ -159,7 +159,13 @@ def _check_shape(gpu, orc, i, kind, B, S, cols, extra):
         if cols > 4096:
             pytest.skip("the backward serves rows up to 4096 columns")
         dout = rand((rows, cols), 0, 1, 1500 + i)
-        d_x, d_scale, d_shift = gpu.ln_modulate_backward(dev(x), scd, dev(dout), 1e-6,
+        # outputs start as NaN: no value may survive from a reused buffer
+        nan = float("nan")
+        d_x = torch.full((rows, cols), nan, dtype=torch.bfloat16, device="cuda")
+        d_scale = torch.full((B, cols), nan, dtype=torch.float32, device="cuda")
+        d_shift = torch.full((B, cols), nan, dtype=torch.float32, device="cuda")
+        d_x, d_scale, d_shift = gpu.ln_modulate_backward(dev(x), scd, dev(dout), 1e-6, d_x=d_x,
+                                                         d_scale=d_scale, d_shift=d_shift,
                                                          mean_out=mean, rstd_out=rstd)
         torch.cuda.synchronize()
         ref = orc.ln_modulate_backward(x, sc, dout, 1e-6, rows_per_batch=S)
