@@ -32,26 +32,34 @@ constexpr int QK_HEAD = 128;
 constexpr int QK_BLOCK = 256;
 
 // HEAD: the head dim, or 0 for a.head_dim (then VPL vectors per lane, masked)
+//
+// The first waves_q wavefronts take q's rows, the rest k's, so no
+// wavefront's rows straddle the two tensors: each wavefront reads and
+// writes through buffer resources at its first row (wavefront-uniform),
+// with 32-bit per-lane offsets -- no 64-bit address arithmetic per lane --
+// and its stores write through the L2 (about 1% faster).
 template <int L, int G, bool NTL, int HEAD = QK_HEAD, int VPL = HEAD / 8 / L>
-__global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
+__global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a, int64_t waves_q) {
   constexpr int RPW = 64 / L;   // rows per wavefront instruction
   const int head = HEAD > 0 ? HEAD : a.head_dim;
   const int nvec = head >> 3;   // 16-byte vectors per row
   const int lane = threadIdx.x & 63;
   const int sub = lane / L;     // row within a group of RPW
   const int part = lane % L;    // lane within the row
-  const int64_t total = a.rows_q + a.rows_k;
   const int64_t wave = (int64_t)blockIdx.x * (QK_BLOCK / 64) + wave_id();
-  const int64_t base = wave * RPW * G;
-  if (base >= total) return;
-
-  auto src = [&](int64_t r) -> const uint16_t * {
-    return r < a.rows_q ? a.q + r * head : a.k + (r - a.rows_q) * head;
-  };
-  auto dst = [&](int64_t r) -> uint16_t * {
-    return r < a.rows_q ? a.q_out + r * head : a.k_out + (r - a.rows_q) * head;
-  };
+  const bool on_k = wave >= waves_q;
+  const int64_t nrows = on_k ? a.rows_k : a.rows_q;
+  const int64_t base = (on_k ? wave - waves_q : wave) * RPW * G;  // first row, within q or k
+  if (base >= nrows) return;
+  const int64_t gbase = on_k ? a.rows_q + base : base;  // ... counted over q then k
+  const uint16_t *src = (on_k ? a.k : a.q) + base * head;
+  uint16_t *dst = (on_k ? a.k_out : a.q_out) + base * head;
+  const __amdgpu_buffer_rsrc_t in_r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(src), (short)0, -1, 0x00020000);
+  const auto out_r = wt_rsrc(dst);
+  const int last = (int)((nrows - base < RPW * G ? nrows - base : RPW * G) - 1);
   auto ok = [&](int k) { return HEAD > 0 || part + L * k < nvec; };
+  constexpr int kNt = 2;  // cache policy: the streaming hint
 
   // Every load unconditional, at a valid address: a load under a branch was
   // waited for inside it, so a lane's loads went out one latency apart.  A
@@ -61,12 +69,20 @@ __global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
   uint4 xv[G][VPL];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int64_t r = base + RPW * g + sub;
-    const int64_t rc = r < total ? r : total - 1;
+    const int lr = RPW * g + sub;  // row within the wavefront's rows
+    const uint32_t rb = (uint32_t)((lr < last ? lr : last) * head * 2);
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       const uint4 zero = {0, 0, 0, 0};
-      const uint4 v = ld16x<NTL>(src(rc) + (ok(k) ? part + L * k : 0) * 8);
+      const uint32_t vo = rb + (uint32_t)((ok(k) ? part + L * k : 0) * 16);
+      uint4 v;
+      if constexpr (NTL) {
+        const u32x4 q = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      in_r, (int)vo, 0, kNt));
+        v.x = q.x; v.y = q.y; v.z = q.z; v.w = q.w;
+      } else {
+        v = ld16(src + vo / 2);
+      }
       xv[g][k] = ok(k) ? v : zero;
     }
   }
@@ -100,19 +116,11 @@ __global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int k = 0; k < VPL; ++k) launder(xv[g][k]);
-  // A wavefront whose rows all lie in q or all in k (every one but the
-  // wavefront across the boundary, when rows_q is not a multiple of its rows)
-  // writes them through one buffer resource at its first row, written
-  // through the L2 (about 1% faster); the one across the boundary stores
-  // row by row.
-  const bool one_side = base + RPW * G <= a.rows_q || base >= a.rows_q;
-  const auto out_r = wt_rsrc(dst(base));
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int64_t r = base + RPW * g + sub;
-    if (r >= total) continue;
-    uint16_t *d = dst(r);
-    const uint32_t rb = (uint32_t)((r - base) * head * 2);  // the row's byte offset
+    const int lr = RPW * g + sub;
+    if (lr > last) continue;
+    const uint32_t rb = (uint32_t)(lr * head * 2);  // the row's byte offset
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       if (!ok(k)) continue;
@@ -120,24 +128,23 @@ __global__ __launch_bounds__(QK_BLOCK) void qk_kernel(const QkArgs a) {
       unpack8(xv[g][k], v);
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] = rstd_f[g] * (v[e] - mean_f[g]);
-      const int vo = (part + L * k) * 8;
-      if (one_side) st16w(out_r, rb + vo * 2, pack8(y));
-      else st16s(d + vo, pack8(y));
+      st16w(out_r, rb + (uint32_t)((part + L * k) * 16), pack8(y));
     }
     if (part == 0) {
-      if (a.mean_out) a.mean_out[r] = mean_f[g];
-      if (a.rstd_out) a.rstd_out[r] = rstd_f[g];
+      if (a.mean_out) a.mean_out[gbase + lr] = mean_f[g];
+      if (a.rstd_out) a.rstd_out[gbase + lr] = rstd_f[g];
     }
   }
 }
 
 template <int L, int G, bool NTL, int HEAD = QK_HEAD, int VPL = HEAD / 8 / L>
 hipError_t launch_qk_cfg(const QkArgs &a, hipStream_t stream) {
-  const int64_t total = a.rows_q + a.rows_k;
-  const int64_t rows_per_block = (QK_BLOCK / 64) * (64 / L) * G;
-  const int64_t grid = (total + rows_per_block - 1) / rows_per_block;
+  const int64_t rows_per_wave = (64 / L) * G;
+  const int64_t waves_q = (a.rows_q + rows_per_wave - 1) / rows_per_wave;
+  const int64_t waves = waves_q + (a.rows_k + rows_per_wave - 1) / rows_per_wave;
+  const int64_t grid = (waves + QK_BLOCK / 64 - 1) / (QK_BLOCK / 64);
   hipLaunchKernelGGL((qk_kernel<L, G, NTL, HEAD, VPL>), dim3((unsigned)grid), dim3(QK_BLOCK), 0,
-                     stream, a);
+                     stream, a, waves_q);
   return hipGetLastError();
 }
 
