@@ -336,6 +336,10 @@ def _wan_run_check(gpu, orc, what, x, bias, gamma, eps):
     # root and divisions are the oracle's: the statistics match to the bit
     assert exact.all(), f"{what}: rstd differs from the oracle's in {int((~exact).sum())} rows"
     assert np.all(d <= 1), f"{what}: SiLU output beyond 1 ulp"
+    if d.size >= 1 << 20:  # (a share is only meaningful over many elements)
+        # the hardware exp2 / reciprocal are within a few 1e-7: only values
+        # that close to a bf16 halfway point may round the other way
+        assert (d == 0).mean() >= 0.9999, f"{what}: SiLU output exact on {(d == 0).mean():.6f}"
     return ref
 
 
