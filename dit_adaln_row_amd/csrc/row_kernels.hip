@@ -518,7 +518,7 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
 // LDS; the sums are exact, so the statistics carry the same bits either way.
 // Everything else is the wavefront-per-row kernel's MOD_LDS path (rows of
 // NV * 512 columns).
-template <int NVW, int NV, bool RMS, bool GATED, int WPB, bool GFIRST>
+template <int NVW, int NV, bool RMS, bool GATED, int WPB, bool GFIRST, bool FOLD = false>
 __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, float4 *lds_sh,
                                             uint4 *lds_sh16, uint4 *lds_w, float4 *lds_w32,
                                             uint4 *lds_s116,
@@ -727,6 +727,15 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = rstd_f * (v[e] - mean_f);
       }
+      if constexpr (FOLD) {  // the folded affine: one fp32 chain, one rounding
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = y[e] * s1v[e];
+          o[e] = p + shv[e];
+        }
+        st16s(a.out + base + col(k), pack8(o));
+        continue;
+      }
       uint4 yq;  // y as stored bf16
       if constexpr (WY) {
         yq = pack8(y);
@@ -757,7 +766,8 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
   }
 }
 
-template <int NV, bool RMS, bool GATED, int P, int WPB = 4, bool REMFIRST = false>
+template <int NV, bool RMS, bool GATED, int P, int WPB = 4, bool REMFIRST = false,
+          bool FOLD = false>
 __global__ __launch_bounds__(64 * WPB) void row_mixed_kernel(const RowArgs a) {
   constexpr bool F32W = RMS && WPB == 8;
   // gated rows: every gate load ahead of the residual stores, except in the
@@ -782,20 +792,20 @@ __global__ __launch_bounds__(64 * WPB) void row_mixed_kernel(const RowArgs a) {
   if (NV <= 8 && g < a.full_blocks) {
     const int64_t row0 = g * WPB;
     if constexpr (NV <= 8)
-      row_segment<NV, NV, RMS, GATED, WPB, GFIRST>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
+      row_segment<NV, NV, RMS, GATED, WPB, GFIRST, FOLD>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
                                                    lds_s116, red, row0, row0 + w, 0);
   } else if constexpr (P == 2) {  // WPB / 2 rows per workgroup, a half per wavefront
     const int64_t row0 = a.full_blocks * WPB + (g - a.full_blocks) * (WPB / 2);
-    row_segment<NV / 2, NV, RMS, GATED, WPB, GFIRST>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
+    row_segment<NV / 2, NV, RMS, GATED, WPB, GFIRST, FOLD>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
                                                      lds_s116, red, row0, row0 + (w >> 1), w & 1);
   } else if constexpr (P == 4) {  // WPB / 4 rows per workgroup, a quarter per wavefront
     const int64_t row0 = a.full_blocks * WPB + (g - a.full_blocks) * (WPB / 4);
-    row_segment<NV / 4, NV, RMS, GATED, WPB, GFIRST>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
+    row_segment<NV / 4, NV, RMS, GATED, WPB, GFIRST, FOLD>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
                                                      lds_s116, red, row0, row0 + (w >> 2), w & 3);
   } else {  // (8-wavefront workgroups) a row per workgroup, an eighth per wavefront
     static_assert(P == 8 && WPB == 8, "eighths: one row per 8-wavefront workgroup");
     const int64_t row0 = a.full_blocks * WPB + (g - a.full_blocks);
-    row_segment<NV / 8, NV, RMS, GATED, WPB, GFIRST>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
+    row_segment<NV / 8, NV, RMS, GATED, WPB, GFIRST, FOLD>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
                                                      lds_s116, red, row0, row0, w);
   }
 }
@@ -923,12 +933,32 @@ hipError_t launch_wave(const RowArgs &a, bool rms, bool gated, bool fold, hipStr
 }
 
 // The folded form at 1024-4096 columns (multiples of 1024): one wavefront per
-// row, modulation rows read per row.
+// row, modulation rows read per row.  A launch of at most half a round of
+// rows (fewer rows than SIMDs) splits every row over the balanced kernel
+// instead, in quarters (at most a quarter round, 2048 or 4096 columns) or
+// halves, so that it spreads over the SIMDs (512 rows of 3072: 4.75 -> 4.13 us,
+// bitwise the same).
 template <int NV>
-hipError_t launch_folded(const RowArgs &a, hipStream_t stream) {
-  const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
+hipError_t launch_folded(const RowArgs &a0, const DeviceInfo &dev, hipStream_t stream) {
+  const int64_t simds = (int64_t)dev.num_cu * 4;
+  if (2 * a0.rows <= simds) {
+    RowArgs a = a0;
+    a.full_blocks = 0;
+    const dim3 block(256);
+    if constexpr (NV % 4 == 0) {
+      if (4 * a.rows <= simds) {
+        hipLaunchKernelGGL((row_mixed_kernel<NV, false, false, 4, 4, false, true>),
+                           dim3((unsigned)a.rows), block, 0, stream, a);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((row_mixed_kernel<NV, false, false, 2, 4, false, true>),
+                       dim3((unsigned)((a.rows + 1) / 2)), block, 0, stream, a);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((a0.rows + 3) / 4)), block(256);
   hipLaunchKernelGGL((row_wave_kernel<NV, true, false, false, MOD_SERIAL, true>), grid, block, 0,
-                     stream, a);
+                     stream, a0);
   return hipGetLastError();
 }
 
@@ -968,10 +998,10 @@ hipError_t launch_row(const RowArgs &a, bool rms, bool gated, bool fold, const D
   // them per row.  Other widths up to 4096: one wavefront per row.
   if (fold) {
     switch (nvec) {
-      case 128: return launch_folded<2>(a, stream);
-      case 256: return launch_folded<4>(a, stream);
-      case 384: return launch_folded<6>(a, stream);
-      case 512: return launch_folded<8>(a, stream);
+      case 128: return launch_folded<2>(a, dev, stream);
+      case 256: return launch_folded<4>(a, dev, stream);
+      case 384: return launch_folded<6>(a, dev, stream);
+      case 512: return launch_folded<8>(a, dev, stream);
       default: break;
     }
   }
