@@ -665,9 +665,10 @@ def copy_calibration(lib, dev, stream, launches=8):
 def _kernel_label(name):
     """Launch kind of a demangled kernel name."""
     if "ditnorm::row_mixed_kernel<" in name:
-        # row_mixed_kernel<NV, RMS, GATED, FOLD>
+        # row_mixed_kernel<NV, RMS, GATED, P, WPB, REMFIRST, FOLD>
         args = [a.strip() for a in name.split("_kernel<", 1)[1].split(">", 1)[0].split(",")]
-        rms, gated, fold = args[1] == "true", args[2] == "true", args[3] == "true"
+        rms, gated = args[1] == "true", args[2] == "true"
+        fold = len(args) >= 7 and args[6] == "true"
         if fold:
             return "ln_modulate_folded"
         return {(False, False): "ln_modulate", (False, True): "gated_ln_modulate",
