@@ -266,6 +266,10 @@ template <bool B>
 struct BoolC {
   static constexpr bool value = B;
 };
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
 
 // How a row kernel obtains its modulation operands (s1 = bf16(1+scale),
 // shift, the RMS weight; the gate always per vector from the caches).
@@ -518,12 +522,21 @@ __global__ __launch_bounds__(256) void row_wave_kernel(const RowArgs a) {
 // LDS; the sums are exact, so the statistics carry the same bits either way.
 // Everything else is the wavefront-per-row kernel's MOD_LDS path (rows of
 // NV * 512 columns).
-template <int NVW, int NV, bool RMS, bool GATED, int WPB, bool GFIRST, bool FOLD = false>
+template <int NVW, int NV, bool RMS, bool GATED, int WPB, bool GFIRST, bool FOLD = false,
+          int TP = 0>
 __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, float4 *lds_sh,
                                             uint4 *lds_sh16, uint4 *lds_w, float4 *lds_w32,
                                             uint4 *lds_s116,
-                                            double (*red)[2], int64_t row0, int64_t row, int seg) {
+                                            double (*red)[2], int64_t row0, int64_t row, int seg,
+                                            int64_t trow0 = -1) {
   constexpr bool SPLIT = NVW != NV;
+  // TP > 0 (whole rows, plain forms): the workgroup also owns the WPB / TP
+  // remainder rows from trow0 on (none if trow0 is negative), a 1/TP part
+  // per wavefront, loaded ahead of the whole row and finished after it
+  static_assert(TP == 0 || (!SPLIT && !GATED && !FOLD && WPB % TP == 0 && NV % TP == 0),
+                "tail: whole plain rows");
+  constexpr int TPD = TP > 0 ? TP : 1;
+  constexpr int NVT = NV / TPD;
   constexpr int NT = 64 * WPB;
   // RMS with 8-wavefront workgroups: the shift and the weight staged as fp32
   constexpr bool F32W = RMS && WPB == 8;
@@ -539,6 +552,16 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
   const uint4 zero = {0, 0, 0, 0};
   auto vid = [&](int k) { return seg * (NVW * 64) + lane + 64 * k; };
   auto col = [&](int k) { return vid(k) * 8; };
+  const int tpart = w % TPD;                   // this wavefront's part of its tail row
+  const int64_t trow = trow0 + w / TPD;
+  const bool tail = TP > 0 && trow0 >= 0 && trow < a.rows;  // uniform over the part's wavefronts
+  const int64_t tbase = (tail ? trow : (live ? row : row0)) * (int64_t)cols;
+  uint4 tv[NVT];
+  if constexpr (TP > 0) {  // unconditional (a wavefront without a tail reads its own row)
+#pragma unroll
+    for (int k = 0; k < NVT; ++k)
+      tv[k] = ld16s(a.x + tbase + (tpart * (NVT * 64) + lane + 64 * k) * 8);
+  }
 
   // modulation rows of the workgroup's first batch, then this segment
   constexpr int FILL = (NV * 64 + NT - 1) / NT;
@@ -600,8 +623,148 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
       lds_sh[mod_slot(j, 1) / 4] = make_float4(sh[4], sh[5], sh[6], sh[7]);
     }
   }
+  if constexpr (TP > 0) {  // the tail part's moments, exchanged with the staging barrier
+    if (tail) {
+      Moments mt = {0.0, 0.0};
+#pragma unroll
+      for (int k = 0; k < NVT; ++k) {
+        float tf[8];
+        unpack8(tv[k], tf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) accumulate(mt, tf[e]);
+      }
+      const double t2 = sum64(mt.s2), t1 = RMS ? 0.0 : sum64(mt.s1);
+      if (lane == 0) {
+        red[w][0] = t1;
+        red[w][1] = t2;
+      }
+    }
+  }
+  // normalise, modulate, store (the run-time choices taken outside the loop)
+  auto normalise = [&](auto with_y, auto from_lds, auto nvc, const float (*xs)[8], int sg,
+                       int64_t bs, float mean_v, float rstd_v, int64_t mov) {
+    constexpr bool WY = decltype(with_y)::value, FROM_LDS = decltype(from_lds)::value;
+    constexpr int NC = decltype(nvc)::value;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      float s1v[8], shv[8], y[8], o[8];
+      const float *v = xs[k];
+      const int j = sg * (NC * 64) + lane + 64 * k;
+      const int64_t cj = (int64_t)j * 8;
+      if constexpr (FROM_LDS && B16) {
+        unpack8(lds_s116[j], s1v);
+        unpack8(lds_sh16[j], shv);
+      } else if constexpr (FROM_LDS) {
+        const float4 a0 = lds_s1[mod_slot(j, 0) / 4], a1 = lds_s1[mod_slot(j, 1) / 4];
+        s1v[0] = a0.x; s1v[1] = a0.y; s1v[2] = a0.z; s1v[3] = a0.w;
+        s1v[4] = a1.x; s1v[5] = a1.y; s1v[6] = a1.z; s1v[7] = a1.w;
+        if constexpr (RMS && !F32W) {
+          unpack8(lds_sh16[j], shv);
+        } else {
+          const float4 c0 = lds_sh[mod_slot(j, 0) / 4], c1 = lds_sh[mod_slot(j, 1) / 4];
+          shv[0] = c0.x; shv[1] = c0.y; shv[2] = c0.z; shv[3] = c0.w;
+          shv[4] = c1.x; shv[5] = c1.y; shv[6] = c1.z; shv[7] = c1.w;
+        }
+      } else {
+        unpack8(ld16(a.scale + mov + cj), s1v);
+        unpack8(ld16(a.shift + mov + cj), shv);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          s1v[e] = 1.0f + s1v[e];
+          s1v[e + 1] = 1.0f + s1v[e + 1];
+          round2(s1v[e], s1v[e + 1]);
+        }
+      }
+      if constexpr (RMS) {
+        float wt[8];
+        if constexpr (F32W) {
+          const float4 w0 = lds_w32[mod_slot(j, 0) / 4], w1 = lds_w32[mod_slot(j, 1) / 4];
+          wt[0] = w0.x; wt[1] = w0.y; wt[2] = w0.z; wt[3] = w0.w;
+          wt[4] = w1.x; wt[5] = w1.y; wt[6] = w1.z; wt[7] = w1.w;
+        } else {
+          unpack8(lds_w[j], wt);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (v[e] * rstd_v) * wt[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = rstd_v * (v[e] - mean_v);
+      }
+      if constexpr (FOLD) {  // the folded affine: one fp32 chain, one rounding
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = y[e] * s1v[e];
+          o[e] = p + shv[e];
+        }
+        st16s(a.out + bs + cj, pack8(o));
+        continue;
+      }
+      uint4 yq;  // y as stored bf16
+      if constexpr (WY) {
+        yq = pack8(y);
+        unpack8(yq, y);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = round1(y[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float q0 = y[e] * s1v[e], q1 = y[e + 1] * s1v[e + 1];
+        round2(q0, q1);
+        o[e] = q0 + shv[e];
+        o[e + 1] = q1 + shv[e + 1];
+      }
+      st16s(a.out + bs + cj, pack8(o));
+      if constexpr (WY) st16(a.y_out + bs + cj, yq);
+    }
+  };
+  using T = BoolC<true>;
+  using F = BoolC<false>;
   if constexpr (!SPLIT) {
     lds_barrier();
+    if constexpr (TP > 0) {  // the tail part, finished while the whole row's loads are in flight
+      if (tail) {
+        const int pw = w - tpart;
+        double t1, t2;
+        if constexpr (TP == 2) {
+          t1 = red[pw][0] + red[pw + 1][0];
+          t2 = red[pw][1] + red[pw + 1][1];
+        } else if constexpr (TP == 4) {
+          t1 = (red[pw][0] + red[pw + 1][0]) + (red[pw + 2][0] + red[pw + 3][0]);
+          t2 = (red[pw][1] + red[pw + 1][1]) + (red[pw + 2][1] + red[pw + 3][1]);
+        } else {
+          static_assert(TP == 8, "tail parts: 2, 4 or 8");
+          t1 = ((red[0][0] + red[1][0]) + (red[2][0] + red[3][0])) +
+               ((red[4][0] + red[5][0]) + (red[6][0] + red[7][0]));
+          t2 = ((red[0][1] + red[1][1]) + (red[2][1] + red[3][1])) +
+               ((red[4][1] + red[5][1]) + (red[6][1] + red[7][1]));
+        }
+        float tmean = 0.0f, trstd;
+        if constexpr (RMS) {
+          trstd = rstd_from(t2 / (double)cols + (double)a.eps);
+        } else {
+          const double tm = t1 / (double)cols;
+          tmean = (float)tm;
+          trstd = rstd_from(clamp_var(__builtin_fma(-t1, tm, t2) / (double)cols) + (double)a.eps);
+        }
+        if (lane == 0 && tpart == 0) {
+          if (a.mean_out) a.mean_out[trow] = tmean;
+          if (a.rstd_out) a.rstd_out[trow] = trstd;
+        }
+        float tf[NVT][8];
+#pragma unroll
+        for (int k = 0; k < NVT; ++k) unpack8(tv[k], tf[k]);
+        const int64_t tmo = (trow / a.rows_per_batch) * a.mod_stride;
+        const IntC<NVT> nt;
+        if (a.y_out) {
+          if (tmo == b0 * a.mod_stride) normalise(T{}, T{}, nt, tf, tpart, tbase, tmean, trstd, tmo);
+          else normalise(T{}, F{}, nt, tf, tpart, tbase, tmean, trstd, tmo);
+        } else {
+          if (tmo == b0 * a.mod_stride) normalise(F{}, T{}, nt, tf, tpart, tbase, tmean, trstd, tmo);
+          else normalise(F{}, F{}, nt, tf, tpart, tbase, tmean, trstd, tmo);
+        }
+      }
+    }
     if (!live) return;  // whole wavefront; no barrier follows
   }
 
@@ -680,94 +843,18 @@ __device__ __forceinline__ void row_segment(const RowArgs &a, float4 *lds_s1, fl
   }
   const bool mod_in_lds = mo == b0 * a.mod_stride;
 
-  // normalise, modulate, store (the run-time choices taken outside the loop)
-  auto normalise = [&](auto with_y, auto from_lds) {
-    constexpr bool WY = decltype(with_y)::value, FROM_LDS = decltype(from_lds)::value;
-#pragma unroll
-    for (int k = 0; k < NVW; ++k) {
-      float s1v[8], shv[8], y[8], o[8];
-      const float *v = xf[k];
-      const int j = vid(k);
-      if constexpr (FROM_LDS && B16) {
-        unpack8(lds_s116[j], s1v);
-        unpack8(lds_sh16[j], shv);
-      } else if constexpr (FROM_LDS) {
-        const float4 a0 = lds_s1[mod_slot(j, 0) / 4], a1 = lds_s1[mod_slot(j, 1) / 4];
-        s1v[0] = a0.x; s1v[1] = a0.y; s1v[2] = a0.z; s1v[3] = a0.w;
-        s1v[4] = a1.x; s1v[5] = a1.y; s1v[6] = a1.z; s1v[7] = a1.w;
-        if constexpr (RMS && !F32W) {
-          unpack8(lds_sh16[j], shv);
-        } else {
-          const float4 c0 = lds_sh[mod_slot(j, 0) / 4], c1 = lds_sh[mod_slot(j, 1) / 4];
-          shv[0] = c0.x; shv[1] = c0.y; shv[2] = c0.z; shv[3] = c0.w;
-          shv[4] = c1.x; shv[5] = c1.y; shv[6] = c1.z; shv[7] = c1.w;
-        }
-      } else {
-        unpack8(ld16(a.scale + mo + col(k)), s1v);
-        unpack8(ld16(a.shift + mo + col(k)), shv);
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          s1v[e] = 1.0f + s1v[e];
-          s1v[e + 1] = 1.0f + s1v[e + 1];
-          round2(s1v[e], s1v[e + 1]);
-        }
-      }
-      if constexpr (RMS) {
-        float wt[8];
-        if constexpr (F32W) {
-          const float4 w0 = lds_w32[mod_slot(j, 0) / 4], w1 = lds_w32[mod_slot(j, 1) / 4];
-          wt[0] = w0.x; wt[1] = w0.y; wt[2] = w0.z; wt[3] = w0.w;
-          wt[4] = w1.x; wt[5] = w1.y; wt[6] = w1.z; wt[7] = w1.w;
-        } else {
-          unpack8(lds_w[j], wt);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = (v[e] * rstd_f) * wt[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = rstd_f * (v[e] - mean_f);
-      }
-      if constexpr (FOLD) {  // the folded affine: one fp32 chain, one rounding
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = y[e] * s1v[e];
-          o[e] = p + shv[e];
-        }
-        st16s(a.out + base + col(k), pack8(o));
-        continue;
-      }
-      uint4 yq;  // y as stored bf16
-      if constexpr (WY) {
-        yq = pack8(y);
-        unpack8(yq, y);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = round1(y[e]);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        float q0 = y[e] * s1v[e], q1 = y[e + 1] * s1v[e + 1];
-        round2(q0, q1);
-        o[e] = q0 + shv[e];
-        o[e + 1] = q1 + shv[e + 1];
-      }
-      st16s(a.out + base + col(k), pack8(o));
-      if constexpr (WY) st16(a.y_out + base + col(k), yq);
-    }
-  };
-  using T = BoolC<true>;
-  using F = BoolC<false>;
+  const IntC<NVW> nw;
   if (a.y_out) {
-    if (mod_in_lds) normalise(T{}, T{});
-    else normalise(T{}, F{});
+    if (mod_in_lds) normalise(T{}, T{}, nw, xf, seg, base, mean_f, rstd_f, mo);
+    else normalise(T{}, F{}, nw, xf, seg, base, mean_f, rstd_f, mo);
   } else {
-    if (mod_in_lds) normalise(F{}, T{});
-    else normalise(F{}, F{});
+    if (mod_in_lds) normalise(F{}, T{}, nw, xf, seg, base, mean_f, rstd_f, mo);
+    else normalise(F{}, F{}, nw, xf, seg, base, mean_f, rstd_f, mo);
   }
 }
 
 template <int NV, bool RMS, bool GATED, int P, int WPB = 4, bool REMFIRST = false,
-          bool FOLD = false>
+          bool FOLD = false, bool TAIL = false>
 __global__ __launch_bounds__(64 * WPB) void row_mixed_kernel(const RowArgs a) {
   constexpr bool F32W = RMS && WPB == 8;
   // gated rows: every gate load ahead of the residual stores, except in the
@@ -789,7 +876,13 @@ __global__ __launch_bounds__(64 * WPB) void row_mixed_kernel(const RowArgs a) {
   }
   // (rows over 4096 columns come only in halves: no whole-row path to hold
   // their registers)
-  if (NV <= 8 && g < a.full_blocks) {
+  if constexpr (TAIL) {  // whole rows; the first workgroups take WPB / P remainder rows each
+    const int64_t row0 = g * WPB;
+    const int64_t tr0 = a.full_blocks * WPB + g * (WPB / P);
+    row_segment<NV, NV, RMS, GATED, WPB, GFIRST, FOLD, P>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
+                                                     lds_s116, red, row0, row0 + w, 0,
+                                                     tr0 < a.rows ? tr0 : -1);
+  } else if (NV <= 8 && g < a.full_blocks) {
     const int64_t row0 = g * WPB;
     if constexpr (NV <= 8)
       row_segment<NV, NV, RMS, GATED, WPB, GFIRST, FOLD>(a, lds_s1, lds_sh, lds_sh16, lds_w, lds_w32,
@@ -812,9 +905,11 @@ __global__ __launch_bounds__(64 * WPB) void row_mixed_kernel(const RowArgs a) {
 
 // Whole rounds of rows (one row per wavefront, one wavefront per SIMD per
 // round) and the remainder in eighths when it is at most an eighth of a round
-// (the 8-wavefront plain RMS form: a row per workgroup; ERNIE's 120 extra rows
-// of 4096 14.27 -> 14.04 us, 1-3% at other such remainders, bitwise
-// unchanged), in quarters when it is at most a quarter round (rows of 2048 or
+// (the 8-wavefront plain RMS form: a row per workgroup, or with exactly four
+// whole rounds a remainder row per whole-row workgroup, see below; ERNIE's
+// 120 extra rows of 4096 14.27 -> 14.04 us in their own workgroups, 1-3% at
+// other such remainders, bitwise unchanged), in quarters when it is at most
+// a quarter round (rows of 2048 or
 // 4096 columns), in halves when it is at most half a round;
 // else every row whole.  A launch of fewer rows than that (no whole round)
 // splits every row the same way, so that it spreads over the SIMDs instead
@@ -830,10 +925,21 @@ __global__ __launch_bounds__(64 * WPB) void row_mixed_kernel(const RowArgs a) {
 // tail: up to 5% slower) and at other widths (room for the remainder beside
 // the whole rows) the remainder stays last.
 template <int NV, int WPB, bool R, bool G>
-static void launch_mixed_kind(const RowArgs &a, int P, bool remfirst, dim3 grid,
+static void launch_mixed_kind(const RowArgs &a, int P, bool remfirst, bool tail, dim3 grid,
                               hipStream_t stream) {
   constexpr int P4 = NV % 4 == 0 ? 4 : 2;
   const dim3 block(64 * WPB);
+  if constexpr (WPB == 8 && NV % 8 == 0 && !G) {
+    if (tail) {  // (the grid holds the whole-row workgroups only)
+      if (P == 8)
+        hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, 8, 8, false, false, true>), grid, block, 0,
+                           stream, a);
+      else
+        hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, 4, 8, false, false, true>), grid, block, 0,
+                           stream, a);
+      return;
+    }
+  }
   if constexpr (NV == 8 && WPB == 4 && G) {
     if (P == 4 && remfirst) {
       hipLaunchKernelGGL((row_mixed_kernel<NV, R, G, 4, 4, true>), grid, block, 0, stream, a);
@@ -887,15 +993,30 @@ static hipError_t launch_mixed_w(const RowArgs &a0, bool rms, bool gated, const 
     a.full_blocks = (a.rows + WPB - 1) / WPB;
     blocks = a.full_blocks;
   }
-  const dim3 grid((unsigned)blocks), block(64 * WPB);
   const bool remfirst = gated && P == 4 && whole > 0 && rem >= 64;
+  // The plain RMS form in 8-wavefront workgroups with exactly four whole
+  // rounds -- every SIMD's four resident wavefronts -- and a remainder of at
+  // most a quarter round: the remainder rows go to the first whole-row
+  // workgroups (WPB / P rows each, a part per wavefront, loaded with the
+  // whole row), not to workgroups of their own.  Those had to wait for whole
+  // rows to finish, and each staged the 48 KB of modulation rows for a single
+  // row: 4100 rows of 4096 13.45 -> 12.61 us, 4160 13.74 -> 12.65, 4216
+  // (eighths) 14.01 -> 12.62, 4225 14.37 -> 13.76, 4350 (quarters) 14.85 ->
+  // 13.98, bitwise the same.  Halves (4500: 15.13 -> 16.33 us), more whole
+  // rounds (5220, 7288, 8292 rows: 2-4% slower) and the 4-wavefront forms
+  // (FLUX LN 11.0 -> 11.9 us, where the remainder's workgroups fit beside the
+  // whole rows) keep the remainder's own workgroups.
+  const bool tail = WPB == 8 && !gated && !split && whole == 4 * simds && rem > 0 &&
+                    4 * rem <= simds;
+  if (tail) blocks = a.full_blocks;
+  const dim3 grid((unsigned)blocks), block(64 * WPB);
   if constexpr (WPB == 8) {  // the plain RMS form only
-    launch_mixed_kind<NV, 8, true, false>(a, P, false, grid, stream);
+    launch_mixed_kind<NV, 8, true, false>(a, P, false, tail, grid, stream);
   } else {
-    if (!rms && !gated) launch_mixed_kind<NV, 4, false, false>(a, P, remfirst, grid, stream);
-    else if (!rms && gated) launch_mixed_kind<NV, 4, false, true>(a, P, remfirst, grid, stream);
-    else if (rms && !gated) launch_mixed_kind<NV, 4, true, false>(a, P, remfirst, grid, stream);
-    else launch_mixed_kind<NV, 4, true, true>(a, P, remfirst, grid, stream);
+    if (!rms && !gated) launch_mixed_kind<NV, 4, false, false>(a, P, remfirst, tail, grid, stream);
+    else if (!rms && gated) launch_mixed_kind<NV, 4, false, true>(a, P, remfirst, false, grid, stream);
+    else if (rms && !gated) launch_mixed_kind<NV, 4, true, false>(a, P, remfirst, tail, grid, stream);
+    else launch_mixed_kind<NV, 4, true, true>(a, P, remfirst, false, grid, stream);
   }
   return hipGetLastError();
 }
