@@ -892,9 +892,13 @@ SPLIT_CASES = [(3072, 4096 + 512, 4096 + 512), (3072, 1024 + 1, 1025), (4096, 20
                # the plain RMS form in 8-wavefront workgroups (at least four whole
                # rounds): eighths (a row per workgroup) up to an eighth of a round,
                # quarters past it, halves, every row whole with a partly live last
-               # workgroup, and only whole rounds
+               # workgroup, and only whole rounds; with exactly four whole rounds
+               # the eighths and quarters ride in the whole-row workgroups (two
+               # quarter rows per workgroup, batch boundaries among them), with
+               # five they keep workgroups of their own
                (4096, 8192 + 100, 12), (4096, 4096 + 128, 8), (4096, 4096 + 129, 13),
-               (4096, 4096 + 300, 7), (4096, 4096 + 700, 11), (4096, 4096, 64)]
+               (4096, 4096 + 300, 7), (4096, 4096 + 700, 11), (4096, 4096, 64),
+               (4096, 4096 + 250, 41), (4096, 5120 + 100, 10)]
 
 
 @pytest.mark.parametrize("cols,rows,rpb", SPLIT_CASES)
